@@ -1,0 +1,20 @@
+"""CPU oracle for Top-theta attention -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, float64 NumPy code that states what the hot path computes, step by
+step, in the notation of "Top-Theta Attention: Sparsifying Transformers by
+Compensated Thresholding" (arXiv 2502.08363).  Only the test-suite, the smoke
+check and the benchmark's CPU-baseline leg may import it.  The HIP library never
+calls into it and shares no code, tables or helpers with it.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against closed forms,
+library routines it does not itself call, brute force on tiny inputs and
+invariants of the method.  One reading is not pinned by anything the pages fix:
+the causal prefix mean used for VMC in prefill (the paper's Eq. 5 averages all n
+rows in non-causal notation) -- parity unpinned for that choice of mu; every
+other step is pinned.
+"""
+from .topth import (  # noqa: F401
+    scores, post_softmax, kth_largest, theta_row, row_weights, topth_row,
+    prefix_mean, prefill, decode, Calibrator, calibration_samples,
+    PrefillResult, DecodeResult, RowResult,
+)
