@@ -1,0 +1,13 @@
+"""Top-theta attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libtopth.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/topth.h``); this package only loads it and marshals torch
+tensors into its calls.  Build the library with
+``python -m calibrated_threshold_pruning_amd.build``.
+"""
+from ._lib import (  # noqa: F401
+    TOPTH_F32, TOPTH_BF16, TOPTH_VMC, TOPTH_SDC_NONE, TOPTH_OP_CALIBRATE, TOPTH_OP_PREFILL,
+    TOPTH_OP_DECODE, TOPTH_MAX_NK, EXPORTS, LIB_PATH, TopthError, load_library,
+    topth_strerror, topth_workspace_size, topth_workspace_init, workspace, topth_calibrate,
+    topth_calibrate_finalize, topth_prefill, topth_decode, topth_vmean,
+)

@@ -1,0 +1,210 @@
+"""ctypes binding of libtopth (argument marshalling only).
+
+Every function has the name of the C entry point it calls and takes torch
+tensors for device buffers: it checks dtype, shape, contiguity and device,
+passes ``data_ptr()`` and the current HIP stream of torch, and raises
+``TopthError`` when the library returns a negative status.  All computation
+happens in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtopth.so")
+
+TOPTH_F32, TOPTH_BF16 = 0, 1
+TOPTH_VMC, TOPTH_SDC_NONE = 0x1, 0x2
+TOPTH_OP_CALIBRATE, TOPTH_OP_PREFILL, TOPTH_OP_DECODE = 0, 1, 2
+TOPTH_MAX_NK = 8
+
+EXPORTS = ("topth_strerror", "topth_workspace_size", "topth_workspace_init", "topth_calibrate",
+           "topth_calibrate_finalize", "topth_prefill", "topth_decode", "topth_vmean")
+
+
+class TopthError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libtopth.so; raise if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m calibrated_threshold_pruning_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz, u = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint
+    lib.topth_strerror.restype = ctypes.c_char_p
+    lib.topth_strerror.argtypes = [i]
+    lib.topth_workspace_size.restype = sz
+    lib.topth_workspace_size.argtypes = [i] * 8
+    lib.topth_workspace_init.restype = i
+    lib.topth_workspace_init.argtypes = [vp, sz, vp]
+    lib.topth_calibrate.restype = i
+    lib.topth_calibrate.argtypes = [vp, vp, i, i, i, i, i, i, i, f, i, vp, i, vp, vp, vp, i, vp, sz, vp]
+    lib.topth_calibrate_finalize.restype = i
+    lib.topth_calibrate_finalize.argtypes = [vp, vp, vp, vp, i, i, i, f, vp, vp]
+    lib.topth_prefill.restype = i
+    lib.topth_prefill.argtypes = [vp, vp, vp, i, i, i, i, i, i, f, vp, i, u, vp, vp, vp, vp, vp, sz, vp]
+    lib.topth_decode.restype = i
+    lib.topth_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, vp, u, vp, vp, vp, vp,
+                                 vp, vp, sz, vp]
+    lib.topth_vmean.restype = i
+    lib.topth_vmean.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise TopthError(fn, status, load_library().topth_strerror(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TOPTH_F32
+    if t.dtype == torch.bfloat16:
+        return TOPTH_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name, dtype=None, shape=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def topth_strerror(status: int) -> str:
+    return load_library().topth_strerror(status).decode()
+
+
+def topth_workspace_size(op: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, d: int,
+                         n_k: int = 1) -> int:
+    return int(load_library().topth_workspace_size(op, B, Hq, Hkv, Lq, Lk, d, n_k))
+
+
+def topth_workspace_init(ws: torch.Tensor, stream=None):
+    _dev(ws, "ws", torch.uint8)
+    _check("topth_workspace_init", load_library().topth_workspace_init(
+        ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def workspace(op: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, d: int, n_k: int = 1,
+              device="cuda") -> torch.Tensor:
+    """Allocate a zero-initialised workspace tensor of the size the library asks for."""
+    n = topth_workspace_size(op, B, Hq, Hkv, Lq, Lk, d, n_k)
+    if n == 0:
+        raise ValueError("no workspace size for these arguments")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    topth_workspace_init(ws)
+    return ws
+
+
+def topth_calibrate(q, k, ks, sum_, sumsq, count, ws, *, scale: float, q_pos0: int = 0,
+                    stream=None):
+    """Accumulate Algorithm-1 samples of S sequences. q [S,Hq,Lq,d], k [S,Hkv,Lk,d];
+    sum_/sumsq float64 and count int32 of shape [n_k,Hq,n_rows]."""
+    S, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    _dev(q, "q"); _dev(k, "k", q.dtype, (S, Hkv, Lk, d))
+    n_k = len(ks)
+    n_rows = sum_.shape[-1]
+    _dev(sum_, "sum", torch.float64, (n_k, Hq, n_rows))
+    _dev(sumsq, "sumsq", torch.float64, (n_k, Hq, n_rows))
+    _dev(count, "count", torch.int32, (n_k, Hq, n_rows))
+    _dev(ws, "ws", torch.uint8)
+    karr = (ctypes.c_int * max(n_k, 1))(*[int(x) for x in ks])
+    _check("topth_calibrate", load_library().topth_calibrate(
+        q.data_ptr(), k.data_ptr(), S, Hq, Hkv, Lq, Lk, d, dt, float(scale), int(q_pos0),
+        ctypes.cast(karr, ctypes.c_void_p), n_k, sum_.data_ptr(), sumsq.data_ptr(),
+        count.data_ptr(), n_rows, ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def topth_calibrate_finalize(sum_, sumsq, count, ks, theta, *, alpha: float = 0.0, stream=None):
+    n_k, Hq, n_rows = sum_.shape
+    _dev(sum_, "sum", torch.float64); _dev(sumsq, "sumsq", torch.float64, sum_.shape)
+    _dev(count, "count", torch.int32, sum_.shape); _dev(theta, "theta", torch.float32, sum_.shape)
+    karr = (ctypes.c_int * max(len(ks), 1))(*[int(x) for x in ks])
+    _check("topth_calibrate_finalize", load_library().topth_calibrate_finalize(
+        sum_.data_ptr(), sumsq.data_ptr(), count.data_ptr(), ctypes.cast(karr, ctypes.c_void_p),
+        len(ks), Hq, n_rows, float(alpha), theta.data_ptr(), _stream(stream)))
+
+
+def topth_prefill(q, k, v, theta, out, *, scale: float, flags: int, kept_count=None, beta=None,
+                  kept_mask=None, ws=None, stream=None):
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    dt = _dtype_code(q)
+    _dev(q, "q"); _dev(k, "k", q.dtype, (B, Hkv, L, d)); _dev(v, "v", q.dtype, (B, Hkv, L, d))
+    _dev(theta, "theta", torch.float32)
+    if theta.dim() != 2 or theta.shape[0] != Hq:
+        raise ValueError("theta must be [Hq, n_rows]")
+    _dev(out, "out", q.dtype, (B, Hq, L, d))
+    kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq, L), optional=True)
+    bt = _dev(beta, "beta", torch.float32, (B, Hq, L), optional=True)
+    km = _dev(kept_mask, "kept_mask", torch.uint8, (B, Hq, L, L), optional=True)
+    wp = _dev(ws, "ws", torch.uint8, optional=True)
+    _check("topth_prefill", load_library().topth_prefill(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, d, dt, float(scale),
+        theta.data_ptr(), theta.shape[1], int(flags), out.data_ptr(), kc, bt, km, wp,
+        0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def topth_decode(q, k_cache, v_cache, seq_lens, theta, out, ws, *, scale: float, flags: int,
+                 v_mean=None, kept_count=None, beta=None, vrows_read=None, kept_mask=None,
+                 stream=None):
+    B, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    dt = _dtype_code(q)
+    _dev(q, "q"); _dev(k_cache, "k_cache", q.dtype, (B, Hkv, Lmax, d))
+    _dev(v_cache, "v_cache", q.dtype, (B, Hkv, Lmax, d))
+    _dev(seq_lens, "seq_lens", torch.int32, (B,))
+    _dev(theta, "theta", torch.float32)
+    if theta.dim() != 2 or theta.shape[0] != Hq:
+        raise ValueError("theta must be [Hq, n_rows]")
+    _dev(out, "out", q.dtype, (B, Hq, d))
+    vm = _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d), optional=True)
+    kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq), optional=True)
+    bt = _dev(beta, "beta", torch.float32, (B, Hq), optional=True)
+    vr = _dev(vrows_read, "vrows_read", torch.int32, (B, Hkv), optional=True)
+    km = _dev(kept_mask, "kept_mask", torch.uint8, (B, Hq, Lmax), optional=True)
+    _dev(ws, "ws", torch.uint8)
+    _check("topth_decode", load_library().topth_decode(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv,
+        Lmax, d, dt, float(scale), theta.data_ptr(), theta.shape[1], vm, int(flags),
+        out.data_ptr(), kc, bt, vr, km, ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def topth_vmean(v, seq_lens, v_mean, stream=None):
+    B, Hkv, Lmax, d = v.shape
+    dt = _dtype_code(v)
+    _dev(v, "v"); _dev(seq_lens, "seq_lens", torch.int32, (B,))
+    _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d))
+    _check("topth_vmean", load_library().topth_vmean(
+        v.data_ptr(), seq_lens.data_ptr(), B, Hkv, Lmax, d, dt, v_mean.data_ptr(), _stream(stream)))

@@ -1,0 +1,184 @@
+// C ABI of libtopth: argument validation, workspace sizing and dispatch.
+// Every argument error is reported before anything is enqueued on the stream;
+// no C++ exception leaves this file.
+#include "topth.h"
+#include "topth_internal.h"
+
+#include <math.h>
+#include <limits.h>
+
+namespace topth {
+// defined in the kernel sources
+bool decode_bf16_supported(int d, int G);
+int launch_decode_bf16(const DecodeParams& p, hipStream_t s);
+int launch_decode_rowwise(const DecodeParams& p, uint32_t* masks_ws, hipStream_t s);
+size_t decode_rowwise_ws_bytes(int B, int Hq, int Lmax);
+int rowwise_max_keys();
+int launch_prefill_rowwise(const PrefillParams& p, float* mu_ws, hipStream_t s);
+int launch_calibrate_rowwise(const CalibParams& p, float* samples_ws, hipStream_t s);
+}  // namespace topth
+
+using namespace topth;
+
+namespace {
+
+bool bad_dims(int B, int Hq, int Hkv, int L, int d) {
+    return B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || (Hq % Hkv) != 0 || (d != 64 && d != 128);
+}
+
+bool bad_dtype(int dtype) { return dtype != TOPTH_F32 && dtype != TOPTH_BF16; }
+
+// elements of a [a][b][c][d] tensor fit comfortably in size_t and in the
+// 32-bit row indices the kernels use for rows
+bool too_big(long long rows, long long cols) {
+    return rows <= 0 || cols <= 0 || rows > (long long)INT_MAX || rows * cols > (1LL << 40);
+}
+
+int map_hip(int e) { return e == 0 ? TOPTH_OK : TOPTH_EHIP; }
+
+size_t prefill_ws(int B, int Hq, int Hkv, int L, int d) {
+    (void)Hq;
+    return (size_t)B * Hkv * L * d * sizeof(float) + 256;
+}
+
+size_t calib_ws(int S, int Hq, int Lq, int n_k) {
+    return (size_t)S * n_k * Hq * Lq * sizeof(float) + 256;
+}
+
+size_t decode_ws(int B, int Hq, int Hkv, int Lmax, int d) {
+    size_t a = decode_ws_bytes(B, Hq, Hkv, Lmax, d);
+    size_t b = kWsHeaderBytes + decode_rowwise_ws_bytes(B, Hq, Lmax) + 256;
+    return a > b ? a : b;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* topth_strerror(int status) {
+    switch (status) {
+        case TOPTH_OK: return "success";
+        case TOPTH_EINVAL: return "invalid argument";
+        case TOPTH_EUNSUPPORTED: return "unsupported shape or type";
+        case TOPTH_EWORKSPACE: return "workspace missing or too small";
+        case TOPTH_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t topth_workspace_size(int op, int B, int Hq, int Hkv, int Lq, int Lk, int d, int n_k) {
+    switch (op) {
+        case TOPTH_OP_CALIBRATE:
+            if (bad_dims(B, Hq, Hkv, Lq, d) || Lk <= 0 || n_k < 1 || n_k > TOPTH_MAX_NK) return 0;
+            return calib_ws(B, Hq, Lq, n_k);
+        case TOPTH_OP_PREFILL:
+            if (bad_dims(B, Hq, Hkv, Lq, d)) return 0;
+            return prefill_ws(B, Hq, Hkv, Lq, d);
+        case TOPTH_OP_DECODE:
+            if (bad_dims(B, Hq, Hkv, Lk, d)) return 0;
+            return decode_ws(B, Hq, Hkv, Lk, d);
+        default:
+            return 0;
+    }
+}
+
+int topth_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws || ws_bytes == 0) return TOPTH_EINVAL;
+    return map_hip(launch_fill_zero(ws, ws_bytes, (hipStream_t)stream));
+}
+
+int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq, int Lk,
+                    int d, int dtype, float scale, int q_pos0, const int* ks, int n_k,
+                    double* sum, double* sumsq, int* count, int n_rows,
+                    void* ws, size_t ws_bytes, void* stream) {
+    if (!q || !k || !ks || !sum || !sumsq || !count) return TOPTH_EINVAL;
+    if (bad_dims(S, Hq, Hkv, Lq, d) || bad_dtype(dtype) || Lk <= 0 || n_rows <= 0) return TOPTH_EINVAL;
+    if (!isfinite(scale) || q_pos0 < 0 || q_pos0 + Lq > Lk) return TOPTH_EINVAL;
+    if (n_k < 1 || n_k > TOPTH_MAX_NK) return TOPTH_EINVAL;
+    for (int t = 0; t < n_k; ++t)
+        if (ks[t] < 1) return TOPTH_EINVAL;
+    if (too_big((long long)S * Hq * Lq, d) || too_big((long long)S * Hkv * Lk, d)) return TOPTH_EUNSUPPORTED;
+    if (Lk > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
+    if (!ws) return TOPTH_EWORKSPACE;
+    const size_t need = calib_ws(S, Hq, Lq, n_k);
+    if (ws_bytes < need) return TOPTH_EWORKSPACE;
+    CalibParams p = {};
+    p.q = q; p.k = k; p.S = S; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk; p.d = d;
+    p.dtype = dtype; p.scale = scale; p.q_pos0 = q_pos0;
+    for (int t = 0; t < n_k; ++t) p.ks[t] = ks[t];
+    p.n_k = n_k; p.sum = sum; p.sumsq = sumsq; p.count = count; p.n_rows = n_rows;
+    p.ws = ws; p.ws_bytes = ws_bytes;
+    return map_hip(launch_calibrate_rowwise(p, (float*)ws, (hipStream_t)stream));
+}
+
+int topth_calibrate_finalize(const double* sum, const double* sumsq, const int* count,
+                             const int* ks, int n_k, int Hq, int n_rows, float alpha,
+                             float* theta, void* stream) {
+    if (!sum || !sumsq || !count || !ks || !theta) return TOPTH_EINVAL;
+    if (n_k < 1 || n_k > TOPTH_MAX_NK || Hq <= 0 || n_rows <= 0 || !isfinite(alpha)) return TOPTH_EINVAL;
+    if ((float)n_rows > 16777216.0f) return TOPTH_EUNSUPPORTED;
+    for (int t = 0; t < n_k; ++t)
+        if (ks[t] < 1) return TOPTH_EINVAL;
+    return map_hip(launch_finalize(sum, sumsq, count, ks, n_k, Hq, n_rows, alpha, theta,
+                                   (hipStream_t)stream));
+}
+
+int topth_prefill(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int L,
+                  int d, int dtype, float scale, const float* theta, int n_rows,
+                  unsigned flags, void* out, int* kept_count, float* beta,
+                  unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream) {
+    if (!q || !k || !v || !theta || !out) return TOPTH_EINVAL;
+    if (bad_dims(B, Hq, Hkv, L, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
+    if (!isfinite(scale) || (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE))) return TOPTH_EINVAL;
+    if (too_big((long long)B * Hq * L, d)) return TOPTH_EUNSUPPORTED;
+    if (L > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
+    const bool vmc = (flags & TOPTH_VMC) && !(flags & TOPTH_SDC_NONE);
+    if (vmc) {
+        if (!ws) return TOPTH_EWORKSPACE;
+        if (ws_bytes < prefill_ws(B, Hq, Hkv, L, d)) return TOPTH_EWORKSPACE;
+    }
+    PrefillParams p = {};
+    p.q = q; p.k = k; p.v = v; p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.d = d; p.dtype = dtype;
+    p.scale = scale; p.theta = theta; p.n_rows = n_rows; p.flags = flags;
+    p.out = out; p.kept_count = kept_count; p.beta = beta; p.kept_mask = kept_mask;
+    p.ws = ws; p.ws_bytes = ws_bytes;
+    return map_hip(launch_prefill_rowwise(p, (float*)ws, (hipStream_t)stream));
+}
+
+int topth_decode(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                 int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                 const float* theta, int n_rows, const float* v_mean, unsigned flags,
+                 void* out, int* kept_count, float* beta, int* vrows_read,
+                 unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !theta || !out) return TOPTH_EINVAL;
+    if (bad_dims(B, Hq, Hkv, Lmax, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
+    if (!isfinite(scale) || (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE))) return TOPTH_EINVAL;
+    if ((flags & TOPTH_VMC) && !(flags & TOPTH_SDC_NONE) && !v_mean) return TOPTH_EINVAL;
+    if (too_big((long long)B * Hkv * Lmax, d)) return TOPTH_EUNSUPPORTED;
+    if ((long long)B * Hkv > kWsMaxGroups) return TOPTH_EUNSUPPORTED;
+    if (!ws) return TOPTH_EWORKSPACE;
+    if (ws_bytes < decode_ws(B, Hq, Hkv, Lmax, d)) return TOPTH_EWORKSPACE;
+    DecodeParams p = {};
+    p.q = q; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lmax = Lmax; p.d = d; p.dtype = dtype; p.scale = scale;
+    p.theta = theta; p.n_rows = n_rows; p.v_mean = v_mean; p.flags = flags;
+    p.out = out; p.kept_count = kept_count; p.beta = beta; p.vrows_read = vrows_read;
+    p.kept_mask = kept_mask; p.ws = ws; p.ws_bytes = ws_bytes;
+    if (dtype == TOPTH_BF16) {
+        if (!decode_bf16_supported(d, Hq / Hkv)) return TOPTH_EUNSUPPORTED;
+        return map_hip(launch_decode_bf16(p, (hipStream_t)stream));
+    }
+    if (Lmax > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
+    return map_hip(launch_decode_rowwise(p, (uint32_t*)((char*)ws + kWsHeaderBytes),
+                                         (hipStream_t)stream));
+}
+
+int topth_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,
+                float* v_mean, void* stream) {
+    if (!v || !seq_lens || !v_mean) return TOPTH_EINVAL;
+    if (bad_dims(B, Hkv, Hkv, Lmax, d) || bad_dtype(dtype)) return TOPTH_EINVAL;
+    if (too_big((long long)B * Hkv * Lmax, d)) return TOPTH_EUNSUPPORTED;
+    return map_hip(launch_vmean(v, seq_lens, B, Hkv, Lmax, d, dtype, v_mean, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,466 @@
+// Row-per-workgroup kernels: one workgroup owns one attention row end to end
+// (scores in LDS, row statistics, threshold, compensation).  They serve the
+// float32 element type for every operation and the bfloat16 prefill and
+// calibration until the tiled kernels take over those shapes.
+//
+// Method: "Top-Theta Attention: Sparsifying Transformers by Compensated
+// Thresholding" -- Eq. 1-3 (scores, softmax, SV), Sec. 3 (keep s >= theta),
+// Sec. 3.1 Algorithm 1 (k-th largest per row, post-softmax), Sec. 3.2.1 Eq. 4
+// (exact SDC: kept weights keep the full denominator), Sec. 3.2.2 Eq. 5-7 (VMC).
+#include "topth_internal.h"
+
+#include <math.h>
+
+namespace topth {
+
+enum RowMode { kRowDecode = 0, kRowPrefill = 1, kRowCalib = 2 };
+
+struct RowArgs {
+    const void* q; const void* k; const void* v; const int* seq_lens;
+    int B, Hq, Hkv, Lq, Lk;       // Lk: key rows per (b, kv) in memory (Lmax for decode)
+    float xscale;                 // scale * log2(e): scores are kept in the log2 domain
+    int q_pos0;
+    const float* theta; int n_rows;
+    const float* mu;              // decode: [B][Hkv][d]; prefill: prefix means [B][Hkv][L][d]
+    unsigned flags;
+    void* out; int* kept_count; float* beta;
+    int ks[8]; int n_k; float* samples;   // calibration: [S][n_k][Hq][Lq]
+    uint32_t* masks; int mask_words;      // decode: kept-key bitmasks [B][Hq][mask_words]
+    unsigned char* kept_mask;             // optional byte mask, [rows][Lk]
+};
+
+constexpr int kRowThreads = 256;
+constexpr int kRowMaxKeysDecl = 32768;   // longest row the row kernels hold in LDS
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < kRowThreads / 64; ++i) r = fmaxf(r, red[i]);
+    return r;
+}
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float r = 0.f;
+    for (int i = 0; i < kRowThreads / 64; ++i) r += red[i];
+    return r;
+}
+__device__ __forceinline__ int block_sum_i(int v, int* red) {
+    v = wave_sum_i(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    int r = 0;
+    for (int i = 0; i < kRowThreads / 64; ++i) r += red[i];
+    return r;
+}
+
+// k-th largest (1-based) of xs[0..n) by a most-significant-digit-first radix
+// select over order-preserving 32-bit keys, 8 bits per pass.
+__device__ float block_kth_largest(const float* xs, int n, int k, unsigned* hist, int* sel) {
+    uint32_t prefix = 0, mask = 0;
+    int kk = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += kRowThreads) hist[i] = 0;
+        __syncthreads();
+        for (int j = threadIdx.x; j < n; j += kRowThreads) {
+            uint32_t u = float_to_ordered(xs[j]);
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int cum = 0, d = 0;
+            for (d = 255; d > 0; --d) {
+                int c = (int)hist[d];
+                if (cum + c >= kk) break;
+                cum += c;
+            }
+            sel[0] = d;
+            sel[1] = kk - cum;
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sel[0] << shift;
+        mask |= 255u << shift;
+        kk = sel[1];
+        __syncthreads();
+    }
+    return ordered_to_float(prefix);
+}
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
+    extern __shared__ float xs[];             // scores (log2 domain), then weights
+    __shared__ float qs[D];
+    __shared__ float redf[kRowThreads / 64];
+    __shared__ int redi[kRowThreads / 64];
+    __shared__ unsigned hist[256];
+    __shared__ int sel[2];
+    __shared__ uint32_t keepbits[MODE == kRowDecode ? kRowMaxKeysDecl / 32 : 1];
+
+    const int row = blockIdx.x;
+    const int i = row % a.Lq;
+    const int h = (row / a.Lq) % a.Hq;
+    const int b = row / (a.Lq * a.Hq);
+    const int g = a.Hq / a.Hkv;
+    const int kv = h / g;
+    int n;
+    if (MODE == kRowDecode) n = min(max(a.seq_lens[b], 1), a.Lk);   // clamp to [1, Lmax]
+    else if (MODE == kRowPrefill) n = i + 1;
+    else n = a.q_pos0 + i + 1;
+    const int rowid = n - 1;
+
+    const T* qrow = (const T*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + i) * D;
+    for (int t = threadIdx.x; t < D; t += kRowThreads) qs[t] = Elem<T>::load(qrow + t);
+    __syncthreads();
+
+    // Eq. 1: scores of the causal row, scaled by 1/sqrt(d) and log2(e)
+    const T* kbase = (const T*)a.k + (size_t)(b * a.Hkv + kv) * a.Lk * D;
+    float mloc = -INFINITY;
+    for (int j = threadIdx.x; j < n; j += kRowThreads) {
+        const T* kr = kbase + (size_t)j * D;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int t = 0; t < D; ++t) acc = fmaf(qs[t], Elem<T>::load(kr + t), acc);
+        const float x = acc * a.xscale;
+        xs[j] = x;
+        mloc = fmaxf(mloc, x);
+    }
+    const float m = block_max(mloc, redf);
+    float lloc = 0.f;
+    for (int j = threadIdx.x; j < n; j += kRowThreads) lloc += exp2f(xs[j] - m);
+    const float lse2 = m + __log2f(block_sum(lloc, redf));   // Eq. 2 denominator, log2 domain
+
+    if (MODE == kRowCalib) {
+        // Algorithm 1 (post-softmax): per target k, the k-th largest s of the row
+        for (int t = 0; t < a.n_k; ++t) {
+            const int kk = a.ks[t];
+            float val = NAN;
+            if (n > kk) {
+                const float xk = block_kth_largest(xs, n, kk, hist, sel);
+                val = exp2f(xk - lse2);
+            }
+            if (threadIdx.x == 0) {
+                const int s = b;
+                a.samples[(((size_t)s * a.n_k + t) * a.Hq + h) * a.Lq + i] = val;
+            }
+        }
+        return;
+    }
+
+    // Sec. 3: keep s >= theta  <=>  x >= log2(theta) + lse2
+    const float th = a.theta[(size_t)h * a.n_rows + min(rowid, a.n_rows - 1)];
+    const float T2 = log2_threshold(th, lse2);
+    if (MODE == kRowDecode) {
+        for (int w = threadIdx.x; w < (n + 31) / 32; w += kRowThreads) keepbits[w] = 0u;
+        __syncthreads();
+    }
+    int cnt = 0;
+    float mass = 0.f;
+    for (int j = threadIdx.x; j < n; j += kRowThreads) {
+        const float x = xs[j];
+        const bool keep = x >= T2;
+        const float w = keep ? exp2f(x - lse2) : 0.f;   // exact SDC: weight = s
+        xs[j] = w;
+        cnt += keep;
+        mass += w;
+        if (MODE == kRowDecode && keep) atomicOr(&keepbits[j >> 5], 1u << (j & 31));
+        if (a.kept_mask) a.kept_mask[(size_t)row * a.Lk + j] = keep ? 1 : 0;
+    }
+    if (MODE == kRowPrefill && a.kept_mask)
+        for (int j = n + threadIdx.x; j < a.Lk; j += kRowThreads) a.kept_mask[(size_t)row * a.Lk + j] = 0;
+    cnt = block_sum_i(cnt, redi);
+    mass = block_sum(mass, redf);
+    __syncthreads();
+
+    const bool renorm = (a.flags & 2u) != 0;
+    const bool vmc = (a.flags & 1u) != 0;
+    const float beta = renorm ? 0.f : 1.f - mass;              // Eq. 6
+    const T* vbase = (const T*)a.v + (size_t)(b * a.Hkv + kv) * a.Lk * D;
+    T* orow = (T*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + i) * D;
+    const float* mu = nullptr;
+    if (vmc && !renorm) {
+        mu = (MODE == kRowDecode) ? a.mu + (size_t)(b * a.Hkv + kv) * D
+                                  : a.mu + ((size_t)(b * a.Hkv + kv) * a.Lq + i) * D;
+    }
+    for (int t = threadIdx.x; t < D; t += kRowThreads) {
+        float acc = 0.f;
+        for (int j = 0; j < n; ++j) {
+            const float w = xs[j];
+            if (w != 0.f) acc = fmaf(w, Elem<T>::load(vbase + (size_t)j * D + t), acc);
+        }
+        if (renorm) acc = (cnt > 0) ? acc / mass : 0.f;
+        if (mu) acc = fmaf(beta, mu[t], acc);                   // Eq. 7
+        Elem<T>::store(orow + t, acc);
+    }
+    if (threadIdx.x == 0) {
+        const size_t o = (size_t)(b * a.Hq + h) * a.Lq + i;
+        if (a.kept_count) a.kept_count[o] = cnt;
+        if (a.beta) a.beta[o] = beta;
+    }
+    if (MODE == kRowDecode && a.masks) {
+        uint32_t* mrow = a.masks + (size_t)(b * a.Hq + h) * a.mask_words;
+        for (int w = threadIdx.x; w < a.mask_words; w += kRowThreads)
+            mrow[w] = (w < (n + 31) / 32) ? keepbits[w] : 0u;
+    }
+}
+
+// number of distinct V rows the GQA group reads: popcount of the OR of its
+// heads' kept-key masks (Sec. 4.6)
+__global__ void union_count_kernel(const uint32_t* masks, int Hq, int Hkv, int mask_words,
+                                   int* vrows_read) {
+    __shared__ int red[4];
+    const int bk = blockIdx.x;
+    const int b = bk / Hkv, kv = bk % Hkv;
+    const int g = Hq / Hkv;
+    int c = 0;
+    for (int w = threadIdx.x; w < mask_words; w += blockDim.x) {
+        uint32_t u = 0;
+        for (int hh = 0; hh < g; ++hh) u |= masks[((size_t)b * Hq + kv * g + hh) * mask_words + w];
+        c += __popc(u);
+    }
+    c = wave_sum_i(c);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) vrows_read[bk] = red[0] + red[1] + red[2] + red[3];
+}
+
+// mean of the first n = seq_lens[b] V rows, Eq. 5 over the cached rows
+template <typename T>
+__global__ void vmean_kernel(const T* v, const int* seq_lens, int Hkv, int Lmax, int D, float* out) {
+    const int bk = blockIdx.x;
+    const int b = bk / Hkv;
+    const int n = min(max(seq_lens[b], 1), Lmax);
+    const T* base = v + (size_t)bk * Lmax * D;
+    for (int t = threadIdx.x; t < D; t += blockDim.x) {
+        double acc = 0.0;
+        for (int j = 0; j < n; ++j) acc += (double)Elem<T>::load(base + (size_t)j * D + t);
+        out[(size_t)bk * D + t] = (float)(acc / (double)n);
+    }
+}
+
+// causal prefix means mu_p = mean of V rows 0..p (Eq. 5 read causally)
+template <typename T>
+__global__ void prefix_mean_kernel(const T* v, int L, int D, float* mu) {
+    const int bk = blockIdx.x;
+    const T* base = v + (size_t)bk * L * D;
+    float* o = mu + (size_t)bk * L * D;
+    for (int t = threadIdx.x; t < D; t += blockDim.x) {
+        double acc = 0.0;
+        for (int p = 0; p < L; ++p) {
+            acc += (double)Elem<T>::load(base + (size_t)p * D + t);
+            o[(size_t)p * D + t] = (float)(acc / (double)(p + 1));
+        }
+    }
+}
+
+// Accumulate per-sequence calibration samples into (sum, sumsq, count), in
+// sequence order, one thread per (k, head, row).
+__global__ void calib_accumulate_kernel(const float* samples, int S, int n_k, int Hq, int Lq,
+                                        int q_pos0, double* sum, double* sumsq, int* count,
+                                        int n_rows) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t per = (size_t)n_k * Hq * Lq;
+    if (idx >= per) return;
+    const int i = (int)(idx % Lq);
+    const int h = (int)((idx / Lq) % Hq);
+    const int t = (int)(idx / ((size_t)Lq * Hq));
+    const int p = q_pos0 + i;
+    if (p >= n_rows) return;
+    double s1 = 0.0, s2 = 0.0;
+    int c = 0;
+    for (int s = 0; s < S; ++s) {
+        const float x = samples[(size_t)s * per + idx];
+        if (x == x) { s1 += (double)x; s2 += (double)x * (double)x; ++c; }
+    }
+    if (c) {
+        const size_t o = ((size_t)t * Hq + h) * n_rows + p;
+        sum[o] += s1; sumsq[o] += s2; count[o] += c;
+    }
+}
+
+// theta = mean + alpha * std of the observed rows; -inf for rows with p+1 <= k;
+// other unobserved rows copy the nearest observed row (smaller row on a tie).
+constexpr int kFinThreads = 256;
+__device__ __forceinline__ float theta_of(const double* sum, const double* sumsq, const int* count,
+                                          size_t o, float alpha) {
+    const double c = (double)count[o];
+    const double mean = sum[o] / c;
+    double var = sumsq[o] / c - mean * mean;
+    if (var < 0.0) var = 0.0;
+    return (float)(mean + (double)alpha * sqrt(var));
+}
+
+struct KList { int k[8]; };
+
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(
+        const double* sum, const double* sumsq, const int* count, int Hq, int n_rows,
+        KList ks, float alpha, float* theta) {
+    __shared__ int first_obs[kFinThreads], last_obs[kFinThreads];
+    const int t = blockIdx.x / Hq, h = blockIdx.x % Hq;
+    const int k = ks.k[t];
+    const size_t base = ((size_t)t * Hq + h) * n_rows;
+    const int seg = (n_rows + kFinThreads - 1) / kFinThreads;
+    const int lo = threadIdx.x * seg, hi = min(n_rows, lo + seg);
+    int f = -1, l = -1;
+    for (int p = lo; p < hi; ++p)
+        if (count[base + p] > 0) { if (f < 0) f = p; l = p; }
+    first_obs[threadIdx.x] = f;
+    last_obs[threadIdx.x] = l;
+    __syncthreads();
+    int prev = -1, next = -1;
+    for (int u = threadIdx.x - 1; u >= 0 && prev < 0; --u) prev = last_obs[u];
+    for (int u = threadIdx.x + 1; u < kFinThreads && next < 0; ++u) next = first_obs[u];
+    // forward pass: nearest observed row at or before p
+    for (int p = lo; p < hi; ++p) {
+        if (count[base + p] > 0) prev = p;
+        theta[base + p] = (float)prev;          // temporary: row index as float
+    }
+    // backward pass: choose between previous and next observed rows
+    for (int p = hi - 1; p >= lo; --p) {
+        if (count[base + p] > 0) next = p;
+        const int pv = (int)theta[base + p];
+        float out;
+        if (p + 1 <= k) out = -INFINITY;
+        else if (count[base + p] > 0) out = theta_of(sum, sumsq, count, base + p, alpha);
+        else if (pv < 0 && next < 0) out = -INFINITY;
+        else {
+            int src;
+            if (pv < 0) src = next;
+            else if (next < 0) src = pv;
+            else src = (p - pv <= next - p) ? pv : next;
+            out = theta_of(sum, sumsq, count, base + src, alpha);
+        }
+        theta[base + p] = out;
+    }
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// ------------------------------------------------------------------ launchers
+template <typename T, int D, int MODE>
+static int launch_rows(const RowArgs& a, int rows, int smem_floats, hipStream_t s) {
+    const size_t smem = (size_t)smem_floats * sizeof(float);
+    if (smem > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)row_kernel<T, D, MODE>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((row_kernel<T, D, MODE>), dim3(rows), dim3(kRowThreads), smem, s, a);
+    return hipGetLastError();
+}
+
+template <int MODE>
+static int dispatch_rows(const RowArgs& a, int d, int dtype, int rows, int smem_floats,
+                         hipStream_t s) {
+    if (dtype == 0) {
+        if (d == 64) return launch_rows<float, 64, MODE>(a, rows, smem_floats, s);
+        return launch_rows<float, 128, MODE>(a, rows, smem_floats, s);
+    }
+    if (d == 64) return launch_rows<uint16_t, 64, MODE>(a, rows, smem_floats, s);
+    return launch_rows<uint16_t, 128, MODE>(a, rows, smem_floats, s);
+}
+
+int rowwise_max_keys() { return kRowMaxKeysDecl; }
+
+size_t decode_rowwise_ws_bytes(int B, int Hq, int Lmax) {
+    return (size_t)B * Hq * ((Lmax + 31) / 32) * sizeof(uint32_t);
+}
+
+int launch_decode_rowwise(const DecodeParams& p, uint32_t* masks_ws, hipStream_t s) {
+    RowArgs a = {};
+    a.q = p.q; a.k = p.k; a.v = p.v; a.seq_lens = p.seq_lens;
+    a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Lq = 1; a.Lk = p.Lmax;
+    a.xscale = p.scale * kLog2e;
+    a.theta = p.theta; a.n_rows = p.n_rows; a.mu = p.v_mean; a.flags = p.flags;
+    a.out = p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.kept_mask = p.kept_mask;
+    a.mask_words = (p.Lmax + 31) / 32;
+    a.masks = p.vrows_read ? masks_ws : nullptr;
+    int e = dispatch_rows<kRowDecode>(a, p.d, p.dtype, p.B * p.Hq, p.Lmax, s);
+    if (e != hipSuccess) return e;
+    if (p.vrows_read) {
+        hipLaunchKernelGGL(union_count_kernel, dim3(p.B * p.Hkv), dim3(256), 0, s,
+                           (const uint32_t*)masks_ws, p.Hq, p.Hkv, a.mask_words, p.vrows_read);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+int launch_prefill_rowwise(const PrefillParams& p, float* mu_ws, hipStream_t s) {
+    const bool vmc = (p.flags & 1u) && !(p.flags & 2u);
+    if (vmc) {
+        if (p.dtype == 0)
+            hipLaunchKernelGGL(prefix_mean_kernel<float>, dim3(p.B * p.Hkv), dim3(128), 0, s,
+                               (const float*)p.v, p.L, p.d, mu_ws);
+        else
+            hipLaunchKernelGGL(prefix_mean_kernel<uint16_t>, dim3(p.B * p.Hkv), dim3(128), 0, s,
+                               (const uint16_t*)p.v, p.L, p.d, mu_ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    RowArgs a = {};
+    a.q = p.q; a.k = p.k; a.v = p.v;
+    a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Lq = p.L; a.Lk = p.L;
+    a.xscale = p.scale * kLog2e;
+    a.theta = p.theta; a.n_rows = p.n_rows; a.mu = mu_ws; a.flags = p.flags;
+    a.out = p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.kept_mask = p.kept_mask;
+    return dispatch_rows<kRowPrefill>(a, p.d, p.dtype, p.B * p.Hq * p.L, p.L, s);
+}
+
+int launch_calibrate_rowwise(const CalibParams& p, float* samples_ws, hipStream_t s) {
+    RowArgs a = {};
+    a.q = p.q; a.k = p.k;
+    a.B = p.S; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Lq = p.Lq; a.Lk = p.Lk;
+    a.xscale = p.scale * kLog2e; a.q_pos0 = p.q_pos0;
+    for (int t = 0; t < 8; ++t) a.ks[t] = p.ks[t];
+    a.n_k = p.n_k; a.samples = samples_ws;
+    int e = dispatch_rows<kRowCalib>(a, p.d, p.dtype, p.S * p.Hq * p.Lq, p.q_pos0 + p.Lq, s);
+    if (e != hipSuccess) return e;
+    const size_t per = (size_t)p.n_k * p.Hq * p.Lq;
+    hipLaunchKernelGGL(calib_accumulate_kernel, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, s,
+                       samples_ws, p.S, p.n_k, p.Hq, p.Lq, p.q_pos0, p.sum, p.sumsq, p.count,
+                       p.n_rows);
+    return hipGetLastError();
+}
+
+int launch_finalize(const double* sum, const double* sumsq, const int* count, const int* ks,
+                    int n_k, int Hq, int n_rows, float alpha, float* theta, hipStream_t s) {
+    KList kl = {};
+    for (int t = 0; t < n_k && t < 8; ++t) kl.k[t] = ks[t];
+    hipLaunchKernelGGL(finalize_kernel, dim3(n_k * Hq), dim3(kFinThreads), 0, s, sum, sumsq, count,
+                       Hq, n_rows, kl, alpha, theta);
+    return hipGetLastError();
+}
+
+int launch_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,
+                 float* v_mean, hipStream_t s) {
+    if (dtype == 0)
+        hipLaunchKernelGGL(vmean_kernel<float>, dim3(B * Hkv), dim3(128), 0, s, (const float*)v,
+                           seq_lens, Hkv, Lmax, d, v_mean);
+    else
+        hipLaunchKernelGGL(vmean_kernel<uint16_t>, dim3(B * Hkv), dim3(128), 0, s,
+                           (const uint16_t*)v, seq_lens, Hkv, Lmax, d, v_mean);
+    return hipGetLastError();
+}
+
+int launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+    const size_t words = bytes / 4;
+    if (words == 0) return hipSuccess;
+    unsigned blocks = (unsigned)((words + 255) / 256);
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, words);
+    return hipGetLastError();
+}
+
+}  // namespace topth

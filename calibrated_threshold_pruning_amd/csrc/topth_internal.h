@@ -1,0 +1,118 @@
+// Internal declarations and device helpers of libtopth (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace topth {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+// Workspace header: status word, then per-group counters of the decode barrier.
+constexpr size_t kWsHeaderBytes = 65536;
+constexpr int kWsCounterOffsetInts = 64;           // counters start at byte 256
+constexpr int kWsMaxGroups = (int)((kWsHeaderBytes / 4 - kWsCounterOffsetInts) / 2);
+constexpr int kStatusSpinTimeout = 1;
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// round-to-nearest-even float -> bfloat16 bits (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float* p) { return *p; }
+    static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {   // bfloat16 stored as raw bits
+    static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+    static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+};
+
+// order-preserving map float -> uint32 (larger float <-> larger key)
+__device__ __forceinline__ uint32_t float_to_ordered(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ordered_to_float(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+// ------------------------------------------------------------ wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// threshold in the log2 domain: keep x >= T  <=>  s = exp2(x - lse2) >= theta.
+// theta <= 0 or -inf keeps every valid element; invalid elements carry x = -inf
+// and never pass because T is clamped to -FLT_MAX.
+__device__ __forceinline__ float log2_threshold(float theta, float lse2) {
+    if (!(theta > 0.0f)) return -3.402823466e38f;
+    return fmaxf(__log2f(theta) + lse2, -3.402823466e38f);
+}
+
+// ------------------------------------------------------------------ launchers
+struct DecodeParams {
+    const void* q; const void* k; const void* v; const int* seq_lens;
+    int B, Hq, Hkv, Lmax, d, dtype; float scale;
+    const float* theta; int n_rows; const float* v_mean; unsigned flags;
+    void* out; int* kept_count; float* beta; int* vrows_read; unsigned char* kept_mask;
+    void* ws; size_t ws_bytes;
+};
+struct PrefillParams {
+    const void* q; const void* k; const void* v;
+    int B, Hq, Hkv, L, d, dtype; float scale;
+    const float* theta; int n_rows; unsigned flags;
+    void* out; int* kept_count; float* beta; unsigned char* kept_mask;
+    void* ws; size_t ws_bytes;
+};
+struct CalibParams {
+    const void* q; const void* k;
+    int S, Hq, Hkv, Lq, Lk, d, dtype; float scale; int q_pos0;
+    int ks[8]; int n_k;
+    double* sum; double* sumsq; int* count; int n_rows;
+    void* ws; size_t ws_bytes;
+};
+
+// Each launcher validates nothing (the ABI layer did) and returns a hipError_t.
+size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lmax, int d);
+int launch_decode(const DecodeParams& p, hipStream_t s);
+size_t prefill_ws_bytes(int B, int Hq, int Hkv, int L, int d);
+int launch_prefill(const PrefillParams& p, hipStream_t s);
+size_t calib_ws_bytes(int S, int Hq, int Lq, int Lk, int d, int n_k);
+int launch_calibrate(const CalibParams& p, hipStream_t s);
+int launch_finalize(const double* sum, const double* sumsq, const int* count, const int* ks,
+                    int n_k, int Hq, int n_rows, float alpha, float* theta, hipStream_t s);
+int launch_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,
+                 float* v_mean, hipStream_t s);
+int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace topth

@@ -1,0 +1,189 @@
+/*
+ * topth.h -- C ABI of libtopth, Top-theta attention for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Method: "Top-Theta Attention: Sparsifying Transformers by Compensated
+ * Thresholding" (arXiv 2502.08363).  Each attention row keeps the post-softmax
+ * elements s_j >= theta[head][row], where theta is a static threshold that
+ * calibration sets to the mean, over calibration sequences, of the row's k-th
+ * largest post-softmax value (Sec. 3.1, Algorithm 1, post-softmax variant).
+ * Kept elements keep their full softmax denominator (exact SDC, Sec. 3.2.1,
+ * Eq. 4) and the discarded mass beta is added back times the mean V row
+ * (VMC, Sec. 3.2.2, Eq. 5-7).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers marked "device" point to GPU memory of the current HIP device;
+ *    pointers marked "host" point to CPU memory read before the call returns.
+ *    The caller owns every buffer; the library allocates no device memory and
+ *    keeps no state between calls except what it leaves in the caller's
+ *    workspace (see "Workspace").
+ *  - Tensors are dense, row-major, head dimension fastest:
+ *      Q [B][Hq][L][d], K and V [B][Hkv][L][d] (decode caches [B][Hkv][Lmax][d]).
+ *  - GQA: query head h reads KV head h / (Hq / Hkv); Hq must be a multiple of
+ *    Hkv (Sec. 2.2 and 4.6 of the paper).  Every head keeps its own selection.
+ *  - Element type: TOPTH_F32 (float) or TOPTH_BF16 (bfloat16) for Q, K, V and
+ *    the attention output; scores, softmax statistics and accumulation are
+ *    float32.  d must be 64 or 128.
+ *  - Row id: query position p, 0-based; a decode step with n cached keys (the
+ *    current token included) is row n - 1.  Rows at or past n_rows of a
+ *    theta slab use the slab's last row.
+ *  - theta slab of one layer: float theta[Hq][n_rows], post-softmax
+ *    probabilities; -INFINITY (or any value <= 0) keeps every element.
+ *  - stream: a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued asynchronously on it; nothing synchronises the host.
+ *  - Errors: argument errors return a negative status before any GPU work
+ *    is enqueued; a failed launch returns TOPTH_EHIP.  No C++ exception
+ *    crosses this interface.  Calls are thread-safe.
+ *
+ * Workspace
+ * ---------
+ *  Decode and calibration need a device workspace of at least
+ *  topth_workspace_size(...) bytes.  Its first TOPTH_WS_HEADER_BYTES hold
+ *  synchronisation counters and a status word; a workspace must be zeroed
+ *  (topth_workspace_init) before its first use, and every call that returns
+ *  TOPTH_OK leaves those counters at zero again, so one workspace can be
+ *  reused by any later call of any size up to its capacity.  Two calls that
+ *  overlap in time must not share a workspace.
+ */
+#ifndef TOPTH_H
+#define TOPTH_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TOPTH_OK = 0,
+    TOPTH_EINVAL = -1,        /* NULL pointer, bad size or inconsistent shape   */
+    TOPTH_EUNSUPPORTED = -2,  /* valid but not implemented (d, dtype, g, size)  */
+    TOPTH_EWORKSPACE = -3,    /* workspace NULL or smaller than required        */
+    TOPTH_EHIP = -4           /* a HIP runtime call or kernel launch failed     */
+} topth_status;
+
+typedef enum { TOPTH_F32 = 0, TOPTH_BF16 = 1 } topth_dtype;
+
+/* flags of topth_prefill / topth_decode */
+#define TOPTH_VMC       0x1u  /* add beta * mu, mu = mean V row (Sec. 3.2.2, Eq. 7)     */
+#define TOPTH_SDC_NONE  0x2u  /* divide kept weights by the kept mass only (softmax
+                                 over the kept set) instead of exact SDC; beta = 0       */
+
+/* op codes of topth_workspace_size */
+#define TOPTH_OP_CALIBRATE 0
+#define TOPTH_OP_PREFILL   1
+#define TOPTH_OP_DECODE    2
+
+#define TOPTH_WS_HEADER_BYTES 4096
+#define TOPTH_MAX_NK 8        /* most k values one calibration call can target */
+
+/* Human-readable text of a status code (static storage). */
+const char* topth_strerror(int status);
+
+/*
+ * Bytes of device workspace an operation needs.  Arguments (unused ones are
+ * ignored):
+ *   TOPTH_OP_CALIBRATE: B = sequences per call S, Hq, Hkv, Lq, Lk, d, n_k
+ *   TOPTH_OP_PREFILL:   B, Hq, Hkv, Lq = Lk = L, d
+ *   TOPTH_OP_DECODE:    B, Hq, Hkv, Lk = Lmax, d
+ * Returns 0 for arguments no call could accept.
+ */
+size_t topth_workspace_size(int op, int B, int Hq, int Hkv, int Lq, int Lk, int d, int n_k);
+
+/* Zero a workspace (device, ws_bytes) on the stream; needed once before the
+ * first call that uses it. */
+int topth_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Calibration, Algorithm 1 of the paper adapted to post-softmax values
+ * (Sec. 3.1): for every sequence s < S, query head h, query row i (position
+ * p = q_pos0 + i, seeing keys 0..p) and target k = ks[t] with p + 1 > k,
+ * take the k-th largest post-softmax value of the row and add it, its square
+ * and a count of one into sum/sumsq/count[t][h][p] (rows p >= n_rows are
+ * skipped).  Sequences are added in order 0..S-1 for every entry, so repeated
+ * calls accumulate deterministically.
+ *   q      device [S][Hq][Lq][d]            k  device [S][Hkv][Lk][d]
+ *   q_pos0 position of query row 0: 0 for prefill-style calibration
+ *          (Lq == Lk), Lk - 1 for decode-style calibration (Lq == 1)
+ *   ks     host [n_k], 1 <= ks[t] ; 1 <= n_k <= TOPTH_MAX_NK
+ *   sum, sumsq device double [n_k][Hq][n_rows]; count device int same shape.
+ *          The caller zeroes them before the first call of a calibration.
+ *   scale  score scale, normally 1/sqrt(d)
+ *   ws     device workspace, topth_workspace_size(TOPTH_OP_CALIBRATE, ...)
+ */
+int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq, int Lk,
+                    int d, int dtype, float scale, int q_pos0, const int* ks, int n_k,
+                    double* sum, double* sumsq, int* count, int n_rows,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Final step of Algorithm 1: theta[t][h][p] = sum/count + alpha * std
+ * (population std from sumsq) for rows that were observed; -INFINITY for rows
+ * with p + 1 <= ks[t]; any other row copies the nearest observed row of the
+ * same (t, h) (the smaller row on a tie), or -INFINITY if none was observed.
+ *   sum, sumsq, count device [n_k][Hq][n_rows]; ks host [n_k];
+ *   theta device float [n_k][Hq][n_rows] (output).
+ */
+int topth_calibrate_finalize(const double* sum, const double* sumsq, const int* count,
+                             const int* ks, int n_k, int Hq, int n_rows, float alpha,
+                             float* theta, void* stream);
+
+/*
+ * Causal Top-theta prefill (Sec. 2.2 prefill phase with Sec. 3 thresholding):
+ * for every (b, h, p): s = softmax over keys 0..p of scale * q.k, keep
+ * s >= theta[h][min(p, n_rows-1)], out = sum_kept s_j V_j (exact SDC), plus
+ * beta * mu_p with TOPTH_VMC, where beta = 1 - sum_kept s and mu_p is the mean
+ * of V rows 0..p.  With TOPTH_SDC_NONE the kept weights are divided by their
+ * sum (out = 0 for a row that keeps nothing) and beta = 0.
+ *   q device [B][Hq][L][d]; k, v device [B][Hkv][L][d]; theta device
+ *   [Hq][n_rows]; out device [B][Hq][L][d] of the input dtype;
+ *   kept_count device int [B][Hq][L] or NULL; beta device float [B][Hq][L]
+ *   or NULL; kept_mask device uint8 [B][Hq][L][L] or NULL: 1 where key j is
+ *   kept by row p (entries j > p are 0); ws device,
+ *   topth_workspace_size(TOPTH_OP_PREFILL, ...).
+ */
+int topth_prefill(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int L,
+                  int d, int dtype, float scale, const float* theta, int n_rows,
+                  unsigned flags, void* out, int* kept_count, float* beta,
+                  unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One generative-decoding step (Sec. 2.2 decode phase, Sec. 3 thresholding):
+ * for every (b, h) with n = seq_lens[b] cached keys: s = softmax over keys
+ * 0..n-1 of scale * q.k, keep s >= theta[h][min(n-1, n_rows-1)], and read
+ * only the V rows that some head of the GQA group keeps (Sec. 4.6).
+ * out = sum_kept s_j V_j (+ beta * v_mean with TOPTH_VMC); TOPTH_SDC_NONE as
+ * in topth_prefill.
+ *   q device [B][Hq][d]; k_cache, v_cache device [B][Hkv][Lmax][d];
+ *   seq_lens device int [B], 1 <= n <= Lmax (values outside are clamped to
+ *   that range); theta device [Hq][n_rows];
+ *   v_mean device float [B][Hkv][d], the running mean of the first n V rows
+ *   (Sec. 3.2.2), required iff TOPTH_VMC; out device [B][Hq][d] of the input
+ *   dtype; kept_count device int [B][Hq] or NULL; beta device float [B][Hq]
+ *   or NULL; vrows_read device int [B][Hkv] or NULL: number of distinct V
+ *   rows read for the group (the union of its heads' kept keys);
+ *   kept_mask device uint8 [B][Hq][Lmax] or NULL: 1 where key j < n is kept
+ *   (entries j >= n are left untouched);
+ *   ws device, zero-initialised once, topth_workspace_size(TOPTH_OP_DECODE, ...).
+ */
+int topth_decode(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                 int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                 const float* theta, int n_rows, const float* v_mean, unsigned flags,
+                 void* out, int* kept_count, float* beta, int* vrows_read,
+                 unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Mean of the first n = seq_lens[b] V rows of each (b, kv head): the mu of
+ * VMC (Sec. 3.2.2, Eq. 5) that topth_decode takes as v_mean.
+ *   v device [B][Hkv][Lmax][d]; seq_lens device int [B]; v_mean device float
+ *   [B][Hkv][d] (output).
+ */
+int topth_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,
+                float* v_mean, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPTH_H */

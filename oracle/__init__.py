@@ -14,7 +14,7 @@ rows in non-causal notation) -- parity unpinned for that choice of mu; every
 other step is pinned.
 """
 from .topth import (  # noqa: F401
-    scores, post_softmax, kth_largest, theta_row, row_weights, topth_row,
+    scores, post_softmax, kth_largest, theta_row, row_weights, row_output, topth_row,
     prefix_mean, prefill, decode, Calibrator, calibration_samples,
     PrefillResult, DecodeResult, RowResult,
 )

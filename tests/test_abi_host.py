@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import calibrated_threshold_pruning_amd as tt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "topth.h")
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(topth_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tt.LIB_PATH):
+        pytest.fail("libtopth.so is not built; run `python -m calibrated_threshold_pruning_amd.build`")
+    return tt.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(tt.EXPORTS)
+
+
+def test_strerror(lib):
+    assert tt.topth_strerror(0) == "success"
+    assert "invalid" in tt.topth_strerror(-1)
+    assert "workspace" in tt.topth_strerror(-3)
+    assert tt.topth_strerror(12345) == "unknown status"
+
+
+def test_workspace_size(lib):
+    ws = tt.topth_workspace_size
+    assert ws(tt.TOPTH_OP_DECODE, 16, 32, 8, 1, 4096, 128) > 65536
+    assert ws(tt.TOPTH_OP_DECODE, 16, 32, 8, 1, 4096, 96) == 0          # d not supported
+    assert ws(tt.TOPTH_OP_DECODE, 16, 30, 8, 1, 4096, 128) == 0         # Hq % Hkv != 0
+    assert ws(tt.TOPTH_OP_PREFILL, 1, 32, 8, 8192, 8192, 128) >= 8 * 8192 * 128 * 4
+    assert ws(tt.TOPTH_OP_CALIBRATE, 4, 8, 8, 2048, 2048, 128, 3) >= 4 * 3 * 8 * 2048 * 4
+    assert ws(tt.TOPTH_OP_CALIBRATE, 4, 8, 8, 2048, 2048, 128, 9) == 0  # too many k
+    assert ws(7, 1, 1, 1, 1, 1, 64) == 0
+    # monotone in the cache length
+    assert ws(tt.TOPTH_OP_DECODE, 8, 64, 8, 1, 32768, 128) > ws(tt.TOPTH_OP_DECODE, 8, 64, 8, 1, 4096, 128)
+
+
+def _decode(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, B=2, Hq=8, Hkv=2, Lmax=64, d=128, dt=1, scale=0.1,
+             theta=FAKE, n_rows=64, vm=FAKE, flags=1, out=FAKE, kc=None, bt=None, vr=None, km=None,
+             ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return lib.topth_decode(a["q"], a["k"], a["v"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["Lmax"],
+                            a["d"], a["dt"], a["scale"], a["theta"], a["n_rows"], a["vm"], a["flags"],
+                            a["out"], a["kc"], a["bt"], a["vr"], a["km"], a["ws"], a["wsb"], None)
+
+
+def test_decode_argument_errors(lib):
+    assert _decode(lib, q=None) == -1
+    assert _decode(lib, lens=None) == -1
+    assert _decode(lib, Hq=6, Hkv=4) == -1
+    assert _decode(lib, d=96) == -1
+    assert _decode(lib, dt=7) == -1
+    assert _decode(lib, B=0) == -1
+    assert _decode(lib, n_rows=0) == -1
+    assert _decode(lib, flags=8) == -1
+    assert _decode(lib, vm=None) == -1                   # VMC needs the running mean
+    assert _decode(lib, scale=float("nan")) == -1
+    assert _decode(lib, ws=None) == -3
+    assert _decode(lib, wsb=100) == -3
+    assert _decode(lib, Hq=24, Hkv=8) == -2              # g = 3: no kernel
+    assert _decode(lib, dt=0, Lmax=40000, wsb=1 << 40) == -2  # float32 rows longer than LDS
+
+
+def test_prefill_argument_errors(lib):
+    def call(**over):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, Hq=4, Hkv=2, L=32, d=64, dt=0, scale=0.1, theta=FAKE,
+                 n_rows=32, flags=1, out=FAKE, ws=FAKE, wsb=1 << 30)
+        a.update(over)
+        return lib.topth_prefill(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["d"],
+                                 a["dt"], a["scale"], a["theta"], a["n_rows"], a["flags"], a["out"],
+                                 None, None, None, a["ws"], a["wsb"], None)
+    assert call(v=None) == -1
+    assert call(theta=None) == -1
+    assert call(L=0) == -1
+    assert call(Hkv=3) == -1
+    assert call(flags=0x10) == -1
+    assert call(ws=None) == -3           # VMC needs the prefix-mean workspace
+    assert call(wsb=16) == -3
+
+
+def test_calibrate_argument_errors(lib):
+    ks = (ctypes.c_int * 3)(64, 128, 256)
+    bad = (ctypes.c_int * 2)(64, 0)
+
+    def call(**over):
+        a = dict(q=FAKE, k=FAKE, S=2, Hq=8, Hkv=8, Lq=256, Lk=256, d=128, dt=1, scale=0.1, qp=0,
+                 ks=ctypes.cast(ks, ctypes.c_void_p), nk=3, sum=FAKE, sumsq=FAKE, count=FAKE,
+                 n_rows=256, ws=FAKE, wsb=1 << 30)
+        a.update(over)
+        return lib.topth_calibrate(a["q"], a["k"], a["S"], a["Hq"], a["Hkv"], a["Lq"], a["Lk"], a["d"],
+                                   a["dt"], a["scale"], a["qp"], a["ks"], a["nk"], a["sum"],
+                                   a["sumsq"], a["count"], a["n_rows"], a["ws"], a["wsb"], None)
+    assert call(ks=None) == -1
+    assert call(nk=0) == -1
+    assert call(nk=9) == -1
+    assert call(ks=ctypes.cast(bad, ctypes.c_void_p), nk=2) == -1
+    assert call(qp=1) == -1                        # q_pos0 + Lq > Lk
+    assert call(sum=None) == -1
+    assert call(ws=None) == -3
+    assert call(wsb=8) == -3
+
+
+def test_finalize_argument_errors(lib):
+    ks = (ctypes.c_int * 1)(4)
+    kp = ctypes.cast(ks, ctypes.c_void_p)
+    assert lib.topth_calibrate_finalize(None, FAKE, FAKE, kp, 1, 2, 8, 0.0, FAKE, None) == -1
+    assert lib.topth_calibrate_finalize(FAKE, FAKE, FAKE, kp, 0, 2, 8, 0.0, FAKE, None) == -1
+    assert lib.topth_calibrate_finalize(FAKE, FAKE, FAKE, kp, 1, 2, 8, float("inf"), FAKE, None) == -1
+
+
+def test_vmean_and_ws_init_argument_errors(lib):
+    assert lib.topth_vmean(None, FAKE, 1, 1, 8, 64, 0, FAKE, None) == -1
+    assert lib.topth_vmean(FAKE, FAKE, 1, 1, 8, 63, 0, FAKE, None) == -1
+    assert lib.topth_workspace_init(None, 16, None) == -1
+    assert lib.topth_workspace_init(FAKE, 0, None) == -1
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tt.topth_vmean(torch.zeros(1, 1, 4, 64), torch.ones(1, dtype=torch.int32),
+                       torch.zeros(1, 1, 64))
+    with pytest.raises(ValueError):
+        tt.topth_decode(q, q, q, None, None, None, None, scale=0.1, flags=0)

@@ -1,0 +1,187 @@
+"""Prefill and calibration parity: HIP path (through the C ABI) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import calibrated_threshold_pruning_amd as tt
+import oracle
+from synth import CONFIG_IDS, ROLE_CALIB, ROLE_TEST, attention_inputs, batch_of_sequences, to_f64
+from parity import check_out, check_row_mask, device, theta_of
+
+pytestmark = pytest.mark.gpu
+
+UNIT = CONFIG_IDS["unit"]
+
+
+# ------------------------------------------------------------------ helpers
+def gpu_calibrate(q, k, ks, n_rows, q_pos0=0, alpha=0.0, chunks=1):
+    """theta [n_k, Hq, n_rows] from the HIP calibration, fed in `chunks` calls."""
+    dev = device()
+    S, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    n_k = len(ks)
+    s1 = torch.zeros(n_k, Hq, n_rows, dtype=torch.float64, device=dev)
+    s2 = torch.zeros_like(s1)
+    cnt = torch.zeros(n_k, Hq, n_rows, dtype=torch.int32, device=dev)
+    per = (S + chunks - 1) // chunks
+    ws = tt.workspace(tt.TOPTH_OP_CALIBRATE, per, Hq, Hkv, Lq, Lk, d, n_k)
+    for c0 in range(0, S, per):
+        tt.topth_calibrate(q[c0:c0 + per].to(dev).contiguous(), k[c0:c0 + per].to(dev).contiguous(),
+                           ks, s1, s2, cnt, ws, scale=1.0 / np.sqrt(d), q_pos0=q_pos0)
+    th = torch.empty(n_k, Hq, n_rows, dtype=torch.float32, device=dev)
+    tt.topth_calibrate_finalize(s1, s2, cnt, ks, th, alpha=alpha)
+    torch.cuda.synchronize()
+    return th.cpu().numpy().astype(np.float64), cnt.cpu().numpy()
+
+
+def oracle_calibrate(q, k, ks, n_rows, q_pos0=0, alpha=0.0):
+    S, Hq = q.shape[0], q.shape[1]
+    d = q.shape[-1]
+    cal = oracle.Calibrator(ks, Hq, n_rows)
+    qf, kf = to_f64(q), to_f64(k)
+    for s in range(S):
+        cal.observe(qf[s], kf[s], 1.0 / np.sqrt(d), q_pos0=q_pos0)
+    return cal.finalize(alpha=alpha), cal.counts()
+
+
+def check_theta(gpu, ref):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(gpu), fin)
+    assert (np.isneginf(gpu) == np.isneginf(ref)).all()
+    rel = np.abs(gpu[fin] - ref[fin]) / np.abs(ref[fin])
+    assert rel.max() <= 1e-5, rel.max()
+
+
+def run_prefill(q, k, v, theta, flags):
+    dev = device()
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    out = torch.empty_like(q, device=dev)
+    kc = torch.full((B, Hq, L), -7, dtype=torch.int32, device=dev)
+    bt = torch.full((B, Hq, L), -7.0, dtype=torch.float32, device=dev)
+    km = torch.zeros((B, Hq, L, L), dtype=torch.uint8, device=dev)
+    ws = tt.workspace(tt.TOPTH_OP_PREFILL, B, Hq, Hkv, L, L, d)
+    tt.topth_prefill(q.to(dev), k.to(dev), v.to(dev),
+                     torch.tensor(theta, dtype=torch.float32, device=dev).contiguous(), out,
+                     scale=1.0 / np.sqrt(d), flags=flags, kept_count=kc, beta=bt, kept_mask=km,
+                     ws=ws)
+    torch.cuda.synchronize()
+    return dict(out=out.float().cpu().numpy(), kc=kc.cpu().numpy(), beta=bt.cpu().numpy(),
+                mask=km.cpu().numpy().astype(bool))
+
+
+def compare_prefill(g, q, k, v, theta, flags, dtype, rows=None):
+    vmc = bool(flags & tt.TOPTH_VMC)
+    renorm = bool(flags & tt.TOPTH_SDC_NONE)
+    qf, kf, vf = to_f64(q), to_f64(k), to_f64(v)
+    B, Hq, L, d = qf.shape
+    G = Hq // kf.shape[1]
+    ref = oracle.prefill(qf, kf, vf, theta, 1.0 / np.sqrt(d), vmc=vmc, renorm=renorm, rows=rows,
+                         keep_rows=True)
+    if rows is None:
+        rows = [(b, h, p) for b in range(B) for h in range(Hq) for p in range(L)]
+    mu_cache = {}
+    n_amb = 0
+    for (b, h, p) in rows:
+        kv = h // G
+        gk = g["mask"][b, h, p, :p + 1]
+        assert not g["mask"][b, h, p, p + 1:].any()
+        th = theta_of(theta, h, p)
+        amb = check_row_mask(gk, ref.s[b][h][p], th, f"b{b} h{h} p{p}")
+        n_amb += amb
+        assert g["kc"][b, h, p] == gk.sum()
+        if amb == 0:
+            assert g["kc"][b, h, p] == ref.kept_count[b, h, p]
+        if (b, kv) not in mu_cache:
+            mu_cache[(b, kv)] = oracle.prefix_mean(vf[b, kv])
+        ro, rb = oracle.row_output(ref.s[b][h][p], gk, vf[b, kv, :p + 1], mu_cache[(b, kv)][p],
+                                   vmc=vmc, renorm=renorm)
+        check_out(g["out"][b, h, p], ro, dtype, f"b{b} h{h} p{p}")
+        assert abs(g["beta"][b, h, p] - rb) <= 1e-5
+    return n_amb
+
+
+# --------------------------------------------------- tiny fp32 prefill workload
+def test_tiny_prefill_f32_calibrate_and_apply():
+    """1 head, d=64, L=256, fp32, causal; theta for k=32 from 64 calibration
+    sequences, applied to 8 test sequences with SDC + VMC."""
+    cfg = CONFIG_IDS["tiny_prefill_f32"]
+    print("tiny prefill f32", flush=True)
+    qc, kc, _ = batch_of_sequences(cfg, ROLE_CALIB, 0, 0, 64, Hq=1, Hkv=1, Lq=256, Lk=256, d=64,
+                                   dtype=torch.float32)
+    th_gpu, cnt_gpu = gpu_calibrate(qc, kc, [32], 256, chunks=4)
+    th_ref, cnt_ref = oracle_calibrate(qc, kc, [32], 256)
+    assert np.array_equal(cnt_gpu, cnt_ref)
+    check_theta(th_gpu, th_ref)
+    theta = th_ref[0]
+    q, k, v = attention_inputs(cfg, ROLE_TEST, 0, 0, B=8, Hq=1, Hkv=1, Lq=256, Lk=256, d=64,
+                               dtype=torch.float32)
+    g = run_prefill(q, k, v, theta, tt.TOPTH_VMC)
+    compare_prefill(g, q, k, v, theta, tt.TOPTH_VMC, torch.float32)
+    kept = g["kc"][:, 0, 32:]
+    ratio = kept.mean() / 32
+    assert 0.3 < ratio < 3.0
+
+
+@pytest.mark.parametrize("flags", [tt.TOPTH_VMC, 0, tt.TOPTH_SDC_NONE])
+def test_prefill_bf16_gqa(flags):
+    Hq, Hkv, L, d = 8, 2, 300, 128
+    qc, kc, _ = batch_of_sequences(UNIT, ROLE_CALIB, 3, 0, 4, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    theta = oracle_calibrate(qc, kc, [24], L)[0][0]
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 3, 0, B=2, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    g = run_prefill(q, k, v, theta, flags)
+    compare_prefill(g, q, k, v, theta, flags, torch.bfloat16)
+
+
+def test_prefill_dense_theta_bf16_d64():
+    Hq, Hkv, L, d = 4, 4, 130, 64
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 4, 0, B=1, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    theta = np.full((Hq, 1), -np.inf)
+    g = run_prefill(q, k, v, theta, tt.TOPTH_VMC)
+    compare_prefill(g, q, k, v, theta, tt.TOPTH_VMC, torch.bfloat16)
+    assert (g["kc"] == np.arange(1, L + 1)).all()
+
+
+# ----------------------------------------------------------------- calibration
+def test_calibrate_bf16_multi_k_prefill_style():
+    Hq, L, d = 4, 300, 128
+    q, k, _ = batch_of_sequences(UNIT, ROLE_CALIB, 5, 0, 6, Hq=Hq, Hkv=Hq, Lq=L, Lk=L, d=d)
+    ks = [8, 32, 100]
+    th_gpu, cnt_gpu = gpu_calibrate(q, k, ks, 320, chunks=2)
+    th_ref, cnt_ref = oracle_calibrate(q, k, ks, 320)
+    assert np.array_equal(cnt_gpu, cnt_ref)
+    check_theta(th_gpu, th_ref)
+
+
+def test_calibrate_decode_style_and_alpha():
+    Hq, Hkv, L, d = 8, 2, 1000, 64
+    q, k, _ = batch_of_sequences(UNIT, ROLE_CALIB, 6, 0, 5, Hq=Hq, Hkv=Hkv, Lq=1, Lk=L, d=d)
+    q = q[:, :, :1].contiguous()
+    for alpha in (0.0, 0.5):
+        th_gpu, _ = gpu_calibrate(q, k, [64], 1024, q_pos0=L - 1, alpha=alpha)
+        th_ref, _ = oracle_calibrate(q, k, [64], 1024, q_pos0=L - 1, alpha=alpha)
+        check_theta(th_gpu, th_ref)
+        assert np.isneginf(th_gpu[0, :, :64]).all()
+        assert (th_gpu[0, :, 64:] == th_gpu[0, :, L - 1:L]).all()   # nearest-row fill
+
+
+def test_decode_matches_prefill_row():
+    """Decode with n = p + 1 keys equals prefill row p (both on the GPU)."""
+    dev = device()
+    Hq, Hkv, L, d = 8, 2, 400, 128
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 7, 0, B=1, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    theta = np.exp(np.random.default_rng(0).uniform(-6, -2, size=(Hq, L)))
+    g = run_prefill(q, k, v, theta, tt.TOPTH_VMC)
+    vf = to_f64(v)
+    for p in (0, 63, 64, 255, 399):
+        vm = torch.tensor(vf[:, :, :p + 1].mean(2), dtype=torch.float32, device=dev)
+        out = torch.empty(1, Hq, d, dtype=torch.bfloat16, device=dev)
+        km = torch.zeros(1, Hq, L, dtype=torch.uint8, device=dev)
+        ws = tt.workspace(tt.TOPTH_OP_DECODE, 1, Hq, Hkv, 1, L, d)
+        tt.topth_decode(q[:, :, p].contiguous().to(dev), k.to(dev), v.to(dev),
+                        torch.tensor([p + 1], dtype=torch.int32, device=dev),
+                        torch.tensor(theta, dtype=torch.float32, device=dev), out, ws,
+                        scale=1.0 / np.sqrt(d), flags=tt.TOPTH_VMC, v_mean=vm, kept_mask=km)
+        torch.cuda.synchronize()
+        assert np.array_equal(km.cpu().numpy()[0, :, :p + 1].astype(bool), g["mask"][0, :, p, :p + 1])
+        assert np.abs(out.float().cpu().numpy()[0] - g["out"][0, :, p]).max() <= 1e-2
