@@ -7,7 +7,7 @@
 // (VMC, Sec. 3.2.2 Eq. 5-7), and -- the point of the method in decoding -- only
 // the V rows that some head of the GQA group keeps are read (Sec. 4.6).
 //
-// Kernel shape (persistent, cooperative launch so every workgroup is resident):
+// Kernel shape (persistent; the grid never exceeds the resident capacity):
 //   work item = (group = (b, kv head), chunk of keys); 4 waves per workgroup.
 //   Phase 1  each wave streams its keys' K rows straight from HBM in the MFMA
 //            B-operand layout and forms the g scores per key with
@@ -29,6 +29,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace topth {
 
 struct DecodeKArgs {
@@ -37,6 +39,7 @@ struct DecodeKArgs {
     uint16_t* out; int* kept_count; float* beta; int* vrows_read; unsigned char* kept_mask;
     int* status; int* counters;
     float2* part_ml; float* part_out; float* part_mass; int* part_cnt; int* part_union;
+    float* ovf_w;      // weights of kept keys that do not fit the LDS list, [B*Hkv*Lmax][GW]
     int B, Hq, Hkv, Lmax, n_rows, chunks, items;
     float xscale;
     unsigned flags;
@@ -54,13 +57,92 @@ struct DecodeCfg {
     static constexpr int THREADS = WAVES * 64;
     static constexpr int KEYS_PER_WG = WAVES * NT * KT;
     static constexpr int GW = G < 4 ? 4 : G;   // heads per LDS weight row (padded to 4)
-    static constexpr int DPL = D / 16;         // V dims per lane in the gather
-    static_assert(STEPS >= 1, "head dimension too small");
+    static constexpr int LPR = G <= 4 ? 16 : 32;  // lanes per V row in the gather
+    static constexpr int RPG = 64 / LPR;       // V rows per wave gather instruction
+    static constexpr int DPL = D / LPR;        // V dims per lane in the gather
+    static constexpr int WKEYS = NT * KT;      // keys of one wave
+    static constexpr int U = G >= 16 ? 4 : 8;  // V-row loads in flight per lane while draining
+    static constexpr int CPR = D / 8;          // 16-byte chunks per K row
+    static constexpr int RPI = 64 / CPR;       // K rows per wave load instruction
+    static constexpr int NLD = KT / RPI;       // load instructions per wave tile
+    static constexpr int STAGE_BYTES = KT * D * 2;              // one staged wave tile
+    static constexpr int NBUF = P == 4 ? 1 : 2;                 // stage buffers per wave
+    static constexpr int CAPW = NBUF * STAGE_BYTES / (GW * 4);  // kept-key weights held in LDS per wave
+    static constexpr int RED_BYTES = WAVES * G * D * 4;         // output partials per workgroup
+    static constexpr int KBUF_BYTES =
+        WAVES * NBUF * STAGE_BYTES > RED_BYTES ? WAVES * NBUF * STAGE_BYTES : RED_BYTES;
+    static_assert(STEPS >= 1 && NLD >= 1, "head dimension too small");
+    static_assert(WKEYS <= 65536, "wave key offsets must fit 16 bits");
 };
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Cross-workgroup data of one group (partials written by one chunk, read by the
+// others) moves through agent-scope atomic stores and loads: they are coherent
+// across the XCDs' separate L2 caches without the L2 write-back and invalidate
+// that a device-wide fence costs.  A writer waits for its stores to complete
+// (s_waitcnt) before it bumps the group's counter; a reader loads only after it
+// has seen the counter.
+__device__ __forceinline__ void publish(float* p, float v) {
+    __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish_i(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float consume(const float* p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ int consume_i(const int* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// sum of n published values base[c * stride], c = 0..n-1, added in order of c;
+// eight independent loads are in flight at a time
+__device__ __forceinline__ float sum_chunks(const float* base, size_t stride, int n) {
+    float x = 0.f;
+    for (int c0 = 0; c0 < n; c0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (c0 + u < n) ? consume(base + (size_t)(c0 + u) * stride) : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x += v[u];
+    }
+    return x;
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0,15:14], expcnt[6:4], lgkmcnt[11:8])
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {                                          // vmcnt(N)
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+
 template <int DPL> struct VVec;
-template <> struct VVec<8> { typedef u32x4 T; };
-template <> struct VVec<4> { typedef uint2 T; };
+template <> struct VVec<8> {
+    typedef u32x4 T;
+    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
+    }
+};
+template <> struct VVec<4> {
+    typedef uint2 T;
+    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u2;
+        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0);
+        return make_uint2(v[0], v[1]);
+    }
+};
+template <> struct VVec<2> {
+    typedef unsigned T;
+    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0);
+    }
+};
 
 __device__ __forceinline__ void unpack_bf16(const u32x4& u, float* f) {
 #pragma unroll
@@ -73,28 +155,48 @@ __device__ __forceinline__ void unpack_bf16(const uint2& u, float* f) {
     f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xffff0000u);
     f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xffff0000u);
 }
+__device__ __forceinline__ void unpack_bf16(const unsigned& u, float* f) {
+    f[0] = __uint_as_float(u << 16); f[1] = __uint_as_float(u & 0xffff0000u);
+}
 
 template <int D, int G, int NT>
-__global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeKArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeKArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     using C = DecodeCfg<D, G, NT>;
+    // K tiles are staged through LDS: each wave loads its tile with 1 KiB
+    // contiguous loads (16-byte chunks of a row permuted by an XOR swizzle) and
+    // reads it back in the MFMA operand layout without bank conflicts.  After
+    // phase 2 the same buffer holds the per-wave output partials.
+    __shared__ __attribute__((aligned(16))) unsigned char s_kbuf[C::KBUF_BYTES];
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[G + 1][D + 8];   // row G stays zero
     __shared__ float s_m[C::WAVES][G], s_l[C::WAVES][G];
     __shared__ float s_T[G], s_lse[G];
-    __shared__ __attribute__((aligned(16))) float s_w[C::WAVES][C::KT][C::GW];
-    __shared__ int s_list[C::WAVES][C::KT];
-    __shared__ float s_red[C::WAVES][G][D];
+    __shared__ unsigned short s_kl[C::WAVES][C::WKEYS];   // kept keys of each wave (offsets from its base)
     __shared__ float s_cm[C::WAVES][G];
     __shared__ int s_cc[C::WAVES][G];
     __shared__ int s_un[C::WAVES];
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int blk = lane >> 4;                 // 16-lane block of the MFMA operands
     const int cc = blk % C::BPT;               // block inside its key tile
     const int tt = blk / C::BPT;               // key tile of this lane
     const int mykey = (lane & 15) + 16 * tt;   // key of this lane inside a wave tile
     const int hb = 4 * cc;                     // first head of this lane's C registers
     const float NEG_INF = -INFINITY;
+    unsigned char* stage = s_kbuf + wave * C::NBUF * C::STAGE_BYTES;
+    float (*s_red)[G][D] = reinterpret_cast<float (*)[G][D]>(s_kbuf);
+
+    // A-operand row of this lane: query head hi of key tile i / GP, or the zero row
+    int qrow_lds;
+    {
+        const int i = lane & 15;
+        const int hi = i % C::GP;
+        qrow_lds = ((i / C::GP == tt) && (hi < G)) ? hi : G;
+    }
+    for (int t = tid; t < D + 8; t += C::THREADS) s_q[G][t] = 0;
 
     for (int item = blockIdx.x; item < a.items; item += gridDim.x) {
         const int group = item / a.chunks, chunk = item % a.chunks;
@@ -102,40 +204,76 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeKArgs a) {
         const int n = min(max(a.seq_lens[b], 1), a.Lmax);   // lengths outside [1, Lmax] are clamped
         const int wbase = chunk * C::KEYS_PER_WG + wave * NT * C::KT;
 
-        // ---- query fragments: A[i][k], row i = lane % 16 (head of key tile i / GP)
-        bf16x8 qa[C::STEPS];
+        // ---- the group's query rows to LDS
         {
-            const int i = lane & 15;
-            const int hi = i % C::GP;
-            const bool valid = (i / C::GP == tt) && (hi < G);
-            const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)kv * G + (valid ? hi : 0)) * D;
-#pragma unroll
-            for (int s = 0; s < C::STEPS; ++s) {
-                const u32x4 raw = *(const u32x4*)(qrow + (s * C::BPT + cc) * 8);
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                qa[s] = __builtin_bit_cast(bf16x8, valid ? raw : z);
+            const uint16_t* qg = a.q + ((size_t)b * a.Hq + (size_t)kv * G) * D;
+            for (int idx = tid; idx < G * (D / 8); idx += C::THREADS) {
+                const int h = idx / (D / 8), c = idx % (D / 8);
+                *(u32x4*)&s_q[h][c * 8] = *(const u32x4*)(qg + (size_t)h * D + c * 8);
             }
         }
+        __syncthreads();
 
         // ---- phase 1: scores of this wave's keys, kept in registers
+        // K of the group goes from HBM straight into this wave's LDS stage
+        // (buffer_load ... lds, 1 KiB per instruction, four or eight whole rows);
+        // the per-lane source offset applies the XOR swizzle, so the LDS slots
+        // come out permuted for conflict-free MFMA-layout reads.  Rows past the
+        // n valid keys read as zero (their scores are masked below).
         const uint16_t* kg = a.k + (size_t)group * a.Lmax * D;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, n * D * 2);
+        constexpr int NVO = C::CPR / C::RPI > 0 ? C::CPR / C::RPI : 1;
+        int vo[NVO];
+#pragma unroll
+        for (int j = 0; j < NVO; ++j) {
+            const int row = j * C::RPI + lane / C::CPR;
+            vo[j] = (lane / C::CPR) * (D * 2) + (((lane % C::CPR) ^ (row % C::CPR)) * 16);
+        }
+        auto issue = [&](int key0, unsigned char* buf) {
+#pragma unroll
+            for (int i = 0; i < C::NLD; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    krs, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, vo[i % NVO],
+                    (key0 + i * C::RPI) * (D * 2), 0, 0);
+        };
         f32x4 sc[NT];
+        if (wbase < n) issue(wbase, stage);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int key0 = wbase + t * C::KT;
             sc[t] = f32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
             if (key0 < n) {
+                unsigned char* cur = stage + (t % C::NBUF) * C::STAGE_BYTES;
+                const bool more = (t + 1 < NT) && (key0 + C::KT < n);
+                if (C::NBUF == 2 && more) {
+                    issue(key0 + C::KT, stage + ((t + 1) % C::NBUF) * C::STAGE_BYTES);
+                    wait_vmem_n<C::NLD>();            // all but the next tile's loads have landed
+                } else {
+                    wait_vmem();                      // this tile's rows have landed in LDS
+                }
+                // two independent accumulators; the step loop is only partly
+                // unrolled so that the LDS reads are not all hoisted into registers
+                f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+                const unsigned char* srow = cur + ((mykey / C::RPI) * 64 + (mykey % C::RPI) * C::CPR) * 16;
+                const int swz = mykey % C::CPR;
+#pragma unroll 2
+                for (int s = 0; s < C::STEPS; s += 2) {
+                    const int c0 = s * C::BPT + cc, c1 = c0 + C::BPT;     // 16-byte chunks of the row
+                    const u32x4 kb0 = *(const u32x4*)(srow + (c0 ^ swz) * 16);
+                    const u32x4 qv0 = *(const u32x4*)&s_q[qrow_lds][c0 * 8];
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, qv0), __builtin_bit_cast(bf16x8, kb0), acc0, 0, 0, 0);
+                    if (s + 1 < C::STEPS) {
+                        const u32x4 kb1 = *(const u32x4*)(srow + (c1 ^ swz) * 16);
+                        const u32x4 qv1 = *(const u32x4*)&s_q[qrow_lds][c1 * 8];
+                        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, qv1), __builtin_bit_cast(bf16x8, kb1), acc1, 0, 0, 0);
+                    }
+                }
+                const f32x4 acc = acc0 + acc1;
+                wait_lds();                           // every read of the stage has returned
+                if (C::NBUF == 1 && more) issue(key0 + C::KT, stage);
                 const int key = key0 + mykey;
-                const int keyc = key < a.Lmax ? key : a.Lmax - 1;
-                const u32x4* kp = (const u32x4*)(kg + (size_t)keyc * D) + cc;
-                u32x4 kb[C::STEPS];
-#pragma unroll
-                for (int s = 0; s < C::STEPS; ++s) kb[s] = kp[s * C::BPT];
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < C::STEPS; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        qa[s], __builtin_bit_cast(bf16x8, kb[s]), acc, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const bool ok = (key < n) && (hb + r < G);
@@ -178,30 +316,32 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeKArgs a) {
             float L = 0.f;
             if (M != NEG_INF)
                 for (int w = 0; w < C::WAVES; ++w) L += s_l[w][tid] * exp2f(s_m[w][tid] - M);
-            a.part_ml[((size_t)group * a.chunks + chunk) * G + tid] = make_float2(M, L);
+            float* pml = reinterpret_cast<float*>(a.part_ml + ((size_t)group * a.chunks + chunk) * G + tid);
+            publish(pml, M);
+            publish(pml + 1, L);
         }
 
         // ---- exchange: wait until every chunk of the group has published
-        __threadfence();
+        __builtin_amdgcn_s_waitcnt(0);        // this wave's published values have landed
         __syncthreads();
         if (tid == 0) {
             int* ctr = a.counters + 2 * group;
-            atomicAdd(ctr, 1);
+            __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             unsigned spins = 0;
             while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.chunks) {
                 __builtin_amdgcn_s_sleep(2);
                 if (++spins > a.spin_limit) { atomicOr(a.status, kStatusSpinTimeout); break; }
             }
-            __threadfence();
         }
         __syncthreads();
         if (tid < G) {
             const float2* pm = a.part_ml + (size_t)group * a.chunks * G + tid;
             float M = NEG_INF;
-            for (int c = 0; c < a.chunks; ++c) M = fmaxf(M, pm[(size_t)c * G].x);
+            const float* pmf = reinterpret_cast<const float*>(pm);
+            for (int c = 0; c < a.chunks; ++c) M = fmaxf(M, consume(pmf + (size_t)c * G * 2));
             float L = 0.f;
             for (int c = 0; c < a.chunks; ++c) {
-                const float2 v = pm[(size_t)c * G];
+                const float2 v = make_float2(consume(pmf + (size_t)c * G * 2), consume(pmf + (size_t)c * G * 2 + 1));
                 if (v.y > 0.f) L += v.y * exp2f(v.x - M);
             }
             const float lse2 = M + __log2f(L);
@@ -232,7 +372,19 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeKArgs a) {
         const unsigned long long keylanes =
             C::BPT == 1 ? ~0ull : (C::BPT == 2 ? 0x0000ffff0000ffffull : 0xffffull);
         const uint16_t* vg = a.v + (size_t)group * a.Lmax * D;
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, n * D * 2);
 
+        // Kept keys (union over the group's heads) of all tiles of this wave are
+        // listed in LDS; their per-head weights go to the wave's K stage, which
+        // phase 2 no longer needs (the first CAPW entries; any further ones, in
+        // rows that keep nearly everything, to the workspace slot of the key).
+        // The list is drained once, with U V-row loads in flight per lane.
+        float (*s_wl)[C::GW] = reinterpret_cast<float (*)[C::GW]>(stage);
+        float* ovf = a.ovf_w + (size_t)group * a.Lmax * C::GW;
+        int lcount = 0;
+        const int vlane = (lane % C::LPR) * C::DPL * 2;
+        const int keylane = lane - 16 * cc;      // lane that stands for this lane's key
+        const unsigned long long below_key = keylane == 0 ? 0ull : (~0ull >> (64 - keylane));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int key0 = wbase + t * C::KT;
@@ -253,38 +405,57 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeKArgs a) {
                 if (C::BPT >= 2) any |= __shfl_xor(any, 16);
                 if (C::BPT == 4) any |= __shfl_xor(any, 32);
                 const unsigned long long bal = __ballot(any) & keylanes;
-                const int cnt = __popcll(bal);
-                if (cnt) {
-                    if (hb < C::GW) {
-                        float4 wv = make_float4(w[0], w[1], w[2], w[3]);
-                        *(float4*)&s_w[wave][mykey][hb] = wv;
+                if (any) {
+                    const int idx = lcount + __popcll(bal & below_key);
+                    const float4 wv = make_float4(w[0], w[1], w[2], w[3]);
+                    if (idx < C::CAPW) *(float4*)&s_wl[idx][hb] = wv;
+                    else {
+                        float* dst = &ovf[(size_t)(key0 + mykey) * C::GW + hb];
+                        publish(dst, wv.x); publish(dst + 1, wv.y); publish(dst + 2, wv.z); publish(dst + 3, wv.w);
                     }
-                    if (any && cc == 0) {
-                        const unsigned long long below = (lane == 0) ? 0ull : (bal & (~0ull >> (64 - lane)));
-                        s_list[wave][__popcll(below)] = mykey;
-                    }
-                    ucount += cnt;
-                    const uint16_t* vt = vg + (size_t)key0 * D + (lane & 15) * C::DPL;
-                    for (int e0 = 0; e0 < cnt; e0 += 4) {
-                        const int e = e0 + blk;
-                        const bool act = e < cnt;
-                        const int kp = act ? s_list[wave][e] : 0;
-                        typename VVec<C::DPL>::T raw = *(const typename VVec<C::DPL>::T*)(vt + (size_t)kp * D);
-                        float vf[C::DPL];
-                        unpack_bf16(raw, vf);
-                        float wh[C::GW];
+                    if (cc == 0) s_kl[wave][idx] = (unsigned short)(t * C::KT + mykey);
+                }
+                lcount += __popcll(bal);
+            }
+        }
+        ucount = lcount;
+        wait_lds();
+        {
+            // entries [0, CAPW) read their weights from LDS, later ones from the workspace
+            const int nl = lcount < C::CAPW ? lcount : C::CAPW;
+            if (lcount > C::CAPW) __builtin_amdgcn_s_waitcnt(0x0F70);
+            for (int e0 = 0; e0 < lcount; e0 += C::RPG * C::U) {
+                typename VVec<C::DPL>::T raw[C::U];
+#pragma unroll
+                for (int u = 0; u < C::U; ++u) {
+                    const int e = e0 + u * C::RPG + lane / C::LPR;
+                    const int key = wbase + (e < lcount ? (int)s_kl[wave][e] : 0);
+                    raw[u] = VVec<C::DPL>::load(vrs, key * (D * 2) + vlane, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < C::U; ++u) {
+                    const int e = e0 + u * C::RPG + lane / C::LPR;
+                    float vf[C::DPL];
+                    unpack_bf16(raw[u], vf);
+                    float wh[C::GW];
+                    if (e < nl) {
 #pragma unroll
                         for (int q4 = 0; q4 < C::GW; q4 += 4) {
-                            const float4 x = *(const float4*)&s_w[wave][kp][q4];
+                            const float4 x = *(const float4*)&s_wl[e][q4];
                             wh[q4] = x.x; wh[q4 + 1] = x.y; wh[q4 + 2] = x.z; wh[q4 + 3] = x.w;
                         }
+                    } else if (e < lcount) {
+                        const float* src = ovf + (size_t)(wbase + s_kl[wave][e]) * C::GW;
 #pragma unroll
-                        for (int h = 0; h < G; ++h) {
-                            const float ww = act ? wh[h] : 0.f;
+                        for (int q = 0; q < C::GW; ++q) wh[q] = consume(src + q);
+                    } else {
 #pragma unroll
-                            for (int i = 0; i < C::DPL; ++i) acc[h][i] = fmaf(ww, vf[i], acc[h][i]);
-                        }
+                        for (int q = 0; q < C::GW; ++q) wh[q] = 0.f;
                     }
+#pragma unroll
+                    for (int h = 0; h < G; ++h)
+#pragma unroll
+                        for (int i = 0; i < C::DPL; ++i) acc[h][i] = fmaf(wh[h], vf[i], acc[h][i]);
                 }
             }
         }
@@ -295,11 +466,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeKArgs a) {
 #pragma unroll
             for (int i = 0; i < C::DPL; ++i) {
                 float x = acc[h][i];
-                x += __shfl_xor(x, 16);
+                if (C::LPR == 16) x += __shfl_xor(x, 16);
                 x += __shfl_xor(x, 32);
                 acc[h][i] = x;
             }
-        if (lane < 16) {
+        __syncthreads();                       // every wave is done with its K staging
+        if (lane < C::LPR) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -330,27 +502,27 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeKArgs a) {
             float x = 0.f;
 #pragma unroll
             for (int w = 0; w < C::WAVES; ++w) x += (&s_red[w][0][0])[idx];
-            a.part_out[pbase * G * D + idx] = x;
+            publish(a.part_out + pbase * G * D + idx, x);
         }
         if (tid < G) {
             float m = 0.f; int c = 0;
             for (int w = 0; w < C::WAVES; ++w) { m += s_cm[w][tid]; c += s_cc[w][tid]; }
-            a.part_mass[pbase * G + tid] = m;
-            a.part_cnt[pbase * G + tid] = c;
+            publish(a.part_mass + pbase * G + tid, m);
+            publish_i(a.part_cnt + pbase * G + tid, c);
         }
         if (tid == 0) {
             int u = 0;
             for (int w = 0; w < C::WAVES; ++w) u += s_un[w];
-            a.part_union[pbase] = u;
+            publish_i(a.part_union + pbase, u);
         }
 
         // ---- the last chunk of the group to finish combines
-        __threadfence();
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
-            const int old = atomicAdd(a.counters + 2 * group + 1, 1);
+            const int old = __hip_atomic_fetch_add(a.counters + 2 * group + 1, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
             s_last = (old == a.chunks - 1);
-            if (s_last) __threadfence();
         }
         __syncthreads();
         if (s_last) {
@@ -358,11 +530,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeKArgs a) {
             const bool vmc = (a.flags & 1u) != 0 && !renorm;
             const size_t g0 = (size_t)group * a.chunks;
             if (tid < G) {
-                float m = 0.f; int c = 0;
-                for (int ch = 0; ch < a.chunks; ++ch) {
-                    m += a.part_mass[(g0 + ch) * G + tid];
-                    c += a.part_cnt[(g0 + ch) * G + tid];
-                }
+                const float m = sum_chunks(a.part_mass + g0 * G + tid, G, a.chunks);
+                int c = 0;
+                for (int ch = 0; ch < a.chunks; ++ch) c += consume_i(a.part_cnt + (g0 + ch) * G + tid);
                 s_cm[0][tid] = m;
                 s_cc[0][tid] = c;
                 const size_t o = (size_t)b * a.Hq + (size_t)kv * G + tid;
@@ -371,14 +541,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeKArgs a) {
             }
             if (tid == 0 && a.vrows_read) {
                 int u = 0;
-                for (int ch = 0; ch < a.chunks; ++ch) u += a.part_union[g0 + ch];
+                for (int ch = 0; ch < a.chunks; ++ch) u += consume_i(a.part_union + g0 + ch);
                 a.vrows_read[group] = u;
             }
             __syncthreads();
             for (int idx = tid; idx < G * D; idx += C::THREADS) {
                 const int h = idx / D, dd = idx % D;
-                float x = 0.f;
-                for (int ch = 0; ch < a.chunks; ++ch) x += a.part_out[((g0 + ch) * G) * D + idx];
+                float x = sum_chunks(a.part_out + g0 * G * D + idx, (size_t)G * D, a.chunks);
                 const float mass = s_cm[0][h];
                 if (renorm) x = (s_cc[0][h] > 0) ? x / mass : 0.f;
                 if (vmc) x = fmaf(1.f - mass, a.v_mean[(size_t)group * D + dd], x);
@@ -391,45 +560,67 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeKArgs a) {
         }
         __syncthreads();
     }
+#endif
 }
 
 // ------------------------------------------------------------------ host side
 namespace {
 
-typedef void (*DecodeKernelFn)(DecodeKArgs);
-
 struct Variant {
-    DecodeKernelFn fn;
+    int (*launch)(int grid, hipStream_t stream, const DecodeKArgs& a);
+    int (*resident)(int* per_cu);
     int keys_per_wg;
-    int nt;
 };
 
+// Register tiles per wave offered for each group size: the largest ones are
+// left out where the scores would no longer fit in registers at two waves per
+// SIMD without spilling.
+constexpr int kMaxVariants = 4;
+
+template <int D, int G, int NT>
+int launch_variant(int grid, hipStream_t stream, const DecodeKArgs& a) {
+    hipLaunchKernelGGL((decode_bf16_kernel<D, G, NT>), dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, int G, int NT>
+int resident_variant(int* per_cu) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, (const void*)decode_bf16_kernel<D, G, NT>,
+                                                        256, 0);
+}
+
+template <int D, int G, int NT>
+Variant make_variant() {
+    return {launch_variant<D, G, NT>, resident_variant<D, G, NT>, DecodeCfg<D, G, NT>::KEYS_PER_WG};
+}
+
 template <int D, int G>
-Variant variant_for(int nt_index) {
-    switch (nt_index) {
-        case 0: return {decode_bf16_kernel<D, G, 4>, DecodeCfg<D, G, 4>::KEYS_PER_WG, 4};
-        case 1: return {decode_bf16_kernel<D, G, 8>, DecodeCfg<D, G, 8>::KEYS_PER_WG, 8};
-        case 2: return {decode_bf16_kernel<D, G, 16>, DecodeCfg<D, G, 16>::KEYS_PER_WG, 16};
-        default:
-            if (G == 16) return {decode_bf16_kernel<D, G, 16>, DecodeCfg<D, G, 16>::KEYS_PER_WG, 16};
-            return {decode_bf16_kernel<D, G, (G == 16 ? 16 : 32)>,
-                    DecodeCfg<D, G, (G == 16 ? 16 : 32)>::KEYS_PER_WG, (G == 16 ? 16 : 32)};
-    }
+int variants_for(Variant* out) {
+    int k = 0;
+    out[k++] = make_variant<D, G, 4>();
+    out[k++] = make_variant<D, G, 8>();
+    if constexpr (G != 16) out[k++] = make_variant<D, G, 16>();
+    if constexpr (G == 1 || G == 8) out[k++] = make_variant<D, G, 32>();
+    return k;
 }
 
-template <int D>
-Variant pick_variant(int G, int nt_index) {
+int variants(int d, int G, Variant* out) {
+    if (d == 64) {
+        switch (G) {
+            case 1: return variants_for<64, 1>(out);
+            case 2: return variants_for<64, 2>(out);
+            case 4: return variants_for<64, 4>(out);
+            case 8: return variants_for<64, 8>(out);
+            default: return variants_for<64, 16>(out);
+        }
+    }
     switch (G) {
-        case 1: return variant_for<D, 1>(nt_index);
-        case 2: return variant_for<D, 2>(nt_index);
-        case 4: return variant_for<D, 4>(nt_index);
-        case 8: return variant_for<D, 8>(nt_index);
-        default: return variant_for<D, 16>(nt_index);
+        case 1: return variants_for<128, 1>(out);
+        case 2: return variants_for<128, 2>(out);
+        case 4: return variants_for<128, 4>(out);
+        case 8: return variants_for<128, 8>(out);
+        default: return variants_for<128, 16>(out);
     }
-}
-
-Variant pick(int d, int G, int nt_index) {
-    return d == 64 ? pick_variant<64>(G, nt_index) : pick_variant<128>(G, nt_index);
 }
 
 int keys_per_wg_min(int G) {
@@ -437,11 +628,24 @@ int keys_per_wg_min(int G) {
     return 4 * 4 * 16 * P;
 }
 
-int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    return cus;
+// Resident workgroups per CU of each kernel variant and the CU count, per
+// device, computed once (the occupancy query is slow next to a decode step).
+struct DeviceInfo {
+    int cus = 0;
+    int occ[2][17][kMaxVariants] = {};   // [d==128][G][variant] -> workgroups per CU (0 = unknown)
+};
+DeviceInfo g_dev[16];
+
+int resident_per_cu(int dev, int d, int G, int vi, const Variant& v, int* out) {
+    int& slot = g_dev[dev].occ[d == 128][G][vi];
+    if (slot == 0) {
+        int per_cu = 0;
+        const int e = v.resident(&per_cu);
+        if (e != hipSuccess) return e;
+        slot = per_cu > 0 ? per_cu : -1;
+    }
+    *out = slot > 0 ? slot : 0;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -461,7 +665,8 @@ size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lmax, int d) {
     bytes += pc * G * sizeof(float);
     bytes += pc * G * sizeof(int);
     bytes += pc * sizeof(int);
-    return bytes + 256;
+    bytes += groups * (size_t)Lmax * (G < 4 ? 4 : G) * sizeof(float);   // weight overflow slots
+    return bytes + 1024;
 }
 
 // Spin limit of the in-kernel exchange; a host test may lower it.
@@ -471,23 +676,34 @@ void decode_set_spin_limit(unsigned v) { g_spin_limit = v; }
 int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     const int G = p.Hq / p.Hkv;
     const int groups = p.B * p.Hkv;
-    const int cus = device_cus();
-    if (cus <= 0) return hipErrorNoDevice;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
+    if (g_dev[dev].cus == 0) {
+        e = hipDeviceGetAttribute(&g_dev[dev].cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
+    const int cus = g_dev[dev].cus;
 
-    // choose the smallest register footprint whose work fits in one resident round
+    // The smallest register footprint whose work fits in one resident round;
+    // otherwise the largest (fewest rounds).  Every workgroup of the grid is
+    // resident at once (grid <= resident capacity), so the chunks of a group
+    // that wait for each other in the exchange always run concurrently.
+    Variant vs[kMaxVariants];
+    const int nv = variants(p.d, G, vs);
     Variant v{};
     int chunks = 0, capacity = 0;
-    for (int ni = 0; ni < 4; ++ni) {
-        Variant cand = pick(p.d, G, ni);
+    for (int vi = 0; vi < nv; ++vi) {
         int per_cu = 0;
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)cand.fn, 256, 0);
+        e = (hipError_t)resident_per_cu(dev, p.d, G, vi, vs[vi], &per_cu);
         if (e != hipSuccess) return e;
-        const int cap = per_cu * cus;
-        const int ch = (p.Lmax + cand.keys_per_wg - 1) / cand.keys_per_wg;
-        v = cand; chunks = ch; capacity = cap;
-        if ((long long)ch * groups <= cap) break;
+        v = vs[vi];
+        capacity = per_cu * cus;
+        chunks = (p.Lmax + v.keys_per_wg - 1) / v.keys_per_wg;
+        if ((long long)chunks * groups <= capacity) break;
     }
-    if (chunks > capacity || capacity <= 0) return hipErrorInvalidConfiguration;
+    if (capacity <= 0 || chunks > capacity) return hipErrorInvalidConfiguration;
     const int items = chunks * groups;
     const int grid = std::min(items, (capacity / chunks) * chunks);
 
@@ -507,6 +723,8 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     a.part_mass = (float*)(ws + off); off += pc * G * sizeof(float);
     a.part_cnt = (int*)(ws + off); off += pc * G * sizeof(int);
     a.part_union = (int*)(ws + off); off += pc * sizeof(int);
+    off = (off + 255) & ~(size_t)255;
+    a.ovf_w = (float*)(ws + off); off += (size_t)groups * p.Lmax * (G < 4 ? 4 : G) * sizeof(float);
     if (off > p.ws_bytes) return hipErrorInvalidValue;
     a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Lmax = p.Lmax; a.n_rows = p.n_rows;
     a.chunks = chunks; a.items = items;
@@ -514,8 +732,7 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     a.flags = p.flags;
     a.spin_limit = g_spin_limit;
 
-    void* args[] = {&a};
-    return hipLaunchCooperativeKernel((const void*)v.fn, dim3(grid), dim3(256), args, 0, stream);
+    return v.launch(grid, stream, a);
 }
 
 }  // namespace topth

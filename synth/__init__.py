@@ -6,5 +6,5 @@ and the HIP path can both be fed from it without sharing any of the method.
 """
 from .gen import (  # noqa: F401
     CONFIG_IDS, ROLE_TEST, ROLE_CALIB, ROLE_PROBE, seed_of, attention_inputs,
-    batch_of_sequences, to_f64,
+    batch_of_sequences, attention_inputs_device, to_f64,
 )

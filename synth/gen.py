@@ -86,6 +86,29 @@ def batch_of_sequences(config_id: int, role: int, layer: int, first: int, count:
     return q, k, v
 
 
+def attention_inputs_device(config_id: int, role: int, layer: int, index: int, *,
+                            B: int, Hq: int, Hkv: int, Lq: int, Lk: int, d: int,
+                            n_sinks: int = 1, dtype: torch.dtype = torch.bfloat16,
+                            device="cuda", with_v: bool = True):
+    """Same recipe as ``attention_inputs`` drawn on the GPU with torch's device
+    generator (float32 draws, so the values differ from the CPU stream; the
+    distribution is the same).  Used where the CPU draw would dominate set-up
+    time (large calibration sets)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_of(config_id, role, layer, index))
+    u = torch.full((d,), 1.0 / float(np.sqrt(d)), device=device)
+    k = torch.randn((B, Hkv, Lk, d), generator=g, device=device)
+    lam = torch.exp(0.5 * torch.randn((B, Hkv, Lk, 1), generator=g, device=device))
+    k = k * lam
+    ns = min(n_sinks, Lk)
+    if ns > 0:
+        k[:, :, :ns, :] += 3.0 * u
+    q = torch.randn((B, Hq, Lq, d), generator=g, device=device) + u
+    v = torch.randn((B, Hkv, Lk, d), generator=g, device=device) if with_v else None
+    cast = (lambda t: t) if dtype == torch.float32 else (lambda t: t.to(dtype))
+    return cast(q).contiguous(), cast(k).contiguous(), None if v is None else cast(v).contiguous()
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a float32/bfloat16 CPU tensor."""
     return t.detach().to(torch.float64).cpu().numpy()

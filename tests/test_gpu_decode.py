@@ -190,3 +190,42 @@ def test_decode_70b_32k_full_size():
     q, k, v, theta, vm = make_case(64, 8, 128, 32768, lens, k=256, n_cal=4, cfg=cfg, n_sinks=4)
     g = run_decode(q, k, v, lens, theta, vm, tt.TOPTH_VMC)
     compare_decode(g, q, k, v, lens, theta, vm, tt.TOPTH_VMC, torch.bfloat16)
+
+
+def test_decode_graph_replay_matches_eager():
+    """Several decode steps captured in one HIP graph: every replay (with eager
+    work and synchronisations in between) reproduces the eager results."""
+    dev = device()
+    Hq, Hkv, d, n = 16, 2, 128, 1200
+    cases = [make_case(Hq, Hkv, d, n, [n, 700], seed_index=10 + i) for i in range(3)]
+    lens = torch.tensor([n, 700], dtype=torch.int32, device=dev)
+    ws = tt.workspace(tt.TOPTH_OP_DECODE, 2, Hq, Hkv, 1, n, d)
+    ins, outs = [], []
+    for q, k, v, theta, vm in cases:
+        ins.append((q.to(dev), k.to(dev), v.to(dev), torch.tensor(theta, dtype=torch.float32, device=dev),
+                    torch.tensor(vm, dtype=torch.float32, device=dev)))
+        outs.append((torch.empty(2, Hq, d, dtype=torch.bfloat16, device=dev),
+                     torch.empty(2, Hq, dtype=torch.int32, device=dev)))
+
+    def run_all():
+        for (q, k, v, th, vm), (o, kc) in zip(ins, outs):
+            tt.topth_decode(q, k, v, lens, th, o, ws, scale=1.0 / np.sqrt(d), flags=tt.TOPTH_VMC,
+                            v_mean=vm, kept_count=kc)
+
+    run_all()
+    torch.cuda.synchronize()
+    eager = [(o.clone(), kc.clone()) for o, kc in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_all()
+    for rep in range(4):
+        for o, kc in outs:
+            o.zero_(); kc.zero_()
+        junk = torch.randn(1 << 20, device=dev).sum()      # unrelated eager work in between
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for (o, kc), (eo, ekc) in zip(outs, eager):
+            assert torch.equal(o, eo), f"replay {rep}: output differs"
+            assert torch.equal(kc, ekc), f"replay {rep}: kept counts differ"
+    assert int(ws[:4].view(torch.int32)[0].item()) == 0
