@@ -44,6 +44,7 @@ struct DecodeKArgs {
     float xscale;
     unsigned flags;
     unsigned spin_limit;
+    int xcd_map;       // 1: chunks of a group on one XCD (grid and items multiples of 8 * chunks)
 };
 
 template <int D, int G, int NT>
@@ -61,13 +62,12 @@ struct DecodeCfg {
     static constexpr int RPG = 64 / LPR;       // V rows per wave gather instruction
     static constexpr int DPL = D / LPR;        // V dims per lane in the gather
     static constexpr int WKEYS = NT * KT;      // keys of one wave
-    static constexpr int U = G >= 16 ? 4 : 8;  // V-row loads in flight per lane while draining
     static constexpr int CPR = D / 8;          // 16-byte chunks per K row
     static constexpr int RPI = 64 / CPR;       // K rows per wave load instruction
     static constexpr int NLD = KT / RPI;       // load instructions per wave tile
     static constexpr int STAGE_BYTES = KT * D * 2;              // one staged wave tile
     static constexpr int NBUF = P == 4 ? 1 : 2;                 // stage buffers per wave
-    static constexpr int CAPW = NBUF * STAGE_BYTES / (GW * 4);  // kept-key weights held in LDS per wave
+    static constexpr int CAPW = (NBUF * STAGE_BYTES - 4096) / (GW * 4);  // kept-key weights in LDS per wave
     static constexpr int RED_BYTES = WAVES * G * D * 4;         // output partials per workgroup
     static constexpr int KBUF_BYTES =
         WAVES * NBUF * STAGE_BYTES > RED_BYTES ? WAVES * NBUF * STAGE_BYTES : RED_BYTES;
@@ -114,6 +114,10 @@ __device__ __forceinline__ float sum_chunks(const float* base, size_t stride, in
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0,15:14], expcnt[6:4], lgkmcnt[11:8])
+// v_exp_f32 as is: results below the normal range flush to zero, which only
+// affects probabilities under 2^-126.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
 template <int N>
@@ -198,7 +202,16 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeKArgs a) {
     }
     for (int t = tid; t < D + 8; t += C::THREADS) s_q[G][t] = 0;
 
-    for (int item = blockIdx.x; item < a.items; item += gridDim.x) {
+    for (int slot = blockIdx.x; slot < a.items; slot += gridDim.x) {
+        // Workgroups are dealt to the 8 XCDs round-robin by index; when the grid
+        // allows it, all chunks of a group go to workgroups of one XCD so that
+        // they stream under the same conditions and reach the exchange together.
+        int item = slot;
+        if (a.xcd_map) {
+            const int per_xcd = gridDim.x / 8;
+            const int round = slot / gridDim.x, r = slot % gridDim.x;
+            item = round * gridDim.x + (r % 8) * per_xcd + r / 8;
+        }
         const int group = item / a.chunks, chunk = item % a.chunks;
         const int b = group / a.Hkv, kv = group % a.Hkv;
         const int n = min(max(a.seq_lens[b], 1), a.Lmax);   // lengths outside [1, Lmax] are clamped
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeKArgs a) {
             float l = 0.f;
             if (m != NEG_INF) {
 #pragma unroll
-                for (int t = 0; t < NT; ++t) l += exp2f(sc[t][r] - m);
+                for (int t = 0; t < NT; ++t) l += fast_exp2(sc[t][r] - m);
             }
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o);
@@ -360,8 +373,6 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeKArgs a) {
             Tr[r] = hv ? s_T[hb + r] : INFINITY;
             Lr[r] = hv ? s_lse[hb + r] : 0.f;
         }
-        float kmass[4] = {0.f, 0.f, 0.f, 0.f};
-        int kcnt[4] = {0, 0, 0, 0};
         int ucount = 0;
         float acc[G][C::DPL];
 #pragma unroll
@@ -375,39 +386,44 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeKArgs a) {
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, n * D * 2);
 
         // Kept keys (union over the group's heads) of all tiles of this wave are
-        // listed in LDS; their per-head weights go to the wave's K stage, which
-        // phase 2 no longer needs (the first CAPW entries; any further ones, in
-        // rows that keep nearly everything, to the workspace slot of the key).
-        // The list is drained once, with U V-row loads in flight per lane.
+        // listed in LDS with their per-head scores, which go to the wave's K
+        // stage (phase 2 no longer needs it): the first CAPW entries there, any
+        // further ones -- rows that keep nearly everything -- to the workspace
+        // slot of the key.  Weights, kept counts and kept mass are then formed
+        // once per listed entry, and the list is drained.
         float (*s_wl)[C::GW] = reinterpret_cast<float (*)[C::GW]>(stage);
         float* ovf = a.ovf_w + (size_t)group * a.Lmax * C::GW;
         int lcount = 0;
         const int vlane = (lane % C::LPR) * C::DPL * 2;
         const int keylane = lane - 16 * cc;      // lane that stands for this lane's key
         const unsigned long long below_key = keylane == 0 ? 0ull : (~0ull >> (64 - keylane));
+        unsigned char* kmask = a.kept_mask ? a.kept_mask + ((size_t)b * a.Hq + (size_t)kv * G) * a.Lmax : nullptr;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int key0 = wbase + t * C::KT;
             if (key0 < n) {
-                float w[4];
-                int any = 0;
+                bool kp[4];
+                bool own = false;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const bool kp = sc[t][r] >= Tr[r];
-                    w[r] = kp ? exp2f(sc[t][r] - Lr[r]) : 0.f;
-                    kcnt[r] += kp ? 1 : 0;
-                    kmass[r] += w[r];
-                    any |= kp ? 1 : 0;
-                    if (a.kept_mask && hb + r < G && key0 + mykey < a.Lmax)
-                        a.kept_mask[((size_t)b * a.Hq + (size_t)kv * G + hb + r) * a.Lmax + key0 + mykey] =
-                            kp ? 1 : 0;
+                    kp[r] = sc[t][r] >= Tr[r];
+                    own |= kp[r];
                 }
-                if (C::BPT >= 2) any |= __shfl_xor(any, 16);
-                if (C::BPT == 4) any |= __shfl_xor(any, 32);
-                const unsigned long long bal = __ballot(any) & keylanes;
+                if (kmask) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (hb + r < G && key0 + mykey < a.Lmax)
+                            kmask[(size_t)(hb + r) * a.Lmax + key0 + mykey] = kp[r] ? 1 : 0;
+                }
+                // union over the key's heads: the lanes of one key sit 16 lanes apart
+                unsigned long long ub = __ballot(own);
+                if (C::BPT >= 2) ub |= ub >> 16;
+                if (C::BPT == 4) ub |= ub >> 32;
+                const unsigned long long bal = ub & keylanes;
+                const int any = (int)((bal >> keylane) & 1ull);
                 if (any) {
                     const int idx = lcount + __popcll(bal & below_key);
-                    const float4 wv = make_float4(w[0], w[1], w[2], w[3]);
+                    const float4 wv = make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]);
                     if (idx < C::CAPW) *(float4*)&s_wl[idx][hb] = wv;
                     else {
                         float* dst = &ovf[(size_t)(key0 + mykey) * C::GW + hb];
@@ -420,23 +436,65 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeKArgs a) {
         }
         ucount = lcount;
         wait_lds();
-        {
-            // entries [0, CAPW) read their weights from LDS, later ones from the workspace
-            const int nl = lcount < C::CAPW ? lcount : C::CAPW;
-            if (lcount > C::CAPW) __builtin_amdgcn_s_waitcnt(0x0F70);
-            for (int e0 = 0; e0 < lcount; e0 += C::RPG * C::U) {
-                typename VVec<C::DPL>::T raw[C::U];
+        // weights of the listed entries, one entry per lane: exact SDC keeps the
+        // full softmax denominator, so the weight of a kept (key, head) is s
+        float kmass_h[G];
+        int kcnt_h[G];
 #pragma unroll
-                for (int u = 0; u < C::U; ++u) {
-                    const int e = e0 + u * C::RPG + lane / C::LPR;
-                    const int key = wbase + (e < lcount ? (int)s_kl[wave][e] : 0);
-                    raw[u] = VVec<C::DPL>::load(vrs, key * (D * 2) + vlane, 0);
+        for (int h = 0; h < G; ++h) { kmass_h[h] = 0.f; kcnt_h[h] = 0; }
+        {
+            const int nl = lcount < C::CAPW ? lcount : C::CAPW;
+            for (int e = lane; e < lcount; e += 64) {
+                float x[C::GW];
+                float* src = e < nl ? &s_wl[e][0] : ovf + (size_t)(wbase + s_kl[wave][e]) * C::GW;
+#pragma unroll
+                for (int h = 0; h < C::GW; ++h) x[h] = e < nl ? src[h] : consume(src + h);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const bool kp = x[h] >= s_T[h];
+                    x[h] = kp ? fast_exp2(x[h] - s_lse[h]) : 0.f;
+                    kmass_h[h] += x[h];
+                    kcnt_h[h] += kp ? 1 : 0;
                 }
 #pragma unroll
-                for (int u = 0; u < C::U; ++u) {
-                    const int e = e0 + u * C::RPG + lane / C::LPR;
+                for (int h = G; h < C::GW; ++h) x[h] = 0.f;
+                if (e < nl) {
+#pragma unroll
+                    for (int q4 = 0; q4 < C::GW; q4 += 4)
+                        *(float4*)&src[q4] = make_float4(x[q4], x[q4 + 1], x[q4 + 2], x[q4 + 3]);
+                } else {
+#pragma unroll
+                    for (int h = 0; h < C::GW; ++h) publish(src + h, x[h]);
+                }
+            }
+        }
+        wait_lds();
+        {
+            // The kept V rows are fetched with buffer_load ... lds into the part
+            // of the stage above the weights (one 1 KiB instruction per RPI rows,
+            // all of a batch in flight at once), then accumulated from LDS.
+            // Weights of entries [0, CAPW) are in LDS, later ones in the workspace.
+            const int nl = lcount < C::CAPW ? lcount : C::CAPW;
+            const int wbytes = (nl * C::GW * 4 + 1023) & ~1023;
+            unsigned char* vbuf = stage + wbytes;
+            const int vrows_cap = ((C::NBUF * C::STAGE_BYTES - wbytes) / (D * 2)) / C::RPI * C::RPI;
+            const int vlds = (lane % C::LPR) * C::DPL * 2;            // this lane's bytes in a row
+            for (int b0 = 0; b0 < lcount; b0 += vrows_cap) {
+                const int nrows = lcount - b0 < vrows_cap ? lcount - b0 : vrows_cap;
+                for (int i = 0; i * C::RPI < nrows; ++i) {
+                    const int e = b0 + i * C::RPI + lane / C::CPR;
+                    const int key = wbase + (e < lcount ? (int)s_kl[wave][e] : 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        vrs, (__attribute__((address_space(3))) void*)(vbuf + i * 1024), 16,
+                        key * (D * 2) + (lane % C::CPR) * 16, 0, 0, 0);
+                }
+                wait_vmem();
+                for (int j = lane / C::LPR; j < nrows; j += C::RPG) {
+                    const int e = b0 + j;
+                    const typename VVec<C::DPL>::T raw =
+                        *(const typename VVec<C::DPL>::T*)(vbuf + j * (D * 2) + vlds);
                     float vf[C::DPL];
-                    unpack_bf16(raw[u], vf);
+                    unpack_bf16(raw, vf);
                     float wh[C::GW];
                     if (e < nl) {
 #pragma unroll
@@ -444,19 +502,17 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeKArgs a) {
                             const float4 x = *(const float4*)&s_wl[e][q4];
                             wh[q4] = x.x; wh[q4 + 1] = x.y; wh[q4 + 2] = x.z; wh[q4 + 3] = x.w;
                         }
-                    } else if (e < lcount) {
+                    } else {
                         const float* src = ovf + (size_t)(wbase + s_kl[wave][e]) * C::GW;
 #pragma unroll
                         for (int q = 0; q < C::GW; ++q) wh[q] = consume(src + q);
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < C::GW; ++q) wh[q] = 0.f;
                     }
 #pragma unroll
                     for (int h = 0; h < G; ++h)
 #pragma unroll
                         for (int i = 0; i < C::DPL; ++i) acc[h][i] = fmaf(wh[h], vf[i], acc[h][i]);
                 }
+                wait_lds();                                   // rows consumed before the next batch
             }
         }
 
@@ -478,22 +534,10 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeKArgs a) {
                 for (int i = 0; i < C::DPL; ++i) s_red[wave][h][lane * C::DPL + i] = acc[h][i];
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float m = kmass[r];
-            int c = kcnt[r];
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) { m += __shfl_xor(m, o); c += __shfl_xor(c, o); }
-            if (C::BPT == 1) {
-                m += __shfl_xor(m, 16); c += __shfl_xor(c, 16);
-                m += __shfl_xor(m, 32); c += __shfl_xor(c, 32);
-            }
-            if (C::BPT == 2) { m += __shfl_xor(m, 32); c += __shfl_xor(c, 32); }
-            kmass[r] = m; kcnt[r] = c;
-        }
-        if ((lane & 15) == 0 && tt == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (hb + r < G) { s_cm[wave][hb + r] = kmass[r]; s_cc[wave][hb + r] = kcnt[r]; }
+        for (int h = 0; h < G; ++h) {
+            const float m = wave_sum(kmass_h[h]);
+            const int c = wave_sum_i(kcnt_h[h]);
+            if (lane == 0) { s_cm[wave][h] = m; s_cc[wave][h] = c; }
         }
         if (lane == 0) s_un[wave] = ucount;
         __syncthreads();
@@ -731,6 +775,7 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     a.xscale = p.scale * kLog2e;
     a.flags = p.flags;
     a.spin_limit = g_spin_limit;
+    a.xcd_map = (grid % (8 * chunks) == 0 && items % grid == 0) ? 1 : 0;
 
     return v.launch(grid, stream, a);
 }
