@@ -15,6 +15,8 @@ int launch_decode_rowwise(const DecodeParams& p, uint32_t* masks_ws, hipStream_t
 size_t decode_rowwise_ws_bytes(int B, int Hq, int Lmax);
 int rowwise_max_keys();
 int launch_prefill_rowwise(const PrefillParams& p, float* mu_ws, hipStream_t s);
+bool prefill_bf16_supported(int d, int G);
+int launch_prefill_bf16(const PrefillParams& p, float* mu_ws, hipStream_t s);
 int launch_calibrate_rowwise(const CalibParams& p, float* samples_ws, hipStream_t s);
 }  // namespace topth
 
@@ -93,7 +95,7 @@ int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq
                     void* ws, size_t ws_bytes, void* stream) {
     if (!q || !k || !ks || !sum || !sumsq || !count) return TOPTH_EINVAL;
     if (bad_dims(S, Hq, Hkv, Lq, d) || bad_dtype(dtype) || Lk <= 0 || n_rows <= 0) return TOPTH_EINVAL;
-    if (!isfinite(scale) || q_pos0 < 0 || q_pos0 + Lq > Lk) return TOPTH_EINVAL;
+    if (!isfinite(scale) || !(scale > 0.0f) || q_pos0 < 0 || q_pos0 + Lq > Lk) return TOPTH_EINVAL;
     if (n_k < 1 || n_k > TOPTH_MAX_NK) return TOPTH_EINVAL;
     for (int t = 0; t < n_k; ++t)
         if (ks[t] < 1) return TOPTH_EINVAL;
@@ -129,9 +131,11 @@ int topth_prefill(const void* q, const void* k, const void* v, int B, int Hq, in
                   unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream) {
     if (!q || !k || !v || !theta || !out) return TOPTH_EINVAL;
     if (bad_dims(B, Hq, Hkv, L, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
-    if (!isfinite(scale) || (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE))) return TOPTH_EINVAL;
+    if (!isfinite(scale) || !(scale > 0.0f) || (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE))) return TOPTH_EINVAL;
     if (too_big((long long)B * Hq * L, d)) return TOPTH_EUNSUPPORTED;
-    if (L > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
+    if (dtype == TOPTH_F32 && L > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
+    if (dtype == TOPTH_BF16 && (!prefill_bf16_supported(d, Hq / Hkv) || (long long)L * d * 2 >= INT_MAX))
+        return TOPTH_EUNSUPPORTED;
     const bool vmc = (flags & TOPTH_VMC) && !(flags & TOPTH_SDC_NONE);
     if (vmc) {
         if (!ws) return TOPTH_EWORKSPACE;
@@ -142,6 +146,7 @@ int topth_prefill(const void* q, const void* k, const void* v, int B, int Hq, in
     p.scale = scale; p.theta = theta; p.n_rows = n_rows; p.flags = flags;
     p.out = out; p.kept_count = kept_count; p.beta = beta; p.kept_mask = kept_mask;
     p.ws = ws; p.ws_bytes = ws_bytes;
+    if (dtype == TOPTH_BF16) return map_hip(launch_prefill_bf16(p, (float*)ws, (hipStream_t)stream));
     return map_hip(launch_prefill_rowwise(p, (float*)ws, (hipStream_t)stream));
 }
 
@@ -152,7 +157,7 @@ int topth_decode(const void* q, const void* k_cache, const void* v_cache, const 
                  unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream) {
     if (!q || !k_cache || !v_cache || !seq_lens || !theta || !out) return TOPTH_EINVAL;
     if (bad_dims(B, Hq, Hkv, Lmax, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
-    if (!isfinite(scale) || (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE))) return TOPTH_EINVAL;
+    if (!isfinite(scale) || !(scale > 0.0f) || (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE))) return TOPTH_EINVAL;
     if ((flags & TOPTH_VMC) && !(flags & TOPTH_SDC_NONE) && !v_mean) return TOPTH_EINVAL;
     if (too_big((long long)B * Hkv * Lmax, d)) return TOPTH_EUNSUPPORTED;
     if ((long long)B * Hkv > kWsMaxGroups) return TOPTH_EUNSUPPORTED;
@@ -165,7 +170,7 @@ int topth_decode(const void* q, const void* k_cache, const void* v_cache, const 
     p.out = out; p.kept_count = kept_count; p.beta = beta; p.vrows_read = vrows_read;
     p.kept_mask = kept_mask; p.ws = ws; p.ws_bytes = ws_bytes;
     if (dtype == TOPTH_BF16) {
-        if (!decode_bf16_supported(d, Hq / Hkv)) return TOPTH_EUNSUPPORTED;
+        if (!decode_bf16_supported(d, Hq / Hkv) || (long long)Lmax * d * 2 >= INT_MAX) return TOPTH_EUNSUPPORTED;
         return map_hip(launch_decode_bf16(p, (hipStream_t)stream));
     }
     if (Lmax > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;

@@ -1,0 +1,394 @@
+// Top-theta prefill for bfloat16 inputs on gfx950.
+//
+// Causal attention of every query row p over keys 0..p ("Top-Theta Attention:
+// Sparsifying Transformers by Compensated Thresholding", Eq. 1-3 with the
+// 1/sqrt(d) scale and causal mask of Sec. 2.2), keeping the post-softmax
+// elements s >= theta[h][p] (Sec. 3), weighting them by s itself (exact SDC,
+// Sec. 3.2.1 Eq. 4) and optionally adding beta * mu_p (VMC, Sec. 3.2.2).
+//
+// Post-softmax thresholding needs the exact row log-sum-exp before the first
+// compare, so every query tile sweeps its causal key range twice:
+//   sweep A  S^T = K Q^T on MFMA; lane-local online (max, sum of exp2); the
+//            four lanes of a row combine into the row LSE at the end.
+//   sweep B  S^T again; compare x >= log2(theta) + lse2; P = exp2(x - lse2)
+//            for kept elements (0 otherwise) is taken straight from the
+//            accumulator registers as the B operand of O^T += V^T P^T, split
+//            into a bf16 high part and a bf16 remainder (two MFMAs).
+// Workgroup: one KV head's query tile, 4 waves, each wave one query head and
+// 32 rows; K tiles of 64 keys are staged by buffer_load...lds into a swizzled,
+// double-buffered LDS tile shared by the waves; V tiles are staged transposed.
+#include "topth_internal.h"
+
+#include <math.h>
+
+namespace topth {
+
+struct PrefillKArgs {
+    const uint16_t* q; const uint16_t* k; const uint16_t* v;
+    const float* theta; const float* mu;
+    uint16_t* out; int* kept_count; float* beta; unsigned char* kept_mask;
+    int B, Hq, Hkv, L, n_rows;
+    float xscale;
+    unsigned flags;
+};
+
+template <int D, int G>
+struct PrefillCfg {
+    static constexpr int HPW = G < 4 ? G : 4;       // query heads per workgroup
+    static constexpr int RBW = 4 / HPW;             // 32-row blocks per workgroup
+    static constexpr int BMT = 32 * RBW;            // query rows per workgroup
+    static constexpr int BN = 64;                   // keys per tile
+    static constexpr int KSTEPS = D / 32;           // MFMA steps over the head dimension
+    static constexpr int DB = D / 16;               // 16-wide dimension blocks of the output
+    static constexpr int CPR = D / 8;               // 16-byte chunks per K row
+    static constexpr int RPI = 64 / CPR;            // K rows per 1 KiB load instruction
+    static constexpr int KTILE = BN * D * 2;        // bytes of one K tile
+    static constexpr int NLD = KTILE / 1024 / 4;    // load instructions per wave per K tile
+    static constexpr int VT_STRIDE = BN + 4;        // bf16 elements per transposed V row (136 B)
+    static constexpr int VCH = BN * CPR / 256;      // V chunks per thread per tile
+};
+
+__device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ void pf_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float pf_f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats to packed bfloat16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+    const pf_f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, pf_bf16x2));
+}
+// P = hi + lo with both parts in bfloat16: the P V product is taken as two bf16
+// MFMAs, which keeps about 16 significant bits of every weight
+__device__ __forceinline__ void split_bf16x2(float a, float b, unsigned& hi, unsigned& lo) {
+    hi = pack_bf16x2(a, b);
+    lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+template <int D, int G, bool MASK>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
+    using C = PrefillCfg<D, G>;
+    __shared__ __attribute__((aligned(16))) unsigned char s_k[2][C::KTILE];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[D][C::VT_STRIDE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lq = lane >> 4;
+    const float NEG_INF = -INFINITY;
+
+    // longest query tiles first: they have the most keys
+    const int nqt = (a.L + C::BMT - 1) / C::BMT;
+    const int qt = nqt - 1 - blockIdx.x;
+    const int kv = blockIdx.y / (G / C::HPW);
+    const int hblk = blockIdx.y % (G / C::HPW);
+    const int b = blockIdx.z;
+    const int h = kv * G + hblk * C::HPW + wave % C::HPW;
+    const int row0 = qt * C::BMT + (wave / C::HPW) * 32;    // first row of this wave
+    const int wg_row_end = min(a.L, (qt + 1) * C::BMT);     // rows of the workgroup end here
+    const int ntiles = (wg_row_end + C::BN - 1) / C::BN;    // causal key tiles of the workgroup
+
+    const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kv) * (size_t)a.L * D;
+    const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kv) * (size_t)a.L * D;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kg), 0, a.L * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vg), 0, a.L * D * 2, 0x00020000);
+
+    // ---- Q^T fragments (B operand): query row row0 + 16 qb + l16, dims 32 s + 8 lq + e
+    bf16x8 qf[2][C::KSTEPS];
+    {
+        const uint16_t* qg = a.q + ((size_t)b * a.Hq + h) * (size_t)a.L * D;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int r = min(row0 + 16 * qb + l16, a.L - 1);
+#pragma unroll
+            for (int s = 0; s < C::KSTEPS; ++s)
+                qf[qb][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qg + (size_t)r * D + 32 * s + 8 * lq));
+        }
+    }
+
+    // ---- K tile staging: each wave moves a quarter of the tile; source offsets
+    // apply an XOR swizzle so that MFMA-layout reads are bank-conflict free
+    constexpr int NVO = C::CPR / C::RPI > 0 ? C::CPR / C::RPI : 1;
+    int vo[NVO];
+#pragma unroll
+    for (int j = 0; j < NVO; ++j) {
+        const int row = j * C::RPI + lane / C::CPR;
+        vo[j] = (lane / C::CPR) * (D * 2) + (((lane % C::CPR) ^ (row % C::CPR)) * 16);
+    }
+    auto issue_k = [&](int tile, int buf) {
+#pragma unroll
+        for (int i = 0; i < C::NLD; ++i) {
+            const int li = wave * C::NLD + i;          // load instruction of the tile
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                krs, (__attribute__((address_space(3))) void*)(&s_k[buf][li * 1024]), 16,
+                vo[li % NVO], (tile * C::BN + li * C::RPI) * (D * 2), 0, 0);
+        }
+    };
+    // S^T block (keys 16 kb + 4 lq + r, query rows 16 qb + l16) of one K tile
+    auto scores = [&](int buf, f32x4 (&st)[2][4]) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int key = 16 * kb + l16;              // A operand row: key of the tile
+            const unsigned char* srow = &s_k[buf][((key / C::RPI) * 64 + (key % C::RPI) * C::CPR) * 16];
+            const int swz = key % C::CPR;
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < C::KSTEPS; ++s) {
+                const int c = 4 * s + lq;               // dims 32 s + 8 lq .. + 7
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(srow + (c ^ swz) * 16));
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][s], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][s], acc1, 0, 0, 0);
+            }
+            st[0][kb] = acc0;
+            st[1][kb] = acc1;
+        }
+    };
+
+    // ======================= sweep A: row log-sum-exp =========================
+    float m_l[2] = {NEG_INF, NEG_INF}, l_l[2] = {0.f, 0.f};
+    issue_k(0, 0);
+    for (int j = 0; j < ntiles; ++j) {
+        pf_wait_vmem();
+        __syncthreads();                                   // tile j complete; tile j-1 no longer read
+        if (j + 1 < ntiles) issue_k(j + 1, (j + 1) & 1);
+        f32x4 st[2][4];
+        scores(j & 1, st);
+        // statistics in raw score units (the scale is positive): max, then
+        // sum of exp2(scale * (s - max)); only tiles that cross the diagonal mask
+        const bool diag = j * C::BN + C::BN - 1 > row0;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = row0 + 16 * qb + l16;
+            if (diag) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (j * C::BN + 16 * kb + 4 * lq + r > row) st[qb][kb][r] = NEG_INF;
+            }
+            float tmax = NEG_INF;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[qb][kb][r]);
+            const float mn = fmaxf(m_l[qb], tmax);
+            if (mn != NEG_INF) {
+                const float nmc = -mn * a.xscale;
+                float sum = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sum += pf_exp2(fmaf(st[qb][kb][r], a.xscale, nmc));
+                l_l[qb] = l_l[qb] * pf_exp2((m_l[qb] - mn) * a.xscale) + sum;
+                m_l[qb] = mn;
+            }
+        }
+    }
+    // the four lanes of a row (16 lanes apart) hold partial statistics
+    float lse2[2], thr[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float M = m_l[qb];                                 // raw units
+        M = fmaxf(M, __shfl_xor(M, 16));
+        M = fmaxf(M, __shfl_xor(M, 32));
+        float part = (m_l[qb] == NEG_INF) ? 0.f : l_l[qb] * pf_exp2((m_l[qb] - M) * a.xscale);
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        lse2[qb] = M * a.xscale + __log2f(part);           // log2 domain
+        const int row = min(row0 + 16 * qb + l16, a.L - 1);
+        const float th = a.theta[(size_t)h * a.n_rows + min(row, a.n_rows - 1)];
+        // keep  s >= theta  <=>  scale * raw >= log2(theta) + lse2; compared in raw
+        // units; the clamp keeps masked (-inf) elements out when theta keeps all
+        thr[qb] = fmaxf(log2_threshold(th, lse2[qb]) / a.xscale, -3.402823466e38f);
+    }
+
+    // ================ sweep B: threshold, exact SDC, P V on MFMA ===============
+    f32x4 o[2][C::DB];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int cnt[2] = {0, 0};
+    float mass[2] = {0.f, 0.f};
+    unsigned char* kmask = MASK ? a.kept_mask + ((size_t)b * a.Hq + h) * (size_t)a.L * a.L : nullptr;
+
+    // V chunks of this thread: chunk id = tid + 256 i -> key id / CPR, dims 8 (id % CPR)
+    u32x4 vr[C::VCH];
+    auto load_v = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < C::VCH; ++i) {
+            const int id = tid + 256 * i;
+            const int key = id / C::CPR, c = id % C::CPR;
+            vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, key * (D * 2) + c * 16, tile * C::BN * (D * 2), 0);
+        }
+    };
+    auto store_vt = [&]() {
+#pragma unroll
+        for (int i = 0; i < C::VCH; ++i) {
+            const int id = tid + 256 * i;
+            const int key = id / C::CPR, c = id % C::CPR;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s_vt[8 * c + 2 * e][key] = (uint16_t)(vr[i][e] & 0xffffu);
+                s_vt[8 * c + 2 * e + 1][key] = (uint16_t)(vr[i][e] >> 16);
+            }
+        }
+    };
+
+    __syncthreads();                                       // sweep A is done with both K buffers
+    issue_k(0, 0);
+    load_v(0);
+    for (int j = 0; j < ntiles; ++j) {
+        pf_wait_vmem();
+        __syncthreads();                                   // (1) K tile j landed; tile j-1 fully used
+        store_vt();
+        if (j + 1 < ntiles) { issue_k(j + 1, (j + 1) & 1); load_v(j + 1); }
+        __syncthreads();                                   // (2) V^T of tile j complete
+        f32x4 st[2][4];
+        scores(j & 1, st);
+        const bool diag = j * C::BN + C::BN - 1 > row0;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = row0 + 16 * qb + l16;
+            if (diag) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (j * C::BN + 16 * kb + 4 * lq + r > row) st[qb][kb][r] = NEG_INF;
+            }
+            if (MASK && row < a.L) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = j * C::BN + 16 * kb + 4 * lq + r;
+                        if (key <= row) kmask[(size_t)row * a.L + key] = st[qb][kb][r] >= thr[qb] ? 1 : 0;
+                    }
+            }
+            const float nlse = -lse2[qb];
+            unsigned pk[4][2], pl[4][2];                   // P^T fragments, packed bf16 (hi, lo)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                float p[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool kp = st[qb][kb][r] >= thr[qb];
+                    p[r] = kp ? pf_exp2(fmaf(st[qb][kb][r], a.xscale, nlse)) : 0.f;
+                    cnt[qb] += kp ? 1 : 0;
+                    mass[qb] += p[r];
+                }
+                split_bf16x2(p[0], p[1], pk[kb][0], pl[kb][0]);
+                split_bf16x2(p[2], p[3], pk[kb][1], pl[kb][1]);
+            }
+            // O^T += V^T P^T over 32 keys per step: keys 16 (2 ks + e / 4) + 4 lq + e % 4
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const u32x4 pv = {pk[2 * ks][0], pk[2 * ks][1], pk[2 * ks + 1][0], pk[2 * ks + 1][1]};
+                const u32x4 pw = {pl[2 * ks][0], pl[2 * ks][1], pl[2 * ks + 1][0], pl[2 * ks + 1][1]};
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
+                const bf16x8 pbl = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) {
+                    const uint16_t* vt = &s_vt[16 * db + l16][32 * ks + 4 * lq];
+                    const uint2 lo = *(const uint2*)vt;
+                    const uint2 hi = *(const uint2*)(vt + 16);
+                    const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
+                    const bf16x8 vtf = __builtin_bit_cast(bf16x8, av);
+                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtf, pb, o[qb][db], 0, 0, 0);
+                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtf, pbl, o[qb][db], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: row totals, SDC_NONE / VMC, output
+    const bool renorm = (a.flags & 2u) != 0;
+    const bool vmc = (a.flags & 1u) != 0 && !renorm;
+    uint16_t* og = a.out + ((size_t)b * a.Hq + h) * (size_t)a.L * D;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        int c = cnt[qb];
+        c += __shfl_xor(c, 16);
+        c += __shfl_xor(c, 32);
+        float m = mass[qb];
+        m += __shfl_xor(m, 16);
+        m += __shfl_xor(m, 32);
+        const int row = row0 + 16 * qb + l16;
+        if (row >= a.L) continue;
+        const float bta = renorm ? 0.f : 1.f - m;
+        const float inv = (renorm && c > 0) ? 1.f / m : 1.f;
+        const float* mu = vmc ? a.mu + (((size_t)b * a.Hkv + kv) * (size_t)a.L + row) * D : nullptr;
+        if (lq == 0) {
+            const size_t ro = ((size_t)b * a.Hq + h) * (size_t)a.L + row;
+            if (a.kept_count) a.kept_count[ro] = c;
+            if (a.beta) a.beta[ro] = bta;
+        }
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int dim = 16 * db + 4 * lq + r;
+                float v = o[qb][db][r];
+                if (renorm) v = c > 0 ? v * inv : 0.f;
+                if (vmc) v = fmaf(bta, mu[dim], v);
+                y[r] = v;
+            }
+            uint2 packed = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            *(uint2*)(og + (size_t)row * D + 16 * db + 4 * lq) = packed;
+        }
+    }
+#endif
+}
+
+// ------------------------------------------------------------------ host side
+int launch_prefix_mean(const void* v, int groups, int L, int d, int dtype, float* mu, hipStream_t s);
+
+bool prefill_bf16_supported(int d, int G) {
+    return (d == 64 || d == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+}
+
+template <int D, int G>
+static int launch_prefill_variant(const PrefillKArgs& a, hipStream_t s) {
+    using C = PrefillCfg<D, G>;
+    const dim3 grid((a.L + C::BMT - 1) / C::BMT, a.Hkv * (G / C::HPW), a.B);
+    // the variant that also writes the kept mask is only used when one is asked for
+    if (a.kept_mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+static int launch_prefill_d(const PrefillKArgs& a, int G, hipStream_t s) {
+    switch (G) {
+        case 1: return launch_prefill_variant<D, 1>(a, s);
+        case 2: return launch_prefill_variant<D, 2>(a, s);
+        case 4: return launch_prefill_variant<D, 4>(a, s);
+        case 8: return launch_prefill_variant<D, 8>(a, s);
+        default: return launch_prefill_variant<D, 16>(a, s);
+    }
+}
+
+int launch_prefill_bf16(const PrefillParams& p, float* mu_ws, hipStream_t s) {
+    const bool vmc = (p.flags & 1u) && !(p.flags & 2u);
+    if (vmc) {
+        const int e = launch_prefix_mean(p.v, p.B * p.Hkv, p.L, p.d, p.dtype, mu_ws, s);
+        if (e != hipSuccess) return e;
+    }
+    PrefillKArgs a = {};
+    a.q = (const uint16_t*)p.q; a.k = (const uint16_t*)p.k; a.v = (const uint16_t*)p.v;
+    a.theta = p.theta; a.mu = vmc ? mu_ws : nullptr;
+    a.out = (uint16_t*)p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.kept_mask = p.kept_mask;
+    a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.L = p.L; a.n_rows = p.n_rows;
+    a.xscale = p.scale * kLog2e;
+    a.flags = p.flags;
+    const int G = p.Hq / p.Hkv;
+    return p.d == 64 ? launch_prefill_d<64>(a, G, s) : launch_prefill_d<128>(a, G, s);
+}
+
+}  // namespace topth

@@ -397,6 +397,15 @@ int launch_decode_rowwise(const DecodeParams& p, uint32_t* masks_ws, hipStream_t
     return e;
 }
 
+int launch_prefix_mean(const void* v, int groups, int L, int d, int dtype, float* mu, hipStream_t s) {
+    if (dtype == 0)
+        hipLaunchKernelGGL(prefix_mean_kernel<float>, dim3(groups), dim3(128), 0, s, (const float*)v, L, d, mu);
+    else
+        hipLaunchKernelGGL(prefix_mean_kernel<uint16_t>, dim3(groups), dim3(128), 0, s, (const uint16_t*)v, L,
+                           d, mu);
+    return hipGetLastError();
+}
+
 int launch_prefill_rowwise(const PrefillParams& p, float* mu_ws, hipStream_t s) {
     const bool vmc = (p.flags & 1u) && !(p.flags & 2u);
     if (vmc) {

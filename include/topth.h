@@ -25,6 +25,7 @@
  *  - Element type: TOPTH_F32 (float) or TOPTH_BF16 (bfloat16) for Q, K, V and
  *    the attention output; scores, softmax statistics and accumulation are
  *    float32.  d must be 64 or 128.
+ *  - scale: the positive score scale, normally 1/sqrt(d).
  *  - Row id: query position p, 0-based; a decode step with n cached keys (the
  *    current token included) is row n - 1.  Rows at or past n_rows of a
  *    theta slab use the slab's last row.
@@ -139,8 +140,8 @@ int topth_calibrate_finalize(const double* sum, const double* sumsq, const int* 
  *   q device [B][Hq][L][d]; k, v device [B][Hkv][L][d]; theta device
  *   [Hq][n_rows]; out device [B][Hq][L][d] of the input dtype;
  *   kept_count device int [B][Hq][L] or NULL; beta device float [B][Hq][L]
- *   or NULL; kept_mask device uint8 [B][Hq][L][L] or NULL: 1 where key j is
- *   kept by row p (entries j > p are 0); ws device,
+ *   or NULL; kept_mask device uint8 [B][Hq][L][L] or NULL: 1 where key j <= p
+ *   is kept by row p (entries j > p are not written); ws device,
  *   topth_workspace_size(TOPTH_OP_PREFILL, ...).
  */
 int topth_prefill(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int L,

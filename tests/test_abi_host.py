@@ -76,6 +76,8 @@ def test_decode_argument_errors(lib):
     assert _decode(lib, flags=8) == -1
     assert _decode(lib, vm=None) == -1                   # VMC needs the running mean
     assert _decode(lib, scale=float("nan")) == -1
+    assert _decode(lib, scale=0.0) == -1
+    assert _decode(lib, scale=-0.1) == -1
     assert _decode(lib, ws=None) == -3
     assert _decode(lib, wsb=100) == -3
     assert _decode(lib, Hq=24, Hkv=8) == -2              # g = 3: no kernel

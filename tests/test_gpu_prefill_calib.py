@@ -166,13 +166,15 @@ def test_calibrate_decode_style_and_alpha():
 
 
 def test_decode_matches_prefill_row():
-    """Decode with n = p + 1 keys equals prefill row p (both on the GPU)."""
+    """Decode with n = p + 1 keys equals prefill row p (both on the GPU): kept
+    masks agree outside the 1e-5 band around theta (the two kernels accumulate
+    q.k in different orders), outputs within the bf16 tolerance."""
     dev = device()
     Hq, Hkv, L, d = 8, 2, 400, 128
     q, k, v = attention_inputs(UNIT, ROLE_TEST, 7, 0, B=1, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
     theta = np.exp(np.random.default_rng(0).uniform(-6, -2, size=(Hq, L)))
     g = run_prefill(q, k, v, theta, tt.TOPTH_VMC)
-    vf = to_f64(v)
+    qf, kf, vf = to_f64(q), to_f64(k), to_f64(v)
     for p in (0, 63, 64, 255, 399):
         vm = torch.tensor(vf[:, :, :p + 1].mean(2), dtype=torch.float32, device=dev)
         out = torch.empty(1, Hq, d, dtype=torch.bfloat16, device=dev)
@@ -183,5 +185,63 @@ def test_decode_matches_prefill_row():
                         torch.tensor(theta, dtype=torch.float32, device=dev), out, ws,
                         scale=1.0 / np.sqrt(d), flags=tt.TOPTH_VMC, v_mean=vm, kept_mask=km)
         torch.cuda.synchronize()
-        assert np.array_equal(km.cpu().numpy()[0, :, :p + 1].astype(bool), g["mask"][0, :, p, :p + 1])
+        dm = km.cpu().numpy()[0, :, :p + 1].astype(bool)
+        for h in range(Hq):
+            s_row, _ = oracle.post_softmax(oracle.scores(qf[0, h, p], kf[0, h // 4, :p + 1], 1.0 / np.sqrt(d)))
+            th = theta_of(theta, h, p)
+            diff = dm[h] != g["mask"][0, h, p, :p + 1]
+            assert not (diff & ~(np.abs(s_row - th) <= 1e-5 * abs(th))).any(), (p, h)
         assert np.abs(out.float().cpu().numpy()[0] - g["out"][0, :, p]).max() <= 1e-2
+
+
+@pytest.mark.parametrize("Hq,Hkv,L,d", [(16, 2, 333, 128), (16, 1, 200, 128), (2, 1, 257, 64), (8, 8, 97, 128)])
+def test_prefill_bf16_group_sizes(Hq, Hkv, L, d):
+    """g = 8, 16, 2, 1 with lengths that leave ragged query and key tiles."""
+    print(f"prefill bf16 Hq={Hq} Hkv={Hkv} L={L} d={d}", flush=True)
+    qc, kc, _ = batch_of_sequences(UNIT, ROLE_CALIB, 8, 0, 2, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    theta = oracle_calibrate(qc, kc, [16], L)[0][0]
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 8, Hq, B=2, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    g = run_prefill(q, k, v, theta, tt.TOPTH_VMC)
+    compare_prefill(g, q, k, v, theta, tt.TOPTH_VMC, torch.bfloat16)
+
+
+def test_prefill_8k_full_size_sampled_rows():
+    """One layer of the 8k prefill workload (32/8 heads, d=128, L=8192, k=128,
+    SDC, no VMC), checked on sampled rows that span the whole causal range."""
+    dev = device()
+    cfg = CONFIG_IDS["prefill_8k"]
+    Hq, Hkv, L, d, k = 32, 8, 8192, 128, 128
+    print("prefill 8k full size", flush=True)
+    # theta from the oracle: decode-style calibration at 24 rows, nearest-row fill between them
+    probe_rows = sorted(set(int(x) for x in np.geomspace(k + 1, L, 24).round()) | {L - 1})
+    cal = oracle.Calibrator([k], Hq, L)
+    scale = 1.0 / np.sqrt(d)
+    for i in range(2):
+        qc, kc, _ = attention_inputs(cfg, ROLE_CALIB, 2, i, B=1, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d, with_v=False)
+        qf, kf = to_f64(qc[0]), to_f64(kc[0])
+        for p in probe_rows:
+            cal.observe(qf[:, p:p + 1], kf[:, :p + 1], scale, q_pos0=p)
+    theta = cal.finalize()[0]
+    q, kk, v = attention_inputs(cfg, ROLE_TEST, 2, 0, B=1, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    out = torch.empty(1, Hq, L, d, dtype=torch.bfloat16, device=dev)
+    kc_ = torch.empty(1, Hq, L, dtype=torch.int32, device=dev)
+    bt = torch.empty(1, Hq, L, dtype=torch.float32, device=dev)
+    tt.topth_prefill(q.to(dev), kk.to(dev), v.to(dev), torch.tensor(theta, dtype=torch.float32, device=dev),
+                     out, scale=scale, flags=0, kept_count=kc_, beta=bt)
+    torch.cuda.synchronize()
+    go, gk, gb = out.float().cpu().numpy(), kc_.cpu().numpy(), bt.cpu().numpy()
+    rng = np.random.default_rng(0)
+    rows = [(0, int(h), int(p)) for h, p in zip(rng.integers(0, Hq, 48), rng.integers(0, L, 48))]
+    rows += [(0, 0, 0), (0, 31, L - 1), (0, 5, 127), (0, 6, 128), (0, 7, 4095)]
+    ref = oracle.prefill(to_f64(q), to_f64(kk), to_f64(v), theta, scale, vmc=False, rows=rows, keep_rows=True)
+    vf = to_f64(v)
+    for (b, h, p) in rows:
+        th = theta_of(theta, h, p)
+        s = ref.s[b][h][p]
+        amb = int((np.abs(s - th) <= 1e-5 * abs(th)).sum()) if np.isfinite(th) else 0
+        if amb == 0:
+            assert gk[b, h, p] == ref.kept_count[b, h, p], (h, p)
+        else:
+            assert abs(gk[b, h, p] - ref.kept_count[b, h, p]) <= amb
+        check_out(go[b, h, p], ref.out[b, h, p], torch.bfloat16, f"h{h} p{p}")
+        assert abs(gb[b, h, p] - ref.beta[b, h, p]) <= 1e-4, (h, p)
