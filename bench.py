@@ -14,6 +14,17 @@ v_mean and seq_lens, divided by the average kernel duration (HIP events on the
 launch stream).  One JSON line is printed; it also carries the roofline object
 and the CPU oracle timed on the host as a reported baseline.
 
+Other workloads (``--workload``):
+  * ``decode_70b_32k``: batch 8, 64/8 heads, 32768 cached keys, 4 sink keys, k=256.
+  * ``prefill_8k``: causal prefill of 4 layers (32/8 heads, d=128, L=8192, bf16;
+    k=512 for layers 0-1, k=128 for layers 2-3; SDC, no VMC).  A step is one
+    ``topth_prefill`` per layer; reported in TFLOP/s (algorithmic: one causal
+    QK^T plus the kept P V; executed MFMA work alongside).
+  * ``calib_sweep``: Algorithm-1 calibration of 8 heads, d=128, L=2048, k in
+    {64, 128, 256}, 512 sequences per layer; a slice of layers is timed and
+    the 32-layer sweep extrapolated.
+The default run also appends a ``prefill_8k`` summary object (fewer steps).
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
@@ -42,6 +53,13 @@ DECODE_WORKLOADS = {
     "decode_8b": dict(B=16, Hq=32, Hkv=8, d=128, n=4096, k=128, calib=256, sinks=1, buffers=3),
     "decode_70b_32k": dict(B=8, Hq=64, Hkv=8, d=128, n=32768, k=256, calib=256, sinks=4, buffers=2),
 }
+
+
+PREFILL_WORKLOAD = dict(B=1, Hq=32, Hkv=8, d=128, L=8192, ks=[512, 512, 128, 128], calib=64,
+                        sinks=1)
+CALIB_WORKLOAD = dict(layers=32, Hq=8, Hkv=8, d=128, L=2048, seqs=512, ks=[64, 128, 256], sinks=1,
+                      chunk=64, timed_layers=2)
+EXP_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9   # v_exp_f32: quarter-rate on 16-lane SIMDs
 
 
 def log(msg):
@@ -226,6 +244,219 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
     return res
 
 
+def calibrate_prefill_theta(w, layer, k, dev):
+    """theta [Hq, L] for one layer from `calib` prefill-style sequences (GPU)."""
+    cfg = CONFIG_IDS["prefill_8k"]
+    Hq, Hkv, d, L = w["Hq"], w["Hkv"], w["d"], w["L"]
+    s1 = torch.zeros(1, Hq, L, dtype=torch.float64, device=dev)
+    s2 = torch.zeros_like(s1)
+    cnt = torch.zeros(1, Hq, L, dtype=torch.int32, device=dev)
+    chunk = 8
+    ws = tt.workspace(tt.TOPTH_OP_CALIBRATE, chunk, Hq, Hkv, L, L, d, 1)
+    for done in range(0, w["calib"], chunk):
+        S = min(chunk, w["calib"] - done)
+        q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, layer, done, B=S, Hq=Hq, Hkv=Hkv, Lq=L,
+                                           Lk=L, d=d, n_sinks=w["sinks"], device=dev, with_v=False)
+        tt.topth_calibrate(q, kk, [k], s1, s2, cnt, ws, scale=1.0 / math.sqrt(d), q_pos0=0)
+        del q, kk
+    theta = torch.empty(1, Hq, L, dtype=torch.float32, device=dev)
+    tt.topth_calibrate_finalize(s1, s2, cnt, [k], theta)
+    torch.cuda.synchronize()
+    return theta[0].contiguous()
+
+
+def oracle_prefill_baseline(q, k, v, theta, w, budget_s=15.0):
+    """Time the CPU oracle on rows of layer 0, KV group 0 (its g query heads), spread
+    over the whole length; report algorithmic TFLOP/s on the same flop count."""
+    import oracle
+    g = w["Hq"] // w["Hkv"]
+    L, d = w["L"], w["d"]
+    qf = to_f64(q[:1, :g].cpu()); kf = to_f64(k[:1, :1].cpu()); vf = to_f64(v[:1, :1].cpu())
+    th = theta[:g].cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(0)
+    rows_all = rng.permutation(L)
+    t0 = time.perf_counter()
+    flops, done = 0.0, 0
+    while time.perf_counter() - t0 < budget_s and done < L:
+        ps = rows_all[done:done + 64]
+        rows = [(0, h, int(p)) for h in range(g) for p in ps]
+        r = oracle.prefill(qf, kf, vf, th, 1.0 / math.sqrt(d), vmc=False, rows=rows)
+        for (_, h, p) in rows:
+            flops += 2.0 * d * (p + 1) + 2.0 * d * r.kept_count[0, h, p]
+        done += len(ps)
+    el = time.perf_counter() - t0
+    model, threads = cpu_info()
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 NumPy oracle prefill of {done} random rows x {g} heads of layer 0 "
+                      f"(KV group 0), {el:.1f} s, host '{model}', {os.cpu_count()} logical CPUs"}
+
+
+def bench_prefill(steps, warmup, with_cpu):
+    w = PREFILL_WORKLOAD
+    dev = torch.device("cuda:0")
+    cfg = CONFIG_IDS["prefill_8k"]
+    B, Hq, Hkv, d, L = w["B"], w["Hq"], w["Hkv"], w["d"], w["L"]
+    n_layers = len(w["ks"])
+    scale = 1.0 / math.sqrt(d)
+    layers = []
+    for li, k in enumerate(w["ks"]):
+        log(f"[bench] prefill_8k: layer {li}: calibrating theta (k={k}) from {w['calib']} sequences")
+        theta = calibrate_prefill_theta(w, li, k, dev)
+        q, kk, v = attention_inputs_device(cfg, ROLE_TEST, li, 0, B=B, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d,
+                                           n_sinks=w["sinks"], device=dev)
+        out = torch.empty_like(q)
+        kc = torch.empty(B, Hq, L, dtype=torch.int32, device=dev)
+        layers.append(dict(k=k, theta=theta, q=q, kk=kk, v=v, out=out, kc=kc))
+    ws = tt.workspace(tt.TOPTH_OP_PREFILL, B, Hq, Hkv, L, L, d)
+
+    def step():
+        for lw in layers:
+            tt.topth_prefill(lw["q"], lw["kk"], lw["v"], lw["theta"], lw["out"], scale=scale, flags=0,
+                             kept_count=lw["kc"], ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    causal = B * Hq * L * (L + 1) / 2                      # causal score elements per layer
+    qk_flops = 2.0 * d * causal * n_layers
+    kept = sum(float(lw["kc"].double().sum().item()) for lw in layers)
+    pv_flops = 2.0 * d * kept
+    per_layer = []
+    for lw in layers:
+        kc = lw["kc"][:, :, lw["k"]:].double()
+        per_layer.append({"k": lw["k"], "kept_over_k": round(kc.mean().item() / lw["k"], 4),
+                          "kept_p10_p50_p90": [round(x, 1) for x in
+                                               torch.quantile(kc.flatten()[::97].float(),
+                                                              torch.tensor([0.1, 0.5, 0.9], device=dev))
+                                               .tolist()],
+                          "elements_kept_frac": round(float(lw["kc"].double().sum().item()) / causal, 5)})
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    span = start.elapsed_time(end) * 1e-3
+    t_step = span / steps
+    algo = (qk_flops + pv_flops) / t_step / 1e12
+    # executed MFMA work: QK^T in both sweeps plus P V as two bf16 products (hi/lo split)
+    executed = 4.0 * qk_flops / t_step / 1e12
+    res = {
+        "metric": METRIC, "value": round(algo, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill_8k", "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "seq_len": L, "layers": n_layers, "k_per_layer": w["ks"],
+                   "calib_sequences": w["calib"], "sdc": "exact", "vmc": False,
+                   "parallelism": "single GPU"},
+        "qk_tflops_algorithmic": round(qk_flops / t_step / 1e12, 2),
+        "mfma_tflops_executed": round(executed, 2),
+        "mfma_executed_frac_of_peak": round(executed / BF16_PEAK_TFLOPS, 4),
+        "per_layer": per_layer,
+        "roofline": {"bound": "mfma", "achieved": round(algo, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(algo / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_bf16_kernel",
+                     "avg_kernel_us": round(t_step / n_layers * 1e6, 2)},
+        "wall_s": round(wall, 4),
+    }
+    if with_cpu:
+        log("[bench] timing the CPU oracle on a sample of the prefill workload")
+        lw = layers[0]
+        res["cpu_baseline"] = oracle_prefill_baseline(lw["q"], lw["kk"], lw["v"], lw["theta"], w)
+    return res
+
+
+def oracle_calib_baseline(w, dev, budget_s=15.0):
+    """Time the CPU oracle's calibration (Algorithm 1) on head 0 of one sequence;
+    report causal score elements per second."""
+    import oracle
+    cfg = CONFIG_IDS["calib_sweep"]
+    q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, 0, 0, B=1, Hq=1, Hkv=1, Lq=w["L"], Lk=w["L"],
+                                       d=w["d"], n_sinks=w["sinks"], device=dev, with_v=False)
+    qf = to_f64(q[0].cpu()); kf = to_f64(kk[0].cpu())
+    rng = np.random.default_rng(0)
+    rows = rng.permutation(w["L"])
+    t0 = time.perf_counter()
+    elems, done = 0, 0
+    while time.perf_counter() - t0 < budget_s and done < w["L"]:
+        for i in rows[done:done + 64]:
+            oracle.calibration_samples(qf[:, i:i + 1], kf, w["ks"], 1.0 / math.sqrt(w["d"]), q_pos0=int(i))
+            elems += int(i) + 1
+        done += 64
+    el = time.perf_counter() - t0
+    model, threads = cpu_info()
+    return {"value": round(elems / el, 1), "unit": "score elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 NumPy oracle calibration of {min(done, w['L'])} random rows of head 0, "
+                      f"sequence 0, layer 0, {el:.1f} s, host '{model}'"}
+
+
+def bench_calib(with_cpu):
+    w = CALIB_WORKLOAD
+    dev = torch.device("cuda:0")
+    cfg = CONFIG_IDS["calib_sweep"]
+    Hq, Hkv, d, L, ks = w["Hq"], w["Hkv"], w["d"], w["L"], w["ks"]
+    n_k = len(ks)
+    scale = 1.0 / math.sqrt(d)
+    ws = tt.workspace(tt.TOPTH_OP_CALIBRATE, w["chunk"], Hq, Hkv, L, L, d, n_k)
+    total_s, wall = 0.0, 0.0
+    thetas = []
+    for layer in range(w["timed_layers"]):
+        s1 = torch.zeros(n_k, Hq, L, dtype=torch.float64, device=dev)
+        s2 = torch.zeros_like(s1)
+        cnt = torch.zeros(n_k, Hq, L, dtype=torch.int32, device=dev)
+        for done in range(0, w["seqs"], w["chunk"]):
+            S = min(w["chunk"], w["seqs"] - done)
+            q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, layer, done, B=S, Hq=Hq, Hkv=Hkv, Lq=L,
+                                               Lk=L, d=d, n_sinks=w["sinks"], device=dev, with_v=False)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            a.record()
+            tt.topth_calibrate(q, kk, ks, s1, s2, cnt, ws, scale=scale, q_pos0=0)
+            if done + S >= w["seqs"]:
+                theta = torch.empty(n_k, Hq, L, dtype=torch.float32, device=dev)
+                tt.topth_calibrate_finalize(s1, s2, cnt, ks, theta)
+            b.record()
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+            total_s += a.elapsed_time(b) * 1e-3
+            del q, kk
+        thetas.append(theta)
+        log(f"[bench] calib_sweep: layer {layer} done ({total_s:.3f} s GPU so far)")
+    seq_layers = w["seqs"] * w["timed_layers"]
+    elems = seq_layers * Hq * L * (L + 1) / 2
+    eps = elems / total_s
+    qk = 2.0 * d * elems / total_s / 1e12
+    full_s = total_s / w["timed_layers"] * w["layers"]
+    fin = torch.isfinite(thetas[0])
+    res = {
+        "metric": METRIC, "value": round(eps / 1e9, 3), "unit": "G score elements/s", "n_gpus": 1,
+        "steps": seq_layers, "warmup": 0, "ms_per_step": round(total_s / seq_layers * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "calib_sweep", "layers_total": w["layers"], "layers_timed": w["timed_layers"],
+                   "heads": Hq, "head_dim": d, "seq_len": L, "sequences": w["seqs"], "ks": ks,
+                   "parallelism": "single GPU"},
+        "sequence_layers_per_s": round(seq_layers / total_s, 2),
+        "full_sweep_s_extrapolated": round(full_s, 3),
+        "theta_tensor_bytes_full_sweep": n_k * w["layers"] * Hq * L * 4,
+        "theta_finite_frac_layer0": round(fin.float().mean().item(), 4),
+        "roofline": {"bound": "alu", "achieved": round(eps / 1e12, 4), "peak": EXP_PEAK_PER_S / 1e12,
+                     "unit": "T exp/s", "frac": round(eps / EXP_PEAK_PER_S, 4), "traffic": None,
+                     "kernel": "calib_bf16_kernel",
+                     "mfma_qk_tflops": round(qk, 2), "mfma_frac": round(qk / BF16_PEAK_TFLOPS, 4)},
+        "wall_s": round(wall, 3),
+    }
+    if with_cpu:
+        log("[bench] timing the CPU oracle on a sample of the calibration workload")
+        res["cpu_baseline"] = oracle_calib_baseline(w, dev)
+    return res
+
+
 def copy_probe(dev, mib=512):
     """One plain elementwise kernel of known traffic (reads and writes `mib` MiB),
     used to scale hardware byte counters."""
@@ -240,7 +471,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_8b", choices=sorted(DECODE_WORKLOADS))
+    ap.add_argument("--workload", default="decode_8b",
+                    choices=sorted(DECODE_WORKLOADS) + ["prefill_8k", "calib_sweep"])
+    ap.add_argument("--no-prefill-summary", action="store_true",
+                    help="default workload only: skip the appended prefill_8k summary")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of "
                     "replaying a captured HIP graph")
@@ -255,8 +489,18 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     tt.load_library()
-    res = bench_decode(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu_baseline,
-                       eager=args.eager)
+    with_cpu = not args.no_cpu_baseline
+    if args.workload == "prefill_8k":
+        res = bench_prefill(args.steps, args.warmup, with_cpu)
+    elif args.workload == "calib_sweep":
+        res = bench_calib(with_cpu)
+    else:
+        res = bench_decode(args.workload, args.steps, args.warmup, with_cpu=with_cpu, eager=args.eager)
+        if args.workload == "decode_8b" and not args.no_prefill_summary:
+            p = bench_prefill(steps=5, warmup=1, with_cpu=False)
+            res["prefill_8k"] = {k: p[k] for k in ("value", "unit", "ms_per_step", "qk_tflops_algorithmic",
+                                                   "mfma_tflops_executed", "mfma_executed_frac_of_peak",
+                                                   "per_layer", "roofline")}
     if args.copy_probe:
         copy_probe(torch.device("cuda:0"))
     print(json.dumps(res), flush=True)

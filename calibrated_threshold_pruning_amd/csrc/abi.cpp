@@ -18,6 +18,8 @@ int launch_prefill_rowwise(const PrefillParams& p, float* mu_ws, hipStream_t s);
 bool prefill_bf16_supported(int d, int G);
 int launch_prefill_bf16(const PrefillParams& p, float* mu_ws, hipStream_t s);
 int launch_calibrate_rowwise(const CalibParams& p, float* samples_ws, hipStream_t s);
+bool calib_bf16_supported(int d, int S, int Hq, int Lq, int q_pos0);
+int launch_calibrate_bf16(const CalibParams& p, float* samples_ws, hipStream_t s);
 }  // namespace topth
 
 using namespace topth;
@@ -100,7 +102,8 @@ int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq
     for (int t = 0; t < n_k; ++t)
         if (ks[t] < 1) return TOPTH_EINVAL;
     if (too_big((long long)S * Hq * Lq, d) || too_big((long long)S * Hkv * Lk, d)) return TOPTH_EUNSUPPORTED;
-    if (Lk > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
+    const bool tiled = dtype == TOPTH_BF16 && calib_bf16_supported(d, S, Hq, Lq, q_pos0);
+    if (!tiled && Lk > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
     if (!ws) return TOPTH_EWORKSPACE;
     const size_t need = calib_ws(S, Hq, Lq, n_k);
     if (ws_bytes < need) return TOPTH_EWORKSPACE;
@@ -110,7 +113,8 @@ int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq
     for (int t = 0; t < n_k; ++t) p.ks[t] = ks[t];
     p.n_k = n_k; p.sum = sum; p.sumsq = sumsq; p.count = count; p.n_rows = n_rows;
     p.ws = ws; p.ws_bytes = ws_bytes;
-    return map_hip(launch_calibrate_rowwise(p, (float*)ws, (hipStream_t)stream));
+    return map_hip(tiled ? launch_calibrate_bf16(p, (float*)ws, (hipStream_t)stream)
+                         : launch_calibrate_rowwise(p, (float*)ws, (hipStream_t)stream));
 }
 
 int topth_calibrate_finalize(const double* sum, const double* sumsq, const int* count,

@@ -427,6 +427,9 @@ int launch_prefill_rowwise(const PrefillParams& p, float* mu_ws, hipStream_t s) 
     return dispatch_rows<kRowPrefill>(a, p.d, p.dtype, p.B * p.Hq * p.L, p.L, s);
 }
 
+int launch_calib_accumulate(const float* samples, int S, int n_k, int Hq, int Lq, int q_pos0,
+                            double* sum, double* sumsq, int* count, int n_rows, hipStream_t s);
+
 int launch_calibrate_rowwise(const CalibParams& p, float* samples_ws, hipStream_t s) {
     RowArgs a = {};
     a.q = p.q; a.k = p.k;
@@ -436,10 +439,15 @@ int launch_calibrate_rowwise(const CalibParams& p, float* samples_ws, hipStream_
     a.n_k = p.n_k; a.samples = samples_ws;
     int e = dispatch_rows<kRowCalib>(a, p.d, p.dtype, p.S * p.Hq * p.Lq, p.q_pos0 + p.Lq, s);
     if (e != hipSuccess) return e;
-    const size_t per = (size_t)p.n_k * p.Hq * p.Lq;
+    return launch_calib_accumulate(samples_ws, p.S, p.n_k, p.Hq, p.Lq, p.q_pos0, p.sum, p.sumsq,
+                                   p.count, p.n_rows, s);
+}
+
+int launch_calib_accumulate(const float* samples, int S, int n_k, int Hq, int Lq, int q_pos0,
+                            double* sum, double* sumsq, int* count, int n_rows, hipStream_t s) {
+    const size_t per = (size_t)n_k * Hq * Lq;
     hipLaunchKernelGGL(calib_accumulate_kernel, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, s,
-                       samples_ws, p.S, p.n_k, p.Hq, p.Lq, p.q_pos0, p.sum, p.sumsq, p.count,
-                       p.n_rows);
+                       samples, S, n_k, Hq, Lq, q_pos0, sum, sumsq, count, n_rows);
     return hipGetLastError();
 }
 

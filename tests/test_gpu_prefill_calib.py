@@ -165,6 +165,72 @@ def test_calibrate_decode_style_and_alpha():
         assert (th_gpu[0, :, 64:] == th_gpu[0, :, L - 1:L]).all()   # nearest-row fill
 
 
+# Shapes that reach every score-column variant of the tiled bf16 calibration
+# (16 columns up to 2048 keys, then 8, 4, 2, 1 as the longest row doubles) and
+# both head/row mappings of a workgroup (several heads of a KV group, several
+# rows of one head).
+CALIB_SHAPES = [
+    # name, Hq, Hkv, Lq, Lk, q_pos0, S, ks, d
+    ("c16_gqa_rows", 8, 2, 300, 300, 0, 3, [16, 64], 128),
+    ("c16_chunk", 2, 1, 100, 400, 300, 2, [32, 200], 64),
+    ("c8_prefill", 1, 1, 2500, 2500, 0, 1, [128], 64),
+    ("c4_decode", 8, 2, 1, 6000, 5999, 3, [64, 256], 128),
+    ("c2_decode", 8, 1, 1, 12000, 11999, 2, [256], 128),
+    ("c1_decode", 2, 2, 1, 30000, 29999, 2, [256, 1000], 64),
+]
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,Lq,Lk,q_pos0,S,ks,d", CALIB_SHAPES,
+                         ids=[c[0] for c in CALIB_SHAPES])
+def test_calibrate_bf16_column_variants(name, Hq, Hkv, Lq, Lk, q_pos0, S, ks, d):
+    print("calibrate", name, flush=True)
+    q, k, _ = batch_of_sequences(UNIT, ROLE_CALIB, 7, 0, S, Hq=Hq, Hkv=Hkv, Lq=Lq, Lk=Lk, d=d)
+    n_rows = q_pos0 + Lq
+    th_gpu, cnt_gpu = gpu_calibrate(q, k, ks, n_rows, q_pos0=q_pos0)
+    th_ref, cnt_ref = oracle_calibrate(q, k, ks, n_rows, q_pos0=q_pos0)
+    assert np.array_equal(cnt_gpu, cnt_ref)
+    check_theta(th_gpu, th_ref)
+
+
+def test_calibrate_bf16_ties():
+    """Keys drawn from three distinct rows: every score row holds long runs of
+    equal values, so the bin of the k-th largest overflows the copy space and
+    the restricted radix select decides (ties count with multiplicity)."""
+    Hq, L, d = 2, 600, 128
+    q, k, _ = batch_of_sequences(UNIT, ROLE_CALIB, 8, 0, 2, Hq=Hq, Hkv=Hq, Lq=L, Lk=L, d=d)
+    k = k[:, :, torch.arange(L) % 3].contiguous()
+    ks = [50, 300]
+    th_gpu, cnt_gpu = gpu_calibrate(q, k, ks, L)
+    th_ref, cnt_ref = oracle_calibrate(q, k, ks, L)
+    assert np.array_equal(cnt_gpu, cnt_ref)
+    check_theta(th_gpu, th_ref)
+
+
+def test_calibrate_sweep_shape_sampled_rows():
+    """Calibration-sweep shape (8 independent heads, d=128, L=2048, k in
+    {64, 128, 256}) on a few sequences: counts on every row, theta on sampled
+    rows against the oracle's mean of per-sequence k-th largest values."""
+    Hq, L, d, S = 8, 2048, 128, 2
+    ks = [64, 128, 256]
+    q, k, _ = batch_of_sequences(CONFIG_IDS["calib_sweep"], ROLE_CALIB, 0, 0, S, Hq=Hq, Hkv=Hq,
+                                 Lq=L, Lk=L, d=d)
+    th_gpu, cnt_gpu = gpu_calibrate(q, k, ks, L)
+    for ki, kk in enumerate(ks):
+        assert (cnt_gpu[ki, :, :kk] == 0).all() and (cnt_gpu[ki, :, kk:] == S).all()
+        assert np.isneginf(th_gpu[ki, :, :kk]).all()
+    rows = [64, 127, 128, 255, 256, 257, 700, 1023, 1500, 2046, 2047]
+    qf, kf = to_f64(q), to_f64(k)
+    for i in rows:
+        obs = {}
+        for s in range(S):
+            for key, t in oracle.calibration_samples(qf[s][:, i:i + 1], kf[s], ks, 1.0 / np.sqrt(d),
+                                                     q_pos0=i).items():
+                obs.setdefault(key, []).append(t)
+        for (ki, h, p), vals in obs.items():
+            ref = float(np.mean(vals))
+            assert abs(th_gpu[ki, h, p] - ref) <= 1e-5 * abs(ref), (ki, h, p)
+
+
 def test_decode_matches_prefill_row():
     """Decode with n = p + 1 keys equals prefill row p (both on the GPU): kept
     masks agree outside the 1e-5 band around theta (the two kernels accumulate
