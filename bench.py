@@ -30,6 +30,7 @@ The default run also appends a ``prefill_8k`` summary object (fewer steps).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -60,6 +61,31 @@ PREFILL_WORKLOAD = dict(B=1, Hq=32, Hkv=8, d=128, L=8192, ks=[512, 512, 128, 128
 CALIB_WORKLOAD = dict(layers=32, Hq=8, Hkv=8, d=128, L=2048, seqs=512, ks=[64, 128, 256], sinks=1,
                       chunk=64, timed_layers=2)
 EXP_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9   # v_exp_f32: quarter-rate on 16-lane SIMDs
+
+
+def measured_traffic(kernel, workload, sources):
+    """HBM bytes per launch from the committed counter summary of `kernel` on
+    `workload` (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel of known
+    size), or None when there is none or `sources` changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip().split()[0] if val.strip() else ""
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_dispatch" not in fields:
+        return None
+    return int(float(fields["traffic_bytes_per_dispatch"]))
+
+
+DECODE_SOURCES = ["calibrated_threshold_pruning_amd/csrc/decode.hip",
+                  "calibrated_threshold_pruning_amd/csrc/topth_internal.h"]
 
 
 def log(msg):
@@ -234,7 +260,10 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
         "vrows_per_group": round(float(np.mean(union_rows)), 1),
         "bytes_read_per_step": int(nbytes),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_bf16_kernel", name, DECODE_SOURCES),
+                     "traffic_unit": "bytes per launch (HBM, counters)",
+                     "algorithmic_bytes_per_launch": int(nbytes),
                      "kernel": "decode_bf16_kernel", "avg_kernel_us": round(avg * 1e6, 3)},
         "wall_s": round(wall, 4),
     }
