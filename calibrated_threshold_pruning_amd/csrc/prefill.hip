@@ -44,14 +44,13 @@ struct PrefillCfg {
     static constexpr int RPI = 64 / CPR;            // K rows per 1 KiB load instruction
     static constexpr int KTILE = BN * D * 2;        // bytes of one K tile
     static constexpr int NLD = KTILE / 1024 / 4;    // load instructions per wave per K tile
-    static constexpr int VT_STRIDE = BN + 4;        // bf16 elements per transposed V row (136 B)
-    static constexpr int VCH = BN * CPR / 256;      // V chunks per thread per tile
 };
 
 __device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ void pf_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
+typedef short pf_i16x4 __attribute__((ext_vector_type(4)));
 typedef float pf_f32x2 __attribute__((ext_vector_type(2)));
 
 // two floats to packed bfloat16, round to nearest even (v_cvt_pk_bf16_f32)
@@ -71,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     using C = PrefillCfg<D, G>;
     __shared__ __attribute__((aligned(16))) unsigned char s_k[2][C::KTILE];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vt[D][C::VT_STRIDE];
+    __shared__ __attribute__((aligned(16))) unsigned char s_v[2][C::KTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -110,8 +109,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         }
     }
 
-    // ---- K tile staging: each wave moves a quarter of the tile; source offsets
-    // apply an XOR swizzle so that MFMA-layout reads are bank-conflict free
+    // ---- K and V tile staging: each wave moves a quarter of the tile; source
+    // offsets apply an XOR swizzle (16-byte chunk c of row r sits in slot
+    // c ^ (r % CPR)) so that MFMA-layout reads are bank-conflict free
     constexpr int NVO = C::CPR / C::RPI > 0 ? C::CPR / C::RPI : 1;
     int vo[NVO];
 #pragma unroll
@@ -119,15 +119,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         const int row = j * C::RPI + lane / C::CPR;
         vo[j] = (lane / C::CPR) * (D * 2) + (((lane % C::CPR) ^ (row % C::CPR)) * 16);
     }
-    auto issue_k = [&](int tile, int buf) {
+    auto issue_tile = [&](__amdgpu_buffer_rsrc_t rs, unsigned char* dst, int tile) {
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i) {
             const int li = wave * C::NLD + i;          // load instruction of the tile
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                krs, (__attribute__((address_space(3))) void*)(&s_k[buf][li * 1024]), 16,
+                rs, (__attribute__((address_space(3))) void*)(dst + li * 1024), 16,
                 vo[li % NVO], (tile * C::BN + li * C::RPI) * (D * 2), 0, 0);
         }
     };
+    auto issue_k = [&](int tile, int buf) { issue_tile(krs, s_k[buf], tile); };
+    auto issue_v = [&](int tile, int buf) { issue_tile(vrs, s_v[buf], tile); };
     // S^T block (keys 16 kb + 4 lq + r, query rows 16 qb + l16) of one K tile
     auto scores = [&](int buf, f32x4 (&st)[2][4]) {
 #pragma unroll
@@ -216,41 +218,44 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
     float mass[2] = {0.f, 0.f};
     unsigned char* kmask = MASK ? a.kept_mask + ((size_t)b * a.Hq + h) * (size_t)a.L * a.L : nullptr;
 
-    // V chunks of this thread: chunk id = tid + 256 i -> key id / CPR, dims 8 (id % CPR)
-    u32x4 vr[C::VCH];
-    auto load_v = [&](int tile) {
+    // V^T fragments (A operand of O^T += V^T P^T) come straight from the
+    // row-major V tile with LDS transpose reads: in each 16-lane group, lane i
+    // receives column i % 4 of the 8-byte rows addressed by lanes i / 4 + 4 e,
+    // e = 0..3.  Lane r of group lq points at V[key(r / 4)][16 db + 4 (r % 4)],
+    // so lane i gets V[key(e)][16 db + i] for four keys.  The keys of k-slot j
+    // follow the P^T fragment: 32 ks + 16 (j / 4) + 4 lq + j % 4.
+    int vtr_off[2];                                        // byte offsets for j / 4 = 0, 1, db = 0
 #pragma unroll
-        for (int i = 0; i < C::VCH; ++i) {
-            const int id = tid + 256 * i;
-            const int key = id / C::CPR, c = id % C::CPR;
-            vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, key * (D * 2) + c * 16, tile * C::BN * (D * 2), 0);
-        }
-    };
-    auto store_vt = [&]() {
-#pragma unroll
-        for (int i = 0; i < C::VCH; ++i) {
-            const int id = tid + 256 * i;
-            const int key = id / C::CPR, c = id % C::CPR;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s_vt[8 * c + 2 * e][key] = (uint16_t)(vr[i][e] & 0xffffu);
-                s_vt[8 * c + 2 * e + 1][key] = (uint16_t)(vr[i][e] >> 16);
-            }
-        }
+    for (int hh = 0; hh < 2; ++hh) {
+        const int key = 16 * hh + 4 * lq + l16 / 4;        // plus 32 ks: same residue mod CPR
+        const int c = (4 * (l16 % 4)) / 8;                 // 16-byte chunk of dims 4 (l16 % 4) .. + 3
+        vtr_off[hh] = key * (D * 2) + ((c ^ (key % C::CPR)) * 16) + ((l16 % 4) & 1) * 8;
+    }
+    auto vt_frag = [&](int buf, int ks, int db) -> bf16x8 {
+        // chunk index of dims 16 db + ... is 2 db + c; the swizzle XORs the chunk
+        // index with key % CPR, and 2 db only touches bits that c does not use
+        const unsigned char* base = &s_v[buf][32 * ks * (D * 2)];
+        const int dboff = (2 * db) * 16;
+        const pf_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) pf_i16x4*)(base + (vtr_off[0] ^ dboff)));
+        const pf_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) pf_i16x4*)(base + (vtr_off[1] ^ dboff)));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, both);
     };
 
     __syncthreads();                                       // sweep A is done with both K buffers
     issue_k(0, 0);
-    load_v(0);
+    issue_v(0, 0);
     for (int j = 0; j < ntiles; ++j) {
         pf_wait_vmem();
-        __syncthreads();                                   // (1) K tile j landed; tile j-1 fully used
-        store_vt();
-        if (j + 1 < ntiles) { issue_k(j + 1, (j + 1) & 1); load_v(j + 1); }
-        __syncthreads();                                   // (2) V^T of tile j complete
+        __syncthreads();                                   // K, V tile j landed; tile j-1 fully used
+        if (j + 1 < ntiles) { issue_k(j + 1, (j + 1) & 1); issue_v(j + 1, (j + 1) & 1); }
         f32x4 st[2][4];
         scores(j & 1, st);
         const bool diag = j * C::BN + C::BN - 1 > row0;
+        unsigned pk[2][4][2], pl[2][4][2];                 // P^T fragments, packed bf16 (hi, lo)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int row = row0 + 16 * qb + l16;
@@ -271,7 +276,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                     }
             }
             const float nlse = -lse2[qb];
-            unsigned pk[4][2], pl[4][2];                   // P^T fragments, packed bf16 (hi, lo)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 float p[4];
@@ -282,25 +286,28 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                     cnt[qb] += kp ? 1 : 0;
                     mass[qb] += p[r];
                 }
-                split_bf16x2(p[0], p[1], pk[kb][0], pl[kb][0]);
-                split_bf16x2(p[2], p[3], pk[kb][1], pl[kb][1]);
+                split_bf16x2(p[0], p[1], pk[qb][kb][0], pl[qb][kb][0]);
+                split_bf16x2(p[2], p[3], pk[qb][kb][1], pl[qb][kb][1]);
             }
-            // O^T += V^T P^T over 32 keys per step: keys 16 (2 ks + e / 4) + 4 lq + e % 4
+        }
+        // O^T += V^T P^T over 32 keys per step; each V^T fragment serves both row blocks
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const u32x4 pv = {pk[2 * ks][0], pk[2 * ks][1], pk[2 * ks + 1][0], pk[2 * ks + 1][1]};
-                const u32x4 pw = {pl[2 * ks][0], pl[2 * ks][1], pl[2 * ks + 1][0], pl[2 * ks + 1][1]};
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
-                const bf16x8 pbl = __builtin_bit_cast(bf16x8, pw);
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 pb[2], pbl[2];
 #pragma unroll
-                for (int db = 0; db < C::DB; ++db) {
-                    const uint16_t* vt = &s_vt[16 * db + l16][32 * ks + 4 * lq];
-                    const uint2 lo = *(const uint2*)vt;
-                    const uint2 hi = *(const uint2*)(vt + 16);
-                    const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
-                    const bf16x8 vtf = __builtin_bit_cast(bf16x8, av);
-                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtf, pb, o[qb][db], 0, 0, 0);
-                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtf, pbl, o[qb][db], 0, 0, 0);
+            for (int qb = 0; qb < 2; ++qb) {
+                const u32x4 pv = {pk[qb][2 * ks][0], pk[qb][2 * ks][1], pk[qb][2 * ks + 1][0], pk[qb][2 * ks + 1][1]};
+                const u32x4 pw = {pl[qb][2 * ks][0], pl[qb][2 * ks][1], pl[qb][2 * ks + 1][0], pl[qb][2 * ks + 1][1]};
+                pb[qb] = __builtin_bit_cast(bf16x8, pv);
+                pbl[qb] = __builtin_bit_cast(bf16x8, pw);
+            }
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+                const bf16x8 vtf = vt_frag(j & 1, ks, db);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtf, pb[qb], o[qb][db], 0, 0, 0);
+                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtf, pbl[qb], o[qb][db], 0, 0, 0);
                 }
             }
         }
