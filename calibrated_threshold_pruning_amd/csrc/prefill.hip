@@ -49,6 +49,18 @@ struct PrefillCfg {
 __device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ void pf_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Scheduling hint for one region: REPS times, NDS LDS reads then NMFMA MFMAs,
+// which puts the reads of the next operand fragments ahead of the MFMAs of the
+// current ones instead of right before them.
+template <int REPS, int NDS, int NMFMA>
+__device__ __forceinline__ void pf_ds_mfma_pipeline() {
+#pragma unroll
+    for (int i = 0; i < REPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
+    }
+}
+
 typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
 typedef short pf_i16x4 __attribute__((ext_vector_type(4)));
 typedef float pf_f32x2 __attribute__((ext_vector_type(2)));
@@ -148,6 +160,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
             st[0][kb] = acc0;
             st[1][kb] = acc1;
         }
+        // the K fragments of key block kb+1 are read while kb's MFMAs run
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::KSTEPS, 0);
+#pragma unroll
+        for (int kb = 0; kb < 3; ++kb) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KSTEPS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, C::KSTEPS, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KSTEPS, 0);
     };
 
     // ======================= sweep A: row log-sum-exp =========================
@@ -311,6 +331,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                 }
             }
         }
+        // the V^T fragment of the next (ks, db) is read while the current one's MFMAs run
+        pf_ds_mfma_pipeline<1, 4, 0>();
+        pf_ds_mfma_pipeline<2 * C::DB - 1, 2, 4>();
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
 
     // ---- epilogue: row totals, SDC_NONE / VMC, output
