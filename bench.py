@@ -52,8 +52,11 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 DECODE_WORKLOADS = {
     "decode_8b": dict(B=16, Hq=32, Hkv=8, d=128, n=4096, k=128, calib=256, sinks=1, buffers=3),
-    "decode_70b_32k": dict(B=8, Hq=64, Hkv=8, d=128, n=32768, k=256, calib=256, sinks=4, buffers=2),
+    "decode_70b_32k": dict(B=8, Hq=64, Hkv=8, d=128, n=32768, k=256, calib=256, sinks=4, buffers=2,
+                           buckets=[("<512", 256, 511), ("512-2048", 512, 2047), ("2048-8192", 2048, 8191),
+                                    (">8192", 8192, 32767)]),
 }
+PROBES_PER_BUCKET = 8
 
 
 PREFILL_WORKLOAD = dict(B=1, Hq=32, Hkv=8, d=128, L=8192, ks=[512, 512, 128, 128], calib=64,
@@ -92,10 +95,23 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def calibrate_decode_theta(name, w, dev):
-    """theta [Hq, n] for k from `calib` decode-style sequences, on the GPU."""
+def probe_rows(w):
+    """Query positions p at which theta is calibrated and k~/k is reported: 8
+    log-spaced rows per bucket (all with p + 1 > k), by bucket name."""
+    out = {}
+    for name, lo, hi in w.get("buckets", []):
+        rows = np.unique(np.round(np.geomspace(max(lo, w["k"]), hi, PROBES_PER_BUCKET)).astype(int))
+        out[name] = [int(r) for r in rows]
+    return out
+
+
+def calibrate_decode_theta(name, w, dev, rows=()):
+    """theta [Hq, n] for k from `calib` decode-style sequences, on the GPU.  Row
+    n - 1 (the timed decode step) and every row in `rows` are calibrated, each
+    with its own query draw; other rows copy the nearest calibrated row."""
     cfg = CONFIG_IDS[name]
     Hq, Hkv, d, n, k = w["Hq"], w["Hkv"], w["d"], w["n"], w["k"]
+    rows = sorted(set(int(r) for r in rows) | {n - 1})
     s1 = torch.zeros(1, Hq, n, dtype=torch.float64, device=dev)
     s2 = torch.zeros_like(s1)
     cnt = torch.zeros(1, Hq, n, dtype=torch.int32, device=dev)
@@ -104,14 +120,38 @@ def calibrate_decode_theta(name, w, dev):
     done = 0
     while done < w["calib"]:
         S = min(chunk, w["calib"] - done)
-        q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, 0, done, B=S, Hq=Hq, Hkv=Hkv, Lq=1, Lk=n,
+        q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, 0, done, B=S, Hq=Hq, Hkv=Hkv, Lq=len(rows), Lk=n,
                                            d=d, n_sinks=w["sinks"], device=dev, with_v=False)
-        tt.topth_calibrate(q, kk, [k], s1, s2, cnt, ws, scale=1.0 / math.sqrt(d), q_pos0=n - 1)
+        for i, p in enumerate(rows):
+            tt.topth_calibrate(q[:, :, i:i + 1].contiguous(), kk, [k], s1, s2, cnt, ws,
+                               scale=1.0 / math.sqrt(d), q_pos0=p)
         done += S
     theta = torch.empty(1, Hq, n, dtype=torch.float32, device=dev)
     tt.topth_calibrate_finalize(s1, s2, cnt, [k], theta)
     torch.cuda.synchronize()
     return theta[0].contiguous()
+
+
+def kept_by_bucket(buckets, buf, theta, w, dev):
+    """Mean k~/k of decode steps at the probe rows of each bucket (seq_len = p + 1,
+    same caches, VMC on)."""
+    q, kk, v = buf
+    B, Hq, Hkv, d = w["B"], w["Hq"], w["Hkv"], w["d"]
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    kc = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    vm = torch.empty(B, Hkv, d, dtype=torch.float32, device=dev)
+    ws = tt.workspace(tt.TOPTH_OP_DECODE, B, Hq, Hkv, 1, w["n"], d)
+    res = {}
+    for name, rows in buckets.items():
+        ratios = []
+        for p in rows:
+            lens = torch.full((B,), p + 1, dtype=torch.int32, device=dev)
+            tt.topth_vmean(v, lens, vm)
+            tt.topth_decode(q, kk, v, lens, theta, out, ws, scale=1.0 / math.sqrt(d), flags=tt.TOPTH_VMC,
+                            v_mean=vm, kept_count=kc)
+            ratios.append(kc.double().mean().item() / w["k"])
+        res[name] = {"kept_over_k": round(float(np.mean(ratios)), 4), "rows": rows}
+    return res
 
 
 def cpu_info():
@@ -173,8 +213,10 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
     cfg = CONFIG_IDS[name]
     B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
     esz = 2
-    log(f"[bench] {name}: calibrating theta from {w['calib']} sequences")
-    theta = calibrate_decode_theta(name, w, dev)
+    buckets = probe_rows(w)
+    log(f"[bench] {name}: calibrating theta from {w['calib']} sequences"
+        + (f" at row {n - 1} and {sum(len(r) for r in buckets.values())} probe rows" if buckets else ""))
+    theta = calibrate_decode_theta(name, w, dev, rows=[p for r in buckets.values() for p in r])
     lens = [n] * B
     lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
     bufs, vms = [], []
@@ -267,6 +309,9 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
                      "kernel": "decode_bf16_kernel", "avg_kernel_us": round(avg * 1e6, 3)},
         "wall_s": round(wall, 4),
     }
+    if buckets:
+        log("[bench] k~/k at the probe rows of each bucket")
+        res["kept_over_k_by_row_bucket"] = kept_by_bucket(buckets, bufs[0], theta, w, dev)
     if with_cpu:
         log("[bench] timing the CPU oracle on a sample of the same workload")
         res["cpu_baseline"] = oracle_decode_baseline(bufs[0], lens, theta, vms[0], w, read_bytes)

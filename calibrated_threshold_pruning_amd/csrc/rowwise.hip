@@ -232,17 +232,40 @@ __global__ void union_count_kernel(const uint32_t* masks, int Hq, int Hkv, int m
     if (threadIdx.x == 0) vrows_read[bk] = red[0] + red[1] + red[2] + red[3];
 }
 
-// mean of the first n = seq_lens[b] V rows, Eq. 5 over the cached rows
-template <typename T>
-__global__ void vmean_kernel(const T* v, const int* seq_lens, int Hkv, int Lmax, int D, float* out) {
+// mean of the first n = seq_lens[b] V rows, Eq. 5 over the cached rows.  One
+// workgroup per (b, KV head): each thread reads 16-byte pieces of rows (CPR
+// threads cover a row, RS rows per pass) and keeps float64 partial sums for
+// its piece, in row order; the RS partial sums of every column are then added
+// in a fixed order, so the result does not depend on scheduling.
+constexpr int kVmeanThreads = 512;
+template <typename T, int D>
+__global__ __launch_bounds__(kVmeanThreads) void vmean_kernel(const T* v, const int* seq_lens, int Hkv,
+                                                               int Lmax, float* out) {
+    constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte piece
+    constexpr int CPR = D / EPC;                      // pieces per row
+    constexpr int RS = kVmeanThreads / CPR;           // rows per pass
+    __shared__ double part[RS][D];
     const int bk = blockIdx.x;
     const int b = bk / Hkv;
     const int n = min(max(seq_lens[b], 1), Lmax);
     const T* base = v + (size_t)bk * Lmax * D;
-    for (int t = threadIdx.x; t < D; t += blockDim.x) {
-        double acc = 0.0;
-        for (int j = 0; j < n; ++j) acc += (double)Elem<T>::load(base + (size_t)j * D + t);
-        out[(size_t)bk * D + t] = (float)(acc / (double)n);
+    const int c = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+    double acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+    for (int j = r0; j < n; j += RS) {
+        const u32x4 raw = *(const u32x4*)(base + (size_t)j * D + c * EPC);
+        const T* x = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] += (double)Elem<T>::load(x + e);
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) part[r0][c * EPC + e] = acc[e];
+    __syncthreads();
+    for (int t = threadIdx.x; t < D; t += kVmeanThreads) {
+        double sum = 0.0;
+        for (int r = 0; r < RS; ++r) sum += part[r][t];
+        out[(size_t)bk * D + t] = (float)(sum / (double)n);
     }
 }
 
@@ -462,12 +485,14 @@ int launch_finalize(const double* sum, const double* sumsq, const int* count, co
 
 int launch_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,
                  float* v_mean, hipStream_t s) {
-    if (dtype == 0)
-        hipLaunchKernelGGL(vmean_kernel<float>, dim3(B * Hkv), dim3(128), 0, s, (const float*)v,
-                           seq_lens, Hkv, Lmax, d, v_mean);
-    else
-        hipLaunchKernelGGL(vmean_kernel<uint16_t>, dim3(B * Hkv), dim3(128), 0, s,
-                           (const uint16_t*)v, seq_lens, Hkv, Lmax, d, v_mean);
+    const dim3 grid(B * Hkv), block(kVmeanThreads);
+    if (dtype == 0) {
+        if (d == 64) hipLaunchKernelGGL((vmean_kernel<float, 64>), grid, block, 0, s, (const float*)v, seq_lens, Hkv, Lmax, v_mean);
+        else hipLaunchKernelGGL((vmean_kernel<float, 128>), grid, block, 0, s, (const float*)v, seq_lens, Hkv, Lmax, v_mean);
+    } else {
+        if (d == 64) hipLaunchKernelGGL((vmean_kernel<uint16_t, 64>), grid, block, 0, s, (const uint16_t*)v, seq_lens, Hkv, Lmax, v_mean);
+        else hipLaunchKernelGGL((vmean_kernel<uint16_t, 128>), grid, block, 0, s, (const uint16_t*)v, seq_lens, Hkv, Lmax, v_mean);
+    }
     return hipGetLastError();
 }
 
