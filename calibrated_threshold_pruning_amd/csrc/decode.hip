@@ -47,6 +47,11 @@ struct DecodeKArgs {
     int xcd_map;       // 1: chunks of a group on one XCD (grid and items multiples of 8 * chunks)
 };
 
+// One workgroup of kDecodeWaves waves per CU: two workgroups on a CU stream at
+// different rates (the older one's loads are served first), which leaves the
+// chunks on the second one, and their groups, behind.
+constexpr int kDecodeWaves = 8;
+
 template <int D, int G, int NT>
 struct DecodeCfg {
     static constexpr int P = (G <= 4) ? 4 : (G == 8 ? 2 : 1);  // key tiles packed per MFMA
@@ -54,7 +59,7 @@ struct DecodeCfg {
     static constexpr int BPT = 4 / P;          // 16-lane blocks per key tile
     static constexpr int KT = 16 * P;          // keys per wave tile
     static constexpr int STEPS = D * P / 32;   // MFMA steps over the head dimension
-    static constexpr int WAVES = 4;
+    static constexpr int WAVES = kDecodeWaves;
     static constexpr int THREADS = WAVES * 64;
     static constexpr int KEYS_PER_WG = WAVES * NT * KT;
     static constexpr int GW = G < 4 ? 4 : G;   // heads per LDS weight row (padded to 4)
@@ -164,7 +169,7 @@ __device__ __forceinline__ void unpack_bf16(const unsigned& u, float* f) {
 }
 
 template <int D, int G, int NT>
-__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeKArgs a) {
+__global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(DecodeKArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     using C = DecodeCfg<D, G, NT>;
     // K tiles are staged through LDS: each wave loads its tile with 1 KiB
@@ -623,14 +628,14 @@ constexpr int kMaxVariants = 4;
 
 template <int D, int G, int NT>
 int launch_variant(int grid, hipStream_t stream, const DecodeKArgs& a) {
-    hipLaunchKernelGGL((decode_bf16_kernel<D, G, NT>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_bf16_kernel<D, G, NT>), dim3(grid), dim3(kDecodeWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D, int G, int NT>
 int resident_variant(int* per_cu) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, (const void*)decode_bf16_kernel<D, G, NT>,
-                                                        256, 0);
+                                                        kDecodeWaves * 64, 0);
 }
 
 template <int D, int G, int NT>
@@ -644,7 +649,7 @@ int variants_for(Variant* out) {
     out[k++] = make_variant<D, G, 4>();
     out[k++] = make_variant<D, G, 8>();
     if constexpr (G != 16) out[k++] = make_variant<D, G, 16>();
-    if constexpr (G == 1 || G == 8) out[k++] = make_variant<D, G, 32>();
+    if constexpr (G == 8) out[k++] = make_variant<D, G, 32>();   // one head: its K list would not fit in LDS
     return k;
 }
 
