@@ -101,6 +101,8 @@ def make_case(Hq, Hkv, d, Lmax, lens, k=32, dtype=torch.bfloat16, n_sinks=1, see
     (8, 4, 64, 520, [520, 17]),               # g=2, d=64
     (16, 1, 128, 400, [400, 200]),            # g=16
     (8, 2, 64, 2500, [2500, 2499, 1024]),     # g=4, d=64, several chunks
+    (8, 2, 128, 4100, [4100, 2049, 2048, 2047]),  # lengths at and around chunk boundaries
+    (16, 1, 64, 300, [300, 33]),              # g=16, d=64
 ])
 def test_decode_bf16_parity(Hq, Hkv, d, Lmax, lens):
     print(f"decode bf16 Hq={Hq} Hkv={Hkv} d={d} Lmax={Lmax} lens={lens}", flush=True)

@@ -142,7 +142,45 @@ def test_prefill_dense_theta_bf16_d64():
     assert (g["kc"] == np.arange(1, L + 1)).all()
 
 
+@pytest.mark.parametrize("L", [1, 2, 64, 65])
+def test_prefill_bf16_edge_lengths(L):
+    """Sequences of one row, one full key tile and one tile plus a key, with
+    theta from calibration (k=1) and VMC."""
+    Hq, Hkv, d = 4, 2, 128
+    qc, kc, _ = batch_of_sequences(UNIT, ROLE_CALIB, 9, 0, 3, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    theta = oracle_calibrate(qc, kc, [1], L)[0][0]
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 9, L, B=2, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    g = run_prefill(q, k, v, theta, tt.TOPTH_VMC)
+    compare_prefill(g, q, k, v, theta, tt.TOPTH_VMC, torch.bfloat16)
+
+
+@pytest.mark.parametrize("flags", [tt.TOPTH_VMC, 0, tt.TOPTH_SDC_NONE])
+def test_prefill_keeps_nothing(flags):
+    """theta above every probability: k~ = 0 on every row, beta = 1; the output
+    is mu (VMC), 0 (exact SDC without VMC) or 0 (SDC_NONE, beta 0)."""
+    Hq, Hkv, L, d = 4, 1, 150, 128
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 10, 0, B=1, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    theta = np.full((Hq, L), 1.5)
+    g = run_prefill(q, k, v, theta, flags)
+    compare_prefill(g, q, k, v, theta, flags, torch.bfloat16)
+    assert (g["kc"] == 0).all()
+
+
 # ----------------------------------------------------------------- calibration
+def test_calibrate_bf16_extreme_k():
+    """Eight targets at once, from k = 1 (the row maximum) to k >= L (no row
+    reaches it: no samples, theta = -inf on every row)."""
+    Hq, L, d = 2, 100, 128
+    q, k, _ = batch_of_sequences(UNIT, ROLE_CALIB, 11, 0, 3, Hq=Hq, Hkv=Hq, Lq=L, Lk=L, d=d)
+    ks = [1, 2, 3, 50, 99, 100, 150, 7]
+    th_gpu, cnt_gpu = gpu_calibrate(q, k, ks, L)
+    th_ref, cnt_ref = oracle_calibrate(q, k, ks, L)
+    assert np.array_equal(cnt_gpu, cnt_ref)
+    check_theta(th_gpu, th_ref)
+    assert np.isneginf(th_gpu[5]).all() and np.isneginf(th_gpu[6]).all()
+    assert (cnt_gpu[5] == 0).all() and (cnt_gpu[6] == 0).all()
+
+
 def test_calibrate_bf16_multi_k_prefill_style():
     Hq, L, d = 4, 300, 128
     q, k, _ = batch_of_sequences(UNIT, ROLE_CALIB, 5, 0, 6, Hq=Hq, Hkv=Hq, Lq=L, Lk=L, d=d)
