@@ -72,7 +72,11 @@ struct DecodeCfg {
     static constexpr int NLD = KT / RPI;       // load instructions per wave tile
     static constexpr int STAGE_BYTES = KT * D * 2;              // one staged wave tile
     static constexpr int NBUF = P == 4 ? 1 : 2;                 // stage buffers per wave
-    static constexpr int CAPW = (NBUF * STAGE_BYTES - 4096) / (GW * 4);  // kept-key weights in LDS per wave
+    // the weighted V sum runs on MFMA in batches of 32 rows where the stage
+    // holds such a batch next to a useful weight list (every group size but 16)
+    static constexpr bool MFMA_ACC = NBUF * STAGE_BYTES >= 32 * D * 2 + 4096;
+    static constexpr int DB = D / 16;                           // 16-dim blocks of the output
+    static constexpr int CAPW = (NBUF * STAGE_BYTES - (MFMA_ACC ? 32 * D * 2 : 4096)) / (GW * 4);  // kept-key weights in LDS per wave
     static constexpr int RED_BYTES = WAVES * G * D * 4;         // output partials per workgroup
     static constexpr int KBUF_BYTES =
         WAVES * NBUF * STAGE_BYTES > RED_BYTES ? WAVES * NBUF * STAGE_BYTES : RED_BYTES;
@@ -152,6 +156,18 @@ template <> struct VVec<2> {
         return __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0);
     }
 };
+
+typedef short dec_i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 dec_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float dec_f32x2 __attribute__((ext_vector_type(2)));
+// (a, b) = hi + lo with both parts packed bfloat16 pairs (round to nearest even):
+// the weights keep about 16 significant bits through the two bf16 MFMAs
+__device__ __forceinline__ void split_bf16x2_pair(float a, float b, unsigned& hi, unsigned& lo) {
+    const dec_f32x2 v = {a, b};
+    hi = __builtin_bit_cast(unsigned, __builtin_convertvector(v, dec_bf16x2));
+    const dec_f32x2 r = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u)};
+    lo = __builtin_bit_cast(unsigned, __builtin_convertvector(r, dec_bf16x2));
+}
 
 __device__ __forceinline__ void unpack_bf16(const u32x4& u, float* f) {
 #pragma unroll
@@ -379,11 +395,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
             Lr[r] = hv ? s_lse[hb + r] : 0.f;
         }
         int ucount = 0;
-        float acc[G][C::DPL];
+        float acc[C::MFMA_ACC ? 1 : G][C::DPL];               // FMA path: [head][dims of this lane]
+        f32x4 oacc[C::MFMA_ACC ? C::DB : 1];                   // MFMA path: O^T blocks (dims x heads)
+        if constexpr (C::MFMA_ACC) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+            for (int db = 0; db < C::DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
 #pragma unroll
-            for (int i = 0; i < C::DPL; ++i) acc[h][i] = 0.f;
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int i = 0; i < C::DPL; ++i) acc[h][i] = 0.f;
+        }
 
         const unsigned long long keylanes =
             C::BPT == 1 ? ~0ull : (C::BPT == 2 ? 0x0000ffff0000ffffull : 0xffffull);
@@ -474,7 +496,85 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
             }
         }
         wait_lds();
-        {
+        if constexpr (C::MFMA_ACC) {
+            // O^T += V^T W over the listed rows, 32 per MFMA step: the kept V
+            // rows are fetched with buffer_load ... lds into the part of the
+            // stage above the weights (16-byte chunk c of batch row j in slot
+            // c ^ (j % CPR)), the tail of the last batch is zeroed, and V^T
+            // fragments come out of LDS transpose reads (in each 16-lane group,
+            // lane i receives column i % 4 of the 8-byte rows addressed by lanes
+            // i / 4 + 4 e).  The k-slot j of lane group lq stands for row
+            // 8 lq + j of the step in both operands.  Weights enter as a bf16
+            // high part and remainder (two MFMAs), heads in the 16 columns.
+            const int nl = lcount < C::CAPW ? lcount : C::CAPW;
+            const int wbytes = (nl * C::GW * 4 + 1023) & ~1023;
+            unsigned char* vbuf = stage + wbytes;
+            const int vrows_cap = ((C::NBUF * C::STAGE_BYTES - wbytes) / (D * 2)) / 32 * 32;
+            const int l16 = lane & 15, lq = lane >> 4;
+            int tr_off[2];                                     // byte offsets of the transpose reads, db = 0
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int j = 8 * lq + 4 * hh + l16 / 4;       // row of the step (steps start at multiples of 32)
+                const int c = (4 * (l16 % 4)) / 8;
+                tr_off[hh] = j * (D * 2) + ((c ^ (j % C::CPR)) * 16) + ((l16 % 4) & 1) * 8;
+            }
+            for (int b0 = 0; b0 < lcount; b0 += vrows_cap) {
+                const int nrows = lcount - b0 < vrows_cap ? lcount - b0 : vrows_cap;
+                const int nrows32 = (nrows + 31) & ~31;
+                for (int i = 0; i * C::RPI < nrows; ++i) {
+                    const int j = i * C::RPI + lane / C::CPR;
+                    const int e = b0 + j;
+                    const int key = wbase + (e < lcount ? (int)s_kl[wave][e] : 0);
+                    const int chunk = (lane % C::CPR) ^ (j % C::CPR);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        vrs, (__attribute__((address_space(3))) void*)(vbuf + i * 1024), 16,
+                        key * (D * 2) + chunk * 16, 0, 0, 0);
+                }
+                {
+                    const int zr0 = (nrows + C::RPI - 1) / C::RPI * C::RPI;   // rows past the loaded ones
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    for (int t = lane; t < (nrows32 - zr0) * C::CPR; t += 64)
+                        *(u32x4*)(vbuf + (zr0 + t / C::CPR) * (D * 2) + (t % C::CPR) * 16) = z;
+                }
+                wait_vmem();
+                wait_lds();
+                for (int j0 = 0; j0 < nrows32; j0 += 32) {
+                    // weights of rows j0 + 8 lq .. + 7 for head l16 (0 past the list or the heads)
+                    float w[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const int e = b0 + j0 + 8 * lq + jj;
+                        float x = 0.f;
+                        if (l16 < G && e < lcount)
+                            x = e < nl ? s_wl[e][l16] : consume(ovf + (size_t)(wbase + s_kl[wave][e]) * C::GW + l16);
+                        w[jj] = x;
+                    }
+                    u32x4 whi, wlo;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        unsigned hi, lo;
+                        split_bf16x2_pair(w[2 * q], w[2 * q + 1], hi, lo);
+                        whi[q] = hi; wlo[q] = lo;
+                    }
+                    const bf16x8 bw = __builtin_bit_cast(bf16x8, whi), bwl = __builtin_bit_cast(bf16x8, wlo);
+                    const unsigned char* vb = vbuf + j0 * (D * 2);
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) {
+                        const int dboff = (2 * db) * 16;       // chunk 2 db + c: XOR on bits c does not use
+                        const dec_i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) dec_i16x4*)(vb + (tr_off[0] ^ dboff)));
+                        const dec_i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) dec_i16x4*)(vb + (tr_off[1] ^ dboff)));
+                        typedef short i16x8 __attribute__((ext_vector_type(8)));
+                        const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                        const bf16x8 va = __builtin_bit_cast(bf16x8, v8);
+                        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bw, oacc[db], 0, 0, 0);
+                        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bwl, oacc[db], 0, 0, 0);
+                    }
+                }
+                wait_lds();                                   // rows consumed before the next batch
+            }
+        } else {
             // The kept V rows are fetched with buffer_load ... lds into the part
             // of the stage above the weights (one 1 KiB instruction per RPI rows,
             // all of a batch in flight at once), then accumulated from LDS.
@@ -522,21 +622,33 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
         }
 
         // ---- partial results of this workgroup
+        if constexpr (C::MFMA_ACC) {
+            __syncthreads();                   // every wave is done with its K staging
+            // lane holds O^T[16 db + 4 lq + r][head l16]
+            const int l16 = lane & 15, lq = lane >> 4;
+            if (l16 < G) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+                for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int i = 0; i < C::DPL; ++i) {
-                float x = acc[h][i];
-                if (C::LPR == 16) x += __shfl_xor(x, 16);
-                x += __shfl_xor(x, 32);
-                acc[h][i] = x;
+                    for (int r = 0; r < 4; ++r) s_red[wave][l16][16 * db + 4 * lq + r] = oacc[db][r];
             }
-        __syncthreads();                       // every wave is done with its K staging
-        if (lane < C::LPR) {
+        } else {
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int i = 0; i < C::DPL; ++i) s_red[wave][h][lane * C::DPL + i] = acc[h][i];
+                for (int i = 0; i < C::DPL; ++i) {
+                    float x = acc[h][i];
+                    if (C::LPR == 16) x += __shfl_xor(x, 16);
+                    x += __shfl_xor(x, 32);
+                    acc[h][i] = x;
+                }
+            __syncthreads();                   // every wave is done with its K staging
+            if (lane < C::LPR) {
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                    for (int i = 0; i < C::DPL; ++i) s_red[wave][h][lane * C::DPL + i] = acc[h][i];
+            }
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
