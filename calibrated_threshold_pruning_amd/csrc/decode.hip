@@ -82,6 +82,10 @@ struct DecodeCfg {
         WAVES * NBUF * STAGE_BYTES > RED_BYTES ? WAVES * NBUF * STAGE_BYTES : RED_BYTES;
     static_assert(STEPS >= 1 && NLD >= 1, "head dimension too small");
     static_assert(WKEYS <= 65536, "wave key offsets must fit 16 bits");
+    static_assert(NT <= 32, "one bit per tile in a 32-bit mask");
+    // spare list slots (one per lane) for stores that keep nothing
+    static constexpr int SPARE = CAPW < WKEYS ? CAPW : WKEYS;
+    static_assert((SPARE + 64) * GW * 4 <= NBUF * STAGE_BYTES, "spare weight rows inside the stage");
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
     __shared__ __attribute__((aligned(16))) uint16_t s_q[G + 1][D + 8];   // row G stays zero
     __shared__ float s_m[C::WAVES][G], s_l[C::WAVES][G];
     __shared__ float s_T[G], s_lse[G];
-    __shared__ unsigned short s_kl[C::WAVES][C::WKEYS];   // kept keys of each wave (offsets from its base)
+    __shared__ unsigned short s_kl[C::WAVES][C::WKEYS + 64];   // kept keys of each wave (offsets from its base), + spare slots
     __shared__ float s_cm[C::WAVES][G];
     __shared__ int s_cc[C::WAVES][G];
     __shared__ int s_un[C::WAVES];
@@ -387,13 +391,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
         __syncthreads();
 
         // ---- phase 2: threshold, compaction, sparse V gather
-        float Tr[4], Lr[4];
+        float Tr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const bool hv = hb + r < G;
             Tr[r] = hv ? s_T[hb + r] : INFINITY;
-            Lr[r] = hv ? s_lse[hb + r] : 0.f;
         }
+        wait_lds();                            // no LDS read is left pending into the tile loop
         int ucount = 0;
         float acc[C::MFMA_ACC ? 1 : G][C::DPL];               // FMA path: [head][dims of this lane]
         f32x4 oacc[C::MFMA_ACC ? C::DB : 1];                   // MFMA path: O^T blocks (dims x heads)
@@ -407,8 +411,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                 for (int i = 0; i < C::DPL; ++i) acc[h][i] = 0.f;
         }
 
-        const unsigned long long keylanes =
-            C::BPT == 1 ? ~0ull : (C::BPT == 2 ? 0x0000ffff0000ffffull : 0xffffull);
         const uint16_t* vg = a.v + (size_t)group * a.Lmax * D;
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, n * D * 2);
 
@@ -423,43 +425,68 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
         int lcount = 0;
         const int vlane = (lane % C::LPR) * C::DPL * 2;
         const int keylane = lane - 16 * cc;      // lane that stands for this lane's key
-        const unsigned long long below_key = keylane == 0 ? 0ull : (~0ull >> (64 - keylane));
         unsigned char* kmask = a.kept_mask ? a.kept_mask + ((size_t)b * a.Hq + (size_t)kv * G) * a.Lmax : nullptr;
+        // the per-head kept mask, only where it is asked for
+        if (kmask) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int key0 = wbase + t * C::KT;
-            if (key0 < n) {
-                bool kp[4];
-                bool own = false;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    kp[r] = sc[t][r] >= Tr[r];
-                    own |= kp[r];
-                }
-                if (kmask) {
+            for (int t = 0; t < NT; ++t) {
+                const int key = wbase + t * C::KT + mykey;
+                if (key < n) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (hb + r < G && key0 + mykey < a.Lmax)
-                            kmask[(size_t)(hb + r) * a.Lmax + key0 + mykey] = kp[r] ? 1 : 0;
+                        if (hb + r < G) kmask[(size_t)(hb + r) * a.Lmax + key] = sc[t][r] >= Tr[r] ? 1 : 0;
                 }
-                // union over the key's heads: the lanes of one key sit 16 lanes apart
-                unsigned long long ub = __ballot(own);
-                if (C::BPT >= 2) ub |= ub >> 16;
-                if (C::BPT == 4) ub |= ub >> 32;
-                const unsigned long long bal = ub & keylanes;
-                const int any = (int)((bal >> keylane) & 1ull);
-                if (any) {
-                    const int idx = lcount + __popcll(bal & below_key);
-                    const float4 wv = make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]);
-                    if (idx < C::CAPW) *(float4*)&s_wl[idx][hb] = wv;
-                    else {
-                        float* dst = &ovf[(size_t)(key0 + mykey) * C::GW + hb];
+            }
+        }
+        // Tiles past the n valid keys hold -inf scores, which never reach a
+        // threshold (thresholds are clamped to -FLT_MAX).  Bit t of kbits: some
+        // head of the group keeps this lane's key of tile t (the lanes of one
+        // key sit 16 lanes apart and are merged).  List slots follow the key
+        // lanes in order, each lane's tiles in order: an exclusive prefix sum
+        // of the per-lane counts, taken bit by bit with ballots.
+        // A head keeps the key when x >= T, i.e. when x - T >= 0 (the rounded
+        // difference of two floats has the sign of the exact one, and -inf - T
+        // is -inf); the maximum over the lane's heads decides with one compare.
+        unsigned kbits = 0u;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float dmax = fmaxf(fmaxf(sc[t][0] - Tr[0], sc[t][1] - Tr[1]),
+                                     fmaxf(sc[t][2] - Tr[2], sc[t][3] - Tr[3]));
+            kbits |= (dmax >= 0.f) ? (1u << t) : 0u;
+        }
+        if (C::BPT >= 2) kbits |= __shfl_xor(kbits, 16);
+        if (C::BPT == 4) kbits |= __shfl_xor(kbits, 32);
+        const int kc = cc == 0 ? __popc(kbits) : 0;
+        int lbase = 0, ltotal = 0;
+#pragma unroll
+        for (int bit = 0; (1 << bit) <= NT; ++bit) {
+            const unsigned long long bb = __ballot((kc >> bit) & 1);
+            lbase += (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bb >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((unsigned)bb, 0u)) << bit;
+            ltotal += __popcll(bb) << bit;
+        }
+        lbase = __shfl(lbase, keylane);
+        {
+            // Weights of the first CAPW entries go to the LDS list, later ones
+            // (rows that keep nearly everything) to the workspace slot of their
+            // key.  Lanes with nothing to store write spare slots of their own,
+            // so the stores need no branch.
+            const bool fits = ltotal <= C::CAPW;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const bool kept = (kbits >> t) & 1u;
+                const int idx = lbase + __popc(kbits & ((1u << t) - 1u));
+                const float4 wv = make_float4(sc[t][0], sc[t][1], sc[t][2], sc[t][3]);
+                *(float4*)&s_wl[(kept && idx < C::CAPW) ? idx : C::SPARE + lane][hb] = wv;
+                s_kl[wave][kept ? idx : C::WKEYS + lane] = (unsigned short)(t * C::KT + mykey);
+                if (!fits) {
+                    if (kept && idx >= C::CAPW) {
+                        float* dst = &ovf[(size_t)(wbase + t * C::KT + mykey) * C::GW + hb];
                         publish(dst, wv.x); publish(dst + 1, wv.y); publish(dst + 2, wv.z); publish(dst + 3, wv.w);
                     }
-                    if (cc == 0) s_kl[wave][idx] = (unsigned short)(t * C::KT + mykey);
                 }
-                lcount += __popcll(bal);
             }
+            lcount = ltotal;
         }
         ucount = lcount;
         wait_lds();
