@@ -31,6 +31,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -66,6 +67,19 @@ CALIB_WORKLOAD = dict(layers=32, Hq=8, Hkv=8, d=128, L=2048, seqs=512, ks=[64, 1
 EXP_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9   # v_exp_f32: quarter-rate on 16-lane SIMDs
 
 
+def code_sha256(sources):
+    """SHA-256 of the code in `sources` with comments and whitespace removed, so
+    that a change to comments alone does not mark counter data as stale."""
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", "", text).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel, workload, sources):
     """HBM bytes per launch from the committed counter summary of `kernel` on
     `workload` (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel of known
@@ -78,11 +92,7 @@ def measured_traffic(kernel, workload, sources):
         if ":" in line:
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip().split()[0] if val.strip() else ""
-    h = hashlib.sha256()
-    for f in sources:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_dispatch" not in fields:
+    if fields.get("source_sha256") != code_sha256(sources) or "traffic_bytes_per_dispatch" not in fields:
         return None
     return int(float(fields["traffic_bytes_per_dispatch"]))
 

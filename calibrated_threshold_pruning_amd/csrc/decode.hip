@@ -8,9 +8,10 @@
 // the V rows that some head of the GQA group keeps are read (Sec. 4.6).
 //
 // Kernel shape (persistent; the grid never exceeds the resident capacity):
-//   work item = (group = (b, kv head), chunk of keys); 4 waves per workgroup.
-//   Phase 1  each wave streams its keys' K rows straight from HBM in the MFMA
-//            B-operand layout and forms the g scores per key with
+//   work item = (group = (b, kv head), chunk of keys); one workgroup of 8 waves
+//   per CU.
+//   Phase 1  each wave stages its keys' K rows in LDS (buffer_load ... lds,
+//            XOR-swizzled) and forms the g scores per key with
 //            v_mfma_f32_16x16x32_bf16 (query heads in the A operand, several
 //            key tiles packed into the 16 rows when g < 16).  Scores stay in
 //            registers; the wave and the workgroup reduce per-head (max, sum
@@ -19,9 +20,9 @@
 //            chunk then combines all partials in the same order, so all see the
 //            same row log-sum-exp.
 //   Phase 2  compare x >= log2(theta) + lse2 per (key, head); OR over the
-//            group's heads; ballot + popcount compaction of the kept keys into
-//            a per-wave LDS list; gather only those V rows with 16 lanes x
-//            16 bytes per 256-byte row; accumulate s * V per head in float32.
+//            group's heads; ballot prefix sums compact the kept keys into a
+//            per-wave LDS list; only those V rows are gathered (buffer_load ...
+//            lds) and O^T += V^T W runs on MFMA from LDS transpose reads.
 //   Combine  the last chunk of a group to finish sums the chunk partials in a
 //            fixed order and applies beta * mu.
 // Reductions never use float atomics, so results are run-to-run identical.
