@@ -137,6 +137,33 @@ def test_decode_dense_and_empty_thresholds():
     assert np.abs(g["out"]).max() == 0.0
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,d,Lmax", [
+    # g=8, d=128: 64 groups x 5 chunks of the 8-tile variant exceed 256 workgroups,
+    # so the 16-tile variant runs (512 keys per wave, 256 in the LDS list)
+    (8, 64, 8, 128, 8200),
+    # g=4, d=64: 128 groups x 3 chunks of the 4-tile variant exceed 256, so the
+    # 8-tile variant runs (512 keys per wave, 256 in the LDS list)
+    (64, 8, 2, 64, 4200),
+])
+def test_decode_dense_overflow(B, Hq, Hkv, d, Lmax):
+    """theta = -inf keeps every key: each wave's kept list outgrows its LDS room and
+    the rest of its weights go through the workspace on the MFMA accumulate path."""
+    print(f"decode dense overflow B={B} Hq={Hq} Hkv={Hkv} d={d} Lmax={Lmax}", flush=True)
+    base = [Lmax, Lmax - 1, Lmax // 2 + 1, Lmax // 2, 1000, 257, 33, 1]
+    lens = [base[i % len(base)] for i in range(B)]
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 0, 7, B=B, Hq=Hq, Hkv=Hkv, Lq=1, Lk=Lmax, d=d,
+                               n_sinks=1, dtype=torch.bfloat16)
+    q = q[:, :, 0].contiguous()
+    vf = to_f64(v)
+    vm = np.stack([[vf[b, h, :lens[b]].mean(0) for h in range(Hkv)] for b in range(B)])
+    vm = vm.astype(np.float32).astype(np.float64)
+    dense = np.full((Hq, Lmax), -np.inf)
+    g = run_decode(q, k, v, lens, dense, vm, tt.TOPTH_VMC)
+    assert (g["vr"] == np.array(lens)[:, None]).all()
+    assert (g["kc"] == np.array(lens)[:, None]).all()
+    compare_decode(g, q, k, v, lens, dense, vm, tt.TOPTH_VMC, torch.bfloat16)
+
+
 def test_decode_f32_parity():
     lens = [333, 100, 1]
     q, k, v, theta, vm = make_case(8, 2, 64, 333, lens, dtype=torch.float32, seed_index=3)
