@@ -116,7 +116,8 @@ def topth_workspace_init(ws: torch.Tensor, stream=None):
 
 def workspace(op: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, d: int, n_k: int = 1,
               device="cuda") -> torch.Tensor:
-    """Allocate a zero-initialised workspace tensor of the size the library asks for."""
+    """Allocate a workspace tensor of the size the library asks for, prepared by
+    topth_workspace_init (header zeroed, decode exchange slots empty)."""
     n = topth_workspace_size(op, B, Hq, Hkv, Lq, Lk, d, n_k)
     if n == 0:
         raise ValueError("no workspace size for these arguments")

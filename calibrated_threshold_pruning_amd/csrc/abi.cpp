@@ -88,7 +88,13 @@ size_t topth_workspace_size(int op, int B, int Hq, int Hkv, int Lq, int Lk, int 
 
 int topth_workspace_init(void* ws, size_t ws_bytes, void* stream) {
     if (!ws || ws_bytes == 0) return TOPTH_EINVAL;
-    return map_hip(launch_fill_zero(ws, ws_bytes, (hipStream_t)stream));
+    // header zero (status word), every slot after it empty
+    const size_t head = ws_bytes < kWsHeaderBytes ? ws_bytes : kWsHeaderBytes;
+    int e = launch_fill_u32(ws, head, 0u, (hipStream_t)stream);
+    if (e == hipSuccess && ws_bytes > kWsHeaderBytes)
+        e = launch_fill_u32((char*)ws + kWsHeaderBytes, ws_bytes - kWsHeaderBytes, kWsSlotEmpty,
+                            (hipStream_t)stream);
+    return map_hip(e);
 }
 
 int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq, int Lk,
@@ -164,7 +170,6 @@ int topth_decode(const void* q, const void* k_cache, const void* v_cache, const 
     if (!isfinite(scale) || !(scale > 0.0f) || (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE))) return TOPTH_EINVAL;
     if ((flags & TOPTH_VMC) && !(flags & TOPTH_SDC_NONE) && !v_mean) return TOPTH_EINVAL;
     if (too_big((long long)B * Hkv * Lmax, d)) return TOPTH_EUNSUPPORTED;
-    if ((long long)B * Hkv > kWsMaxGroups) return TOPTH_EUNSUPPORTED;
     if (!ws) return TOPTH_EWORKSPACE;
     if (ws_bytes < decode_ws(B, Hq, Hkv, Lmax, d)) return TOPTH_EWORKSPACE;
     DecodeParams p = {};

@@ -38,8 +38,10 @@ struct DecodeKArgs {
     const uint16_t* q; const uint16_t* k; const uint16_t* v; const int* seq_lens;
     const float* theta; const float* v_mean;
     uint16_t* out; int* kept_count; float* beta; int* vrows_read; unsigned char* kept_mask;
-    int* status; int* counters;
-    float2* part_ml; float* part_out; float* part_mass; int* part_cnt; int* part_union;
+    int* status;
+    // exchange slots, kWsSlotEmpty until published: (max, sum of exp2) per chunk
+    // and head as one 64-bit word, and the partial outputs of chunks 1.. for chunk 0
+    unsigned long long* part_ml; float* part_out; float* part_mass; int* part_cnt; int* part_union;
     float* ovf_w;      // weights of kept keys that do not fit the LDS list, [B*Hkv*Lmax][GW]
     int B, Hq, Hkv, Lmax, n_rows, chunks, items;
     float xscale;
@@ -110,19 +112,53 @@ __device__ __forceinline__ float consume(const float* p) {
     return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT));
 }
-__device__ __forceinline__ int consume_i(const int* p) {
+// Exchange slots hold kWsSlotEmpty (in every 32-bit word) until their chunk
+// publishes them.  A reader issues the loads of up to eight slots together and
+// re-polls the ones still empty; the combining chunk, the last reader of every
+// slot of its group, sets each slot back to empty.
+constexpr unsigned long long kSlot64Empty = ((unsigned long long)kWsSlotEmpty << 32) | kWsSlotEmpty;
+__device__ __forceinline__ unsigned long long load64(const unsigned long long* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// sum of n published values base[c * stride], c = 0..n-1, added in order of c;
-// eight independent loads are in flight at a time
-__device__ __forceinline__ float sum_chunks(const float* base, size_t stride, int n) {
-    float x = 0.f;
-    for (int c0 = 0; c0 < n; c0 += 8) {
-        float v[8];
+__device__ __forceinline__ unsigned load32(const void* p) {
+    return __hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store32(void* p, unsigned v) {
+    __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long wait_slot64(const unsigned long long* p, unsigned long long v,
+                                                        unsigned limit, int* status) {
+    for (unsigned spins = 0; v == kSlot64Empty; v = load64(p)) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > limit) { atomicOr(status, kStatusSpinTimeout); break; }
+    }
+    return v;
+}
+__device__ __forceinline__ unsigned wait_slot32(const void* p, unsigned v, unsigned limit, int* status) {
+    for (unsigned spins = 0; v == kWsSlotEmpty; v = load32(p)) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > limit) { atomicOr(status, kStatusSpinTimeout); break; }
+    }
+    return v;
+}
+// first + base[c * stride] for c = 1 .. n-1, added in order of c (float or int
+// words); every slot read is set back to empty
+template <typename T>
+__device__ __forceinline__ T gather_chunks(T* base, size_t stride, int n, T first, unsigned limit,
+                                           int* status) {
+    T x = first;
+    for (int c0 = 1; c0 < n; c0 += 8) {
+        unsigned v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (c0 + u < n) ? consume(base + (size_t)(c0 + u) * stride) : 0.f;
+        for (int u = 0; u < 8; ++u) v[u] = (c0 + u < n) ? load32(base + (size_t)(c0 + u) * stride) : 0u;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x += v[u];
+        for (int u = 0; u < 8; ++u) {
+            if (c0 + u < n) {
+                T* p = base + (size_t)(c0 + u) * stride;
+                x += __builtin_bit_cast(T, wait_slot32(p, v[u], limit, status));
+                store32(p, kWsSlotEmpty);
+            }
+        }
     }
     return x;
 }
@@ -205,7 +241,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
     __shared__ float s_cm[C::WAVES][G];
     __shared__ int s_cc[C::WAVES][G];
     __shared__ int s_un[C::WAVES];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -355,33 +390,33 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
             float L = 0.f;
             if (M != NEG_INF)
                 for (int w = 0; w < C::WAVES; ++w) L += s_l[w][tid] * exp2f(s_m[w][tid] - M);
-            float* pml = reinterpret_cast<float*>(a.part_ml + ((size_t)group * a.chunks + chunk) * G + tid);
-            publish(pml, M);
-            publish(pml + 1, L);
-        }
-
-        // ---- exchange: wait until every chunk of the group has published
-        __builtin_amdgcn_s_waitcnt(0);        // this wave's published values have landed
-        __syncthreads();
-        if (tid == 0) {
-            int* ctr = a.counters + 2 * group;
-            __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            unsigned spins = 0;
-            while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.chunks) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins > a.spin_limit) { atomicOr(a.status, kStatusSpinTimeout); break; }
-            }
-        }
-        __syncthreads();
-        if (tid < G) {
-            const float2* pm = a.part_ml + (size_t)group * a.chunks * G + tid;
-            float M = NEG_INF;
-            const float* pmf = reinterpret_cast<const float*>(pm);
-            for (int c = 0; c < a.chunks; ++c) M = fmaxf(M, consume(pmf + (size_t)c * G * 2));
-            float L = 0.f;
-            for (int c = 0; c < a.chunks; ++c) {
-                const float2 v = make_float2(consume(pmf + (size_t)c * G * 2), consume(pmf + (size_t)c * G * 2 + 1));
-                if (v.y > 0.f) L += v.y * exp2f(v.x - M);
+            // ---- exchange: publish (M, L), then merge every chunk's pair in
+            // chunk order (this chunk's own from registers), so that all chunks
+            // of the group reach the same LSE
+            unsigned long long* ml = a.part_ml + (size_t)group * a.chunks * G + tid;   // chunk c: ml[c * G]
+            const unsigned long long mine = ((unsigned long long)__float_as_uint(L) << 32) | __float_as_uint(M);
+            if (a.chunks > 1)
+                __hip_atomic_store(ml + (size_t)chunk * G, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            M = NEG_INF;
+            L = 0.f;
+            for (int c0 = 0; c0 < a.chunks; c0 += 4) {        // four slots in flight (the scores hold most registers)
+                unsigned long long v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int c = c0 + u;
+                    v[u] = (c < a.chunks && c != chunk) ? load64(ml + (size_t)c * G) : mine;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (c0 + u < a.chunks) {
+                        const unsigned long long x = wait_slot64(ml + (size_t)(c0 + u) * G, v[u], a.spin_limit, a.status);
+                        const float m = __uint_as_float((unsigned)x), l = __uint_as_float((unsigned)(x >> 32));
+                        if (l > 0.f) {
+                            if (m > M) { L = L * exp2f(M - m) + l; M = m; }
+                            else L += l * exp2f(m - M);
+                        }
+                    }
+                }
             }
             const float lse2 = M + __log2f(L);
             const int h = kv * G + tid;
@@ -687,64 +722,64 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
         if (lane == 0) s_un[wave] = ucount;
         __syncthreads();
         const size_t pbase = (size_t)group * a.chunks + chunk;
-        for (int idx = tid; idx < G * D; idx += C::THREADS) {
-            float x = 0.f;
+        if (chunk > 0) {
+            // ---- chunks 1..: publish the partials for chunk 0
+            for (int idx = tid; idx < G * D; idx += C::THREADS) {
+                float x = 0.f;
 #pragma unroll
-            for (int w = 0; w < C::WAVES; ++w) x += (&s_red[w][0][0])[idx];
-            publish(a.part_out + pbase * G * D + idx, x);
-        }
-        if (tid < G) {
-            float m = 0.f; int c = 0;
-            for (int w = 0; w < C::WAVES; ++w) { m += s_cm[w][tid]; c += s_cc[w][tid]; }
-            publish(a.part_mass + pbase * G + tid, m);
-            publish_i(a.part_cnt + pbase * G + tid, c);
-        }
-        if (tid == 0) {
-            int u = 0;
-            for (int w = 0; w < C::WAVES; ++w) u += s_un[w];
-            publish_i(a.part_union + pbase, u);
-        }
-
-        // ---- the last chunk of the group to finish combines
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) {
-            const int old = __hip_atomic_fetch_add(a.counters + 2 * group + 1, 1, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (old == a.chunks - 1);
-        }
-        __syncthreads();
-        if (s_last) {
+                for (int w = 0; w < C::WAVES; ++w) x += (&s_red[w][0][0])[idx];
+                publish(a.part_out + pbase * G * D + idx, x);
+            }
+            if (tid < G) {
+                float m = 0.f; int c = 0;
+                for (int w = 0; w < C::WAVES; ++w) { m += s_cm[w][tid]; c += s_cc[w][tid]; }
+                publish(a.part_mass + pbase * G + tid, m);
+                publish_i(a.part_cnt + pbase * G + tid, c);
+            }
+            if (tid == 0) {
+                int u = 0;
+                for (int w = 0; w < C::WAVES; ++w) u += s_un[w];
+                publish_i(a.part_union + pbase, u);
+            }
+        } else {
+            // ---- chunk 0 combines, adding the partials in chunk order
             const bool renorm = (a.flags & 2u) != 0;
             const bool vmc = (a.flags & 1u) != 0 && !renorm;
             const size_t g0 = (size_t)group * a.chunks;
             if (tid < G) {
-                const float m = sum_chunks(a.part_mass + g0 * G + tid, G, a.chunks);
-                int c = 0;
-                for (int ch = 0; ch < a.chunks; ++ch) c += consume_i(a.part_cnt + (g0 + ch) * G + tid);
+                float m = 0.f; int c = 0;
+                for (int w = 0; w < C::WAVES; ++w) { m += s_cm[w][tid]; c += s_cc[w][tid]; }
+                m = gather_chunks(a.part_mass + g0 * G + tid, G, a.chunks, m, a.spin_limit, a.status);
+                c = gather_chunks(a.part_cnt + g0 * G + tid, G, a.chunks, c, a.spin_limit, a.status);
                 s_cm[0][tid] = m;
                 s_cc[0][tid] = c;
                 const size_t o = (size_t)b * a.Hq + (size_t)kv * G + tid;
                 if (a.kept_count) a.kept_count[o] = c;
                 if (a.beta) a.beta[o] = renorm ? 0.f : 1.f - m;
+                // every chunk has passed the exchange (it published after it):
+                // its slots are empty again for the next call
+                if (a.chunks > 1)
+                    for (int ch = 0; ch < a.chunks; ++ch)
+                        __hip_atomic_store(a.part_ml + (g0 + ch) * G + tid, kSlot64Empty, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
             }
-            if (tid == 0 && a.vrows_read) {
+            if (tid == 0) {
                 int u = 0;
-                for (int ch = 0; ch < a.chunks; ++ch) u += consume_i(a.part_union + g0 + ch);
-                a.vrows_read[group] = u;
+                for (int w = 0; w < C::WAVES; ++w) u += s_un[w];
+                u = gather_chunks(a.part_union + g0, 1, a.chunks, u, a.spin_limit, a.status);
+                if (a.vrows_read) a.vrows_read[group] = u;
             }
             __syncthreads();
             for (int idx = tid; idx < G * D; idx += C::THREADS) {
                 const int h = idx / D, dd = idx % D;
-                float x = sum_chunks(a.part_out + g0 * G * D + idx, (size_t)G * D, a.chunks);
+                float x = 0.f;
+#pragma unroll
+                for (int w = 0; w < C::WAVES; ++w) x += (&s_red[w][0][0])[idx];
+                x = gather_chunks(a.part_out + g0 * G * D + idx, (size_t)G * D, a.chunks, x, a.spin_limit, a.status);
                 const float mass = s_cm[0][h];
                 if (renorm) x = (s_cc[0][h] > 0) ? x / mass : 0.f;
                 if (vmc) x = fmaf(1.f - mass, a.v_mean[(size_t)group * D + dd], x);
                 a.out[((size_t)b * a.Hq + (size_t)kv * G + h) * D + dd] = f32_to_bf16_bits(x);
-            }
-            if (tid == 0) {
-                __hip_atomic_store(a.counters + 2 * group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.counters + 2 * group + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         __syncthreads();
@@ -849,7 +884,7 @@ size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lmax, int d) {
     const size_t chunks = (size_t)((Lmax + keys_per_wg_min(G) - 1) / keys_per_wg_min(G));
     const size_t pc = groups * chunks;
     size_t bytes = kWsHeaderBytes;
-    bytes += pc * G * sizeof(float2);
+    bytes += pc * G * sizeof(unsigned long long);
     bytes += pc * G * d * sizeof(float);
     bytes += pc * G * sizeof(float);
     bytes += pc * G * sizeof(int);
@@ -896,7 +931,7 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     const int items = chunks * groups;
     const int grid = std::min(items, (capacity / chunks) * chunks);
 
-    // workspace carve-up (the header holds status and counters)
+    // workspace carve-up (the header holds the status word)
     char* ws = (char*)p.ws;
     DecodeKArgs a = {};
     a.q = (const uint16_t*)p.q; a.k = (const uint16_t*)p.k; a.v = (const uint16_t*)p.v;
@@ -904,10 +939,9 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     a.out = (uint16_t*)p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.vrows_read = p.vrows_read;
     a.kept_mask = p.kept_mask;
     a.status = (int*)ws;
-    a.counters = (int*)ws + kWsCounterOffsetInts;
     size_t off = kWsHeaderBytes;
     const size_t pc = (size_t)items;
-    a.part_ml = (float2*)(ws + off); off += pc * G * sizeof(float2);
+    a.part_ml = (unsigned long long*)(ws + off); off += pc * G * sizeof(unsigned long long);
     a.part_out = (float*)(ws + off); off += pc * G * p.d * sizeof(float);
     a.part_mass = (float*)(ws + off); off += pc * G * sizeof(float);
     a.part_cnt = (int*)(ws + off); off += pc * G * sizeof(int);

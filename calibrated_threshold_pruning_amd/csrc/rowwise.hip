@@ -213,8 +213,9 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
 }
 
 // number of distinct V rows the GQA group reads: popcount of the OR of its
-// heads' kept-key masks (Sec. 4.6)
-__global__ void union_count_kernel(const uint32_t* masks, int Hq, int Hkv, int mask_words,
+// heads' kept-key masks (Sec. 4.6).  The mask words live in the decode
+// workspace; each is set back to the empty-slot pattern once read.
+__global__ void union_count_kernel(uint32_t* masks, int Hq, int Hkv, int mask_words,
                                    int* vrows_read) {
     __shared__ int red[4];
     const int bk = blockIdx.x;
@@ -223,7 +224,11 @@ __global__ void union_count_kernel(const uint32_t* masks, int Hq, int Hkv, int m
     int c = 0;
     for (int w = threadIdx.x; w < mask_words; w += blockDim.x) {
         uint32_t u = 0;
-        for (int hh = 0; hh < g; ++hh) u |= masks[((size_t)b * Hq + kv * g + hh) * mask_words + w];
+        for (int hh = 0; hh < g; ++hh) {
+            uint32_t* m = masks + ((size_t)b * Hq + kv * g + hh) * mask_words + w;
+            u |= *m;
+            *m = kWsSlotEmpty;
+        }
         c += __popc(u);
     }
     c = wave_sum_i(c);
@@ -365,10 +370,10 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     }
 }
 
-__global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
+__global__ void fill_u32_kernel(uint32_t* p, size_t n_words, uint32_t value) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;
          i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
+        p[i] = value;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -414,7 +419,7 @@ int launch_decode_rowwise(const DecodeParams& p, uint32_t* masks_ws, hipStream_t
     if (e != hipSuccess) return e;
     if (p.vrows_read) {
         hipLaunchKernelGGL(union_count_kernel, dim3(p.B * p.Hkv), dim3(256), 0, s,
-                           (const uint32_t*)masks_ws, p.Hq, p.Hkv, a.mask_words, p.vrows_read);
+                           masks_ws, p.Hq, p.Hkv, a.mask_words, p.vrows_read);
         e = hipGetLastError();
     }
     return e;
@@ -496,12 +501,12 @@ int launch_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, i
     return hipGetLastError();
 }
 
-int launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+int launch_fill_u32(void* p, size_t bytes, uint32_t value, hipStream_t s) {
     const size_t words = bytes / 4;
     if (words == 0) return hipSuccess;
     unsigned blocks = (unsigned)((words + 255) / 256);
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, words);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, words, value);
     return hipGetLastError();
 }
 

@@ -15,10 +15,12 @@ typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWave = 64;
 
-// Workspace header: status word, then per-group counters of the decode barrier.
+// Workspace: a header (status word at byte 0, the rest reserved), then the
+// decode exchange slots.  An empty slot holds kWsSlotEmpty in every 32-bit
+// word: a NaN payload that float arithmetic never produces (it returns the
+// default NaN 0x7FC00000) and no count or length reaches as an integer.
 constexpr size_t kWsHeaderBytes = 65536;
-constexpr int kWsCounterOffsetInts = 64;           // counters start at byte 256
-constexpr int kWsMaxGroups = (int)((kWsHeaderBytes / 4 - kWsCounterOffsetInts) / 2);
+constexpr uint32_t kWsSlotEmpty = 0x7FC0DEADu;
 constexpr int kStatusSpinTimeout = 1;
 
 // ---------------------------------------------------------------- conversions
@@ -113,6 +115,6 @@ int launch_finalize(const double* sum, const double* sumsq, const int* count, co
                     int n_k, int Hq, int n_rows, float alpha, float* theta, hipStream_t s);
 int launch_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,
                  float* v_mean, hipStream_t s);
-int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+int launch_fill_u32(void* p, size_t bytes, uint32_t value, hipStream_t s);
 
 }  // namespace topth

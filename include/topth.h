@@ -39,13 +39,16 @@
  *
  * Workspace
  * ---------
- *  Decode and calibration need a device workspace of at least
- *  topth_workspace_size(...) bytes.  Its first TOPTH_WS_HEADER_BYTES hold
- *  synchronisation counters and a status word; a workspace must be zeroed
- *  (topth_workspace_init) before its first use, and every call that returns
- *  TOPTH_OK leaves those counters at zero again, so one workspace can be
- *  reused by any later call of any size up to its capacity.  Two calls that
- *  overlap in time must not share a workspace.
+ *  Decode and calibration (and prefill with VMC) need a device workspace of
+ *  at least topth_workspace_size(...) bytes.  Calibration and prefill use it
+ *  as plain scratch.  Decode keeps a status word in its first
+ *  TOPTH_WS_HEADER_BYTES and, after them, the slots through which the key
+ *  chunks of one (batch, KV head) exchange partial results: a decode
+ *  workspace must be prepared by topth_workspace_init before its first use,
+ *  and every decode call that returns TOPTH_OK leaves it prepared again, so it
+ *  serves any later decode call of any size up to its capacity.  A workspace
+ *  that a calibration or prefill call has used must be prepared again before
+ *  a decode call.  Two calls that overlap in time must not share a workspace.
  */
 #ifndef TOPTH_H
 #define TOPTH_H
@@ -92,8 +95,9 @@ const char* topth_strerror(int status);
  */
 size_t topth_workspace_size(int op, int B, int Hq, int Hkv, int Lq, int Lk, int d, int n_k);
 
-/* Zero a workspace (device, ws_bytes) on the stream; needed once before the
- * first call that uses it. */
+/* Prepare a workspace (device, ws_bytes) on the stream: the header is zeroed
+ * and every exchange slot after it marked empty.  Needed before the first
+ * decode call that uses it (see "Workspace"). */
 int topth_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /*

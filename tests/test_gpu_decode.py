@@ -164,6 +164,25 @@ def test_decode_dense_overflow(B, Hq, Hkv, d, Lmax):
     compare_decode(g, q, k, v, lens, dense, vm, tt.TOPTH_VMC, torch.bfloat16)
 
 
+def test_decode_workspace_shared_by_f32_and_bf16_calls():
+    """An fp32 decode call (row kernels, kept-key masks in the workspace) between
+    bf16 calls on the same workspace: the bf16 result is bit-identical to the one
+    on a fresh workspace, so the fp32 call leaves the exchange slots empty."""
+    lens = [4100, 2049]                            # several key chunks per group
+    qb, kb, vb, thb, vmb = make_case(8, 2, 128, 4100, lens, seed_index=8)
+    qf, kf, vf, thf, vmf = make_case(8, 2, 128, 4100, lens, dtype=torch.float32, seed_index=9)
+    fresh = run_decode(qb, kb, vb, lens, thb, vmb, tt.TOPTH_VMC)
+    ws = tt.workspace(tt.TOPTH_OP_DECODE, 2, 8, 2, 1, 4100, 128)
+    gb1 = run_decode(qb, kb, vb, lens, thb, vmb, tt.TOPTH_VMC, ws=ws)
+    gf = run_decode(qf, kf, vf, lens, thf, vmf, tt.TOPTH_VMC, ws=ws)
+    gb2 = run_decode(qb, kb, vb, lens, thb, vmb, tt.TOPTH_VMC, ws=ws)
+    for key in fresh:
+        assert np.array_equal(fresh[key], gb1[key]), key
+        assert np.array_equal(fresh[key], gb2[key]), key
+    compare_decode(gf, qf, kf, vf, lens, thf, vmf, tt.TOPTH_VMC, torch.float32)
+    compare_decode(gb2, qb, kb, vb, lens, thb, vmb, tt.TOPTH_VMC, torch.bfloat16)
+
+
 def test_decode_f32_parity():
     lens = [333, 100, 1]
     q, k, v, theta, vm = make_case(8, 2, 64, 333, lens, dtype=torch.float32, seed_index=3)
