@@ -68,12 +68,15 @@ EXP_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9   # v_exp_f32: quarter-rate on 16-lane
 
 
 def code_sha256(sources):
-    """SHA-256 of the code in `sources` with comments and whitespace removed, so
-    that a change to comments alone does not mark counter data as stale."""
+    """SHA-256 of the device code in `sources` (a .hip file up to its host-side
+    section) with comments and whitespace removed, so that edits to comments or
+    to host code alone do not mark counter data as stale."""
     h = hashlib.sha256()
     for f in sources:
         with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
             text = fh.read()
+        if f.endswith(".hip"):
+            text = text.split("// ------------------------------------------------------------------ host side")[0]
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
         h.update(re.sub(r"\s+", "", text).encode())

@@ -788,6 +788,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
 }
 
 // ------------------------------------------------------------------ host side
+}  // namespace topth
+
+#include <atomic>
+
+namespace topth {
+
 namespace {
 
 struct Variant {
@@ -854,21 +860,25 @@ int keys_per_wg_min(int G) {
 
 // Resident workgroups per CU of each kernel variant and the CU count, per
 // device, computed once (the occupancy query is slow next to a decode step).
+// Entries are atomics: concurrent first calls may both run the query, and
+// both store the same value.
 struct DeviceInfo {
-    int cus = 0;
-    int occ[2][17][kMaxVariants] = {};   // [d==128][G][variant] -> workgroups per CU (0 = unknown)
+    std::atomic<int> cus{0};
+    std::atomic<int> occ[2][17][kMaxVariants] = {};   // [d==128][G][variant] -> workgroups per CU (0 = unknown)
 };
 DeviceInfo g_dev[16];
 
 int resident_per_cu(int dev, int d, int G, int vi, const Variant& v, int* out) {
-    int& slot = g_dev[dev].occ[d == 128][G][vi];
-    if (slot == 0) {
+    std::atomic<int>& slot = g_dev[dev].occ[d == 128][G][vi];
+    int val = slot.load(std::memory_order_relaxed);
+    if (val == 0) {
         int per_cu = 0;
         const int e = v.resident(&per_cu);
         if (e != hipSuccess) return e;
-        slot = per_cu > 0 ? per_cu : -1;
+        val = per_cu > 0 ? per_cu : -1;
+        slot.store(val, std::memory_order_relaxed);
     }
-    *out = slot > 0 ? slot : 0;
+    *out = val > 0 ? val : 0;
     return hipSuccess;
 }
 
@@ -894,8 +904,8 @@ size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lmax, int d) {
 }
 
 // Spin limit of the in-kernel exchange; a host test may lower it.
-static unsigned g_spin_limit = 1u << 22;
-void decode_set_spin_limit(unsigned v) { g_spin_limit = v; }
+static std::atomic<unsigned> g_spin_limit{1u << 22};
+void decode_set_spin_limit(unsigned v) { g_spin_limit.store(v, std::memory_order_relaxed); }
 
 int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     const int G = p.Hq / p.Hkv;
@@ -904,11 +914,12 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
-    if (g_dev[dev].cus == 0) {
-        e = hipDeviceGetAttribute(&g_dev[dev].cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = g_dev[dev].cus.load(std::memory_order_relaxed);
+    if (cus == 0) {
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
+        g_dev[dev].cus.store(cus, std::memory_order_relaxed);
     }
-    const int cus = g_dev[dev].cus;
 
     // The smallest register footprint whose work fits in one resident round;
     // otherwise the largest (fewest rounds).  Every workgroup of the grid is
@@ -953,7 +964,7 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     a.chunks = chunks; a.items = items;
     a.xscale = p.scale * kLog2e;
     a.flags = p.flags;
-    a.spin_limit = g_spin_limit;
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     a.xcd_map = (grid % (8 * chunks) == 0 && items % grid == 0) ? 1 : 0;
 
     return v.launch(grid, stream, a);
