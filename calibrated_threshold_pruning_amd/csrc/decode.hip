@@ -16,15 +16,15 @@
 //            key tiles packed into the 16 rows when g < 16).  Scores stay in
 //            registers; the wave and the workgroup reduce per-head (max, sum
 //            of exp2) and publish them.
-//   Exchange the chunks of a group meet at a counter in the workspace; every
-//            chunk then combines all partials in the same order, so all see the
-//            same row log-sum-exp.
+//   Exchange every chunk of a group publishes its per-head (max, sum of exp2)
+//            to a workspace slot and polls all of the group's slots; each then
+//            merges them in chunk order, so all see the same row log-sum-exp.
 //   Phase 2  compare x >= log2(theta) + lse2 per (key, head); OR over the
 //            group's heads; ballot prefix sums compact the kept keys into a
 //            per-wave LDS list; only those V rows are gathered (buffer_load ...
 //            lds) and O^T += V^T W runs on MFMA from LDS transpose reads.
-//   Combine  the last chunk of a group to finish sums the chunk partials in a
-//            fixed order and applies beta * mu.
+//   Combine  chunk 0 of each group polls the other chunks' partial outputs,
+//            sums them in chunk order, applies beta * mu and empties the slots.
 // Reductions never use float atomics, so results are run-to-run identical.
 #include "topth_internal.h"
 
@@ -98,9 +98,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // Cross-workgroup data of one group (partials written by one chunk, read by the
 // others) moves through agent-scope atomic stores and loads: they are coherent
 // across the XCDs' separate L2 caches without the L2 write-back and invalidate
-// that a device-wide fence costs.  A writer waits for its stores to complete
-// (s_waitcnt) before it bumps the group's counter; a reader loads only after it
-// has seen the counter.
+// that a device-wide fence costs.  Every published word is one store, and a
+// reader polls the word itself until it no longer holds the empty pattern, so
+// no counter or fence orders them.
 __device__ __forceinline__ void publish(float* p, float v) {
     __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
             // O^T += V^T W over the listed rows, 32 per MFMA step: the kept V
             // rows are fetched with buffer_load ... lds into the part of the
             // stage above the weights (16-byte chunk c of batch row j in slot
-            // c ^ (j % CPR)), the tail of the last batch is zeroed, and V^T
+            // c ^ (j % CPR)), the rows past the batch's end up to its 32-row step are zeroed, and V^T
             // fragments come out of LDS transpose reads (in each 16-lane group,
             // lane i receives column i % 4 of the 8-byte rows addressed by lanes
             // i / 4 + 4 e).  The k-slot j of lane group lq stands for row
