@@ -103,6 +103,9 @@ def make_case(Hq, Hkv, d, Lmax, lens, k=32, dtype=torch.bfloat16, n_sinks=1, see
     (8, 2, 64, 2500, [2500, 2499, 1024]),     # g=4, d=64, several chunks
     (8, 2, 128, 4100, [4100, 2049, 2048, 2047]),  # lengths at and around chunk boundaries
     (16, 1, 64, 300, [300, 33]),              # g=16, d=64
+    # one KV head, 10 chunks of 2048 keys per group: the exchange and the combine
+    # poll in several batches, and the short row leaves most of its chunks empty
+    (4, 1, 128, 20000, [20000, 100]),
 ])
 def test_decode_bf16_parity(Hq, Hkv, d, Lmax, lens):
     print(f"decode bf16 Hq={Hq} Hkv={Hkv} d={d} Lmax={Lmax} lens={lens}", flush=True)
