@@ -12,9 +12,15 @@ invariants of the method.  One reading is not pinned by anything the pages fix:
 the causal prefix mean used for VMC in prefill (the paper's Eq. 5 averages all n
 rows in non-causal notation) -- parity unpinned for that choice of mu; every
 other step is pinned.
+
+``oracle.presoftmax`` holds the pre-softmax variant (thresholds on the scores,
+Algorithm 1 in its printed form) with the three estimates of the discarded
+softmax mass of Sec. 3.2.1 (exact, exp-threshold, offline-calibrated); it is
+pinned by ``tests/test_oracle_presoftmax_pins.py``.
 """
 from .topth import (  # noqa: F401
     scores, post_softmax, kth_largest, theta_row, row_weights, row_output, topth_row,
     prefix_mean, prefill, decode, Calibrator, calibration_samples,
     PrefillResult, DecodeResult, RowResult,
 )
+from . import presoftmax  # noqa: F401,E402
