@@ -23,7 +23,11 @@ Other workloads (``--workload``):
   * ``calib_sweep``: Algorithm-1 calibration of 8 heads, d=128, L=2048, k in
     {64, 128, 256}, 512 sequences per layer; a slice of layers is timed and
     the 32-layer sweep extrapolated.
-The default run also appends a ``prefill_8k`` summary object (fewer steps).
+  * ``prefill_8k_pre``: the prefill workload in the pre-softmax form (thresholds
+    on the scores, calibrated on the scores; exp-threshold estimate of the
+    discarded mass, gamma = 0.05): one sweep over the keys per query tile.
+The default run also appends ``prefill_8k`` and ``prefill_8k_pre`` summary
+objects (fewer steps).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -65,6 +69,7 @@ PREFILL_WORKLOAD = dict(B=1, Hq=32, Hkv=8, d=128, L=8192, ks=[512, 512, 128, 128
 CALIB_WORKLOAD = dict(layers=32, Hq=8, Hkv=8, d=128, L=2048, seqs=512, ks=[64, 128, 256], sinks=1,
                       chunk=64, timed_layers=2)
 EXP_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9   # v_exp_f32: quarter-rate on 16-lane SIMDs
+PRE_GAMMA = 0.05                            # exp-threshold estimate of the discarded mass
 
 
 def code_sha256(sources):
@@ -331,31 +336,43 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
     return res
 
 
-def calibrate_prefill_theta(w, layer, k, dev):
-    """theta [Hq, L] for one layer from `calib` prefill-style sequences (GPU)."""
+def calibrate_prefill_theta(w, layer, k, dev, pre=False):
+    """theta [Hq, L] for one layer from `calib` prefill-style sequences (GPU);
+    with `pre`, thresholds on the scores and also the offline E~ table."""
     cfg = CONFIG_IDS["prefill_8k"]
     Hq, Hkv, d, L = w["Hq"], w["Hkv"], w["d"], w["L"]
     s1 = torch.zeros(1, Hq, L, dtype=torch.float64, device=dev)
     s2 = torch.zeros_like(s1)
+    es = torch.zeros_like(s1)
     cnt = torch.zeros(1, Hq, L, dtype=torch.int32, device=dev)
     chunk = 8
-    ws = tt.workspace(tt.TOPTH_OP_CALIBRATE, chunk, Hq, Hkv, L, L, d, 1)
+    op = tt.TOPTH_OP_CALIBRATE_PRE_E if pre else tt.TOPTH_OP_CALIBRATE
+    ws = tt.workspace(op, chunk, Hq, Hkv, L, L, d, 1)
     for done in range(0, w["calib"], chunk):
         S = min(chunk, w["calib"] - done)
         q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, layer, done, B=S, Hq=Hq, Hkv=Hkv, Lq=L,
                                            Lk=L, d=d, n_sinks=w["sinks"], device=dev, with_v=False)
-        tt.topth_calibrate(q, kk, [k], s1, s2, cnt, ws, scale=1.0 / math.sqrt(d), q_pos0=0)
+        if pre:
+            tt.topth_calibrate_pre(q, kk, [k], s1, s2, cnt, ws, scale=1.0 / math.sqrt(d), q_pos0=0, esum=es)
+        else:
+            tt.topth_calibrate(q, kk, [k], s1, s2, cnt, ws, scale=1.0 / math.sqrt(d), q_pos0=0)
         del q, kk
     theta = torch.empty(1, Hq, L, dtype=torch.float32, device=dev)
     tt.topth_calibrate_finalize(s1, s2, cnt, [k], theta)
+    if not pre:
+        torch.cuda.synchronize()
+        return theta[0].contiguous()
+    et = torch.empty_like(theta)
+    tt.topth_calibrate_finalize_etilde(es, cnt, [k], et)
     torch.cuda.synchronize()
-    return theta[0].contiguous()
+    return theta[0].contiguous(), et[0].contiguous()
 
 
-def oracle_prefill_baseline(q, k, v, theta, w, budget_s=15.0):
+def oracle_prefill_baseline(q, k, v, theta, w, budget_s=15.0, pre=False):
     """Time the CPU oracle on rows of layer 0, KV group 0 (its g query heads), spread
     over the whole length; report algorithmic TFLOP/s on the same flop count."""
     import oracle
+    from oracle import presoftmax
     g = w["Hq"] // w["Hkv"]
     L, d = w["L"], w["d"]
     qf = to_f64(q[:1, :g].cpu()); kf = to_f64(k[:1, :1].cpu()); vf = to_f64(v[:1, :1].cpu())
@@ -367,18 +384,23 @@ def oracle_prefill_baseline(q, k, v, theta, w, budget_s=15.0):
     while time.perf_counter() - t0 < budget_s and done < L:
         ps = rows_all[done:done + 64]
         rows = [(0, h, int(p)) for h in range(g) for p in ps]
-        r = oracle.prefill(qf, kf, vf, th, 1.0 / math.sqrt(d), vmc=False, rows=rows)
+        if pre:
+            r = presoftmax.prefill_pre(qf, kf, vf, th, 1.0 / math.sqrt(d), sdc="expth", vmc=False,
+                                       gamma=PRE_GAMMA, rows=rows)
+        else:
+            r = oracle.prefill(qf, kf, vf, th, 1.0 / math.sqrt(d), vmc=False, rows=rows)
         for (_, h, p) in rows:
             flops += 2.0 * d * (p + 1) + 2.0 * d * r.kept_count[0, h, p]
         done += len(ps)
     el = time.perf_counter() - t0
     model, threads = cpu_info()
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"float64 NumPy oracle prefill of {done} random rows x {g} heads of layer 0 "
+            "sample": f"float64 NumPy oracle {'pre-softmax ' if pre else ''}prefill of {done} random rows x {g} heads of layer 0 "
                       f"(KV group 0), {el:.1f} s, host '{model}', {os.cpu_count()} logical CPUs"}
 
 
-def bench_prefill(steps, warmup, with_cpu):
+def bench_prefill(steps, warmup, with_cpu, pre=False):
+    name = "prefill_8k_pre" if pre else "prefill_8k"
     w = PREFILL_WORKLOAD
     dev = torch.device("cuda:0")
     cfg = CONFIG_IDS["prefill_8k"]
@@ -387,8 +409,10 @@ def bench_prefill(steps, warmup, with_cpu):
     scale = 1.0 / math.sqrt(d)
     layers = []
     for li, k in enumerate(w["ks"]):
-        log(f"[bench] prefill_8k: layer {li}: calibrating theta (k={k}) from {w['calib']} sequences")
-        theta = calibrate_prefill_theta(w, li, k, dev)
+        log(f"[bench] {name}: layer {li}: calibrating theta (k={k}) from {w['calib']} sequences")
+        theta = calibrate_prefill_theta(w, li, k, dev, pre=pre)
+        if pre:
+            theta = theta[0]                # the exp-threshold estimate needs no E~ table
         q, kk, v = attention_inputs_device(cfg, ROLE_TEST, li, 0, B=B, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d,
                                            n_sinks=w["sinks"], device=dev)
         out = torch.empty_like(q)
@@ -398,8 +422,12 @@ def bench_prefill(steps, warmup, with_cpu):
 
     def step():
         for lw in layers:
-            tt.topth_prefill(lw["q"], lw["kk"], lw["v"], lw["theta"], lw["out"], scale=scale, flags=0,
-                             kept_count=lw["kc"], ws=ws)
+            if pre:
+                tt.topth_prefill_pre(lw["q"], lw["kk"], lw["v"], lw["theta"], lw["out"], scale=scale,
+                                     flags=tt.TOPTH_SDC_EXPTH, gamma=PRE_GAMMA, kept_count=lw["kc"], ws=ws)
+            else:
+                tt.topth_prefill(lw["q"], lw["kk"], lw["v"], lw["theta"], lw["out"], scale=scale, flags=0,
+                                 kept_count=lw["kc"], ws=ws)
 
     step()
     torch.cuda.synchronize()
@@ -430,15 +458,17 @@ def bench_prefill(steps, warmup, with_cpu):
     span = start.elapsed_time(end) * 1e-3
     t_step = span / steps
     algo = (qk_flops + pv_flops) / t_step / 1e12
-    # executed MFMA work: QK^T in both sweeps plus P V as two bf16 products (hi/lo split)
-    executed = 4.0 * qk_flops / t_step / 1e12
+    # executed MFMA work: QK^T in both sweeps (one in the pre-softmax form) plus
+    # P V as two bf16 products (hi/lo split)
+    executed = (3.0 if pre else 4.0) * qk_flops / t_step / 1e12
     res = {
         "metric": METRIC, "value": round(algo, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "prefill_8k", "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+        "config": {"workload": name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "seq_len": L, "layers": n_layers, "k_per_layer": w["ks"],
-                   "calib_sequences": w["calib"], "sdc": "exact", "vmc": False,
+                   "calib_sequences": w["calib"], "threshold": "pre-softmax" if pre else "post-softmax",
+                   "sdc": f"exp-threshold (gamma {PRE_GAMMA})" if pre else "exact", "vmc": False,
                    "parallelism": "single GPU"},
         "qk_tflops_algorithmic": round(qk_flops / t_step / 1e12, 2),
         "mfma_tflops_executed": round(executed, 2),
@@ -453,7 +483,7 @@ def bench_prefill(steps, warmup, with_cpu):
     if with_cpu:
         log("[bench] timing the CPU oracle on a sample of the prefill workload")
         lw = layers[0]
-        res["cpu_baseline"] = oracle_prefill_baseline(lw["q"], lw["kk"], lw["v"], lw["theta"], w)
+        res["cpu_baseline"] = oracle_prefill_baseline(lw["q"], lw["kk"], lw["v"], lw["theta"], w, pre=pre)
     return res
 
 
@@ -559,7 +589,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_8b",
-                    choices=sorted(DECODE_WORKLOADS) + ["prefill_8k", "calib_sweep"])
+                    choices=sorted(DECODE_WORKLOADS) + ["prefill_8k", "prefill_8k_pre", "calib_sweep"])
     ap.add_argument("--no-prefill-summary", action="store_true",
                     help="default workload only: skip the appended prefill_8k summary")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -577,17 +607,19 @@ def main():
         sys.exit(2)
     tt.load_library()
     with_cpu = not args.no_cpu_baseline
-    if args.workload == "prefill_8k":
-        res = bench_prefill(args.steps, args.warmup, with_cpu)
+    if args.workload in ("prefill_8k", "prefill_8k_pre"):
+        res = bench_prefill(args.steps, args.warmup, with_cpu, pre=args.workload == "prefill_8k_pre")
     elif args.workload == "calib_sweep":
         res = bench_calib(with_cpu)
     else:
         res = bench_decode(args.workload, args.steps, args.warmup, with_cpu=with_cpu, eager=args.eager)
         if args.workload == "decode_8b" and not args.no_prefill_summary:
             p = bench_prefill(steps=5, warmup=1, with_cpu=False)
-            res["prefill_8k"] = {k: p[k] for k in ("value", "unit", "ms_per_step", "qk_tflops_algorithmic",
-                                                   "mfma_tflops_executed", "mfma_executed_frac_of_peak",
-                                                   "per_layer", "roofline")}
+            keys = ("value", "unit", "ms_per_step", "qk_tflops_algorithmic", "mfma_tflops_executed",
+                    "mfma_executed_frac_of_peak", "per_layer", "roofline")
+            res["prefill_8k"] = {k: p[k] for k in keys}
+            p = bench_prefill(steps=5, warmup=1, with_cpu=False, pre=True)
+            res["prefill_8k_pre"] = {k: p[k] for k in keys + ("config",)}
     if args.copy_probe:
         copy_probe(torch.device("cuda:0"))
     print(json.dumps(res), flush=True)

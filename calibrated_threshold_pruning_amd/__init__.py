@@ -10,4 +10,6 @@ from ._lib import (  # noqa: F401
     TOPTH_OP_DECODE, TOPTH_MAX_NK, EXPORTS, LIB_PATH, TopthError, load_library,
     topth_strerror, topth_workspace_size, topth_workspace_init, workspace, topth_calibrate,
     topth_calibrate_finalize, topth_prefill, topth_decode, topth_vmean,
+    TOPTH_SDC_EXPTH, TOPTH_SDC_OFFLINE, TOPTH_OP_CALIBRATE_PRE_E, topth_calibrate_pre,
+    topth_calibrate_finalize_etilde, topth_prefill_pre, topth_decode_pre,
 )

@@ -18,11 +18,14 @@ LIB_PATH = os.path.join(_HERE, "libtopth.so")
 
 TOPTH_F32, TOPTH_BF16 = 0, 1
 TOPTH_VMC, TOPTH_SDC_NONE = 0x1, 0x2
-TOPTH_OP_CALIBRATE, TOPTH_OP_PREFILL, TOPTH_OP_DECODE = 0, 1, 2
+TOPTH_SDC_EXPTH, TOPTH_SDC_OFFLINE = 0x4, 0x8
+TOPTH_OP_CALIBRATE, TOPTH_OP_PREFILL, TOPTH_OP_DECODE, TOPTH_OP_CALIBRATE_PRE_E = 0, 1, 2, 3
 TOPTH_MAX_NK = 8
 
 EXPORTS = ("topth_strerror", "topth_workspace_size", "topth_workspace_init", "topth_calibrate",
-           "topth_calibrate_finalize", "topth_prefill", "topth_decode", "topth_vmean")
+           "topth_calibrate_finalize", "topth_prefill", "topth_decode", "topth_vmean",
+           "topth_calibrate_pre", "topth_calibrate_finalize_etilde", "topth_prefill_pre",
+           "topth_decode_pre")
 
 
 class TopthError(RuntimeError):
@@ -61,6 +64,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  vp, vp, sz, vp]
     lib.topth_vmean.restype = i
     lib.topth_vmean.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
+    lib.topth_calibrate_pre.restype = i
+    lib.topth_calibrate_pre.argtypes = [vp, vp, i, i, i, i, i, i, i, f, i, vp, i, vp, vp, vp, vp, i, vp,
+                                        sz, vp]
+    lib.topth_calibrate_finalize_etilde.restype = i
+    lib.topth_calibrate_finalize_etilde.argtypes = [vp, vp, vp, i, i, i, vp, vp]
+    lib.topth_prefill_pre.restype = i
+    lib.topth_prefill_pre.argtypes = [vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, u, f, vp, vp, vp, vp,
+                                      vp, sz, vp]
+    lib.topth_decode_pre.restype = i
+    lib.topth_decode_pre.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, vp, u, f, vp, vp,
+                                     vp, vp, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -209,3 +223,89 @@ def topth_vmean(v, seq_lens, v_mean, stream=None):
     _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d))
     _check("topth_vmean", load_library().topth_vmean(
         v.data_ptr(), seq_lens.data_ptr(), B, Hkv, Lmax, d, dt, v_mean.data_ptr(), _stream(stream)))
+
+
+# --------------------------------------------------------------- pre-softmax
+def topth_calibrate_pre(q, k, ks, sum_, sumsq, count, ws, *, scale: float, q_pos0: int = 0,
+                        esum=None, stream=None):
+    """Algorithm 1 on the scores (k-th largest score per row); with ``esum``
+    [n_k,Hq,n_rows] float64 also the discarded mass of each row's top-k."""
+    S, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    _dev(q, "q"); _dev(k, "k", q.dtype, (S, Hkv, Lk, d))
+    n_k = len(ks)
+    n_rows = sum_.shape[-1]
+    _dev(sum_, "sum", torch.float64, (n_k, Hq, n_rows))
+    _dev(sumsq, "sumsq", torch.float64, (n_k, Hq, n_rows))
+    _dev(count, "count", torch.int32, (n_k, Hq, n_rows))
+    ep = _dev(esum, "esum", torch.float64, (n_k, Hq, n_rows), optional=True)
+    _dev(ws, "ws", torch.uint8)
+    karr = (ctypes.c_int * max(n_k, 1))(*[int(x) for x in ks])
+    _check("topth_calibrate_pre", load_library().topth_calibrate_pre(
+        q.data_ptr(), k.data_ptr(), S, Hq, Hkv, Lq, Lk, d, dt, float(scale), int(q_pos0),
+        ctypes.cast(karr, ctypes.c_void_p), n_k, sum_.data_ptr(), sumsq.data_ptr(),
+        count.data_ptr(), ep, n_rows, ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def topth_calibrate_finalize_etilde(esum, count, ks, e_tilde, *, stream=None):
+    n_k, Hq, n_rows = esum.shape
+    _dev(esum, "esum", torch.float64); _dev(count, "count", torch.int32, esum.shape)
+    _dev(e_tilde, "e_tilde", torch.float32, esum.shape)
+    karr = (ctypes.c_int * max(len(ks), 1))(*[int(x) for x in ks])
+    _check("topth_calibrate_finalize_etilde", load_library().topth_calibrate_finalize_etilde(
+        esum.data_ptr(), count.data_ptr(), ctypes.cast(karr, ctypes.c_void_p), len(ks), Hq, n_rows,
+        e_tilde.data_ptr(), _stream(stream)))
+
+
+def _table(t, name, Hq, n_rows=None, optional=False):
+    p = _dev(t, name, torch.float32, optional=optional)
+    if p is not None and (t.dim() != 2 or t.shape[0] != Hq or (n_rows is not None and t.shape[1] != n_rows)):
+        raise ValueError(f"{name} must be [Hq, n_rows]")
+    return p
+
+
+def topth_prefill_pre(q, k, v, theta, out, *, scale: float, flags: int, gamma: float = 0.05,
+                      e_tilde=None, kept_count=None, beta=None, kept_mask=None, ws=None, stream=None):
+    """Pre-softmax prefill: theta [Hq,n_rows] in score units; e_tilde [Hq,n_rows]
+    for TOPTH_SDC_OFFLINE."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    dt = _dtype_code(q)
+    _dev(q, "q"); _dev(k, "k", q.dtype, (B, Hkv, L, d)); _dev(v, "v", q.dtype, (B, Hkv, L, d))
+    _table(theta, "theta", Hq)
+    et = _table(e_tilde, "e_tilde", Hq, theta.shape[1], optional=True)
+    _dev(out, "out", q.dtype, (B, Hq, L, d))
+    kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq, L), optional=True)
+    bt = _dev(beta, "beta", torch.float32, (B, Hq, L), optional=True)
+    km = _dev(kept_mask, "kept_mask", torch.uint8, (B, Hq, L, L), optional=True)
+    wp = _dev(ws, "ws", torch.uint8, optional=True)
+    _check("topth_prefill_pre", load_library().topth_prefill_pre(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq, Hkv, L, d, dt, float(scale),
+        theta.data_ptr(), et, theta.shape[1], int(flags), float(gamma), out.data_ptr(), kc, bt, km, wp,
+        0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def topth_decode_pre(q, k_cache, v_cache, seq_lens, theta, out, ws, *, scale: float, flags: int,
+                     gamma: float = 0.05, e_tilde=None, v_mean=None, kept_count=None, beta=None,
+                     vrows_read=None, kept_mask=None, stream=None):
+    """Pre-softmax decoding step: theta [Hq,n_rows] in score units."""
+    B, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    dt = _dtype_code(q)
+    _dev(q, "q"); _dev(k_cache, "k_cache", q.dtype, (B, Hkv, Lmax, d))
+    _dev(v_cache, "v_cache", q.dtype, (B, Hkv, Lmax, d))
+    _dev(seq_lens, "seq_lens", torch.int32, (B,))
+    _table(theta, "theta", Hq)
+    et = _table(e_tilde, "e_tilde", Hq, theta.shape[1], optional=True)
+    _dev(out, "out", q.dtype, (B, Hq, d))
+    vm = _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d), optional=True)
+    kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq), optional=True)
+    bt = _dev(beta, "beta", torch.float32, (B, Hq), optional=True)
+    vr = _dev(vrows_read, "vrows_read", torch.int32, (B, Hkv), optional=True)
+    km = _dev(kept_mask, "kept_mask", torch.uint8, (B, Hq, Lmax), optional=True)
+    _dev(ws, "ws", torch.uint8)
+    _check("topth_decode_pre", load_library().topth_decode_pre(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv,
+        Lmax, d, dt, float(scale), theta.data_ptr(), et, theta.shape[1], vm, int(flags), float(gamma),
+        out.data_ptr(), kc, bt, vr, km, ws.data_ptr(), ws.numel(), _stream(stream)))

@@ -49,6 +49,16 @@ size_t calib_ws(int S, int Hq, int Lq, int n_k) {
     return (size_t)S * n_k * Hq * Lq * sizeof(float) + 256;
 }
 
+// flags of the pre-softmax calls: VMC plus at most one estimate of E~
+bool bad_pre_flags(unsigned flags, const float* e_tilde, float gamma) {
+    if (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE | TOPTH_SDC_EXPTH | TOPTH_SDC_OFFLINE)) return true;
+    const unsigned est = flags & (TOPTH_SDC_NONE | TOPTH_SDC_EXPTH | TOPTH_SDC_OFFLINE);
+    if (est & (est - 1)) return true;                         // more than one estimate
+    if ((flags & TOPTH_SDC_OFFLINE) && !e_tilde) return true;
+    if ((flags & TOPTH_SDC_EXPTH) && !(isfinite(gamma) && gamma >= 0.0f)) return true;
+    return false;
+}
+
 size_t decode_ws(int B, int Hq, int Hkv, int Lmax, int d) {
     size_t a = decode_ws_bytes(B, Hq, Hkv, Lmax, d);
     size_t b = kWsHeaderBytes + decode_rowwise_ws_bytes(B, Hq, Lmax) + 256;
@@ -75,6 +85,9 @@ size_t topth_workspace_size(int op, int B, int Hq, int Hkv, int Lq, int Lk, int 
         case TOPTH_OP_CALIBRATE:
             if (bad_dims(B, Hq, Hkv, Lq, d) || Lk <= 0 || n_k < 1 || n_k > TOPTH_MAX_NK) return 0;
             return calib_ws(B, Hq, Lq, n_k);
+        case TOPTH_OP_CALIBRATE_PRE_E:   // value samples, then discarded-mass samples
+            if (bad_dims(B, Hq, Hkv, Lq, d) || Lk <= 0 || n_k < 1 || n_k > TOPTH_MAX_NK) return 0;
+            return 2 * calib_ws(B, Hq, Lq, n_k);
         case TOPTH_OP_PREFILL:
             if (bad_dims(B, Hq, Hkv, Lq, d)) return 0;
             return prefill_ws(B, Hq, Hkv, Lq, d);
@@ -97,10 +110,14 @@ int topth_workspace_init(void* ws, size_t ws_bytes, void* stream) {
     return map_hip(e);
 }
 
-int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq, int Lk,
-                    int d, int dtype, float scale, int q_pos0, const int* ks, int n_k,
-                    double* sum, double* sumsq, int* count, int n_rows,
-                    void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int calibrate_common(const void* q, const void* k, int S, int Hq, int Hkv, int Lq, int Lk,
+                     int d, int dtype, float scale, int q_pos0, const int* ks, int n_k,
+                     double* sum, double* sumsq, int* count, int n_rows,
+                     void* ws, size_t ws_bytes, void* stream, bool pre, double* esum) {
     if (!q || !k || !ks || !sum || !sumsq || !count) return TOPTH_EINVAL;
     if (bad_dims(S, Hq, Hkv, Lq, d) || bad_dtype(dtype) || Lk <= 0 || n_rows <= 0) return TOPTH_EINVAL;
     if (!isfinite(scale) || !(scale > 0.0f) || q_pos0 < 0 || q_pos0 + Lq > Lk) return TOPTH_EINVAL;
@@ -111,7 +128,7 @@ int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq
     const bool tiled = dtype == TOPTH_BF16 && calib_bf16_supported(d, S, Hq, Lq, q_pos0);
     if (!tiled && Lk > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
     if (!ws) return TOPTH_EWORKSPACE;
-    const size_t need = calib_ws(S, Hq, Lq, n_k);
+    const size_t need = (esum ? 2 : 1) * calib_ws(S, Hq, Lq, n_k);
     if (ws_bytes < need) return TOPTH_EWORKSPACE;
     CalibParams p = {};
     p.q = q; p.k = k; p.S = S; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk; p.d = d;
@@ -119,8 +136,39 @@ int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq
     for (int t = 0; t < n_k; ++t) p.ks[t] = ks[t];
     p.n_k = n_k; p.sum = sum; p.sumsq = sumsq; p.count = count; p.n_rows = n_rows;
     p.ws = ws; p.ws_bytes = ws_bytes;
+    p.pre = pre; p.esum = esum;
     return map_hip(tiled ? launch_calibrate_bf16(p, (float*)ws, (hipStream_t)stream)
                          : launch_calibrate_rowwise(p, (float*)ws, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq, int Lk,
+                    int d, int dtype, float scale, int q_pos0, const int* ks, int n_k,
+                    double* sum, double* sumsq, int* count, int n_rows,
+                    void* ws, size_t ws_bytes, void* stream) {
+    return calibrate_common(q, k, S, Hq, Hkv, Lq, Lk, d, dtype, scale, q_pos0, ks, n_k, sum, sumsq,
+                            count, n_rows, ws, ws_bytes, stream, false, nullptr);
+}
+
+int topth_calibrate_pre(const void* q, const void* k, int S, int Hq, int Hkv, int Lq, int Lk,
+                        int d, int dtype, float scale, int q_pos0, const int* ks, int n_k,
+                        double* sum, double* sumsq, int* count, double* esum, int n_rows,
+                        void* ws, size_t ws_bytes, void* stream) {
+    return calibrate_common(q, k, S, Hq, Hkv, Lq, Lk, d, dtype, scale, q_pos0, ks, n_k, sum, sumsq,
+                            count, n_rows, ws, ws_bytes, stream, true, esum);
+}
+
+int topth_calibrate_finalize_etilde(const double* esum, const int* count, const int* ks, int n_k,
+                                    int Hq, int n_rows, float* e_tilde, void* stream) {
+    if (!esum || !count || !ks || !e_tilde) return TOPTH_EINVAL;
+    if (n_k < 1 || n_k > TOPTH_MAX_NK || Hq <= 0 || n_rows <= 0) return TOPTH_EINVAL;
+    if ((float)n_rows > 16777216.0f) return TOPTH_EUNSUPPORTED;
+    for (int t = 0; t < n_k; ++t)
+        if (ks[t] < 1) return TOPTH_EINVAL;
+    return map_hip(launch_finalize_etilde(esum, count, ks, n_k, Hq, n_rows, e_tilde, (hipStream_t)stream));
 }
 
 int topth_calibrate_finalize(const double* sum, const double* sumsq, const int* count,
@@ -135,13 +183,20 @@ int topth_calibrate_finalize(const double* sum, const double* sumsq, const int* 
                                    (hipStream_t)stream));
 }
 
-int topth_prefill(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int L,
-                  int d, int dtype, float scale, const float* theta, int n_rows,
-                  unsigned flags, void* out, int* kept_count, float* beta,
-                  unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int prefill_common(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int L,
+                   int d, int dtype, float scale, const float* theta, int n_rows,
+                   unsigned flags, void* out, int* kept_count, float* beta,
+                   unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream,
+                   bool pre, const float* e_tilde, float gamma) {
     if (!q || !k || !v || !theta || !out) return TOPTH_EINVAL;
     if (bad_dims(B, Hq, Hkv, L, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
-    if (!isfinite(scale) || !(scale > 0.0f) || (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE))) return TOPTH_EINVAL;
+    if (!isfinite(scale) || !(scale > 0.0f)) return TOPTH_EINVAL;
+    if (pre ? bad_pre_flags(flags, e_tilde, gamma) : (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE)) != 0)
+        return TOPTH_EINVAL;
     if (too_big((long long)B * Hq * L, d)) return TOPTH_EUNSUPPORTED;
     if (dtype == TOPTH_F32 && L > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
     if (dtype == TOPTH_BF16 && (!prefill_bf16_supported(d, Hq / Hkv) || (long long)L * d * 2 >= INT_MAX))
@@ -156,18 +211,46 @@ int topth_prefill(const void* q, const void* k, const void* v, int B, int Hq, in
     p.scale = scale; p.theta = theta; p.n_rows = n_rows; p.flags = flags;
     p.out = out; p.kept_count = kept_count; p.beta = beta; p.kept_mask = kept_mask;
     p.ws = ws; p.ws_bytes = ws_bytes;
+    if (pre) { p.flags |= kFlagPre; p.e_tilde = e_tilde; p.gamma = gamma; }
     if (dtype == TOPTH_BF16) return map_hip(launch_prefill_bf16(p, (float*)ws, (hipStream_t)stream));
     return map_hip(launch_prefill_rowwise(p, (float*)ws, (hipStream_t)stream));
 }
 
-int topth_decode(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
-                 int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
-                 const float* theta, int n_rows, const float* v_mean, unsigned flags,
-                 void* out, int* kept_count, float* beta, int* vrows_read,
-                 unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream) {
+}  // namespace
+
+extern "C" {
+
+int topth_prefill(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int L,
+                  int d, int dtype, float scale, const float* theta, int n_rows,
+                  unsigned flags, void* out, int* kept_count, float* beta,
+                  unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream) {
+    return prefill_common(q, k, v, B, Hq, Hkv, L, d, dtype, scale, theta, n_rows, flags, out,
+                          kept_count, beta, kept_mask, ws, ws_bytes, stream, false, nullptr, 0.f);
+}
+
+int topth_prefill_pre(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int L,
+                      int d, int dtype, float scale, const float* theta, const float* e_tilde,
+                      int n_rows, unsigned flags, float gamma, void* out, int* kept_count,
+                      float* beta, unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream) {
+    return prefill_common(q, k, v, B, Hq, Hkv, L, d, dtype, scale, theta, n_rows, flags, out,
+                          kept_count, beta, kept_mask, ws, ws_bytes, stream, true, e_tilde, gamma);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_common(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                  int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                  const float* theta, int n_rows, const float* v_mean, unsigned flags,
+                  void* out, int* kept_count, float* beta, int* vrows_read,
+                  unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream,
+                  bool pre, const float* e_tilde, float gamma) {
     if (!q || !k_cache || !v_cache || !seq_lens || !theta || !out) return TOPTH_EINVAL;
     if (bad_dims(B, Hq, Hkv, Lmax, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
-    if (!isfinite(scale) || !(scale > 0.0f) || (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE))) return TOPTH_EINVAL;
+    if (!isfinite(scale) || !(scale > 0.0f)) return TOPTH_EINVAL;
+    if (pre ? bad_pre_flags(flags, e_tilde, gamma) : (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE)) != 0)
+        return TOPTH_EINVAL;
     if ((flags & TOPTH_VMC) && !(flags & TOPTH_SDC_NONE) && !v_mean) return TOPTH_EINVAL;
     if (too_big((long long)B * Hkv * Lmax, d)) return TOPTH_EUNSUPPORTED;
     if (!ws) return TOPTH_EWORKSPACE;
@@ -178,6 +261,7 @@ int topth_decode(const void* q, const void* k_cache, const void* v_cache, const 
     p.theta = theta; p.n_rows = n_rows; p.v_mean = v_mean; p.flags = flags;
     p.out = out; p.kept_count = kept_count; p.beta = beta; p.vrows_read = vrows_read;
     p.kept_mask = kept_mask; p.ws = ws; p.ws_bytes = ws_bytes;
+    if (pre) { p.flags |= kFlagPre; p.e_tilde = e_tilde; p.gamma = gamma; }
     if (dtype == TOPTH_BF16) {
         if (!decode_bf16_supported(d, Hq / Hkv) || (long long)Lmax * d * 2 >= INT_MAX) return TOPTH_EUNSUPPORTED;
         return map_hip(launch_decode_bf16(p, (hipStream_t)stream));
@@ -185,6 +269,31 @@ int topth_decode(const void* q, const void* k_cache, const void* v_cache, const 
     if (Lmax > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
     return map_hip(launch_decode_rowwise(p, (uint32_t*)((char*)ws + kWsHeaderBytes),
                                          (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int topth_decode(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                 int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                 const float* theta, int n_rows, const float* v_mean, unsigned flags,
+                 void* out, int* kept_count, float* beta, int* vrows_read,
+                 unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream) {
+    return decode_common(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Lmax, d, dtype, scale, theta,
+                         n_rows, v_mean, flags, out, kept_count, beta, vrows_read, kept_mask, ws,
+                         ws_bytes, stream, false, nullptr, 0.f);
+}
+
+int topth_decode_pre(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                     int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                     const float* theta, const float* e_tilde, int n_rows, const float* v_mean,
+                     unsigned flags, float gamma, void* out, int* kept_count, float* beta,
+                     int* vrows_read, unsigned char* kept_mask, void* ws, size_t ws_bytes,
+                     void* stream) {
+    return decode_common(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Lmax, d, dtype, scale, theta,
+                         n_rows, v_mean, flags, out, kept_count, beta, vrows_read, kept_mask, ws,
+                         ws_bytes, stream, true, e_tilde, gamma);
 }
 
 int topth_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,

@@ -24,6 +24,11 @@
 //     the bin.
 // Samples go to a [S][n_k][Hq][Lq] buffer and are summed over the sequences
 // in a fixed order afterwards.
+//
+// Pre-softmax form (Algorithm 1 as printed): the sample is the k-th largest
+// score itself, in score units; optionally also the discarded mass of the
+// row's top-k relative to the row maximum (the offline estimate of E~ in
+// Sec. 3.2.1), from one more pass over the column's scores.
 #include "topth_internal.h"
 
 #include <math.h>
@@ -44,6 +49,8 @@ struct CalibKArgs {
     float xscale;       // scale * log2(e)
     int ks[8]; int n_k;
     float* samples;     // [S][n_k][Hq][Lq]
+    float* esamples;    // pre-softmax: discarded mass of the top-k, same shape, or NULL
+    int pre;            // 1: samples are k-th largest scores (pre-softmax)
 };
 
 template <int C>
@@ -79,6 +86,22 @@ __device__ __forceinline__ int col_exscan(int v, int* red) {
     return x - v + off;
 }
 
+// Sum of v over the threads of one column, added in a fixed order (every
+// thread of the workgroup must call it; every thread of the column gets it).
+template <int WPC>
+__device__ __forceinline__ float col_sum(float v, float* red) {
+    float x = wave_sum(v);
+    if constexpr (WPC > 1) {
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) red[wave] = x;
+        __syncthreads();
+        x = 0.f;
+        for (int i = wave / WPC * WPC; i < wave / WPC * WPC + WPC; ++i) x += red[i];
+        __syncthreads();
+    }
+    return x;
+}
+
 // bin of score x in a column with maximum m: bins of 1/bs log2 units below m,
 // the last bin open-ended; monotone non-increasing in x
 template <int NB>
@@ -105,6 +128,7 @@ __global__ __launch_bounds__(kCalThreads) void calib_bf16_kernel(CalibKArgs a) {
     uint32_t* hist = reinterpret_cast<uint32_t*>(xs + C * a.nks);   // [C][NB]
     __shared__ float s_stat[kCalWaves][16][3];                      // per wave: max, sum, score sum
     __shared__ int redi[kCalWaves];
+    __shared__ float redf[kCalWaves];
     __shared__ int s_bin[C][8], s_rank[C][8], s_cnt[C][8], s_fill[C][8];
     __shared__ float s_val[C][8];
     __shared__ int s_dig[C], s_kk[C];
@@ -416,17 +440,48 @@ __global__ __launch_bounds__(kCalThreads) void calib_bf16_kernel(CalibKArgs a) {
     }
     __syncthreads();
 
+    if (a.esamples) {
+        // discarded mass of each top-k: the elements below x_k, plus the ties
+        // at x_k beyond the k-th, in the frame of the row maximum m
+        float el[8];
+        int ge[8];
+        float xk[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) { el[t] = 0.f; ge[t] = 0; xk[t] = t < a.n_k ? s_val[c][t] : INFINITY; }
+        for (int j = u; j < n; j += TPC) {
+            const float x = xr[j];
+            const float e = __builtin_amdgcn_exp2f(x - m);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (x < xk[t]) el[t] += e;
+                else ++ge[t];
+            }
+        }
+        float ev = NAN;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (t < a.n_k) {                       // uniform: every thread holds n_k
+                const float es = col_sum<WPC>(el[t], redf);
+                const int gs = (int)col_sum<WPC>((float)ge[t], redf);
+                if (u == t) ev = es + (float)(gs - a.ks[t]) * __builtin_amdgcn_exp2f(xk[t] - m);
+            }
+        }
+        if (live && u < a.n_k)
+            a.esamples[(((size_t)s * a.n_k + u) * a.Hq + hh) * a.Lq + ii] = n > a.ks[u] ? ev : NAN;
+    }
     if (live && u < a.n_k) {
         const int t = u;
+        const float xk = s_val[c][t];
         a.samples[(((size_t)s * a.n_k + t) * a.Hq + hh) * a.Lq + ii] =
-            n > a.ks[t] ? exp2f(s_val[c][t] - lse2) : NAN;
+            n > a.ks[t] ? (a.pre ? xk * 0.69314718055994531f : exp2f(xk - lse2)) : NAN;
     }
 #endif
 }
 
 // ------------------------------------------------------------------ host side
-int launch_calib_accumulate(const float* samples, int S, int n_k, int Hq, int Lq, int q_pos0,
-                            double* sum, double* sumsq, int* count, int n_rows, hipStream_t s);
+int launch_calib_accumulate(const float* samples, const float* esamples, int S, int n_k, int Hq, int Lq,
+                            int q_pos0, double* sum, double* sumsq, int* count, double* esum, int n_rows,
+                            hipStream_t s);
 
 // score columns per workgroup: 16 columns of at most 2048 keys, halving the
 // columns each time the longest causal row doubles (0: longer than 32768)
@@ -471,6 +526,9 @@ int launch_calibrate_bf16(const CalibParams& p, float* samples_ws, hipStream_t s
     for (int t = 0; t < 8; ++t) a.ks[t] = t < p.n_k ? p.ks[t] : 0;
     a.n_k = p.n_k;
     a.samples = samples_ws;
+    a.pre = p.pre ? 1 : 0;
+    // the discarded-mass samples follow the value samples in the workspace
+    a.esamples = p.esum ? samples_ws + (size_t)p.S * p.n_k * p.Hq * p.Lq : nullptr;
     const int keys = p.q_pos0 + p.Lq;
     const int cols = calib_columns(keys);
     // 16-key tiles, plus 4 floats so that consecutive columns start in different LDS banks
@@ -485,8 +543,8 @@ int launch_calibrate_bf16(const CalibParams& p, float* samples_ws, hipStream_t s
     a.nwg = (unsigned)a.nblk * (unsigned)a.ngh * (unsigned)p.S;
     const int e = p.d == 64 ? launch_calib_d<64>(a, cols, s) : launch_calib_d<128>(a, cols, s);
     if (e != hipSuccess) return e;
-    return launch_calib_accumulate(samples_ws, p.S, p.n_k, p.Hq, p.Lq, p.q_pos0, p.sum, p.sumsq, p.count,
-                                   p.n_rows, s);
+    return launch_calib_accumulate(samples_ws, a.esamples, p.S, p.n_k, p.Hq, p.Lq, p.q_pos0, p.sum, p.sumsq,
+                                   p.count, p.esum, p.n_rows, s);
 }
 
 }  // namespace topth

@@ -48,6 +48,8 @@ struct DecodeKArgs {
     unsigned flags;
     unsigned spin_limit;
     int xcd_map;       // 1: chunks of a group on one XCD (grid and items multiples of 8 * chunks)
+    const float* e_tilde;   // pre-softmax offline estimate of E~ [Hq][n_rows], or NULL
+    float gamma;            // pre-softmax exp-threshold estimate
 };
 
 // One workgroup of kDecodeWaves waves per CU: two workgroups on a CU stream at
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
     __shared__ __attribute__((aligned(16))) unsigned char s_kbuf[C::KBUF_BYTES];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[G + 1][D + 8];   // row G stays zero
     __shared__ float s_m[C::WAVES][G], s_l[C::WAVES][G];
-    __shared__ float s_T[G], s_lse[G];
+    __shared__ float s_T[G], s_lse[G], s_M[G];
     __shared__ unsigned short s_kl[C::WAVES][C::WKEYS + 64];   // kept keys of each wave (offsets from its base), + spare slots
     __shared__ float s_cm[C::WAVES][G];
     __shared__ int s_cc[C::WAVES][G];
@@ -421,8 +423,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
             const float lse2 = M + __log2f(L);
             const int h = kv * G + tid;
             const float th = a.theta[(size_t)h * a.n_rows + min(n - 1, a.n_rows - 1)];
-            s_T[tid] = log2_threshold(th, lse2);
+            // post-softmax: s >= theta; pre-softmax (kFlagPre): a >= theta
+            s_T[tid] = (a.flags & kFlagPre) ? pre_log2_threshold(th) : log2_threshold(th, lse2);
             s_lse[tid] = lse2;
+            s_M[tid] = M;
         }
         __syncthreads();
 
@@ -751,11 +755,26 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                 for (int w = 0; w < C::WAVES; ++w) { m += s_cm[w][tid]; c += s_cc[w][tid]; }
                 m = gather_chunks(a.part_mass + g0 * G + tid, G, a.chunks, m, a.spin_limit, a.status);
                 c = gather_chunks(a.part_cnt + g0 * G + tid, G, a.chunks, c, a.spin_limit, a.status);
+                // Eq. 4 scale of the kept softmax values and the Eq. 6 beta; the
+                // pre-softmax estimates of E~ relative to the full denominator:
+                // exp-threshold gamma (n - k~) e^(theta - lse), offline E~ e^(max - lse)
+                const int hq = kv * G + tid;
+                const int rowid = min(n - 1, a.n_rows - 1);
+                float etn = 0.f;
+                if (a.flags & kFlagExpth)
+                    etn = a.gamma * (float)(n - c) *
+                          exp2f(a.theta[(size_t)hq * a.n_rows + rowid] * kLog2e - s_lse[tid]);
+                if (a.flags & kFlagOffline)
+                    etn = a.e_tilde[(size_t)hq * a.n_rows + rowid] * exp2f(s_M[tid] - s_lse[tid]);
+                float fsc, bta;
+                sdc_scale(a.flags, m, c, etn, fsc, bta);
                 s_cm[0][tid] = m;
                 s_cc[0][tid] = c;
+                s_T[tid] = fsc;                // the threshold is no longer needed
+                s_M[tid] = bta;
                 const size_t o = (size_t)b * a.Hq + (size_t)kv * G + tid;
                 if (a.kept_count) a.kept_count[o] = c;
-                if (a.beta) a.beta[o] = renorm ? 0.f : 1.f - m;
+                if (a.beta) a.beta[o] = bta;
                 // every chunk has passed the exchange (it published after it):
                 // its slots are empty again for the next call
                 if (a.chunks > 1)
@@ -778,7 +797,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                 x = gather_chunks(a.part_out + g0 * G * D + idx, (size_t)G * D, a.chunks, x, a.spin_limit, a.status);
                 const float mass = s_cm[0][h];
                 if (renorm) x = (s_cc[0][h] > 0) ? x / mass : 0.f;
-                if (vmc) x = fmaf(1.f - mass, a.v_mean[(size_t)group * D + dd], x);
+                else if (a.flags & (kFlagExpth | kFlagOffline)) x *= s_T[h];
+                if (vmc) x = fmaf(s_M[h], a.v_mean[(size_t)group * D + dd], x);
                 a.out[((size_t)b * a.Hq + (size_t)kv * G + h) * D + dd] = f32_to_bf16_bits(x);
             }
         }
@@ -947,6 +967,7 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     DecodeKArgs a = {};
     a.q = (const uint16_t*)p.q; a.k = (const uint16_t*)p.k; a.v = (const uint16_t*)p.v;
     a.seq_lens = p.seq_lens; a.theta = p.theta; a.v_mean = p.v_mean;
+    a.e_tilde = p.e_tilde; a.gamma = p.gamma;
     a.out = (uint16_t*)p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.vrows_read = p.vrows_read;
     a.kept_mask = p.kept_mask;
     a.status = (int*)ws;

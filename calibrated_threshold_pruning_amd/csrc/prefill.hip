@@ -17,6 +17,14 @@
 // Workgroup: one KV head's query tile, 4 waves, each wave one query head and
 // 32 rows; K tiles of 64 keys are staged by buffer_load...lds into a swizzled,
 // double-buffered LDS tile shared by the waves; V tiles are staged transposed.
+//
+// Pre-softmax form (PRE): the compare a >= theta needs no row statistics, so
+// sweep A is skipped and sweep B alone keeps an online softmax: a row-uniform
+// reference maximum, raised lazily (only when a tile's maximum exceeds it by
+// more than 2^8 in exp2 units, which bounds every weight by 256), with the
+// output accumulators, the full sum and the kept sum R rescaled when it moves.
+// The epilogue divides by R + E~ for the chosen estimate of the discarded mass
+// (Sec. 3.2.1: exact, exp-threshold, offline-calibrated, or none).
 #include "topth_internal.h"
 
 #include <math.h>
@@ -30,6 +38,9 @@ struct PrefillKArgs {
     int B, Hq, Hkv, L, n_rows;
     float xscale;
     unsigned flags;
+    float scale;                 // score scale (pre-softmax thresholds are in score units)
+    const float* e_tilde;        // offline estimate of E~ [Hq][n_rows] or NULL
+    float gamma;                 // exp-threshold estimate
 };
 
 template <int D, int G>
@@ -77,7 +88,7 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, unsigned& hi, uns
     lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
-template <int D, int G, bool MASK>
+template <int D, int G, bool MASK, bool PRE>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     using C = PrefillCfg<D, G>;
@@ -172,8 +183,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 
     // ======================= sweep A: row log-sum-exp =========================
     float m_l[2] = {NEG_INF, NEG_INF}, l_l[2] = {0.f, 0.f};
-    issue_k(0, 0);
-    for (int j = 0; j < ntiles; ++j) {
+    if constexpr (!PRE) issue_k(0, 0);
+    for (int j = 0; j < (PRE ? 0 : ntiles); ++j) {
         pf_wait_vmem();
         __syncthreads();                                   // tile j complete; tile j-1 no longer read
         if (j + 1 < ntiles) issue_k(j + 1, (j + 1) & 1);
@@ -214,6 +225,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
     float lse2[2], thr[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+        if constexpr (PRE) {
+            // keep a >= theta  <=>  raw >= theta / scale; -inf keeps every valid element
+            const int row = min(row0 + 16 * qb + l16, a.L - 1);
+            const float th = a.theta[(size_t)h * a.n_rows + min(row, a.n_rows - 1)];
+            thr[qb] = fmaxf(th / a.scale, -3.402823466e38f);
+            lse2[qb] = 0.f;
+            continue;
+        }
         float M = m_l[qb];                                 // raw units
         M = fmaxf(M, __shfl_xor(M, 16));
         M = fmaxf(M, __shfl_xor(M, 32));
@@ -236,6 +255,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         for (int db = 0; db < C::DB; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     int cnt[2] = {0, 0};
     float mass[2] = {0.f, 0.f};
+    // PRE: reference maximum (raw units, lags the true one by < 8 / xscale),
+    // true row maximum, and the sum over all elements, all row-uniform frames
+    float mref[2] = {NEG_INF, NEG_INF}, mtop[2] = {NEG_INF, NEG_INF}, lall[2] = {0.f, 0.f};
     unsigned char* kmask = MASK ? a.kept_mask + ((size_t)b * a.Hq + h) * (size_t)a.L * a.L : nullptr;
 
     // V^T fragments (A operand of O^T += V^T P^T) come straight from the
@@ -265,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         return __builtin_bit_cast(bf16x8, both);
     };
 
-    __syncthreads();                                       // sweep A is done with both K buffers
+    if constexpr (!PRE) __syncthreads();                   // sweep A is done with both K buffers
     issue_k(0, 0);
     issue_v(0, 0);
     for (int j = 0; j < ntiles; ++j) {
@@ -295,14 +317,41 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                         if (key <= row) kmask[(size_t)row * a.L + key] = st[qb][kb][r] >= thr[qb] ? 1 : 0;
                     }
             }
-            const float nlse = -lse2[qb];
+            float nlse = -lse2[qb];
+            if constexpr (PRE) {
+                float tmax = NEG_INF;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[qb][kb][r]);
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                mtop[qb] = fmaxf(mtop[qb], tmax);
+                if ((tmax - mref[qb]) * a.xscale > 8.f) {         // also the first tile (mref = -inf)
+                    const float f = pf_exp2((mref[qb] - tmax) * a.xscale);
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) o[qb][db][r] *= f;
+                    lall[qb] *= f;
+                    mass[qb] *= f;
+                    mref[qb] = tmax;
+                }
+                nlse = mref[qb] == NEG_INF ? 0.f : -mref[qb] * a.xscale;
+            }
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 float p[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const bool kp = st[qb][kb][r] >= thr[qb];
-                    p[r] = kp ? pf_exp2(fmaf(st[qb][kb][r], a.xscale, nlse)) : 0.f;
+                    if constexpr (PRE) {
+                        const float e = pf_exp2(fmaf(st[qb][kb][r], a.xscale, nlse));
+                        lall[qb] += e;
+                        p[r] = kp ? e : 0.f;
+                    } else {
+                        p[r] = kp ? pf_exp2(fmaf(st[qb][kb][r], a.xscale, nlse)) : 0.f;
+                    }
                     cnt[qb] += kp ? 1 : 0;
                     mass[qb] += p[r];
                 }
@@ -351,8 +400,26 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         m += __shfl_xor(m, 32);
         const int row = row0 + 16 * qb + l16;
         if (row >= a.L) continue;
-        const float bta = renorm ? 0.f : 1.f - m;
-        const float inv = (renorm && c > 0) ? 1.f / m : 1.f;
+        float bta = renorm ? 0.f : 1.f - m;
+        float inv = (renorm && c > 0) ? 1.f / m : 1.f;
+        if constexpr (PRE) {
+            // Eq. 4: kept weights exp(a - max) / (R + E~), all in the frame mref
+            float l = lall[qb];
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            const int rid = min(row, a.n_rows - 1);
+            float den;
+            if (renorm) den = m;
+            else if (a.flags & kFlagExpth)           // gamma (n - k~) e^(theta - a_ref)
+                den = m + a.gamma * (float)(row + 1 - c) *
+                              pf_exp2(a.theta[(size_t)h * a.n_rows + rid] * kLog2e - mref[qb] * a.xscale);
+            else if (a.flags & kFlagOffline)         // E~ is relative to the true row maximum
+                den = m + a.e_tilde[(size_t)h * a.n_rows + rid] * pf_exp2((mtop[qb] - mref[qb]) * a.xscale);
+            else den = l;                            // exact: R + E
+            const bool ok = den > 0.f && !(renorm && c == 0);
+            inv = ok ? 1.f / den : 0.f;
+            bta = (ok && !renorm) ? 1.f - m * inv : 0.f;
+        }
         const float* mu = vmc ? a.mu + (((size_t)b * a.Hkv + kv) * (size_t)a.L + row) * D : nullptr;
         if (lq == 0) {
             const size_t ro = ((size_t)b * a.Hq + h) * (size_t)a.L + row;
@@ -366,7 +433,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int dim = 16 * db + 4 * lq + r;
                 float v = o[qb][db][r];
-                if (renorm) v = c > 0 ? v * inv : 0.f;
+                if (PRE || renorm) v = c > 0 ? v * inv : 0.f;
                 if (vmc) v = fmaf(bta, mu[dim], v);
                 y[r] = v;
             }
@@ -389,8 +456,13 @@ static int launch_prefill_variant(const PrefillKArgs& a, hipStream_t s) {
     using C = PrefillCfg<D, G>;
     const dim3 grid((a.L + C::BMT - 1) / C::BMT, a.Hkv * (G / C::HPW), a.B);
     // the variant that also writes the kept mask is only used when one is asked for
-    if (a.kept_mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false>), grid, dim3(256), 0, s, a);
+    if (a.flags & kFlagPre) {
+        if (a.kept_mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, true>), grid, dim3(256), 0, s, a);
+    } else {
+        if (a.kept_mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, false>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, false>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -418,6 +490,9 @@ int launch_prefill_bf16(const PrefillParams& p, float* mu_ws, hipStream_t s) {
     a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.L = p.L; a.n_rows = p.n_rows;
     a.xscale = p.scale * kLog2e;
     a.flags = p.flags;
+    a.scale = p.scale;
+    a.e_tilde = p.e_tilde;
+    a.gamma = p.gamma;
     const int G = p.Hq / p.Hkv;
     return p.d == 64 ? launch_prefill_d<64>(a, G, s) : launch_prefill_d<128>(a, G, s);
 }

@@ -7,6 +7,10 @@
 // Thresholding" -- Eq. 1-3 (scores, softmax, SV), Sec. 3 (keep s >= theta),
 // Sec. 3.1 Algorithm 1 (k-th largest per row, post-softmax), Sec. 3.2.1 Eq. 4
 // (exact SDC: kept weights keep the full denominator), Sec. 3.2.2 Eq. 5-7 (VMC).
+// With kFlagPre the same kernels run the pre-softmax form: keep a >= theta on
+// the scores, calibrate the k-th largest score (Algorithm 1 as printed) and the
+// discarded mass of the top-k, and scale the kept softmax values by one of the
+// Sec. 3.2.1 estimates of E~ (exact, exp-threshold, offline-calibrated).
 #include "topth_internal.h"
 
 #include <math.h>
@@ -25,6 +29,8 @@ struct RowArgs {
     unsigned flags;
     void* out; int* kept_count; float* beta;
     int ks[8]; int n_k; float* samples;   // calibration: [S][n_k][Hq][Lq]
+    float* esamples;                      // pre-softmax calibration: discarded mass, same shape, or NULL
+    const float* e_tilde; float gamma;    // pre-softmax SDC estimates
     uint32_t* masks; int mask_words;      // decode: kept-key bitmasks [B][Hq][mask_words]
     unsigned char* kept_mask;             // optional byte mask, [rows][Lk]
 };
@@ -138,26 +144,44 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
     for (int j = threadIdx.x; j < n; j += kRowThreads) lloc += exp2f(xs[j] - m);
     const float lse2 = m + __log2f(block_sum(lloc, redf));   // Eq. 2 denominator, log2 domain
 
+    const bool pre = (a.flags & kFlagPre) != 0;
     if (MODE == kRowCalib) {
-        // Algorithm 1 (post-softmax): per target k, the k-th largest s of the row
+        // Algorithm 1: per target k, the k-th largest s of the row (post-softmax)
+        // or the k-th largest score a itself (pre-softmax)
         for (int t = 0; t < a.n_k; ++t) {
             const int kk = a.ks[t];
-            float val = NAN;
+            float val = NAN, ev = NAN;
             if (n > kk) {
                 const float xk = block_kth_largest(xs, n, kk, hist, sel);
-                val = exp2f(xk - lse2);
+                val = pre ? xk * 0.69314718055994531f : exp2f(xk - lse2);
+                if (a.esamples) {
+                    // discarded mass of the top-k in the frame of the row maximum:
+                    // the elements below x_k, plus the ties at x_k beyond the k-th
+                    float el = 0.f;
+                    int ge = 0;
+                    for (int j = threadIdx.x; j < n; j += kRowThreads) {
+                        const float x = xs[j];
+                        if (x < xk) el += exp2f(x - m);
+                        else ++ge;
+                    }
+                    el = block_sum(el, redf);
+                    ge = block_sum_i(ge, redi);
+                    ev = el + (float)(ge - kk) * exp2f(xk - m);
+                }
             }
             if (threadIdx.x == 0) {
-                const int s = b;
-                a.samples[(((size_t)s * a.n_k + t) * a.Hq + h) * a.Lq + i] = val;
+                const size_t o = (((size_t)b * a.n_k + t) * a.Hq + h) * a.Lq + i;
+                a.samples[o] = val;
+                if (a.esamples) a.esamples[o] = ev;
             }
         }
         return;
     }
 
-    // Sec. 3: keep s >= theta  <=>  x >= log2(theta) + lse2
+    // Sec. 3: keep s >= theta  <=>  x >= log2(theta) + lse2 (post-softmax), or
+    // a >= theta  <=>  x >= theta * log2(e) (pre-softmax)
     const float th = a.theta[(size_t)h * a.n_rows + min(rowid, a.n_rows - 1)];
-    const float T2 = log2_threshold(th, lse2);
+    const float T2 = pre ? pre_log2_threshold(th) : log2_threshold(th, lse2);
     if (MODE == kRowDecode) {
         for (int w = threadIdx.x; w < (n + 31) / 32; w += kRowThreads) keepbits[w] = 0u;
         __syncthreads();
@@ -182,7 +206,14 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
 
     const bool renorm = (a.flags & 2u) != 0;
     const bool vmc = (a.flags & 1u) != 0;
-    const float beta = renorm ? 0.f : 1.f - mass;              // Eq. 6
+    // Eq. 4 scale of the kept softmax values and Eq. 6 beta; the estimates of
+    // E~ relative to the full denominator e^lse: exp-threshold gamma (n - k~)
+    // e^(theta - lse), offline E~ e^(max - lse) (E~ is relative to the row max)
+    float etn = 0.f;
+    if (a.flags & kFlagExpth) etn = a.gamma * (float)(n - cnt) * exp2f(th * kLog2e - lse2);
+    if (a.flags & kFlagOffline) etn = a.e_tilde[(size_t)h * a.n_rows + min(rowid, a.n_rows - 1)] * exp2f(m - lse2);
+    float fsc, beta;
+    sdc_scale(a.flags, mass, cnt, etn, fsc, beta);
     const T* vbase = (const T*)a.v + (size_t)(b * a.Hkv + kv) * a.Lk * D;
     T* orow = (T*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + i) * D;
     const float* mu = nullptr;
@@ -197,6 +228,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
             if (w != 0.f) acc = fmaf(w, Elem<T>::load(vbase + (size_t)j * D + t), acc);
         }
         if (renorm) acc = (cnt > 0) ? acc / mass : 0.f;
+        else if (a.flags & (kFlagExpth | kFlagOffline)) acc *= fsc;
         if (mu) acc = fmaf(beta, mu[t], acc);                   // Eq. 7
         Elem<T>::store(orow + t, acc);
     }
@@ -291,9 +323,9 @@ __global__ void prefix_mean_kernel(const T* v, int L, int D, float* mu) {
 
 // Accumulate per-sequence calibration samples into (sum, sumsq, count), in
 // sequence order, one thread per (k, head, row).
-__global__ void calib_accumulate_kernel(const float* samples, int S, int n_k, int Hq, int Lq,
-                                        int q_pos0, double* sum, double* sumsq, int* count,
-                                        int n_rows) {
+__global__ void calib_accumulate_kernel(const float* samples, const float* esamples, int S, int n_k,
+                                        int Hq, int Lq, int q_pos0, double* sum, double* sumsq,
+                                        int* count, double* esum, int n_rows) {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t per = (size_t)n_k * Hq * Lq;
     if (idx >= per) return;
@@ -302,15 +334,19 @@ __global__ void calib_accumulate_kernel(const float* samples, int S, int n_k, in
     const int t = (int)(idx / ((size_t)Lq * Hq));
     const int p = q_pos0 + i;
     if (p >= n_rows) return;
-    double s1 = 0.0, s2 = 0.0;
+    double s1 = 0.0, s2 = 0.0, e1 = 0.0;
     int c = 0;
     for (int s = 0; s < S; ++s) {
         const float x = samples[(size_t)s * per + idx];
-        if (x == x) { s1 += (double)x; s2 += (double)x * (double)x; ++c; }
+        if (x == x) {
+            s1 += (double)x; s2 += (double)x * (double)x; ++c;
+            if (esamples) e1 += (double)esamples[(size_t)s * per + idx];
+        }
     }
     if (c) {
         const size_t o = ((size_t)t * Hq + h) * n_rows + p;
         sum[o] += s1; sumsq[o] += s2; count[o] += c;
+        if (esum) esum[o] += e1;
     }
 }
 
@@ -328,9 +364,14 @@ __device__ __forceinline__ float theta_of(const double* sum, const double* sumsq
 
 struct KList { int k[8]; };
 
+// With ETILDE the same rules give the offline estimate of the discarded mass:
+// its mean for observed rows, 0 where nothing is discarded (p+1 <= k) or no
+// row of the head was observed, the nearest observed row elsewhere.
+template <bool ETILDE>
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
         const double* sum, const double* sumsq, const int* count, int Hq, int n_rows,
         KList ks, float alpha, float* theta) {
+    const float none = ETILDE ? 0.f : -INFINITY;
     __shared__ int first_obs[kFinThreads], last_obs[kFinThreads];
     const int t = blockIdx.x / Hq, h = blockIdx.x % Hq;
     const int k = ks.k[t];
@@ -356,9 +397,9 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
         if (count[base + p] > 0) next = p;
         const int pv = (int)theta[base + p];
         float out;
-        if (p + 1 <= k) out = -INFINITY;
+        if (p + 1 <= k) out = none;
         else if (count[base + p] > 0) out = theta_of(sum, sumsq, count, base + p, alpha);
-        else if (pv < 0 && next < 0) out = -INFINITY;
+        else if (pv < 0 && next < 0) out = none;
         else {
             int src;
             if (pv < 0) src = next;
@@ -412,6 +453,7 @@ int launch_decode_rowwise(const DecodeParams& p, uint32_t* masks_ws, hipStream_t
     a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Lq = 1; a.Lk = p.Lmax;
     a.xscale = p.scale * kLog2e;
     a.theta = p.theta; a.n_rows = p.n_rows; a.mu = p.v_mean; a.flags = p.flags;
+    a.e_tilde = p.e_tilde; a.gamma = p.gamma;
     a.out = p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.kept_mask = p.kept_mask;
     a.mask_words = (p.Lmax + 31) / 32;
     a.masks = p.vrows_read ? masks_ws : nullptr;
@@ -451,12 +493,14 @@ int launch_prefill_rowwise(const PrefillParams& p, float* mu_ws, hipStream_t s) 
     a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Lq = p.L; a.Lk = p.L;
     a.xscale = p.scale * kLog2e;
     a.theta = p.theta; a.n_rows = p.n_rows; a.mu = mu_ws; a.flags = p.flags;
+    a.e_tilde = p.e_tilde; a.gamma = p.gamma;
     a.out = p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.kept_mask = p.kept_mask;
     return dispatch_rows<kRowPrefill>(a, p.d, p.dtype, p.B * p.Hq * p.L, p.L, s);
 }
 
-int launch_calib_accumulate(const float* samples, int S, int n_k, int Hq, int Lq, int q_pos0,
-                            double* sum, double* sumsq, int* count, int n_rows, hipStream_t s);
+int launch_calib_accumulate(const float* samples, const float* esamples, int S, int n_k, int Hq, int Lq,
+                            int q_pos0, double* sum, double* sumsq, int* count, double* esum, int n_rows,
+                            hipStream_t s);
 
 int launch_calibrate_rowwise(const CalibParams& p, float* samples_ws, hipStream_t s) {
     RowArgs a = {};
@@ -465,17 +509,22 @@ int launch_calibrate_rowwise(const CalibParams& p, float* samples_ws, hipStream_
     a.xscale = p.scale * kLog2e; a.q_pos0 = p.q_pos0;
     for (int t = 0; t < 8; ++t) a.ks[t] = p.ks[t];
     a.n_k = p.n_k; a.samples = samples_ws;
+    a.flags = p.pre ? kFlagPre : 0u;
+    // the discarded-mass samples follow the value samples in the workspace
+    float* es = p.esum ? samples_ws + (size_t)p.S * p.n_k * p.Hq * p.Lq : nullptr;
+    a.esamples = es;
     int e = dispatch_rows<kRowCalib>(a, p.d, p.dtype, p.S * p.Hq * p.Lq, p.q_pos0 + p.Lq, s);
     if (e != hipSuccess) return e;
-    return launch_calib_accumulate(samples_ws, p.S, p.n_k, p.Hq, p.Lq, p.q_pos0, p.sum, p.sumsq,
-                                   p.count, p.n_rows, s);
+    return launch_calib_accumulate(samples_ws, es, p.S, p.n_k, p.Hq, p.Lq, p.q_pos0, p.sum, p.sumsq,
+                                   p.count, p.esum, p.n_rows, s);
 }
 
-int launch_calib_accumulate(const float* samples, int S, int n_k, int Hq, int Lq, int q_pos0,
-                            double* sum, double* sumsq, int* count, int n_rows, hipStream_t s) {
+int launch_calib_accumulate(const float* samples, const float* esamples, int S, int n_k, int Hq, int Lq,
+                            int q_pos0, double* sum, double* sumsq, int* count, double* esum, int n_rows,
+                            hipStream_t s) {
     const size_t per = (size_t)n_k * Hq * Lq;
     hipLaunchKernelGGL(calib_accumulate_kernel, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, s,
-                       samples, S, n_k, Hq, Lq, q_pos0, sum, sumsq, count, n_rows);
+                       samples, esamples, S, n_k, Hq, Lq, q_pos0, sum, sumsq, count, esum, n_rows);
     return hipGetLastError();
 }
 
@@ -483,8 +532,18 @@ int launch_finalize(const double* sum, const double* sumsq, const int* count, co
                     int n_k, int Hq, int n_rows, float alpha, float* theta, hipStream_t s) {
     KList kl = {};
     for (int t = 0; t < n_k && t < 8; ++t) kl.k[t] = ks[t];
-    hipLaunchKernelGGL(finalize_kernel, dim3(n_k * Hq), dim3(kFinThreads), 0, s, sum, sumsq, count,
+    hipLaunchKernelGGL(finalize_kernel<false>, dim3(n_k * Hq), dim3(kFinThreads), 0, s, sum, sumsq, count,
                        Hq, n_rows, kl, alpha, theta);
+    return hipGetLastError();
+}
+
+int launch_finalize_etilde(const double* esum, const int* count, const int* ks, int n_k, int Hq,
+                           int n_rows, float* e_tilde, hipStream_t s) {
+    KList kl = {};
+    for (int t = 0; t < n_k && t < 8; ++t) kl.k[t] = ks[t];
+    // alpha = 0: sumsq is never read
+    hipLaunchKernelGGL(finalize_kernel<true>, dim3(n_k * Hq), dim3(kFinThreads), 0, s, esum, esum, count,
+                       Hq, n_rows, kl, 0.f, e_tilde);
     return hipGetLastError();
 }
 

@@ -81,6 +81,36 @@ __device__ __forceinline__ float log2_threshold(float theta, float lse2) {
     return fmaxf(__log2f(theta) + lse2, -3.402823466e38f);
 }
 
+// pre-softmax threshold in the log2 domain: keep x = a * log2(e) >= T  <=>  a >= theta;
+// theta = -inf keeps every valid element (invalid ones carry x = -inf)
+__device__ __forceinline__ float pre_log2_threshold(float theta) {
+    return fmaxf(theta * kLog2e, -3.402823466e38f);
+}
+
+// Flag bits of the kernels (the public TOPTH_* values, plus kFlagPre for the
+// pre-softmax calls).  kFlagExpth / kFlagOffline select the estimate of the
+// discarded softmax mass E~; neither (and not kFlagNone) means exact E.
+constexpr unsigned kFlagVmc = 0x1u, kFlagNone = 0x2u, kFlagExpth = 0x4u, kFlagOffline = 0x8u;
+constexpr unsigned kFlagPre = 0x100u;
+
+// Scale f and beta of a row from its kept post-softmax mass S = R / (R + E),
+// written in the frame where the full denominator R + E is 1 (Eq. 4):
+// out = f * sum_kept s_j V_j + beta * mu with f = 1 / (S + E~ / (R + E)) and
+// beta = 1 - f * S.  etn = E~ / (R + E): 1 - S for exact SDC (f = 1), 0 for
+// no compensation (f = 1 / S, beta = 0).  A zero denominator gives f = beta = 0.
+__device__ __forceinline__ void sdc_scale(unsigned flags, float S, int kept, float etn, float& f,
+                                          float& beta) {
+    if (!(flags & kFlagNone) && !(flags & (kFlagExpth | kFlagOffline))) {   // exact
+        f = 1.f;
+        beta = 1.f - S;
+        return;
+    }
+    const float den = (flags & kFlagNone) ? S : S + etn;
+    if (!(den > 0.f) || ((flags & kFlagNone) && kept == 0)) { f = 0.f; beta = 0.f; return; }
+    f = 1.f / den;
+    beta = (flags & kFlagNone) ? 0.f : 1.f - f * S;
+}
+
 // ------------------------------------------------------------------ launchers
 struct DecodeParams {
     const void* q; const void* k; const void* v; const int* seq_lens;
@@ -88,6 +118,7 @@ struct DecodeParams {
     const float* theta; int n_rows; const float* v_mean; unsigned flags;
     void* out; int* kept_count; float* beta; int* vrows_read; unsigned char* kept_mask;
     void* ws; size_t ws_bytes;
+    const float* e_tilde; float gamma;    // pre-softmax calls only
 };
 struct PrefillParams {
     const void* q; const void* k; const void* v;
@@ -95,6 +126,7 @@ struct PrefillParams {
     const float* theta; int n_rows; unsigned flags;
     void* out; int* kept_count; float* beta; unsigned char* kept_mask;
     void* ws; size_t ws_bytes;
+    const float* e_tilde; float gamma;    // pre-softmax calls only
 };
 struct CalibParams {
     const void* q; const void* k;
@@ -102,6 +134,7 @@ struct CalibParams {
     int ks[8]; int n_k;
     double* sum; double* sumsq; int* count; int n_rows;
     void* ws; size_t ws_bytes;
+    bool pre; double* esum;               // pre-softmax samples; E~ sums or NULL
 };
 
 // Each launcher validates nothing (the ABI layer did) and returns a hipError_t.
@@ -113,6 +146,8 @@ size_t calib_ws_bytes(int S, int Hq, int Lq, int Lk, int d, int n_k);
 int launch_calibrate(const CalibParams& p, hipStream_t s);
 int launch_finalize(const double* sum, const double* sumsq, const int* count, const int* ks,
                     int n_k, int Hq, int n_rows, float alpha, float* theta, hipStream_t s);
+int launch_finalize_etilde(const double* esum, const int* count, const int* ks, int n_k, int Hq,
+                           int n_rows, float* e_tilde, hipStream_t s);
 int launch_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,
                  float* v_mean, hipStream_t s);
 int launch_fill_u32(void* p, size_t bytes, uint32_t value, hipStream_t s);

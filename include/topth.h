@@ -69,17 +69,22 @@ typedef enum {
 
 typedef enum { TOPTH_F32 = 0, TOPTH_BF16 = 1 } topth_dtype;
 
-/* flags of topth_prefill / topth_decode */
+/* flags of topth_prefill / topth_decode (and of the _pre calls below) */
 #define TOPTH_VMC       0x1u  /* add beta * mu, mu = mean V row (Sec. 3.2.2, Eq. 7)     */
 #define TOPTH_SDC_NONE  0x2u  /* divide kept weights by the kept mass only (softmax
                                  over the kept set) instead of exact SDC; beta = 0       */
+/* estimates of the discarded softmax mass E~, pre-softmax calls only (Sec. 3.2.1);
+   with none of TOPTH_SDC_NONE / _EXPTH / _OFFLINE set, E~ is the exact E      */
+#define TOPTH_SDC_EXPTH   0x4u  /* exp-threshold: E~ = gamma (n - k~) exp(theta - max a) */
+#define TOPTH_SDC_OFFLINE 0x8u  /* offline-calibrated: E~ = e_tilde[h][row]              */
 
 /* op codes of topth_workspace_size */
 #define TOPTH_OP_CALIBRATE 0
 #define TOPTH_OP_PREFILL   1
 #define TOPTH_OP_DECODE    2
+#define TOPTH_OP_CALIBRATE_PRE_E 3   /* topth_calibrate_pre with esum != NULL */
 
-#define TOPTH_WS_HEADER_BYTES 4096
+#define TOPTH_WS_HEADER_BYTES 65536
 #define TOPTH_MAX_NK 8        /* most k values one calibration call can target */
 
 /* Human-readable text of a status code (static storage). */
@@ -91,6 +96,10 @@ const char* topth_strerror(int status);
  *   TOPTH_OP_CALIBRATE: B = sequences per call S, Hq, Hkv, Lq, Lk, d, n_k
  *   TOPTH_OP_PREFILL:   B, Hq, Hkv, Lq = Lk = L, d
  *   TOPTH_OP_DECODE:    B, Hq, Hkv, Lk = Lmax, d
+ *   TOPTH_OP_CALIBRATE_PRE_E: as TOPTH_OP_CALIBRATE (topth_calibrate_pre also
+ *                       collecting the discarded mass; without it, the
+ *                       TOPTH_OP_CALIBRATE size serves)
+ *   TOPTH_OP_PREFILL and TOPTH_OP_DECODE sizes serve the _pre calls too.
  * Returns 0 for arguments no call could accept.
  */
 size_t topth_workspace_size(int op, int B, int Hq, int Hkv, int Lq, int Lk, int d, int n_k);
@@ -186,6 +195,70 @@ int topth_decode(const void* q, const void* k_cache, const void* v_cache, const 
  */
 int topth_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,
                 float* v_mean, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Pre-softmax Top-theta (the paper's Algorithm 1 in its printed form, and
+ * Sec. 3.2.1): thresholds are on the scores a = scale * q.k themselves, in
+ * score units, and the kept elements are weighted by softmax over the kept
+ * scores times R / (R + E~) (Eq. 4), where R and E are the sums of exp(a - max a)
+ * over the kept and the discarded elements and E~ estimates E.  VMC adds
+ * beta * mu with beta = E~ / (R + E~) (Sec. 3.2.2, case (ii)).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Calibration in the pre-softmax form: as topth_calibrate, but the sample of
+ * a row is its k-th largest score a (not a post-softmax value).  With
+ * esum != NULL the call also adds, per row, the discarded mass of the row's
+ * top-k selection, E = sum over the elements outside the k largest of
+ * exp(a - max a), into esum[t][h][p] (device double, same shape as sum; the
+ * offline estimate of E~, Sec. 3.2.1 item 1).  ws must then hold
+ * topth_workspace_size(TOPTH_OP_CALIBRATE_PRE_E, ...) bytes.  The thresholds
+ * come from topth_calibrate_finalize, the E~ table from
+ * topth_calibrate_finalize_etilde.
+ */
+int topth_calibrate_pre(const void* q, const void* k, int S, int Hq, int Hkv, int Lq, int Lk,
+                        int d, int dtype, float scale, int q_pos0, const int* ks, int n_k,
+                        double* sum, double* sumsq, int* count, double* esum, int n_rows,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Offline E~ table from the sums of topth_calibrate_pre: e_tilde[t][h][p] =
+ * esum / count for observed rows; 0 for rows with p + 1 <= ks[t] (nothing is
+ * discarded); any other row copies the nearest observed row of the same (t, h)
+ * (the smaller row on a tie), or 0 if none was observed.
+ *   esum device double, count device int [n_k][Hq][n_rows]; ks host [n_k];
+ *   e_tilde device float [n_k][Hq][n_rows] (output).
+ */
+int topth_calibrate_finalize_etilde(const double* esum, const int* count, const int* ks, int n_k,
+                                    int Hq, int n_rows, float* e_tilde, void* stream);
+
+/*
+ * Causal pre-softmax prefill: keep a >= theta[h][min(p, n_rows-1)] (theta in
+ * score units, -INFINITY keeps all); out = sum_kept w_j V_j (+ beta * mu_p
+ * with TOPTH_VMC), w_j = exp(a_j - max a) / (R + E~), with E~ by flags:
+ * exact E (default), TOPTH_SDC_EXPTH (gamma >= 0), TOPTH_SDC_OFFLINE (e_tilde
+ * device float [Hq][n_rows], required), TOPTH_SDC_NONE (E~ = 0, beta = 0).  A
+ * row with R + E~ = 0 outputs 0 with beta = 0.  At most one of the three
+ * estimate flags.  Other arguments as topth_prefill; the bfloat16 path makes
+ * one sweep over the keys (no row log-sum-exp pass).
+ */
+int topth_prefill_pre(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int L,
+                      int d, int dtype, float scale, const float* theta, const float* e_tilde,
+                      int n_rows, unsigned flags, float gamma, void* out, int* kept_count,
+                      float* beta, unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One pre-softmax decoding step: keep a >= theta[h][min(n-1, n_rows-1)] and
+ * weight as topth_prefill_pre (n = seq_lens[b] keys); v_mean is required iff
+ * TOPTH_VMC without TOPTH_SDC_NONE.  Other arguments, the workspace contract
+ * and vrows_read as topth_decode.
+ */
+int topth_decode_pre(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                     int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                     const float* theta, const float* e_tilde, int n_rows, const float* v_mean,
+                     unsigned flags, float gamma, void* out, int* kept_count, float* beta,
+                     int* vrows_read, unsigned char* kept_mask, void* ws, size_t ws_bytes,
+                     void* stream);
 
 #ifdef __cplusplus
 }

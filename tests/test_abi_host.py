@@ -146,3 +146,60 @@ def test_binding_rejects_cpu_tensors(lib):
                        torch.zeros(1, 1, 64))
     with pytest.raises(ValueError):
         tt.topth_decode(q, q, q, None, None, None, None, scale=0.1, flags=0)
+
+
+# ------------------------------------------------------------- pre-softmax calls
+def _decode_pre(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, B=2, Hq=8, Hkv=2, Lmax=64, d=128, dt=1, scale=0.1,
+             theta=FAKE, et=None, n_rows=64, vm=FAKE, flags=1, gamma=0.05, out=FAKE, kc=None, bt=None,
+             vr=None, km=None, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return lib.topth_decode_pre(a["q"], a["k"], a["v"], a["lens"], a["B"], a["Hq"], a["Hkv"], a["Lmax"],
+                                a["d"], a["dt"], a["scale"], a["theta"], a["et"], a["n_rows"], a["vm"],
+                                a["flags"], a["gamma"], a["out"], a["kc"], a["bt"], a["vr"], a["km"],
+                                a["ws"], a["wsb"], None)
+
+
+def _prefill_pre(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, Hq=8, Hkv=2, L=64, d=128, dt=1, scale=0.1, theta=FAKE,
+             et=None, n_rows=64, flags=0, gamma=0.05, out=FAKE, kc=None, bt=None, km=None, ws=None, wsb=0)
+    a.update(over)
+    return lib.topth_prefill_pre(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["d"], a["dt"],
+                                 a["scale"], a["theta"], a["et"], a["n_rows"], a["flags"], a["gamma"],
+                                 a["out"], a["kc"], a["bt"], a["km"], a["ws"], a["wsb"], None)
+
+
+def test_pre_flag_errors(lib):
+    E, O, N = tt.TOPTH_SDC_EXPTH, tt.TOPTH_SDC_OFFLINE, tt.TOPTH_SDC_NONE
+    for call in (_decode_pre, _prefill_pre):
+        assert call(lib, flags=E | O) == -1                 # two estimates
+        assert call(lib, flags=E | N) == -1
+        assert call(lib, flags=O) == -1                     # offline needs the E~ table
+        assert call(lib, flags=E, gamma=float("nan")) == -1
+        assert call(lib, flags=E, gamma=-0.5) == -1
+        assert call(lib, flags=0x10) == -1
+        assert call(lib, theta=None) == -1
+        assert call(lib, scale=0.0) == -1
+    assert _decode_pre(lib, flags=tt.TOPTH_VMC, vm=None) == -1   # VMC needs the running mean
+    assert _decode_pre(lib, ws=None) == -3
+    assert _prefill_pre(lib, flags=tt.TOPTH_VMC) == -3            # VMC needs the prefix-mean workspace
+    # the post-softmax calls take no estimate flags
+    assert _decode(lib, flags=tt.TOPTH_VMC | E) == -1
+
+
+def test_calibrate_pre_errors_and_workspace(lib):
+    ws = tt.topth_workspace_size
+    base = ws(tt.TOPTH_OP_CALIBRATE, 4, 8, 8, 2048, 2048, 128, 3)
+    assert ws(tt.TOPTH_OP_CALIBRATE_PRE_E, 4, 8, 8, 2048, 2048, 128, 3) == 2 * base
+    karr = (ctypes.c_int * 1)(32)
+    kp = ctypes.cast(karr, ctypes.c_void_p)
+
+    def cal(esum, wsb):
+        return lib.topth_calibrate_pre(FAKE, FAKE, 4, 8, 8, 2048, 2048, 128, 1, 0.1, 0, kp, 1,
+                                       FAKE, FAKE, FAKE, esum, 2048, FAKE, wsb, None)
+    one = ws(tt.TOPTH_OP_CALIBRATE, 4, 8, 8, 2048, 2048, 128, 1)
+    assert cal(FAKE, one) == -3                            # the E~ samples need twice the room
+    assert lib.topth_calibrate_pre(None, FAKE, 4, 8, 8, 2048, 2048, 128, 1, 0.1, 0, kp, 1,
+                                   FAKE, FAKE, FAKE, None, 2048, FAKE, one, None) == -1
+    assert lib.topth_calibrate_finalize_etilde(None, FAKE, kp, 1, 8, 2048, FAKE, None) == -1
+    assert lib.topth_calibrate_finalize_etilde(FAKE, FAKE, kp, 0, 8, 2048, FAKE, None) == -1
