@@ -57,15 +57,23 @@ class PreRowResult:
 
 
 def pre_weights(a, theta: float, *, sdc: str, gamma: float = 0.05, e_tilde: float = 0.0):
-    """Keep mask, weights and beta of one row under pre-softmax Top-theta.
+    """Keep mask, weights and beta of one row under pre-softmax Top-theta:
+    keep = a >= theta, then ``pre_weights_for_mask``."""
+    a = _as64(a)
+    keep = a >= theta
+    w, beta = pre_weights_for_mask(a, keep, theta, sdc=sdc, gamma=gamma, e_tilde=e_tilde)
+    return keep, w, beta
 
-    keep = a >= theta; weights follow Eq. 4: softmax over the kept scores times
-    R / (R + E~), with E~ chosen by ``sdc`` (see the module notes)."""
+
+def pre_weights_for_mask(a, keep, theta: float, *, sdc: str, gamma: float = 0.05,
+                         e_tilde: float = 0.0):
+    """Weights and beta for a given kept set: Eq. 4, softmax over the kept
+    scores times R / (R + E~), with E~ chosen by ``sdc`` (see the module notes)."""
     if sdc not in SDC_MODES:
         raise ValueError(f"unknown SDC estimate {sdc!r}")
     a = _as64(a)
+    keep = np.asarray(keep, dtype=bool)
     n = a.size
-    keep = a >= theta
     kt = int(keep.sum())
     m = float(a.max())
     e = np.exp(a - m)
@@ -87,7 +95,7 @@ def pre_weights(a, theta: float, *, sdc: str, gamma: float = 0.05, e_tilde: floa
         beta = 0.0 if sdc == "none" else 1.0 - R / (R + Et)   # = E~ / (R + E~)
     else:
         beta = 0.0
-    return keep, w, beta
+    return w, beta
 
 
 def pre_row(a, V, theta: float, mu, *, sdc: str, vmc: bool, gamma: float = 0.05,

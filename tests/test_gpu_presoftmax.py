@@ -145,7 +145,7 @@ def compare_prefill_pre(q, k, v, theta, et, sdc, vmc, g, dtype, rows):
         mu = np.zeros(d)
         if vmc:
             if (b, kv) not in mu_cache:
-                mu_cache[(b, kv)] = np.cumsum(vf[b, kv], axis=0) / np.arange(1, L + 1)[:, None]
+                mu_cache[(b, kv)] = pre.prefix_mean(vf[b, kv])
             mu = mu_cache[(b, kv)][p]
         check_pre_row(gk, a, thv, vf[b, kv, :p + 1], mu, sdc, pre.table_row(et, h, p), vmc,
                       out_g[b, h, p], bt_g[b, h, p], dtype, f"b{b} h{h} p{p}")
