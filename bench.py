@@ -123,13 +123,14 @@ def probe_rows(w):
     return out
 
 
-def calibrate_decode_theta(name, w, dev, rows=()):
+def calibrate_decode_theta(name, w, dev, rows=(), include_last=True, with_count=False):
     """theta [Hq, n] for k from `calib` decode-style sequences, on the GPU.  Row
-    n - 1 (the timed decode step) and every row in `rows` are calibrated, each
-    with its own query draw; other rows copy the nearest calibrated row."""
+    n - 1 (the timed decode step, unless `include_last` is False) and every row
+    in `rows` are calibrated, each with its own query draw; other rows copy the
+    nearest calibrated row.  With `with_count`, also the [1, Hq, n] counts."""
     cfg = CONFIG_IDS[name]
     Hq, Hkv, d, n, k = w["Hq"], w["Hkv"], w["d"], w["n"], w["k"]
-    rows = sorted(set(int(r) for r in rows) | {n - 1})
+    rows = sorted(set(int(r) for r in rows) | ({n - 1} if include_last else set()))
     s1 = torch.zeros(1, Hq, n, dtype=torch.float64, device=dev)
     s2 = torch.zeros_like(s1)
     cnt = torch.zeros(1, Hq, n, dtype=torch.int32, device=dev)
@@ -147,7 +148,28 @@ def calibrate_decode_theta(name, w, dev, rows=()):
     theta = torch.empty(1, Hq, n, dtype=torch.float32, device=dev)
     tt.topth_calibrate_finalize(s1, s2, cnt, [k], theta)
     torch.cuda.synchronize()
+    if with_count:
+        return theta[0].contiguous(), cnt
     return theta[0].contiguous()
+
+
+def theta_extrapolation(name, w, dev, buckets, buf, limit=2048):
+    """k~/k on rows past the calibrated range: theta calibrated only at the
+    probe rows below `limit`, then applied at the longer probe rows either as
+    the nearest calibrated row or as a least-squares fit of ln(theta) in
+    ln(p + 1) (degree 1 and 2), next to theta calibrated at the rows themselves."""
+    short = [p for rows in buckets.values() for p in rows if p < limit]
+    theta_near, cnt = calibrate_decode_theta(name, w, dev, rows=short, include_last=False, with_count=True)
+    far = {b: rows for b, rows in buckets.items() if min(rows) >= limit}
+    out = {"calibrated_rows": f"{len(short)} probe rows below {limit}",
+           "nearest": kept_by_bucket(far, buf, theta_near, w, dev)}
+    for deg in (1, 2):
+        coef = torch.empty(1, w["Hq"], deg + 1, dtype=torch.float64, device=dev)
+        tt.topth_theta_fit(theta_near[None].contiguous(), cnt, coef, degree=deg, log_domain=True)
+        fitted = torch.empty(1, w["Hq"], w["n"], dtype=torch.float32, device=dev)
+        tt.topth_theta_eval(coef, [w["k"]], fitted, log_domain=True)
+        out[f"fitted_log_degree{deg}"] = kept_by_bucket(far, buf, fitted[0].contiguous(), w, dev)
+    return out
 
 
 def kept_by_bucket(buckets, buf, theta, w, dev):
@@ -330,6 +352,8 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
     if buckets:
         log("[bench] k~/k at the probe rows of each bucket")
         res["kept_over_k_by_row_bucket"] = kept_by_bucket(buckets, bufs[0], theta, w, dev)
+        log("[bench] k~/k past the calibrated rows: nearest row against a fitted theta(n)")
+        res["theta_extrapolation"] = theta_extrapolation(name, w, dev, buckets, bufs[0])
     if with_cpu:
         log("[bench] timing the CPU oracle on a sample of the same workload")
         res["cpu_baseline"] = oracle_decode_baseline(bufs[0], lens, theta, vms[0], w, read_bytes)

@@ -25,7 +25,7 @@ TOPTH_MAX_NK = 8
 EXPORTS = ("topth_strerror", "topth_workspace_size", "topth_workspace_init", "topth_calibrate",
            "topth_calibrate_finalize", "topth_prefill", "topth_decode", "topth_vmean",
            "topth_calibrate_pre", "topth_calibrate_finalize_etilde", "topth_prefill_pre",
-           "topth_decode_pre")
+           "topth_decode_pre", "topth_vmean_append", "topth_theta_fit", "topth_theta_eval")
 
 
 class TopthError(RuntimeError):
@@ -72,6 +72,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topth_prefill_pre.restype = i
     lib.topth_prefill_pre.argtypes = [vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, u, f, vp, vp, vp, vp,
                                       vp, sz, vp]
+    lib.topth_vmean_append.restype = i
+    lib.topth_vmean_append.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp]
+    lib.topth_theta_fit.restype = i
+    lib.topth_theta_fit.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
+    lib.topth_theta_eval.restype = i
+    lib.topth_theta_eval.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
     lib.topth_decode_pre.restype = i
     lib.topth_decode_pre.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, vp, u, f, vp, vp,
                                      vp, vp, vp, vp, sz, vp]
@@ -309,3 +315,39 @@ def topth_decode_pre(q, k_cache, v_cache, seq_lens, theta, out, ws, *, scale: fl
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv,
         Lmax, d, dt, float(scale), theta.data_ptr(), et, theta.shape[1], vm, int(flags), float(gamma),
         out.data_ptr(), kc, bt, vr, km, ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+# ----------------------------------------------------------- serving helpers
+def topth_vmean_append(v_cache, old_lens, new_lens, v_mean, stream=None):
+    """v_mean [B,Hkv,d] (mean of the first old_lens rows) becomes the mean of the
+    first new_lens rows of v_cache [B,Hkv,Lmax,d]."""
+    B, Hkv, Lmax, d = v_cache.shape
+    dt = _dtype_code(v_cache)
+    _dev(v_cache, "v_cache"); _dev(old_lens, "old_lens", torch.int32, (B,))
+    _dev(new_lens, "new_lens", torch.int32, (B,)); _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d))
+    _check("topth_vmean_append", load_library().topth_vmean_append(
+        v_cache.data_ptr(), old_lens.data_ptr(), new_lens.data_ptr(), B, Hkv, Lmax, d, dt,
+        v_mean.data_ptr(), _stream(stream)))
+
+
+def topth_theta_fit(theta, count, coef, *, degree: int, log_domain: bool, stream=None):
+    """Fit coef [n_k,Hq,degree+1] (float64) to the observed rows of theta/count [n_k,Hq,n_rows]."""
+    n_k, Hq, n_rows = theta.shape
+    _dev(theta, "theta", torch.float32); _dev(count, "count", torch.int32, theta.shape)
+    _dev(coef, "coef", torch.float64, (n_k, Hq, degree + 1))
+    _check("topth_theta_fit", load_library().topth_theta_fit(
+        theta.data_ptr(), count.data_ptr(), n_k, Hq, n_rows, int(degree), int(bool(log_domain)),
+        coef.data_ptr(), _stream(stream)))
+
+
+def topth_theta_eval(coef, ks, theta_out, *, log_domain: bool, stream=None):
+    """theta_out [n_k,Hq,n_out] from fitted coefficients coef [n_k,Hq,degree+1]."""
+    n_k, Hq, m = coef.shape
+    _dev(coef, "coef", torch.float64)
+    _dev(theta_out, "theta_out", torch.float32)
+    if theta_out.dim() != 3 or tuple(theta_out.shape[:2]) != (n_k, Hq) or len(ks) != n_k:
+        raise ValueError("theta_out must be [n_k, Hq, n_out] and ks of length n_k")
+    karr = (ctypes.c_int * max(n_k, 1))(*[int(x) for x in ks])
+    _check("topth_theta_eval", load_library().topth_theta_eval(
+        coef.data_ptr(), ctypes.cast(karr, ctypes.c_void_p), n_k, Hq, m - 1, int(bool(log_domain)),
+        theta_out.shape[2], theta_out.data_ptr(), _stream(stream)))

@@ -20,6 +20,13 @@ int launch_prefill_bf16(const PrefillParams& p, float* mu_ws, hipStream_t s);
 int launch_calibrate_rowwise(const CalibParams& p, float* samples_ws, hipStream_t s);
 bool calib_bf16_supported(int d, int S, int Hq, int Lq, int q_pos0);
 int launch_calibrate_bf16(const CalibParams& p, float* samples_ws, hipStream_t s);
+int max_fit_degree();
+int launch_vmean_append(const void* v, const int* old_lens, const int* new_lens, int B, int Hkv, int Lmax,
+                        int d, int dtype, float* v_mean, hipStream_t s);
+int launch_theta_fit(const float* theta, const int* count, int n_k, int Hq, int n_rows, int degree,
+                     int log_domain, double* coef, hipStream_t s);
+int launch_theta_eval(const double* coef, const int* ks, int n_k, int Hq, int degree, int log_domain,
+                      int n_out, float* theta_out, hipStream_t s);
 }  // namespace topth
 
 using namespace topth;
@@ -302,6 +309,37 @@ int topth_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, in
     if (bad_dims(B, Hkv, Hkv, Lmax, d) || bad_dtype(dtype)) return TOPTH_EINVAL;
     if (too_big((long long)B * Hkv * Lmax, d)) return TOPTH_EUNSUPPORTED;
     return map_hip(launch_vmean(v, seq_lens, B, Hkv, Lmax, d, dtype, v_mean, (hipStream_t)stream));
+}
+
+int topth_vmean_append(const void* v_cache, const int* old_lens, const int* new_lens, int B, int Hkv,
+                       int Lmax, int d, int dtype, float* v_mean, void* stream) {
+    if (!v_cache || !old_lens || !new_lens || !v_mean) return TOPTH_EINVAL;
+    if (bad_dims(B, Hkv, Hkv, Lmax, d) || bad_dtype(dtype)) return TOPTH_EINVAL;
+    if (too_big((long long)B * Hkv * Lmax, d)) return TOPTH_EUNSUPPORTED;
+    return map_hip(launch_vmean_append(v_cache, old_lens, new_lens, B, Hkv, Lmax, d, dtype, v_mean,
+                                       (hipStream_t)stream));
+}
+
+int topth_theta_fit(const float* theta, const int* count, int n_k, int Hq, int n_rows, int degree,
+                    int log_domain, double* coef, void* stream) {
+    if (!theta || !count || !coef) return TOPTH_EINVAL;
+    if (n_k < 1 || n_k > TOPTH_MAX_NK || Hq <= 0 || n_rows <= 0) return TOPTH_EINVAL;
+    if (degree < 0 || degree > max_fit_degree()) return TOPTH_EINVAL;
+    if ((long long)n_k * Hq > INT_MAX) return TOPTH_EUNSUPPORTED;
+    return map_hip(launch_theta_fit(theta, count, n_k, Hq, n_rows, degree, log_domain != 0, coef,
+                                    (hipStream_t)stream));
+}
+
+int topth_theta_eval(const double* coef, const int* ks, int n_k, int Hq, int degree, int log_domain,
+                     int n_out, float* theta_out, void* stream) {
+    if (!coef || !ks || !theta_out) return TOPTH_EINVAL;
+    if (n_k < 1 || n_k > TOPTH_MAX_NK || Hq <= 0 || n_out <= 0) return TOPTH_EINVAL;
+    if (degree < 0 || degree > max_fit_degree()) return TOPTH_EINVAL;
+    for (int t = 0; t < n_k; ++t)
+        if (ks[t] < 1) return TOPTH_EINVAL;
+    if ((long long)n_k * Hq > 65535) return TOPTH_EUNSUPPORTED;     // one grid row per (t, h)
+    return map_hip(launch_theta_eval(coef, ks, n_k, Hq, degree, log_domain != 0, n_out, theta_out,
+                                     (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -260,6 +260,50 @@ int topth_decode_pre(const void* q, const void* k_cache, const void* v_cache, co
                      int* vrows_read, unsigned char* kept_mask, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* ------------------------------------------------------------------------
+ * Decode-serving helpers
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Running mean of V for VMC (Sec. 3.2.2: during generative decoding mu is kept
+ * as a running mean instead of being recomputed): after rows
+ * old_lens[b] .. new_lens[b]-1 of each (b, KV head) have been written to the
+ * cache, v_mean (the mean of the first old_lens[b] rows on entry) becomes the
+ * mean of the first new_lens[b] rows: (old * mu + sum of the new rows) / new.
+ * A batch element with old_lens[b] = 0 starts fresh (v_mean is not read).
+ *   v_cache device [B][Hkv][Lmax][d]; old_lens, new_lens device int [B]
+ *   (clamped to 1 <= new <= Lmax and 0 <= old <= new); v_mean device float
+ *   [B][Hkv][d], updated in place.  The sums are float64 in row order.
+ */
+int topth_vmean_append(const void* v_cache, const int* old_lens, const int* new_lens, int B, int Hkv,
+                       int Lmax, int d, int dtype, float* v_mean, void* stream);
+
+/*
+ * Thresholds as a function of the row position, for rows no calibration
+ * sequence reached (the paper fits the per-row thresholds to the sequence
+ * length; the function is not given, so this library uses a least-squares
+ * polynomial of degree 0..3 in x = ln(p + 1)).  topth_theta_fit fits, per
+ * (t, h), the rows with count > 0 of a finalized slab: on ln(theta) when
+ * log_domain != 0 (post-softmax thresholds, which fall roughly as a power of
+ * the row length; rows with theta <= 0 are skipped), on theta otherwise
+ * (pre-softmax thresholds).
+ *   theta device float, count device int [n_k][Hq][n_rows];
+ *   coef device double [n_k][Hq][degree + 1], highest power first (output);
+ *   NaN coefficients where fewer than degree + 1 rows are usable.
+ */
+int topth_theta_fit(const float* theta, const int* count, int n_k, int Hq, int n_rows, int degree,
+                    int log_domain, double* coef, void* stream);
+
+/*
+ * Evaluate fitted thresholds into a slab of n_out rows (which may be longer
+ * than the calibrated one): theta_out[t][h][p] = poly(ln(p + 1)), exponentiated
+ * when log_domain != 0, for p + 1 > ks[t]; -INFINITY (keep all) below.
+ *   coef device double [n_k][Hq][degree + 1]; ks host [n_k];
+ *   theta_out device float [n_k][Hq][n_out] (output).
+ */
+int topth_theta_eval(const double* coef, const int* ks, int n_k, int Hq, int degree, int log_domain,
+                     int n_out, float* theta_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,82 @@
+"""Float64 reference of the decode-serving helpers around Top-theta (test
+infrastructure only).
+
+Source: "Top-Theta Attention: Sparsifying Transformers by Compensated
+Thresholding" (arXiv 2502.08363), cited as [TT], and the Pith verdict page on
+the same paper, which paraphrases the paper's lost technical details.
+
+* Running mean of V ([TT] §3.2.2, after Eq. 7: during generative decoding mu
+  "can be maintained as a running mean"): appending rows n_old..n_new-1 to a
+  cache whose first n_old rows have mean mu_old gives the mean of the first
+  n_new rows, mu_new = (n_old * mu_old + sum of the new rows) / n_new.  This is
+  Eq. 5 over the longer cache, rewritten; a cache with n_old = 0 starts fresh.
+* Fitted thresholds (Pith verdict page: rows longer than the calibrated ones
+  use "the nearest calibrated threshold or a fitted function", and the paper
+  "fits the per-row thresholds as a function of sequence length, compressing
+  hundreds of parameters into a few fitted coefficients"; the function itself
+  is lost with the paper's Fig. 3 and technical details).  Reading: a
+  least-squares polynomial of low degree in x = ln(p + 1) through the
+  calibrated rows of each (k, head) -- on ln(theta) for post-softmax thresholds
+  (probabilities, which fall roughly as a power of the row length) and on theta
+  itself for pre-softmax thresholds (scores).  Evaluated at every row with
+  p + 1 > k; rows with p + 1 <= k keep everything (-inf).  **Parity unpinned**
+  by the pages: the function form is a reading; the pins check the fit itself
+  (exact recovery of data that lie on such a polynomial, library least squares).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .topth import _as64
+
+
+def running_mean_append(mu_old, n_old: int, V_new) -> np.ndarray:
+    """mu of the first n_old + m rows from mu of the first n_old rows and the m
+    appended rows V_new [m, d]."""
+    V_new = _as64(V_new)
+    n_new = int(n_old) + V_new.shape[0]
+    if n_new <= 0:
+        raise ValueError("empty cache")
+    total = V_new.sum(axis=0)
+    if n_old > 0:
+        total = total + int(n_old) * _as64(mu_old)
+    return total / n_new
+
+
+def fit_theta(theta_table, observed, degree: int, log_domain: bool):
+    """Coefficients (highest power first) of the least-squares polynomial of
+    ``degree`` in ln(p + 1) through the rows p where ``observed`` is true, on
+    ln(theta) if ``log_domain`` else on theta; one row of coefficients per
+    head.  theta_table and observed are [Hq, R].  A head with fewer than
+    degree + 1 usable rows gets NaN coefficients; in the log domain rows with
+    theta <= 0 are not usable."""
+    th = _as64(theta_table)
+    obs = np.asarray(observed, dtype=bool)
+    Hq, R = th.shape
+    coef = np.full((Hq, degree + 1), np.nan)
+    x_all = np.log(np.arange(R) + 1.0)
+    for h in range(Hq):
+        use = obs[h] & np.isfinite(th[h])
+        if log_domain:
+            use &= th[h] > 0
+        if use.sum() < degree + 1:
+            continue
+        y = np.log(th[h][use]) if log_domain else th[h][use]
+        coef[h] = np.polyfit(x_all[use], y, degree)
+    return coef
+
+
+def eval_theta(coef, k: int, n_out: int, log_domain: bool) -> np.ndarray:
+    """theta [Hq, n_out] from the fitted coefficients: the polynomial at
+    ln(p + 1) (exponentiated in the log domain) for p + 1 > k, -inf below."""
+    coef = _as64(coef)
+    Hq = coef.shape[0]
+    x = np.log(np.arange(n_out) + 1.0)
+    out = np.full((Hq, n_out), -np.inf)
+    for h in range(Hq):
+        v = np.polyval(coef[h], x)
+        if log_domain:
+            v = np.exp(v)
+        rows = np.arange(n_out) + 1 > k
+        out[h, rows] = v[rows]
+    return out

@@ -203,3 +203,17 @@ def test_calibrate_pre_errors_and_workspace(lib):
                                    FAKE, FAKE, FAKE, None, 2048, FAKE, one, None) == -1
     assert lib.topth_calibrate_finalize_etilde(None, FAKE, kp, 1, 8, 2048, FAKE, None) == -1
     assert lib.topth_calibrate_finalize_etilde(FAKE, FAKE, kp, 0, 8, 2048, FAKE, None) == -1
+
+
+def test_serving_helper_errors(lib):
+    karr = (ctypes.c_int * 1)(32)
+    kp = ctypes.cast(karr, ctypes.c_void_p)
+    assert lib.topth_vmean_append(None, FAKE, FAKE, 2, 8, 64, 128, 1, FAKE, None) == -1
+    assert lib.topth_vmean_append(FAKE, FAKE, FAKE, 2, 8, 64, 96, 1, FAKE, None) == -1     # d
+    assert lib.topth_vmean_append(FAKE, FAKE, FAKE, 2, 8, 64, 128, 5, FAKE, None) == -1    # dtype
+    assert lib.topth_theta_fit(FAKE, FAKE, 1, 8, 64, 4, 1, FAKE, None) == -1               # degree > 3
+    assert lib.topth_theta_fit(FAKE, FAKE, 1, 8, 64, -1, 1, FAKE, None) == -1
+    assert lib.topth_theta_fit(FAKE, None, 1, 8, 64, 1, 1, FAKE, None) == -1
+    assert lib.topth_theta_eval(FAKE, kp, 1, 8, 2, 1, 0, FAKE, None) == -1                 # n_out
+    assert lib.topth_theta_eval(FAKE, None, 1, 8, 2, 1, 100, FAKE, None) == -1
+    assert lib.topth_theta_eval(FAKE, kp, 9, 8, 2, 1, 100, FAKE, None) == -1               # n_k
