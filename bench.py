@@ -163,12 +163,18 @@ def theta_extrapolation(name, w, dev, buckets, buf, limit=2048):
     far = {b: rows for b, rows in buckets.items() if min(rows) >= limit}
     out = {"calibrated_rows": f"{len(short)} probe rows below {limit}",
            "nearest": kept_by_bucket(far, buf, theta_near, w, dev)}
-    for deg in (1, 2):
+    # near p + 1 = k the k-th largest is close to the row minimum, so theta first
+    # rises with the row length before it falls: fits over all calibrated rows,
+    # and fits over the rows with p + 1 >= 4 k only
+    far_cnt = cnt.clone()
+    far_cnt[:, :, :4 * w["k"] - 1] = 0
+    for label, c, deg in (("fitted_log_degree1", cnt, 1), ("fitted_log_degree2", cnt, 2),
+                          ("fitted_log_degree1_rows_from_4k", far_cnt, 1)):
         coef = torch.empty(1, w["Hq"], deg + 1, dtype=torch.float64, device=dev)
-        tt.topth_theta_fit(theta_near[None].contiguous(), cnt, coef, degree=deg, log_domain=True)
+        tt.topth_theta_fit(theta_near[None].contiguous(), c, coef, degree=deg, log_domain=True)
         fitted = torch.empty(1, w["Hq"], w["n"], dtype=torch.float32, device=dev)
         tt.topth_theta_eval(coef, [w["k"]], fitted, log_domain=True)
-        out[f"fitted_log_degree{deg}"] = kept_by_bucket(far, buf, fitted[0].contiguous(), w, dev)
+        out[label] = kept_by_bucket(far, buf, fitted[0].contiguous(), w, dev)
     return out
 
 
