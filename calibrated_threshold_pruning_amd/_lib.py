@@ -25,7 +25,8 @@ TOPTH_MAX_NK = 8
 EXPORTS = ("topth_strerror", "topth_workspace_size", "topth_workspace_init", "topth_calibrate",
            "topth_calibrate_finalize", "topth_prefill", "topth_decode", "topth_vmean",
            "topth_calibrate_pre", "topth_calibrate_finalize_etilde", "topth_prefill_pre",
-           "topth_decode_pre", "topth_vmean_append", "topth_theta_fit", "topth_theta_eval")
+           "topth_decode_pre", "topth_vmean_append", "topth_theta_fit", "topth_theta_eval",
+           "topth_decode_gqa")
 
 
 class TopthError(RuntimeError):
@@ -78,6 +79,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topth_theta_fit.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
     lib.topth_theta_eval.restype = i
     lib.topth_theta_eval.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
+    lib.topth_decode_gqa.restype = i
+    lib.topth_decode_gqa.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, vp, u, i, i, vp, vp, vp,
+                                     vp, vp, vp, sz, vp]
     lib.topth_decode_pre.restype = i
     lib.topth_decode_pre.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, vp, u, f, vp, vp,
                                      vp, vp, vp, vp, sz, vp]
@@ -351,3 +355,28 @@ def topth_theta_eval(coef, ks, theta_out, *, log_domain: bool, stream=None):
     _check("topth_theta_eval", load_library().topth_theta_eval(
         coef.data_ptr(), ctypes.cast(karr, ctypes.c_void_p), n_k, Hq, m - 1, int(bool(log_domain)),
         theta_out.shape[2], theta_out.data_ptr(), _stream(stream)))
+
+
+def topth_decode_gqa(q, k_cache, v_cache, seq_lens, theta, out, ws, *, scale: float, flags: int,
+                     min_votes: int = 1, augment: bool = False, v_mean=None, kept_count=None, beta=None,
+                     vrows_read=None, kept_mask=None, stream=None):
+    """Decoding step with the GQA selection variants: load keys kept by at least
+    ``min_votes`` heads of the group; ``augment`` gives every head all of them."""
+    B, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    dt = _dtype_code(q)
+    _dev(q, "q"); _dev(k_cache, "k_cache", q.dtype, (B, Hkv, Lmax, d))
+    _dev(v_cache, "v_cache", q.dtype, (B, Hkv, Lmax, d))
+    _dev(seq_lens, "seq_lens", torch.int32, (B,))
+    _table(theta, "theta", Hq)
+    _dev(out, "out", q.dtype, (B, Hq, d))
+    vm = _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d), optional=True)
+    kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq), optional=True)
+    bt = _dev(beta, "beta", torch.float32, (B, Hq), optional=True)
+    vr = _dev(vrows_read, "vrows_read", torch.int32, (B, Hkv), optional=True)
+    km = _dev(kept_mask, "kept_mask", torch.uint8, (B, Hq, Lmax), optional=True)
+    _dev(ws, "ws", torch.uint8)
+    _check("topth_decode_gqa", load_library().topth_decode_gqa(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv,
+        Lmax, d, dt, float(scale), theta.data_ptr(), theta.shape[1], vm, int(flags), int(min_votes),
+        int(bool(augment)), out.data_ptr(), kc, bt, vr, km, ws.data_ptr(), ws.numel(), _stream(stream)))

@@ -252,7 +252,7 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
                   const float* theta, int n_rows, const float* v_mean, unsigned flags,
                   void* out, int* kept_count, float* beta, int* vrows_read,
                   unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream,
-                  bool pre, const float* e_tilde, float gamma) {
+                  bool pre, const float* e_tilde, float gamma, int min_votes = 1, int augment = 0) {
     if (!q || !k_cache || !v_cache || !seq_lens || !theta || !out) return TOPTH_EINVAL;
     if (bad_dims(B, Hq, Hkv, Lmax, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
     if (!isfinite(scale) || !(scale > 0.0f)) return TOPTH_EINVAL;
@@ -269,6 +269,7 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
     p.out = out; p.kept_count = kept_count; p.beta = beta; p.vrows_read = vrows_read;
     p.kept_mask = kept_mask; p.ws = ws; p.ws_bytes = ws_bytes;
     if (pre) { p.flags |= kFlagPre; p.e_tilde = e_tilde; p.gamma = gamma; }
+    p.min_votes = min_votes; p.augment = augment ? 1 : 0;
     if (dtype == TOPTH_BF16) {
         if (!decode_bf16_supported(d, Hq / Hkv) || (long long)Lmax * d * 2 >= INT_MAX) return TOPTH_EUNSUPPORTED;
         return map_hip(launch_decode_bf16(p, (hipStream_t)stream));
@@ -340,6 +341,19 @@ int topth_theta_eval(const double* coef, const int* ks, int n_k, int Hq, int deg
     if ((long long)n_k * Hq > 65535) return TOPTH_EUNSUPPORTED;     // one grid row per (t, h)
     return map_hip(launch_theta_eval(coef, ks, n_k, Hq, degree, log_domain != 0, n_out, theta_out,
                                      (hipStream_t)stream));
+}
+
+int topth_decode_gqa(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                     int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                     const float* theta, int n_rows, const float* v_mean, unsigned flags,
+                     int min_votes, int augment, void* out, int* kept_count, float* beta,
+                     int* vrows_read, unsigned char* kept_mask, void* ws, size_t ws_bytes,
+                     void* stream) {
+    if (Hkv <= 0 || Hq <= 0 || (Hq % Hkv) != 0) return TOPTH_EINVAL;
+    if (min_votes < 1 || min_votes > Hq / Hkv || (augment != 0 && augment != 1)) return TOPTH_EINVAL;
+    return decode_common(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Lmax, d, dtype, scale, theta,
+                         n_rows, v_mean, flags, out, kept_count, beta, vrows_read, kept_mask, ws,
+                         ws_bytes, stream, false, nullptr, 0.f, min_votes, augment);
 }
 
 }  // extern "C"

@@ -50,6 +50,8 @@ struct DecodeKArgs {
     int xcd_map;       // 1: chunks of a group on one XCD (grid and items multiples of 8 * chunks)
     const float* e_tilde;   // pre-softmax offline estimate of E~ [Hq][n_rows], or NULL
     float gamma;            // pre-softmax exp-threshold estimate
+    int min_votes;          // GQA: load a key when at least this many heads keep it (<= 1: any)
+    int augment;            // GQA: every head uses all loaded keys, not only its own
 };
 
 // One workgroup of kDecodeWaves waves per CU: two workgroups on a CU stream at
@@ -165,6 +167,45 @@ __device__ __forceinline__ T gather_chunks(T* base, size_t stride, int n, T firs
     return x;
 }
 
+// Bit-sliced vote counts: plane i holds bit i of one count per tile bit.
+// votes_add adds a 0/1 mask; votes_merge adds the counts of the lane `o` lanes
+// away; votes_at_least gives the tiles whose count is >= m (m uniform).
+__device__ __forceinline__ void votes_add(unsigned (&pl)[5], unsigned m) {
+    unsigned carry = m;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const unsigned c = pl[i] & carry;
+        pl[i] ^= carry;
+        carry = c;
+    }
+}
+__device__ __forceinline__ void votes_merge(unsigned (&pl)[5], int o) {
+    unsigned q[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) q[i] = __shfl_xor(pl[i], o);
+    unsigned carry = 0u;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const unsigned s = pl[i] ^ q[i] ^ carry;
+        carry = (pl[i] & q[i]) | (carry & (pl[i] ^ q[i]));
+        pl[i] = s;
+    }
+}
+__device__ __forceinline__ unsigned votes_at_least(const unsigned (&pl)[5], int m) {
+    if (m > 31) return 0u;                        // more than any group's heads
+    unsigned gt = 0u, eq = ~0u;
+#pragma unroll
+    for (int i = 4; i >= 0; --i) {
+        if ((m >> i) & 1) {
+            eq &= pl[i];
+        } else {
+            gt |= eq & pl[i];
+            eq &= ~pl[i];
+        }
+    }
+    return gt | eq;
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0,15:14], expcnt[6:4], lgkmcnt[11:8])
 // v_exp_f32 as is: results below the normal range flush to zero, which only
 // affects probabilities under 2^-126.
@@ -227,7 +268,10 @@ __device__ __forceinline__ void unpack_bf16(const unsigned& u, float* f) {
     f[0] = __uint_as_float(u << 16); f[1] = __uint_as_float(u & 0xffff0000u);
 }
 
-template <int D, int G, int NT>
+// VOTE: the GQA selection variants (a key is loaded when at least min_votes
+// heads keep it; augment gives every head all loaded keys); the plain
+// per-head selection is compiled without them.
+template <int D, int G, int NT, bool VOTE>
 __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(DecodeKArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     using C = DecodeCfg<D, G, NT>;
@@ -467,17 +511,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
         const int keylane = lane - 16 * cc;      // lane that stands for this lane's key
         unsigned char* kmask = a.kept_mask ? a.kept_mask + ((size_t)b * a.Hq + (size_t)kv * G) * a.Lmax : nullptr;
         // the per-head kept mask, only where it is asked for
-        if (kmask) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int key = wbase + t * C::KT + mykey;
-                if (key < n) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (hb + r < G) kmask[(size_t)(hb + r) * a.Lmax + key] = sc[t][r] >= Tr[r] ? 1 : 0;
-                }
-            }
-        }
         // Tiles past the n valid keys hold -inf scores, which never reach a
         // threshold (thresholds are clamped to -FLT_MAX).  Bit t of kbits: some
         // head of the group keeps this lane's key of tile t (the lanes of one
@@ -488,14 +521,59 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
         // difference of two floats has the sign of the exact one, and -inf - T
         // is -inf); the maximum over the lane's heads decides with one compare.
         unsigned kbits = 0u;
+        if constexpr (!VOTE) {
+            if (kmask) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const float dmax = fmaxf(fmaxf(sc[t][0] - Tr[0], sc[t][1] - Tr[1]),
-                                     fmaxf(sc[t][2] - Tr[2], sc[t][3] - Tr[3]));
-            kbits |= (dmax >= 0.f) ? (1u << t) : 0u;
+                for (int t = 0; t < NT; ++t) {
+                    const int key = wbase + t * C::KT + mykey;
+                    if (key < n) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (hb + r < G) kmask[(size_t)(hb + r) * a.Lmax + key] = sc[t][r] >= Tr[r] ? 1 : 0;
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float dmax = fmaxf(fmaxf(sc[t][0] - Tr[0], sc[t][1] - Tr[1]),
+                                         fmaxf(sc[t][2] - Tr[2], sc[t][3] - Tr[3]));
+                kbits |= (dmax >= 0.f) ? (1u << t) : 0u;
+            }
+            if (C::BPT >= 2) kbits |= __shfl_xor(kbits, 16);
+            if (C::BPT == 4) kbits |= __shfl_xor(kbits, 32);
+        } else {
+            // GQA selection variants (Sec. 4.6): count, per key, the heads of
+            // the group that keep it -- bit-sliced over the tiles (plane i holds
+            // bit i of every tile's count), summed over the lanes that share the
+            // key -- and load the key when the count reaches min_votes
+            unsigned pl[5] = {0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                unsigned hm = 0u;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) hm |= (sc[t][r] - Tr[r] >= 0.f) ? (1u << t) : 0u;
+                votes_add(pl, hm);
+            }
+            if (C::BPT >= 2) votes_merge(pl, 16);
+            if (C::BPT == 4) votes_merge(pl, 32);
+            kbits = votes_at_least(pl, a.min_votes < 1 ? 1 : a.min_votes);
+            if (kmask) {
+                // per head: loaded, and kept by the head itself unless every
+                // head uses all loaded keys
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int key = wbase + t * C::KT + mykey;
+                    if (key < n) {
+                        const bool ld = (kbits >> t) & 1u;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (hb + r < G)
+                                kmask[(size_t)(hb + r) * a.Lmax + key] =
+                                    (ld && (a.augment || sc[t][r] >= Tr[r])) ? 1 : 0;
+                    }
+                }
+            }
         }
-        if (C::BPT >= 2) kbits |= __shfl_xor(kbits, 16);
-        if (C::BPT == 4) kbits |= __shfl_xor(kbits, 32);
         const int kc = cc == 0 ? __popc(kbits) : 0;
         int lbase = 0, ltotal = 0;
 #pragma unroll
@@ -545,7 +623,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                 for (int h = 0; h < C::GW; ++h) x[h] = e < nl ? src[h] : consume(src + h);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    const bool kp = x[h] >= s_T[h];
+                    const bool kp = (VOTE && a.augment) || x[h] >= s_T[h];
                     x[h] = kp ? fast_exp2(x[h] - s_lse[h]) : 0.f;
                     kmass_h[h] += x[h];
                     kcnt_h[h] += kp ? 1 : 0;
@@ -827,49 +905,52 @@ struct Variant {
 // SIMD without spilling.
 constexpr int kMaxVariants = 4;
 
-template <int D, int G, int NT>
+template <int D, int G, int NT, bool VOTE>
 int launch_variant(int grid, hipStream_t stream, const DecodeKArgs& a) {
-    hipLaunchKernelGGL((decode_bf16_kernel<D, G, NT>), dim3(grid), dim3(kDecodeWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_bf16_kernel<D, G, NT, VOTE>), dim3(grid), dim3(kDecodeWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int D, int G, int NT>
+template <int D, int G, int NT, bool VOTE>
 int resident_variant(int* per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, (const void*)decode_bf16_kernel<D, G, NT>,
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, (const void*)decode_bf16_kernel<D, G, NT, VOTE>,
                                                         kDecodeWaves * 64, 0);
 }
 
-template <int D, int G, int NT>
+template <int D, int G, int NT, bool VOTE>
 Variant make_variant() {
-    return {launch_variant<D, G, NT>, resident_variant<D, G, NT>, DecodeCfg<D, G, NT>::KEYS_PER_WG};
+    return {launch_variant<D, G, NT, VOTE>, resident_variant<D, G, NT, VOTE>, DecodeCfg<D, G, NT>::KEYS_PER_WG};
 }
 
-template <int D, int G>
+// The vote variants leave out 32 tiles per wave: the vote count's registers
+// next to 32 score tiles would spill.
+template <int D, int G, bool VOTE>
 int variants_for(Variant* out) {
     int k = 0;
-    out[k++] = make_variant<D, G, 4>();
-    out[k++] = make_variant<D, G, 8>();
-    if constexpr (G != 16) out[k++] = make_variant<D, G, 16>();
-    if constexpr (G == 8) out[k++] = make_variant<D, G, 32>();   // one head: its K list would not fit in LDS
+    out[k++] = make_variant<D, G, 4, VOTE>();
+    out[k++] = make_variant<D, G, 8, VOTE>();
+    if constexpr (G != 16) out[k++] = make_variant<D, G, 16, VOTE>();
+    if constexpr (G == 8 && !VOTE) out[k++] = make_variant<D, G, 32, VOTE>();   // one head: its K list would not fit in LDS
     return k;
 }
 
+template <bool VOTE>
 int variants(int d, int G, Variant* out) {
     if (d == 64) {
         switch (G) {
-            case 1: return variants_for<64, 1>(out);
-            case 2: return variants_for<64, 2>(out);
-            case 4: return variants_for<64, 4>(out);
-            case 8: return variants_for<64, 8>(out);
-            default: return variants_for<64, 16>(out);
+            case 1: return variants_for<64, 1, VOTE>(out);
+            case 2: return variants_for<64, 2, VOTE>(out);
+            case 4: return variants_for<64, 4, VOTE>(out);
+            case 8: return variants_for<64, 8, VOTE>(out);
+            default: return variants_for<64, 16, VOTE>(out);
         }
     }
     switch (G) {
-        case 1: return variants_for<128, 1>(out);
-        case 2: return variants_for<128, 2>(out);
-        case 4: return variants_for<128, 4>(out);
-        case 8: return variants_for<128, 8>(out);
-        default: return variants_for<128, 16>(out);
+        case 1: return variants_for<128, 1, VOTE>(out);
+        case 2: return variants_for<128, 2, VOTE>(out);
+        case 4: return variants_for<128, 4, VOTE>(out);
+        case 8: return variants_for<128, 8, VOTE>(out);
+        default: return variants_for<128, 16, VOTE>(out);
     }
 }
 
@@ -884,12 +965,12 @@ int keys_per_wg_min(int G) {
 // both store the same value.
 struct DeviceInfo {
     std::atomic<int> cus{0};
-    std::atomic<int> occ[2][17][kMaxVariants] = {};   // [d==128][G][variant] -> workgroups per CU (0 = unknown)
+    std::atomic<int> occ[2][2][17][kMaxVariants] = {};   // [vote][d==128][G][variant] -> workgroups per CU (0 = unknown)
 };
 DeviceInfo g_dev[16];
 
-int resident_per_cu(int dev, int d, int G, int vi, const Variant& v, int* out) {
-    std::atomic<int>& slot = g_dev[dev].occ[d == 128][G][vi];
+int resident_per_cu(int dev, bool vote, int d, int G, int vi, const Variant& v, int* out) {
+    std::atomic<int>& slot = g_dev[dev].occ[vote][d == 128][G][vi];
     int val = slot.load(std::memory_order_relaxed);
     if (val == 0) {
         int per_cu = 0;
@@ -946,12 +1027,13 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     // resident at once (grid <= resident capacity), so the chunks of a group
     // that wait for each other in the exchange always run concurrently.
     Variant vs[kMaxVariants];
-    const int nv = variants(p.d, G, vs);
+    const bool vote = p.min_votes > 1 || p.augment;
+    const int nv = vote ? variants<true>(p.d, G, vs) : variants<false>(p.d, G, vs);
     Variant v{};
     int chunks = 0, capacity = 0;
     for (int vi = 0; vi < nv; ++vi) {
         int per_cu = 0;
-        e = (hipError_t)resident_per_cu(dev, p.d, G, vi, vs[vi], &per_cu);
+        e = (hipError_t)resident_per_cu(dev, vote, p.d, G, vi, vs[vi], &per_cu);
         if (e != hipSuccess) return e;
         v = vs[vi];
         capacity = per_cu * cus;
@@ -968,6 +1050,7 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     a.q = (const uint16_t*)p.q; a.k = (const uint16_t*)p.k; a.v = (const uint16_t*)p.v;
     a.seq_lens = p.seq_lens; a.theta = p.theta; a.v_mean = p.v_mean;
     a.e_tilde = p.e_tilde; a.gamma = p.gamma;
+    a.min_votes = p.min_votes; a.augment = p.augment;
     a.out = (uint16_t*)p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.vrows_read = p.vrows_read;
     a.kept_mask = p.kept_mask;
     a.status = (int*)ws;

@@ -33,6 +33,11 @@ struct RowArgs {
     const float* e_tilde; float gamma;    // pre-softmax SDC estimates
     uint32_t* masks; int mask_words;      // decode: kept-key bitmasks [B][Hq][mask_words]
     unsigned char* kept_mask;             // optional byte mask, [rows][Lk]
+    // decode GQA selection variants (Sec. 4.6), two passes: 1 writes each
+    // head's kept-key bits to masks; 2 reads the group's bits, loads a key
+    // when at least min_votes heads keep it and keeps, per head, its own
+    // loaded keys or (augment) all of them
+    int gqa_pass, min_votes, augment;
 };
 
 constexpr int kRowThreads = 256;
@@ -186,11 +191,26 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
         for (int w = threadIdx.x; w < (n + 31) / 32; w += kRowThreads) keepbits[w] = 0u;
         __syncthreads();
     }
+    if (MODE == kRowDecode && a.gqa_pass == 1) {
+        for (int j = threadIdx.x; j < n; j += kRowThreads)
+            if (xs[j] >= T2) atomicOr(&keepbits[j >> 5], 1u << (j & 31));
+        __syncthreads();
+        uint32_t* mrow = a.masks + (size_t)(b * a.Hq + h) * a.mask_words;
+        for (int w = threadIdx.x; w < a.mask_words; w += kRowThreads)
+            mrow[w] = (w < (n + 31) / 32) ? keepbits[w] : 0u;
+        return;
+    }
     int cnt = 0;
     float mass = 0.f;
     for (int j = threadIdx.x; j < n; j += kRowThreads) {
         const float x = xs[j];
-        const bool keep = x >= T2;
+        bool keep = x >= T2;
+        if (MODE == kRowDecode && a.gqa_pass == 2) {
+            int votes = 0;
+            for (int hh = 0; hh < g; ++hh)
+                votes += (a.masks[(size_t)(b * a.Hq + kv * g + hh) * a.mask_words + (j >> 5)] >> (j & 31)) & 1u;
+            keep = votes >= a.min_votes && (a.augment || keep);
+        }
         const float w = keep ? exp2f(x - lse2) : 0.f;   // exact SDC: weight = s
         xs[j] = w;
         cnt += keep;
@@ -237,7 +257,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(RowArgs a) {
         if (a.kept_count) a.kept_count[o] = cnt;
         if (a.beta) a.beta[o] = beta;
     }
-    if (MODE == kRowDecode && a.masks) {
+    if (MODE == kRowDecode && a.masks && a.gqa_pass == 0) {
         uint32_t* mrow = a.masks + (size_t)(b * a.Hq + h) * a.mask_words;
         for (int w = threadIdx.x; w < a.mask_words; w += kRowThreads)
             mrow[w] = (w < (n + 31) / 32) ? keepbits[w] : 0u;
@@ -267,6 +287,33 @@ __global__ void union_count_kernel(uint32_t* masks, int Hq, int Hkv, int mask_wo
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
     __syncthreads();
     if (threadIdx.x == 0) vrows_read[bk] = red[0] + red[1] + red[2] + red[3];
+}
+
+// number of V rows the GQA group loads under the vote rule (keys kept by at
+// least min_votes of its heads); the mask words are set back to the
+// empty-slot pattern once read.
+__global__ void votes_count_kernel(uint32_t* masks, int Hq, int Hkv, int mask_words, int min_votes,
+                                   int* vrows_read) {
+    __shared__ int red[4];
+    const int bk = blockIdx.x;
+    const int b = bk / Hkv, kv = bk % Hkv;
+    const int g = Hq / Hkv;
+    int c = 0;
+    for (int w = threadIdx.x; w < mask_words; w += blockDim.x) {
+        for (int bit = 0; bit < 32; ++bit) {
+            int v = 0;
+            for (int hh = 0; hh < g; ++hh)
+                v += (masks[((size_t)b * Hq + kv * g + hh) * mask_words + w] >> bit) & 1u;
+            c += v >= min_votes ? 1 : 0;
+        }
+    }
+    __syncthreads();                      // every word of the group is read before any is reset
+    for (int w = threadIdx.x; w < mask_words; w += blockDim.x)
+        for (int hh = 0; hh < g; ++hh) masks[((size_t)b * Hq + kv * g + hh) * mask_words + w] = kWsSlotEmpty;
+    c = wave_sum_i(c);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0 && vrows_read) vrows_read[bk] = red[0] + red[1] + red[2] + red[3];
 }
 
 // mean of the first n = seq_lens[b] V rows, Eq. 5 over the cached rows.  One
@@ -456,6 +503,21 @@ int launch_decode_rowwise(const DecodeParams& p, uint32_t* masks_ws, hipStream_t
     a.e_tilde = p.e_tilde; a.gamma = p.gamma;
     a.out = p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.kept_mask = p.kept_mask;
     a.mask_words = (p.Lmax + 31) / 32;
+    if (p.min_votes > 1 || p.augment) {
+        // GQA selection variants: every head's kept bits first, then the outputs
+        a.masks = masks_ws;
+        a.min_votes = p.min_votes < 1 ? 1 : p.min_votes;
+        a.augment = p.augment;
+        a.gqa_pass = 1;
+        int e = dispatch_rows<kRowDecode>(a, p.d, p.dtype, p.B * p.Hq, p.Lmax, s);
+        if (e != hipSuccess) return e;
+        a.gqa_pass = 2;
+        e = dispatch_rows<kRowDecode>(a, p.d, p.dtype, p.B * p.Hq, p.Lmax, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(votes_count_kernel, dim3(p.B * p.Hkv), dim3(256), 0, s,
+                           masks_ws, p.Hq, p.Hkv, a.mask_words, a.min_votes, p.vrows_read);
+        return hipGetLastError();
+    }
     a.masks = p.vrows_read ? masks_ws : nullptr;
     int e = dispatch_rows<kRowDecode>(a, p.d, p.dtype, p.B * p.Hq, p.Lmax, s);
     if (e != hipSuccess) return e;

@@ -119,6 +119,7 @@ struct DecodeParams {
     void* out; int* kept_count; float* beta; int* vrows_read; unsigned char* kept_mask;
     void* ws; size_t ws_bytes;
     const float* e_tilde; float gamma;    // pre-softmax calls only
+    int min_votes; int augment;           // GQA selection variants (0, 0: plain per-head selection)
 };
 struct PrefillParams {
     const void* q; const void* k; const void* v;

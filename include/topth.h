@@ -304,6 +304,25 @@ int topth_theta_fit(const float* theta, const int* count, int n_k, int Hq, int n
 int topth_theta_eval(const double* coef, const int* ks, int n_k, int Hq, int degree, int log_domain,
                      int n_out, float* theta_out, void* stream);
 
+/*
+ * One decoding step with the GQA selection variants of Sec. 4.6 (post-softmax
+ * thresholds, as topth_decode): a key is loaded for a (batch, KV head) group
+ * when at least min_votes (1 .. Hq/Hkv) of the group's heads keep it
+ * (s >= theta), which discards V rows requested by only a few heads; with
+ * augment = 0 each head then uses its own kept keys among the loaded ones,
+ * with augment = 1 every head uses all loaded keys ("augmenting each head's
+ * selections with the group's union"), weighted by its own post-softmax
+ * values.  min_votes = 1, augment = 0 is topth_decode.  kept_count counts the
+ * keys a head uses; vrows_read the loaded keys; kept_mask marks, per head, the
+ * keys it uses.  Other arguments and the workspace contract as topth_decode.
+ */
+int topth_decode_gqa(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                     int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                     const float* theta, int n_rows, const float* v_mean, unsigned flags,
+                     int min_votes, int augment, void* out, int* kept_count, float* beta,
+                     int* vrows_read, unsigned char* kept_mask, void* ws, size_t ws_bytes,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

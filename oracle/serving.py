@@ -80,3 +80,39 @@ def eval_theta(coef, k: int, n_out: int, log_domain: bool) -> np.ndarray:
         rows = np.arange(n_out) + 1 > k
         out[h, rows] = v[rows]
     return out
+
+
+def decode_gqa(q, K_cache, V_cache, seq_lens, theta, v_mean, scale: float, *, vmc: bool,
+               min_votes: int = 1, augment: bool = False, renorm: bool = False):
+    """One decoding step with the GQA selection variants of [TT] §4.6: a key is
+    loaded for a (b, KV head) group when at least ``min_votes`` of its g heads
+    keep it (s >= theta); each head then uses its own kept keys among those
+    (``augment`` False: "discarding V-rows requested by only a few heads") or
+    all of them ("augmenting each head's selections with the group's union"),
+    weighted by its own post-softmax values (exact SDC) and VMC as in Eq. 5-7.
+    min_votes = 1 without augment is the plain per-head selection."""
+    from .topth import DecodeResult, post_softmax, row_output, scores, theta_row
+    q = _as64(q); K_cache = _as64(K_cache); V_cache = _as64(V_cache)
+    B, Hq, d = q.shape
+    Hkv = K_cache.shape[1]
+    g = Hq // Hkv
+    out = np.zeros((B, Hq, d)); kept = np.zeros((B, Hq), dtype=np.int64)
+    beta = np.zeros((B, Hq)); vrows = np.zeros((B, Hkv), dtype=np.int64)
+    s_rows = [[None] * Hq for _ in range(B)]
+    k_rows = [[None] * Hq for _ in range(B)]
+    for b in range(B):
+        n = int(seq_lens[b])
+        for kv in range(Hkv):
+            heads = range(kv * g, (kv + 1) * g)
+            s = {h: post_softmax(scores(q[b, h], K_cache[b, kv, :n], scale))[0] for h in heads}
+            own = {h: s[h] >= theta_row(theta, h, n - 1) for h in heads}
+            votes = np.sum([own[h] for h in heads], axis=0)
+            loaded = votes >= min_votes
+            vrows[b, kv] = int(loaded.sum())
+            for h in heads:
+                keep = loaded if augment else (loaded & own[h])
+                mu = _as64(v_mean[b, kv]) if vmc else np.zeros(d)
+                o, bt = row_output(s[h], keep, V_cache[b, kv, :n], mu, vmc=vmc, renorm=renorm)
+                out[b, h] = o; kept[b, h] = int(keep.sum()); beta[b, h] = bt
+                s_rows[b][h] = s[h]; k_rows[b][h] = keep
+    return DecodeResult(out, kept, beta, vrows, s_rows, k_rows)

@@ -217,3 +217,13 @@ def test_serving_helper_errors(lib):
     assert lib.topth_theta_eval(FAKE, kp, 1, 8, 2, 1, 0, FAKE, None) == -1                 # n_out
     assert lib.topth_theta_eval(FAKE, None, 1, 8, 2, 1, 100, FAKE, None) == -1
     assert lib.topth_theta_eval(FAKE, kp, 9, 8, 2, 1, 100, FAKE, None) == -1               # n_k
+
+
+def test_decode_gqa_errors(lib):
+    def call(mv, aug, Hq=8, Hkv=2):
+        return lib.topth_decode_gqa(FAKE, FAKE, FAKE, FAKE, 2, Hq, Hkv, 64, 128, 1, 0.1, FAKE, 64, FAKE, 1,
+                                    mv, aug, FAKE, None, None, None, None, FAKE, 1 << 30, None)
+    assert call(0, 0) == -1          # min_votes below 1
+    assert call(5, 0) == -1          # more votes than heads in the group (g = 4)
+    assert call(2, 2) == -1          # augment is 0 or 1
+    assert call(2, 0, Hq=6, Hkv=4) == -1

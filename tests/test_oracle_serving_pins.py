@@ -88,3 +88,64 @@ def test_fit_needs_enough_rows_and_skips_unusable_ones():
     assert np.isnan(serving.fit_theta(th, obs, 2, True)[1]).all()
     assert np.isfinite(serving.fit_theta(th, obs, 2, False)[1]).all()
     assert np.isfinite(serving.fit_theta(th, obs, 2, True)[2]).all()
+
+
+# ----------------------------------------------------- GQA selection variants
+def _gqa_case(seed, B=2, Hq=8, Hkv=2, n=40, d=6):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, d))
+    K = rng.standard_normal((B, Hkv, n, d)) * 1.5
+    V = rng.standard_normal((B, Hkv, n, d))
+    theta = np.full((Hq, n), 0.03)
+    vm = V.mean(axis=2)
+    return q, K, V, [n, n - 13], theta, vm
+
+
+def test_gqa_default_is_plain_decode():
+    import oracle
+    q, K, V, lens, th, vm = _gqa_case(1)
+    a = serving.decode_gqa(q, K, V, lens, th, vm, 0.5, vmc=True)
+    b = oracle.decode(q, K, V, lens, th, vm, 0.5, vmc=True)
+    np.testing.assert_allclose(a.out, b.out, rtol=1e-13, atol=1e-15)
+    assert (a.kept_count == b.kept_count).all() and (a.vrows_read == b.vrows_read).all()
+
+
+def test_gqa_loaded_sets_by_subset_enumeration():
+    """The loaded set for min_votes = m is the union, over every m-subset of the
+    group's heads, of the keys all heads of the subset keep (itertools);
+    m = 1 is the union, m = g the intersection (Python sets)."""
+    import itertools
+    import oracle
+    q, K, V, lens, th, vm = _gqa_case(2)
+    g = 4
+    base = oracle.decode(q, K, V, lens, th, vm, 0.5, vmc=False)
+    for m in range(1, g + 2):
+        r = serving.decode_gqa(q, K, V, lens, th, vm, 0.5, vmc=False, min_votes=m, augment=True)
+        for b in range(2):
+            for kv in range(2):
+                sets = [set(np.flatnonzero(base.keep[b][h]).tolist()) for h in range(kv * g, (kv + 1) * g)]
+                want = set()
+                for sub in itertools.combinations(range(g), m):
+                    want |= set.intersection(*[sets[i] for i in sub])
+                assert r.vrows_read[b, kv] == len(want)
+                for h in range(kv * g, (kv + 1) * g):
+                    assert set(np.flatnonzero(r.keep[b][h]).tolist()) == want
+                if m == 1:
+                    assert want == set.union(*sets)
+                if m == g:
+                    assert want == set.intersection(*sets)
+
+
+def test_gqa_discard_keeps_own_keys_inside_the_loaded_set():
+    import oracle
+    q, K, V, lens, th, vm = _gqa_case(3)
+    base = oracle.decode(q, K, V, lens, th, vm, 0.5, vmc=True)
+    r = serving.decode_gqa(q, K, V, lens, th, vm, 0.5, vmc=True, min_votes=2)
+    for b in range(2):
+        for h in range(8):
+            assert not (r.keep[b][h] & ~base.keep[b][h]).any()
+            s = base.s[b][h]
+            w = np.where(r.keep[b][h], s, 0.0)
+            mu = vm[b, h // 4]
+            np.testing.assert_allclose(r.out[b, h], w @ V[b, h // 4, :lens[b]] + (1 - w.sum()) * mu,
+                                       rtol=1e-12, atol=1e-14)
