@@ -47,9 +47,16 @@ bool too_big(long long rows, long long cols) {
 
 int map_hip(int e) { return e == 0 ? TOPTH_OK : TOPTH_EHIP; }
 
+// prefix means of V (VMC), then a float16 copy of V and a flag word (bf16 P V
+// in float16); a workspace with only the first part still serves VMC
+size_t prefill_ws_vmc(int B, int Hkv, int L, int d) {
+    return (size_t)B * Hkv * L * d * sizeof(float) + 256;
+}
 size_t prefill_ws(int B, int Hq, int Hkv, int L, int d) {
     (void)Hq;
-    return (size_t)B * Hkv * L * d * sizeof(float) + 256;
+    const size_t mu = ((size_t)B * Hkv * L * d * sizeof(float) + 255) & ~(size_t)255;
+    const size_t v16 = ((size_t)B * Hkv * L * d * sizeof(uint16_t) + 255) & ~(size_t)255;
+    return mu + v16 + 256;
 }
 
 size_t calib_ws(int S, int Hq, int Lq, int n_k) {
@@ -211,7 +218,7 @@ int prefill_common(const void* q, const void* k, const void* v, int B, int Hq, i
     const bool vmc = (flags & TOPTH_VMC) && !(flags & TOPTH_SDC_NONE);
     if (vmc) {
         if (!ws) return TOPTH_EWORKSPACE;
-        if (ws_bytes < prefill_ws(B, Hq, Hkv, L, d)) return TOPTH_EWORKSPACE;
+        if (ws_bytes < prefill_ws_vmc(B, Hkv, L, d)) return TOPTH_EWORKSPACE;
     }
     PrefillParams p = {};
     p.q = q; p.k = k; p.v = v; p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.d = d; p.dtype = dtype;

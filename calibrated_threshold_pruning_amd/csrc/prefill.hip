@@ -25,6 +25,15 @@
 // output accumulators, the full sum and the kept sum R rescaled when it moves.
 // The epilogue divides by R + E~ for the chosen estimate of the discarded mass
 // (Sec. 3.2.1: exact, exp-threshold, offline-calibrated, or none).
+//
+// P V in float16: when the caller's workspace has room, a pre-pass copies V to
+// float16 (exact for bfloat16 values of magnitude up to 16, which it checks)
+// and the P V product takes one f16 MFMA per block with P rounded to float16
+// (relative error 2^-11, so at most 2^-11 * 16 < 1e-2 on any output) instead
+// of the two bf16 MFMAs of the high/low split.  A V element beyond 16 (or not
+// finite) sets a flag.  Both kernels (F16 and not) are launched; each reads
+// the flag first and only the one that matches it does the work (the other
+// grid exits at once), so neither carries the other's registers.
 #include "topth_internal.h"
 
 #include <math.h>
@@ -41,6 +50,8 @@ struct PrefillKArgs {
     float scale;                 // score scale (pre-softmax thresholds are in score units)
     const float* e_tilde;        // offline estimate of E~ [Hq][n_rows] or NULL
     float gamma;                 // exp-threshold estimate
+    const uint16_t* v16;         // float16 copy of V, or NULL (bf16 high/low split for P V)
+    const unsigned* vflag;       // nonzero: some V element is beyond the float16 bound
 };
 
 template <int D, int G>
@@ -73,6 +84,8 @@ __device__ __forceinline__ void pf_ds_mfma_pipeline() {
 }
 
 typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 pf_f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 pf_f16x8 __attribute__((ext_vector_type(8)));
 typedef short pf_i16x4 __attribute__((ext_vector_type(4)));
 typedef float pf_f32x2 __attribute__((ext_vector_type(2)));
 
@@ -81,6 +94,11 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
     const pf_f32x2 v = {lo, hi};
     return __builtin_bit_cast(unsigned, __builtin_convertvector(v, pf_bf16x2));
 }
+// two floats to packed float16, round to nearest even
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
+    const pf_f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, pf_f16x2));
+}
 // P = hi + lo with both parts in bfloat16: the P V product is taken as two bf16
 // MFMAs, which keeps about 16 significant bits of every weight
 __device__ __forceinline__ void split_bf16x2(float a, float b, unsigned& hi, unsigned& lo) {
@@ -88,7 +106,7 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, unsigned& hi, uns
     lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
-template <int D, int G, bool MASK, bool PRE>
+template <int D, int G, bool MASK, bool PRE, bool F16>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     using C = PrefillCfg<D, G>;
@@ -112,8 +130,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
     const int wg_row_end = min(a.L, (qt + 1) * C::BMT);     // rows of the workgroup end here
     const int ntiles = (wg_row_end + C::BN - 1) / C::BN;    // causal key tiles of the workgroup
 
+    // P V in float16 when a float16 copy of V exists and every V element fits
+    // (the flag is uniform: the grid that does not match it exits here)
+    constexpr bool f16pv = F16;
+    if (a.vflag != nullptr && ((*a.vflag == 0u) != F16)) return;
     const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kv) * (size_t)a.L * D;
-    const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kv) * (size_t)a.L * D;
+    const uint16_t* vg = (f16pv ? a.v16 : a.v) + ((size_t)b * a.Hkv + kv) * (size_t)a.L * D;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kg), 0, a.L * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
@@ -355,11 +377,38 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                     cnt[qb] += kp ? 1 : 0;
                     mass[qb] += p[r];
                 }
-                split_bf16x2(p[0], p[1], pk[qb][kb][0], pl[qb][kb][0]);
-                split_bf16x2(p[2], p[3], pk[qb][kb][1], pl[qb][kb][1]);
+                if constexpr (f16pv) {
+                    pk[qb][kb][0] = pack_f16x2(p[0], p[1]);
+                    pk[qb][kb][1] = pack_f16x2(p[2], p[3]);
+                } else {
+                    split_bf16x2(p[0], p[1], pk[qb][kb][0], pl[qb][kb][0]);
+                    split_bf16x2(p[2], p[3], pk[qb][kb][1], pl[qb][kb][1]);
+                }
             }
         }
         // O^T += V^T P^T over 32 keys per step; each V^T fragment serves both row blocks
+        if constexpr (f16pv) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                pf_f16x8 pb[2];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    const u32x4 pv = {pk[qb][2 * ks][0], pk[qb][2 * ks][1], pk[qb][2 * ks + 1][0], pk[qb][2 * ks + 1][1]};
+                    pb[qb] = __builtin_bit_cast(pf_f16x8, pv);
+                }
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) {
+                    const pf_f16x8 vtf = __builtin_bit_cast(pf_f16x8, vt_frag(j & 1, ks, db));
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vtf, pb[qb], o[qb][db], 0, 0, 0);
+                }
+            }
+            pf_ds_mfma_pipeline<1, 4, 0>();
+            pf_ds_mfma_pipeline<2 * C::DB - 1, 2, 2>();
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            continue;
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 pb[2], pbl[2];
@@ -444,6 +493,24 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 #endif
 }
 
+// float16 copy of a bfloat16 V (16-byte pieces); any element beyond 16 in
+// magnitude, or not finite, sets *flag (every writer stores the same value).
+__global__ void v_to_f16_kernel(const uint16_t* v, size_t n8, uint16_t* v16, unsigned* flag) {
+    bool bad = false;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (size_t)gridDim.x * blockDim.x) {
+        const u32x4 raw = *(const u32x4*)(v + 8 * i);
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float lo = __uint_as_float(raw[w] << 16), hi = __uint_as_float(raw[w] & 0xffff0000u);
+            bad |= !(fabsf(lo) <= 16.0f) || !(fabsf(hi) <= 16.0f);
+            o[w] = pack_f16x2(lo, hi);
+        }
+        *(u32x4*)(v16 + 8 * i) = o;
+    }
+    if (bad) *flag = 1u;
+}
+
 // ------------------------------------------------------------------ host side
 int launch_prefix_mean(const void* v, int groups, int L, int d, int dtype, float* mu, hipStream_t s);
 
@@ -455,13 +522,26 @@ template <int D, int G>
 static int launch_prefill_variant(const PrefillKArgs& a, hipStream_t s) {
     using C = PrefillCfg<D, G>;
     const dim3 grid((a.L + C::BMT - 1) / C::BMT, a.Hkv * (G / C::HPW), a.B);
-    // the variant that also writes the kept mask is only used when one is asked for
-    if (a.flags & kFlagPre) {
-        if (a.kept_mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, true>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, true>), grid, dim3(256), 0, s, a);
+    // the variant that also writes the kept mask is only used when one is asked
+    // for; with a float16 copy of V both P V forms are launched (one exits)
+    const bool pre = (a.flags & kFlagPre) != 0, mask = a.kept_mask != nullptr;
+    if (a.v16) {
+        if (pre) {
+            if (mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, true, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, true, true>), grid, dim3(256), 0, s, a);
+        } else {
+            if (mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, false, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, false, true>), grid, dim3(256), 0, s, a);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (pre) {
+        if (mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, true, false>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, true, false>), grid, dim3(256), 0, s, a);
     } else {
-        if (a.kept_mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, false>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, false>), grid, dim3(256), 0, s, a);
+        if (mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, false, false>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, false, false>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }
@@ -477,10 +557,30 @@ static int launch_prefill_d(const PrefillKArgs& a, int G, hipStream_t s) {
     }
 }
 
+size_t prefill_mu_bytes(int B, int Hkv, int L, int d) { return (size_t)B * Hkv * L * d * sizeof(float); }
+size_t prefill_v16_bytes(int B, int Hkv, int L, int d) { return (size_t)B * Hkv * L * d * sizeof(uint16_t); }
+
 int launch_prefill_bf16(const PrefillParams& p, float* mu_ws, hipStream_t s) {
     const bool vmc = (p.flags & 1u) && !(p.flags & 2u);
     if (vmc) {
         const int e = launch_prefix_mean(p.v, p.B * p.Hkv, p.L, p.d, p.dtype, mu_ws, s);
+        if (e != hipSuccess) return e;
+    }
+    // workspace: [prefix means][float16 V][flag]; the float16 P V path needs all of it
+    const size_t mu_b = (prefill_mu_bytes(p.B, p.Hkv, p.L, p.d) + 255) & ~(size_t)255;
+    const size_t v16_b = (prefill_v16_bytes(p.B, p.Hkv, p.L, p.d) + 255) & ~(size_t)255;
+    uint16_t* v16 = nullptr;
+    unsigned* vflag = nullptr;
+    if (p.ws && p.ws_bytes >= mu_b + v16_b + 256) {
+        v16 = (uint16_t*)((char*)p.ws + mu_b);
+        vflag = (unsigned*)((char*)p.ws + mu_b + v16_b);
+        int e = launch_fill_u32(vflag, 4, 0u, s);
+        if (e != hipSuccess) return e;
+        const size_t n8 = (size_t)p.B * p.Hkv * p.L * p.d / 8;
+        unsigned blocks = (unsigned)((n8 + 255) / 256);
+        if (blocks > 8192) blocks = 8192;
+        hipLaunchKernelGGL(v_to_f16_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)p.v, n8, v16, vflag);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     PrefillKArgs a = {};
@@ -493,6 +593,8 @@ int launch_prefill_bf16(const PrefillParams& p, float* mu_ws, hipStream_t s) {
     a.scale = p.scale;
     a.e_tilde = p.e_tilde;
     a.gamma = p.gamma;
+    a.v16 = v16;
+    a.vflag = vflag;
     const int G = p.Hq / p.Hkv;
     return p.d == 64 ? launch_prefill_d<64>(a, G, s) : launch_prefill_d<128>(a, G, s);
 }

@@ -52,7 +52,9 @@ def check_theta(gpu, ref):
     assert rel.max() <= 1e-5, rel.max()
 
 
-def run_prefill(q, k, v, theta, flags):
+def run_prefill(q, k, v, theta, flags, with_ws=True):
+    """with_ws: the full prefill workspace (bf16: P V in float16 when every V
+    element is within 16 in magnitude); False: none (bf16 high/low split)."""
     dev = device()
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
@@ -60,7 +62,7 @@ def run_prefill(q, k, v, theta, flags):
     kc = torch.full((B, Hq, L), -7, dtype=torch.int32, device=dev)
     bt = torch.full((B, Hq, L), -7.0, dtype=torch.float32, device=dev)
     km = torch.zeros((B, Hq, L, L), dtype=torch.uint8, device=dev)
-    ws = tt.workspace(tt.TOPTH_OP_PREFILL, B, Hq, Hkv, L, L, d)
+    ws = tt.workspace(tt.TOPTH_OP_PREFILL, B, Hq, Hkv, L, L, d) if with_ws else None
     tt.topth_prefill(q.to(dev), k.to(dev), v.to(dev),
                      torch.tensor(theta, dtype=torch.float32, device=dev).contiguous(), out,
                      scale=1.0 / np.sqrt(d), flags=flags, kept_count=kc, beta=bt, kept_mask=km,
@@ -349,3 +351,24 @@ def test_prefill_8k_full_size_sampled_rows():
             assert abs(gk[b, h, p] - ref.kept_count[b, h, p]) <= amb
         check_out(go[b, h, p], ref.out[b, h, p], torch.bfloat16, f"h{h} p{p}")
         assert abs(gb[b, h, p] - ref.beta[b, h, p]) <= 1e-4, (h, p)
+
+
+@pytest.mark.parametrize("case", ["f16", "large_v", "no_ws"])
+def test_prefill_bf16_pv_forms(case):
+    """The P V product runs in float16 when the workspace holds a float16 copy
+    of V and every V element is within 16 in magnitude; a larger element (here
+    one of 40 and one of -1000) or no workspace selects the bfloat16 high/low
+    split.  Every form meets the bf16 tolerance against the oracle."""
+    print(f"prefill bf16 P V form {case}", flush=True)
+    Hq, Hkv, L, d = 8, 2, 200, 128
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 0, 9, B=1, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    if case == "large_v":
+        v[0, 1, 0, 3] = 40.0
+        v[0, 0, 150, 7] = -1000.0
+    theta = oracle_calibrate(*batch_of_sequences(UNIT, ROLE_CALIB, 0, 20, 2, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)[:2],
+                             [16], L)[0][0]
+    for flags in (0, tt.TOPTH_VMC):
+        if case == "no_ws" and flags & tt.TOPTH_VMC:
+            continue                     # VMC needs the workspace
+        g = run_prefill(q, k, v, theta, flags, with_ws=case != "no_ws")
+        compare_prefill(g, q, k, v, theta, flags, torch.bfloat16)
