@@ -47,7 +47,8 @@ def test_workspace_size(lib):
     assert ws(tt.TOPTH_OP_DECODE, 16, 32, 8, 1, 4096, 128) > 65536
     assert ws(tt.TOPTH_OP_DECODE, 16, 32, 8, 1, 4096, 96) == 0          # d not supported
     assert ws(tt.TOPTH_OP_DECODE, 16, 30, 8, 1, 4096, 128) == 0         # Hq % Hkv != 0
-    assert ws(tt.TOPTH_OP_PREFILL, 1, 32, 8, 8192, 8192, 128) >= 8 * 8192 * 128 * 4
+    # prefix means (fp32) and the float16 copy of V
+    assert ws(tt.TOPTH_OP_PREFILL, 1, 32, 8, 8192, 8192, 128) >= 8 * 8192 * 128 * (4 + 2)
     assert ws(tt.TOPTH_OP_CALIBRATE, 4, 8, 8, 2048, 2048, 128, 3) >= 4 * 3 * 8 * 2048 * 4
     assert ws(tt.TOPTH_OP_CALIBRATE, 4, 8, 8, 2048, 2048, 128, 9) == 0  # too many k
     assert ws(7, 1, 1, 1, 1, 1, 64) == 0
