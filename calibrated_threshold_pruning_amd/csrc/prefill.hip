@@ -106,7 +106,9 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, unsigned& hi, uns
     lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
-template <int D, int G, bool MASK, bool PRE, bool F16>
+// MASS: the kept mass of each row is summed (VMC, SDC_NONE, the beta output
+// and every pre-softmax estimate need it); without it sweep B skips that sum.
+template <int D, int G, bool MASK, bool PRE, bool F16, bool MASS>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     using C = PrefillCfg<D, G>;
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                         p[r] = kp ? pf_exp2(fmaf(st[qb][kb][r], a.xscale, nlse)) : 0.f;
                     }
                     cnt[qb] += kp ? 1 : 0;
-                    mass[qb] += p[r];
+                    if constexpr (MASS) mass[qb] += p[r];
                 }
                 if constexpr (f16pv) {
                     pk[qb][kb][0] = pack_f16x2(p[0], p[1]);
@@ -518,31 +520,33 @@ bool prefill_bf16_supported(int d, int G) {
     return (d == 64 || d == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
+template <int D, int G, bool PRE, bool F16, bool MASS>
+static void launch_form(const PrefillKArgs& a, dim3 grid, hipStream_t s) {
+    if (a.kept_mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, PRE, F16, MASS>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, PRE, F16, MASS>), grid, dim3(256), 0, s, a);
+}
+
+template <int D, int G, bool F16>
+static void launch_pv_form(const PrefillKArgs& a, dim3 grid, hipStream_t s, bool pre, bool mass) {
+    if (pre) launch_form<D, G, true, F16, true>(a, grid, s);
+    else if (mass) launch_form<D, G, false, F16, true>(a, grid, s);
+    else launch_form<D, G, false, F16, false>(a, grid, s);
+}
+
 template <int D, int G>
 static int launch_prefill_variant(const PrefillKArgs& a, hipStream_t s) {
     using C = PrefillCfg<D, G>;
     const dim3 grid((a.L + C::BMT - 1) / C::BMT, a.Hkv * (G / C::HPW), a.B);
     // the variant that also writes the kept mask is only used when one is asked
     // for; with a float16 copy of V both P V forms are launched (one exits)
-    const bool pre = (a.flags & kFlagPre) != 0, mask = a.kept_mask != nullptr;
+    const bool pre = (a.flags & kFlagPre) != 0;
+    const bool mass = pre || (a.flags & (kFlagVmc | kFlagNone)) != 0 || a.beta != nullptr;
     if (a.v16) {
-        if (pre) {
-            if (mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, true, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, true, true>), grid, dim3(256), 0, s, a);
-        } else {
-            if (mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, false, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, false, true>), grid, dim3(256), 0, s, a);
-        }
+        launch_pv_form<D, G, true>(a, grid, s, pre, mass);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (pre) {
-        if (mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, true, false>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, true, false>), grid, dim3(256), 0, s, a);
-    } else {
-        if (mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, false, false>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, false, false>), grid, dim3(256), 0, s, a);
-    }
+    launch_pv_form<D, G, false>(a, grid, s, pre, mass);
     return hipGetLastError();
 }
 
