@@ -154,8 +154,13 @@ int topth_calibrate_finalize(const double* sum, const double* sumsq, const int* 
  *   [Hq][n_rows]; out device [B][Hq][L][d] of the input dtype;
  *   kept_count device int [B][Hq][L] or NULL; beta device float [B][Hq][L]
  *   or NULL; kept_mask device uint8 [B][Hq][L][L] or NULL: 1 where key j <= p
- *   is kept by row p (entries j > p are not written); ws device,
- *   topth_workspace_size(TOPTH_OP_PREFILL, ...).
+ *   is kept by row p (entries j > p are not written); ws device, or NULL
+ *   without TOPTH_VMC.  With topth_workspace_size(TOPTH_OP_PREFILL, ...)
+ *   bytes the bfloat16 path copies V to float16 there and, when every V
+ *   element is within 16 in magnitude, forms P V in float16 (P rounded to
+ *   float16: at most 2^-11 * 16 absolute error per output); otherwise, or
+ *   with a smaller workspace (VMC needs the first B*Hkv*L*d floats of it for
+ *   the prefix means), P V uses a bfloat16 high/low split of P.
  */
 int topth_prefill(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int L,
                   int d, int dtype, float scale, const float* theta, int n_rows,
