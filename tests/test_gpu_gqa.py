@@ -74,3 +74,32 @@ def test_decode_gqa_variants(dtype, Hq, Hkv, d, Lmax, lens, seed, min_votes, aug
                 assert (kmg[b, h, :lens[b]] == ref.keep[b][h]).all(), (b, h)
                 check_out(og[b, h], ref.out[b, h], dtype, f"b{b} h{h}")
                 assert abs(btg[b, h] - ref.beta[b, h]) <= 1e-5
+
+
+def test_decode_gqa_without_optional_outputs():
+    """No kept mask, counts, beta or union size: same output bits as with them."""
+    print("decode_gqa bare", flush=True)
+    dev = device()
+    Hq, Hkv, d, Lmax, lens = 16, 2, 128, 4100, [4100, 700]
+    q, k, v, theta, vm = _case(Hq, Hkv, d, Lmax, lens, torch.bfloat16, 1)
+    outs = []
+    for full in (True, False):
+        B = len(lens)
+        out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+        extra = dict(kept_count=torch.empty(B, Hq, dtype=torch.int32, device=dev),
+                     beta=torch.empty(B, Hq, dtype=torch.float32, device=dev),
+                     vrows_read=torch.empty(B, Hkv, dtype=torch.int32, device=dev),
+                     kept_mask=torch.zeros(B, Hq, Lmax, dtype=torch.uint8, device=dev)) if full else {}
+        ws = tt.workspace(tt.TOPTH_OP_DECODE, B, Hq, Hkv, 1, Lmax, d)
+        tt.topth_decode_gqa(q.to(dev), k.to(dev), v.to(dev), torch.tensor(lens, dtype=torch.int32, device=dev),
+                            torch.tensor(theta, dtype=torch.float32, device=dev), out, ws,
+                            scale=1.0 / np.sqrt(d), flags=tt.TOPTH_VMC, min_votes=3, augment=True,
+                            v_mean=torch.tensor(vm, dtype=torch.float32, device=dev), **extra)
+        torch.cuda.synchronize()
+        outs.append(out.float().cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    ref = serving.decode_gqa(to_f64(q), to_f64(k), to_f64(v), lens, theta, vm, 1.0 / np.sqrt(d), vmc=True,
+                             min_votes=3, augment=True)
+    for b in range(len(lens)):
+        for h in range(Hq):
+            check_out(outs[1][b, h], ref.out[b, h], torch.bfloat16, f"b{b} h{h}")

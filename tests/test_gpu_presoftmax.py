@@ -69,6 +69,8 @@ def calib_tables(cfg, Hq, Hkv, L, d, k, n_seq, dtype, q_pos0=0, Lq=None):
     (torch.bfloat16, 4, 2, 300, 128, [8, 32, 100], 0, 300),   # tiled kernel, prefill-style
     (torch.bfloat16, 8, 2, 1500, 64, [64], 1499, 1),          # tiled kernel, decode-style
     (torch.float32, 2, 1, 200, 64, [16, 199], 0, 200),        # row kernel
+    (torch.bfloat16, 2, 1, 2100, 64, [64, 700], 0, 2100),    # 8 columns of 2 waves each
+    (torch.bfloat16, 4, 1, 5000, 128, [64, 300], 4999, 1),   # 4 columns of 4 waves each
 ])
 def test_calibrate_pre_parity(dtype, Hq, Hkv, L, d, ks, q_pos0, Lq):
     print(f"calibrate_pre {dtype} Hq={Hq} L={L} ks={ks} q_pos0={q_pos0}", flush=True)
@@ -349,3 +351,25 @@ def test_decode_pre_edge_thresholds(sdc):
     g = run_decode_pre(q, k, v, lens, theta, et, vm, MODES[sdc] | tt.TOPTH_VMC, dev)
     compare_decode_pre(q, k, v, lens, theta, et, vm, sdc, sdc != "none", g, torch.bfloat16)
     assert (g[3][:, 1] == 0).all() and (g[3][:, 0] == np.array(lens)).all()
+
+
+@pytest.mark.parametrize("sdc", ["expth", "offline"])
+def test_decode_pre_bf16_without_optional_outputs(sdc):
+    """The launch a server makes: no kept mask, counts, beta or union size."""
+    print(f"decode_pre bf16 bare sdc={sdc}", flush=True)
+    dev = device()
+    Hq, Hkv, d, Lmax, lens = 16, 2, 128, 4100, [4100, 2049]
+    q, k, v, theta, et, vm = decode_case(Hq, Hkv, d, Lmax, lens, torch.bfloat16, 2)
+    full = run_decode_pre(q, k, v, lens, theta, et, vm, MODES[sdc] | tt.TOPTH_VMC, dev)
+    out = torch.empty(len(lens), Hq, d, dtype=torch.bfloat16, device=dev)
+    ws = tt.workspace(tt.TOPTH_OP_DECODE, len(lens), Hq, Hkv, 1, Lmax, d)
+    tt.topth_decode_pre(q.to(dev), k.to(dev), v.to(dev), torch.tensor(lens, dtype=torch.int32, device=dev),
+                        torch.tensor(theta, dtype=torch.float32, device=dev), out, ws,
+                        scale=1.0 / np.sqrt(d), flags=MODES[sdc] | tt.TOPTH_VMC, gamma=GAMMA,
+                        e_tilde=torch.tensor(et, dtype=torch.float32, device=dev),
+                        v_mean=torch.tensor(vm, dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32)[0].item()) == 0, "exchange wait timed out"
+    # the same kernels with and without the optional outputs give the same bits
+    assert np.array_equal(out.float().cpu().numpy(), full[0])
+    compare_decode_pre(q, k, v, lens, theta, et, vm, sdc, True, full, torch.bfloat16)
