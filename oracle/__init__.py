@@ -17,6 +17,12 @@ other step is pinned.
 Algorithm 1 in its printed form) with the three estimates of the discarded
 softmax mass of Sec. 3.2.1 (exact, exp-threshold, offline-calibrated); it is
 pinned by ``tests/test_oracle_presoftmax_pins.py``.
+
+``oracle.serving`` holds the decode-serving helpers (running V mean under
+KV-cache appends, thresholds fitted to the row position) and the GQA selection
+variants of Sec. 4.6, pinned by ``tests/test_oracle_serving_pins.py``; the
+fitted function's form is a reading the pages do not fix (parity unpinned for
+that choice).
 """
 from .topth import (  # noqa: F401
     scores, post_softmax, kth_largest, theta_row, row_weights, row_output, topth_row,
@@ -24,3 +30,4 @@ from .topth import (  # noqa: F401
     PrefillResult, DecodeResult, RowResult,
 )
 from . import presoftmax  # noqa: F401,E402
+from . import serving  # noqa: F401,E402
