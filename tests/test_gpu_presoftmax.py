@@ -313,6 +313,7 @@ def compare_decode_pre(q, k, v, lens, theta, et, vm, sdc, vmc, g, dtype):
     (8, 2, 128, 1000, [1000, 537, 1]),        # g=4, ragged, single-key row
     (16, 2, 128, 4100, [4100, 2049]),         # g=8, several chunks
     (4, 4, 64, 300, [300, 129]),              # g=1, d=64
+    (16, 1, 64, 600, [600, 90]),              # g=16 (FMA accumulate), d=64
 ])
 def test_decode_pre_bf16(sdc, Hq, Hkv, d, Lmax, lens):
     print(f"decode_pre bf16 sdc={sdc} Hq={Hq} Hkv={Hkv} d={d} lens={lens}", flush=True)
