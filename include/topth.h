@@ -294,7 +294,10 @@ int topth_vmean_append(const void* v_cache, const int* old_lens, const int* new_
  * (pre-softmax thresholds).
  *   theta device float, count device int [n_k][Hq][n_rows];
  *   coef device double [n_k][Hq][degree + 1], highest power first (output);
- *   NaN coefficients where fewer than degree + 1 rows are usable.
+ *   NaN coefficients where fewer than degree + 1 rows are usable.  The fit
+ *   solves the normal equations in float64: a cubic over a narrow range of
+ *   ln(p + 1) is ill-conditioned, and its coefficients (not its values) may
+ *   then differ in the leading digits from an orthogonal-factorisation solve.
  */
 int topth_theta_fit(const float* theta, const int* count, int n_k, int Hq, int n_rows, int degree,
                     int log_domain, double* coef, void* stream);
