@@ -355,6 +355,9 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
                      "kernel": "decode_bf16_kernel", "avg_kernel_us": round(avg * 1e6, 3)},
         "wall_s": round(wall, 4),
     }
+    if name == "decode_8b":
+        log("[bench] GQA selection variants on the same caches")
+        res["gqa_variants"] = gqa_variants(bufs, vms, lens_d, theta, w, dev, read_bytes, steps=min(steps, 100))
     if buckets:
         log("[bench] k~/k at the probe rows of each bucket")
         res["kept_over_k_by_row_bucket"] = kept_by_bucket(buckets, bufs[0], theta, w, dev)
@@ -363,6 +366,54 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
     if with_cpu:
         log("[bench] timing the CPU oracle on a sample of the same workload")
         res["cpu_baseline"] = oracle_decode_baseline(bufs[0], lens, theta, vms[0], w, read_bytes)
+    return res
+
+
+def gqa_variants(bufs, vms, lens_d, theta, w, dev, read_bytes, steps):
+    """V rows loaded per group, mean kept keys per head and step time of the
+    GQA selection variants (keys kept by at least m heads; every head using
+    all loaded keys), each over `steps` graph-replayed steps on the same
+    rotating caches; bytes counted as for the plain decode step."""
+    B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
+    g = Hq // Hkv
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    kc = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    vr = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    ws = tt.workspace(tt.TOPTH_OP_DECODE, B, Hq, Hkv, 1, n, d)
+    res = {}
+    for label, m, aug in (("min_votes_2", 2, False), ("min_votes_g", g, False), ("augment_union", 1, True),
+                          ("augment_min_votes_2", 2, True)):
+        def step(i):
+            q, kk, v = bufs[i % len(bufs)]
+            tt.topth_decode_gqa(q, kk, v, lens_d, theta, out, ws, scale=1.0 / math.sqrt(d), flags=tt.TOPTH_VMC,
+                                min_votes=m, augment=aug, v_mean=vms[i % len(bufs)], kept_count=kc,
+                                vrows_read=vr)
+        nb, kept, rows = [], [], []
+        for i in range(len(bufs)):
+            step(i)
+            torch.cuda.synchronize()
+            nb.append(read_bytes(B, vr.sum().item()))
+            kept.append(kc.float().mean().item() / w["k"])
+            rows.append(vr.float().mean().item())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        avg = start.elapsed_time(end) * 1e-3 / steps
+        nbytes = sum(nb[i % len(bufs)] for i in range(steps)) / steps
+        res[label] = {"vrows_per_group": round(float(np.mean(rows)), 1),
+                      "kept_over_k": round(float(np.mean(kept)), 4),
+                      "us_per_step": round(avg * 1e6, 2), "GB_per_s": round(nbytes / avg / 1e9, 1)}
+    status = int(ws[:4].view(torch.int32)[0].item())
+    if status != 0:
+        raise RuntimeError(f"decode exchange wait timed out (status {status})")
     return res
 
 
