@@ -684,7 +684,7 @@ def main():
                     help="also run one elementwise kernel of known size (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "topth runs on one GPU; --gpus must be 1 "
                           "(multi-GPU sharding is described, not implemented)"}))
         sys.exit(2)
     if not torch.cuda.is_available():
