@@ -358,6 +358,8 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
     if name == "decode_8b":
         log("[bench] GQA selection variants on the same caches")
         res["gqa_variants"] = gqa_variants(bufs, vms, lens_d, theta, w, dev, read_bytes, steps=min(steps, 100))
+        log("[bench] decode-serving helpers: running V mean and fitted theta")
+        res["serving_helpers"] = serving_helpers(bufs, vms, lens_d, theta, w, dev, steps=min(steps, 100))
     if buckets:
         log("[bench] k~/k at the probe rows of each bucket")
         res["kept_over_k_by_row_bucket"] = kept_by_bucket(buckets, bufs[0], theta, w, dev)
@@ -411,6 +413,67 @@ def gqa_variants(bufs, vms, lens_d, theta, w, dev, read_bytes, steps):
         res[label] = {"vrows_per_group": round(float(np.mean(rows)), 1),
                       "kept_over_k": round(float(np.mean(kept)), 4),
                       "us_per_step": round(avg * 1e6, 2), "GB_per_s": round(nbytes / avg / 1e9, 1)}
+    status = int(ws[:4].view(torch.int32)[0].item())
+    if status != 0:
+        raise RuntimeError(f"decode exchange wait timed out (status {status})")
+    return res
+
+
+def replay_us(step, steps):
+    """Average µs per step of `steps` calls captured into one HIP graph (after
+    one untimed replay), from HIP events on the replay stream."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / steps
+
+
+def serving_helpers(bufs, vms, lens_d, theta, w, dev, steps):
+    """Per-token cost of the decode-serving helpers at the decode shape: the
+    running V mean after appending one row per sequence, alone, followed by the
+    decode step that uses it, and fused into that step (topth_decode_append);
+    and evaluating a fitted theta(n) (one k, degree 1 in ln(p + 1), log domain)
+    for every row of the cache.  The means are updated in copies, so the
+    benchmark's own v_mean stays as it was."""
+    B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
+    old = torch.full((B,), n - 1, dtype=torch.int32, device=dev)
+    mus = [vm.clone() for vm in vms]
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    ws = tt.workspace(tt.TOPTH_OP_DECODE, B, Hq, Hkv, 1, n, d)
+
+    def append(i):
+        tt.topth_vmean_append(bufs[i % len(bufs)][2], old, lens_d, mus[i % len(bufs)])
+
+    def append_and_decode(i):
+        append(i)
+        q, kk, v = bufs[i % len(bufs)]
+        tt.topth_decode(q, kk, v, lens_d, theta, out, ws, scale=1.0 / math.sqrt(d), flags=tt.TOPTH_VMC,
+                        v_mean=mus[i % len(bufs)])
+
+    def decode_append(i):
+        q, kk, v = bufs[i % len(bufs)]
+        tt.topth_decode_append(q, kk, v, lens_d, theta, out, ws, mus[i % len(bufs)], scale=1.0 / math.sqrt(d),
+                               flags=tt.TOPTH_VMC)
+
+    coef = torch.tensor([[[-1.0, math.log(0.5)]] * Hq], dtype=torch.float64, device=dev)
+    th_out = torch.empty(1, Hq, n, dtype=torch.float32, device=dev)
+
+    def evaluate(i):
+        tt.topth_theta_eval(coef, [w["k"]], th_out, log_domain=True)
+
+    res = {"vmean_append_us": round(replay_us(append, steps), 2),
+           "decode_step_with_vmean_append_us": round(replay_us(append_and_decode, steps), 2),
+           "decode_append_fused_us": round(replay_us(decode_append, steps), 2),
+           "theta_eval_all_rows_us": round(replay_us(evaluate, steps), 2),
+           "vmean_append_bytes": B * Hkv * d * 2 + 2 * B * Hkv * d * 4}
     status = int(ws[:4].view(torch.int32)[0].item())
     if status != 0:
         raise RuntimeError(f"decode exchange wait timed out (status {status})")

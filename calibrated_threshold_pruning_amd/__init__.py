@@ -12,5 +12,5 @@ from ._lib import (  # noqa: F401
     topth_calibrate_finalize, topth_prefill, topth_decode, topth_vmean,
     TOPTH_SDC_EXPTH, TOPTH_SDC_OFFLINE, TOPTH_OP_CALIBRATE_PRE_E, topth_calibrate_pre,
     topth_calibrate_finalize_etilde, topth_prefill_pre, topth_decode_pre,
-    topth_vmean_append, topth_theta_fit, topth_theta_eval, topth_decode_gqa,
+    topth_vmean_append, topth_theta_fit, topth_theta_eval, topth_decode_gqa, topth_decode_append,
 )

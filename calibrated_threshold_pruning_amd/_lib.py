@@ -26,7 +26,7 @@ EXPORTS = ("topth_strerror", "topth_workspace_size", "topth_workspace_init", "to
            "topth_calibrate_finalize", "topth_prefill", "topth_decode", "topth_vmean",
            "topth_calibrate_pre", "topth_calibrate_finalize_etilde", "topth_prefill_pre",
            "topth_decode_pre", "topth_vmean_append", "topth_theta_fit", "topth_theta_eval",
-           "topth_decode_gqa")
+           "topth_decode_gqa", "topth_decode_append")
 
 
 class TopthError(RuntimeError):
@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topth_decode.restype = i
     lib.topth_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, vp, u, vp, vp, vp, vp,
                                  vp, vp, sz, vp]
+    lib.topth_decode_append.restype = i
+    lib.topth_decode_append.argtypes = list(lib.topth_decode.argtypes)
     lib.topth_vmean.restype = i
     lib.topth_vmean.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
     lib.topth_calibrate_pre.restype = i
@@ -223,6 +225,33 @@ def topth_decode(q, k_cache, v_cache, seq_lens, theta, out, ws, *, scale: float,
     _check("topth_decode", load_library().topth_decode(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv,
         Lmax, d, dt, float(scale), theta.data_ptr(), theta.shape[1], vm, int(flags),
+        out.data_ptr(), kc, bt, vr, km, ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def topth_decode_append(q, k_cache, v_cache, seq_lens, theta, out, ws, v_mean, *, scale: float, flags: int,
+                        kept_count=None, beta=None, vrows_read=None, kept_mask=None, stream=None):
+    """topth_decode that first appends row n - 1 to the running mean v_mean
+    [B,Hkv,d] (mean of rows 0..n-2 on entry, of rows 0..n-1 on return) and
+    uses the updated mean for VMC."""
+    B, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    dt = _dtype_code(q)
+    _dev(q, "q"); _dev(k_cache, "k_cache", q.dtype, (B, Hkv, Lmax, d))
+    _dev(v_cache, "v_cache", q.dtype, (B, Hkv, Lmax, d))
+    _dev(seq_lens, "seq_lens", torch.int32, (B,))
+    _dev(theta, "theta", torch.float32)
+    if theta.dim() != 2 or theta.shape[0] != Hq:
+        raise ValueError("theta must be [Hq, n_rows]")
+    _dev(out, "out", q.dtype, (B, Hq, d))
+    _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d))
+    kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq), optional=True)
+    bt = _dev(beta, "beta", torch.float32, (B, Hq), optional=True)
+    vr = _dev(vrows_read, "vrows_read", torch.int32, (B, Hkv), optional=True)
+    km = _dev(kept_mask, "kept_mask", torch.uint8, (B, Hq, Lmax), optional=True)
+    _dev(ws, "ws", torch.uint8)
+    _check("topth_decode_append", load_library().topth_decode_append(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv,
+        Lmax, d, dt, float(scale), theta.data_ptr(), theta.shape[1], v_mean.data_ptr(), int(flags),
         out.data_ptr(), kc, bt, vr, km, ws.data_ptr(), ws.numel(), _stream(stream)))
 
 

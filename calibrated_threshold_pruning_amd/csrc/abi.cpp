@@ -259,7 +259,8 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
                   const float* theta, int n_rows, const float* v_mean, unsigned flags,
                   void* out, int* kept_count, float* beta, int* vrows_read,
                   unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream,
-                  bool pre, const float* e_tilde, float gamma, int min_votes = 1, int augment = 0) {
+                  bool pre, const float* e_tilde, float gamma, int min_votes = 1, int augment = 0,
+                  float* v_mean_append = nullptr) {
     if (!q || !k_cache || !v_cache || !seq_lens || !theta || !out) return TOPTH_EINVAL;
     if (bad_dims(B, Hq, Hkv, Lmax, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
     if (!isfinite(scale) || !(scale > 0.0f)) return TOPTH_EINVAL;
@@ -279,9 +280,15 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
     p.min_votes = min_votes; p.augment = augment ? 1 : 0;
     if (dtype == TOPTH_BF16) {
         if (!decode_bf16_supported(d, Hq / Hkv) || (long long)Lmax * d * 2 >= INT_MAX) return TOPTH_EUNSUPPORTED;
+        p.v_mean_append = v_mean_append;              // the kernel appends row n - 1 itself
         return map_hip(launch_decode_bf16(p, (hipStream_t)stream));
     }
     if (Lmax > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
+    if (v_mean_append) {                              // fp32: the stand-alone update first, same stream
+        const int e = launch_vmean_append(v_cache, nullptr, seq_lens, B, Hkv, Lmax, d, dtype, v_mean_append,
+                                          (hipStream_t)stream);
+        if (e != 0) return map_hip(e);
+    }
     return map_hip(launch_decode_rowwise(p, (uint32_t*)((char*)ws + kWsHeaderBytes),
                                          (hipStream_t)stream));
 }
@@ -298,6 +305,17 @@ int topth_decode(const void* q, const void* k_cache, const void* v_cache, const 
     return decode_common(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Lmax, d, dtype, scale, theta,
                          n_rows, v_mean, flags, out, kept_count, beta, vrows_read, kept_mask, ws,
                          ws_bytes, stream, false, nullptr, 0.f);
+}
+
+int topth_decode_append(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                        int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                        const float* theta, int n_rows, float* v_mean, unsigned flags,
+                        void* out, int* kept_count, float* beta, int* vrows_read,
+                        unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream) {
+    if (!v_mean) return TOPTH_EINVAL;                 // the running mean is always updated
+    return decode_common(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Lmax, d, dtype, scale, theta,
+                         n_rows, v_mean, flags, out, kept_count, beta, vrows_read, kept_mask, ws,
+                         ws_bytes, stream, false, nullptr, 0.f, 1, 0, v_mean);
 }
 
 int topth_decode_pre(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,

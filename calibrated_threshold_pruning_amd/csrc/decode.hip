@@ -52,6 +52,9 @@ struct DecodeKArgs {
     float gamma;            // pre-softmax exp-threshold estimate
     int min_votes;          // GQA: load a key when at least this many heads keep it (<= 1: any)
     int augment;            // GQA: every head uses all loaded keys, not only its own
+    // running V mean to update in place (the mean of rows 0..n-2 becomes that of
+    // rows 0..n-1) and to use for VMC; NULL: v_mean is used as given
+    float* v_mean_append;
 };
 
 // One workgroup of kDecodeWaves waves per CU: two workgroups on a CU stream at
@@ -287,6 +290,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
     __shared__ float s_cm[C::WAVES][G];
     __shared__ int s_cc[C::WAVES][G];
     __shared__ int s_un[C::WAVES];
+    __shared__ float s_mu[D];                  // the appended running mean of V
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -866,6 +870,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                 u = gather_chunks(a.part_union + g0, 1, a.chunks, u, a.spin_limit, a.status);
                 if (a.vrows_read) a.vrows_read[group] = u;
             }
+            // running mean of V (Sec. 3.2.2, kept during generation): rows
+            // 0..n-2 had mean mu; with row n-1 appended it is
+            // ((n-1) mu + V[n-1]) / n, formed in float64 like the stand-alone update
+            float* const mu_rw = a.v_mean_append;
+            if (mu_rw != nullptr)
+                for (int dd = tid; dd < D; dd += C::THREADS) {
+                    const double prev = n > 1 ? (double)(n - 1) * (double)mu_rw[(size_t)group * D + dd] : 0.0;
+                    const double vn = (double)bf16_bits_to_f32(a.v[((size_t)group * a.Lmax + (n - 1)) * D + dd]);
+                    s_mu[dd] = (float)((prev + vn) / (double)n);
+                }
             __syncthreads();
             for (int idx = tid; idx < G * D; idx += C::THREADS) {
                 const int h = idx / D, dd = idx % D;
@@ -876,9 +890,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                 const float mass = s_cm[0][h];
                 if (renorm) x = (s_cc[0][h] > 0) ? x / mass : 0.f;
                 else if (a.flags & (kFlagExpth | kFlagOffline)) x *= s_T[h];
-                if (vmc) x = fmaf(s_M[h], a.v_mean[(size_t)group * D + dd], x);
+                if (vmc) x = fmaf(s_M[h], mu_rw != nullptr ? s_mu[dd] : a.v_mean[(size_t)group * D + dd], x);
                 a.out[((size_t)b * a.Hq + (size_t)kv * G + h) * D + dd] = f32_to_bf16_bits(x);
             }
+            // every read of the previous mean happened before the barrier above
+            if (mu_rw != nullptr)
+                for (int dd = tid; dd < D; dd += C::THREADS) mu_rw[(size_t)group * D + dd] = s_mu[dd];
         }
         __syncthreads();
     }
@@ -1048,7 +1065,7 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     char* ws = (char*)p.ws;
     DecodeKArgs a = {};
     a.q = (const uint16_t*)p.q; a.k = (const uint16_t*)p.k; a.v = (const uint16_t*)p.v;
-    a.seq_lens = p.seq_lens; a.theta = p.theta; a.v_mean = p.v_mean;
+    a.seq_lens = p.seq_lens; a.theta = p.theta; a.v_mean = p.v_mean; a.v_mean_append = p.v_mean_append;
     a.e_tilde = p.e_tilde; a.gamma = p.gamma;
     a.min_votes = p.min_votes; a.augment = p.augment;
     a.out = (uint16_t*)p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.vrows_read = p.vrows_read;

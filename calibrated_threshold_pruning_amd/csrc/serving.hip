@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kAppendThreads) void vmean_append_kernel(
     const int bk = blockIdx.x;
     const int b = bk / Hkv;
     const int n_new = min(max(new_lens[b], 1), Lmax);
-    const int n_old = min(max(old_lens[b], 0), n_new);
+    const int n_old = old_lens ? min(max(old_lens[b], 0), n_new) : n_new - 1;   // NULL: one row appended
     const T* base = v + (size_t)bk * Lmax * D;
     const int c = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
     double acc[EPC];

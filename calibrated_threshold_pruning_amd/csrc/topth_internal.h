@@ -120,6 +120,7 @@ struct DecodeParams {
     void* ws; size_t ws_bytes;
     const float* e_tilde; float gamma;    // pre-softmax calls only
     int min_votes; int augment;           // GQA selection variants (0, 0: plain per-head selection)
+    float* v_mean_append;                 // non-NULL: append row n - 1 to this running mean, then use it
 };
 struct PrefillParams {
     const void* q; const void* k; const void* v;

@@ -201,6 +201,28 @@ int topth_decode(const void* q, const void* k_cache, const void* v_cache, const 
 int topth_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,
                 float* v_mean, void* stream);
 
+/*
+ * One decoding step that also keeps the running V mean (Sec. 3.2.2, after
+ * Eq. 7: during generation mu is maintained as a running mean).  Arguments
+ * and results as topth_decode, except v_mean, which is read and written:
+ *   v_mean device float [B][Hkv][d], required.  On entry it holds the mean of
+ *          V rows 0..n-2 of each (b, kv head), n = seq_lens[b] clamped to
+ *          [1, Lmax] (ignored when n = 1); row n-1 is the token just appended.
+ *          On return it holds the mean of rows 0..n-1, ((n-1) mu + V[n-1]) / n
+ *          formed in float64 and stored as float, and that is the mu the VMC
+ *          term of this step uses.  It is updated whatever the flags are.
+ * The result equals topth_vmean_append(old = n-1, new = n) followed by
+ * topth_decode.  For bf16 the update runs inside the decode kernel (no extra
+ * launch); for fp32 the update kernel runs first on the same stream.  Calling
+ * twice for the same n appends row n-1 twice.  Errors as topth_decode;
+ * TOPTH_EINVAL also for v_mean == NULL.
+ */
+int topth_decode_append(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                        int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                        const float* theta, int n_rows, float* v_mean, unsigned flags,
+                        void* out, int* kept_count, float* beta, int* vrows_read,
+                        unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Pre-softmax Top-theta (the paper's Algorithm 1 in its printed form, and
  * Sec. 3.2.1): thresholds are on the scores a = scale * q.k themselves, in

@@ -228,3 +228,14 @@ def test_decode_gqa_errors(lib):
     assert call(5, 0) == -1          # more votes than heads in the group (g = 4)
     assert call(2, 2) == -1          # augment is 0 or 1
     assert call(2, 0, Hq=6, Hkv=4) == -1
+
+
+def test_decode_append_errors(lib):
+    def call(vm=FAKE, flags=1, d=128, ws=FAKE):
+        return lib.topth_decode_append(FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 64, d, 1, 0.1, FAKE, 64, vm, flags,
+                                       FAKE, None, None, None, None, ws, 1 << 30, None)
+    assert call(vm=None) == -1              # the running mean is always read and updated
+    assert call(vm=None, flags=0) == -1
+    assert call(flags=0x10) == -1           # unknown flag
+    assert call(d=96) == -1
+    assert call(ws=None) == -3

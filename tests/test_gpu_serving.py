@@ -92,3 +92,69 @@ def test_theta_fit_and_eval(degree, log_domain):
                 np.testing.assert_allclose(cg[t, h], cr[h], rtol=1e-6, atol=1e-9, err_msg=f"t{t} h{h}")
             assert np.isneginf(og[t, h, :ks[t]]).all()
             np.testing.assert_allclose(og[t, h, ks[t]:], ref[h, ks[t]:], rtol=1e-5, atol=1e-30)
+
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,d,Lmax,lens", [
+    (torch.bfloat16, 8, 2, 128, 1000, [1000, 537, 1]),       # g = 4, a single-key row
+    (torch.bfloat16, 16, 2, 128, 4100, [4100, 2049]),        # g = 8, several chunks per group
+    (torch.bfloat16, 16, 1, 64, 600, [600, 90]),             # g = 16 (FMA accumulation)
+    (torch.float32, 8, 2, 64, 500, [500, 77]),               # row kernels: update kernel first
+])
+def test_decode_append_fused(dtype, Hq, Hkv, d, Lmax, lens):
+    """topth_decode_append appends row n - 1 to the running mean and decodes
+    with it.  Over two steps (n, then n + 1 where the cache has room; a row at
+    the end of the cache starts again from the mean of its first n - 1 rows)
+    the updated mean and the output equal, bit for bit, the stand-alone update
+    followed by topth_decode; the mean is that of the cached rows (1e-5
+    relative) and masks, counts and outputs match the oracle."""
+    print(f"decode_append {dtype} Hq={Hq} Hkv={Hkv} d={d} lens={lens}", flush=True)
+    from test_gpu_decode import compare_decode, decode_theta
+    dev = device()
+    B = len(lens)
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 11, 0, B=B, Hq=Hq, Hkv=Hkv, Lq=1, Lk=Lmax, d=d, dtype=dtype)
+    q = q[:, :, 0].contiguous()
+    vf = to_f64(v)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    scale = 1.0 / np.sqrt(d)
+    ws_a = tt.workspace(tt.TOPTH_OP_DECODE, B, Hq, Hkv, 1, Lmax, d)
+    ws_b = tt.workspace(tt.TOPTH_OP_DECODE, B, Hq, Hkv, 1, Lmax, d)
+
+    def mean_before(b, h, n):           # rows 0..n-2; for n = 1 a value the update must ignore
+        return vf[b, h, :n - 1].mean(0) if n > 1 else np.full(d, 123.0)
+
+    mu_a = torch.tensor(np.stack([[mean_before(b, h, lens[b]) for h in range(Hkv)] for b in range(B)]),
+                        dtype=torch.float32, device=dev)
+    mu_b = mu_a.clone()
+    steps = [lens, [min(n + 1, Lmax) for n in lens]]
+    for step, lens_s in enumerate(steps):
+        if step == 1:
+            for b in range(B):
+                if lens_s[b] == steps[0][b]:
+                    for h in range(Hkv):
+                        mu_a[b, h] = torch.tensor(mean_before(b, h, lens_s[b]), dtype=torch.float32)
+                        mu_b[b, h] = mu_a[b, h]
+        theta = decode_theta(UNIT, Hq, Hkv, d, lens_s, 24, 3, dtype, 1, n_rows=Lmax)
+        th = torch.tensor(theta, dtype=torch.float32, device=dev)
+        ln = torch.tensor(lens_s, dtype=torch.int32, device=dev)
+        out_a = torch.empty(B, Hq, d, dtype=dtype, device=dev)
+        out_b = torch.empty_like(out_a)
+        kc = torch.full((B, Hq), -7, dtype=torch.int32, device=dev)
+        bt = torch.full((B, Hq), -7.0, dtype=torch.float32, device=dev)
+        vr = torch.full((B, Hkv), -7, dtype=torch.int32, device=dev)
+        km = torch.zeros((B, Hq, Lmax), dtype=torch.uint8, device=dev)
+        tt.topth_decode_append(qd, kd, vd, ln, th, out_a, ws_a, mu_a, scale=scale, flags=tt.TOPTH_VMC,
+                               kept_count=kc, beta=bt, vrows_read=vr, kept_mask=km)
+        old = torch.tensor([n - 1 for n in lens_s], dtype=torch.int32, device=dev)
+        tt.topth_vmean_append(vd, old, ln, mu_b)
+        tt.topth_decode(qd, kd, vd, ln, th, out_b, ws_b, scale=scale, flags=tt.TOPTH_VMC, v_mean=mu_b)
+        torch.cuda.synchronize()
+        assert int(ws_a[:4].view(torch.int32)[0].item()) == 0, "exchange wait timed out"
+        assert torch.equal(mu_a, mu_b), "fused and stand-alone running means differ"
+        assert torch.equal(out_a, out_b), "fused and two-call outputs differ"
+        exact = np.stack([[vf[b, h, :lens_s[b]].mean(0) for h in range(Hkv)] for b in range(B)])
+        mu_g = mu_a.cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(mu_g, exact, rtol=1e-5, atol=1e-6)
+        g = dict(out=out_a.float().cpu().numpy(), kc=kc.cpu().numpy(), beta=bt.cpu().numpy(),
+                 vr=vr.cpu().numpy(), mask=km.cpu().numpy().astype(bool))
+        compare_decode(g, q, k, v, lens_s, theta, mu_g, tt.TOPTH_VMC, dtype)
