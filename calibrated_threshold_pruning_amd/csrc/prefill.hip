@@ -70,6 +70,12 @@ struct PrefillCfg {
 
 __device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ void pf_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// wait until at most N vector memory loads of this wave are outstanding (N < 16)
+template <int N>
+__device__ __forceinline__ void pf_wait_vmem_n() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // Scheduling hint for one region: REPS times, NDS LDS reads then NMFMA MFMAs,
 // which puts the reads of the next operand fragments ahead of the MFMAs of the
@@ -112,8 +118,9 @@ template <int D, int G, bool MASK, bool PRE, bool F16, bool MASS>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     using C = PrefillCfg<D, G>;
-    __shared__ __attribute__((aligned(16))) unsigned char s_k[2][C::KTILE];
-    __shared__ __attribute__((aligned(16))) unsigned char s_v[2][C::KTILE];
+    // four tile slots: sweep B double-buffers K in slots 0-1 and V in slots
+    // 2-3; sweep A, which reads no V, rotates K through all four
+    __shared__ __attribute__((aligned(16))) unsigned char s_kv[4][C::KTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -175,14 +182,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                 vo[li % NVO], (tile * C::BN + li * C::RPI) * (D * 2), 0, 0);
         }
     };
-    auto issue_k = [&](int tile, int buf) { issue_tile(krs, s_k[buf], tile); };
-    auto issue_v = [&](int tile, int buf) { issue_tile(vrs, s_v[buf], tile); };
+    auto issue_k = [&](int tile, int slot) { issue_tile(krs, s_kv[slot], tile); };
+    auto issue_v = [&](int tile, int buf) { issue_tile(vrs, s_kv[2 + buf], tile); };
     // S^T block (keys 16 kb + 4 lq + r, query rows 16 qb + l16) of one K tile
     auto scores = [&](int buf, f32x4 (&st)[2][4]) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int key = 16 * kb + l16;              // A operand row: key of the tile
-            const unsigned char* srow = &s_k[buf][((key / C::RPI) * 64 + (key % C::RPI) * C::CPR) * 16];
+            const unsigned char* srow = &s_kv[buf][((key / C::RPI) * 64 + (key % C::RPI) * C::CPR) * 16];
             const int swz = key % C::CPR;
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -206,14 +213,24 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
     };
 
     // ======================= sweep A: row log-sum-exp =========================
+    // K tiles go three ahead through the four slots: at step j the loads of
+    // tiles j+1 and j+2 may still be in flight (loads retire in issue order,
+    // so waiting until at most their count is outstanding completes tile j)
     float m_l[2] = {NEG_INF, NEG_INF}, l_l[2] = {0.f, 0.f};
-    if constexpr (!PRE) issue_k(0, 0);
+    if constexpr (!PRE) {
+        issue_k(0, 0);
+        if (ntiles > 1) issue_k(1, 1);
+        if (ntiles > 2) issue_k(2, 2);
+    }
     for (int j = 0; j < (PRE ? 0 : ntiles); ++j) {
-        pf_wait_vmem();
+        const int ahead = ntiles - 1 - j;
+        if (ahead >= 2) pf_wait_vmem_n<2 * C::NLD>();
+        else if (ahead == 1) pf_wait_vmem_n<C::NLD>();
+        else pf_wait_vmem();
         __syncthreads();                                   // tile j complete; tile j-1 no longer read
-        if (j + 1 < ntiles) issue_k(j + 1, (j + 1) & 1);
+        if (j + 3 < ntiles) issue_k(j + 3, (j + 3) & 3);
         f32x4 st[2][4];
-        scores(j & 1, st);
+        scores(j & 3, st);
         // statistics in raw score units (the scale is positive): max, then
         // sum of exp2(scale * (s - max)); only tiles that cross the diagonal mask
         const bool diag = j * C::BN + C::BN - 1 > row0;
@@ -300,7 +317,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
     auto vt_frag = [&](int buf, int ks, int db) -> bf16x8 {
         // chunk index of dims 16 db + ... is 2 db + c; the swizzle XORs the chunk
         // index with key % CPR, and 2 db only touches bits that c does not use
-        const unsigned char* base = &s_v[buf][32 * ks * (D * 2)];
+        const unsigned char* base = &s_kv[2 + buf][32 * ks * (D * 2)];
         const int dboff = (2 * db) * 16;
         const pf_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) pf_i16x4*)(base + (vtr_off[0] ^ dboff)));
