@@ -158,3 +158,57 @@ def test_decode_append_fused(dtype, Hq, Hkv, d, Lmax, lens):
         g = dict(out=out_a.float().cpu().numpy(), kc=kc.cpu().numpy(), beta=bt.cpu().numpy(),
                  vr=vr.cpu().numpy(), mask=km.cpu().numpy().astype(bool))
         compare_decode(g, q, k, v, lens_s, theta, mu_g, tt.TOPTH_VMC, dtype)
+
+
+def test_decode_append_steps_in_a_graph():
+    """Three generation steps (n, n + 1, n + 2 cached rows) of
+    topth_decode_append captured in one HIP graph: every replay (the running
+    mean reset eagerly before each, with synchronisations between) gives the
+    same outputs and the same running mean, bit for bit, as the steps run
+    eagerly; the workspace slots left empty by each step serve the next."""
+    print("decode_append graph", flush=True)
+    from test_gpu_decode import decode_theta
+    dev = device()
+    Hq, Hkv, d, Lmax, B = 8, 2, 128, 700, 2
+    base = [600, 333]
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 12, 0, B=B, Hq=Hq, Hkv=Hkv, Lq=1, Lk=Lmax, d=d,
+                               dtype=torch.bfloat16)
+    q = q[:, :, 0].contiguous()
+    vf = to_f64(v)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    steps = [[n + s for n in base] for s in range(3)]
+    theta = torch.tensor(decode_theta(UNIT, Hq, Hkv, d, sum(steps, []), 24, 2, torch.bfloat16, 1, n_rows=Lmax),
+                         dtype=torch.float32, device=dev)
+    lens = [torch.tensor(st, dtype=torch.int32, device=dev) for st in steps]
+    mu0 = torch.tensor(np.stack([[vf[b, h, :base[b] - 1].mean(0) for h in range(Hkv)] for b in range(B)]),
+                       dtype=torch.float32, device=dev)
+    mu = mu0.clone()
+    outs = [torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev) for _ in steps]
+    ws = tt.workspace(tt.TOPTH_OP_DECODE, B, Hq, Hkv, 1, Lmax, d)
+
+    def run():
+        for s in range(len(steps)):
+            tt.topth_decode_append(qd, kd, vd, lens[s], theta, outs[s], ws, mu, scale=1.0 / np.sqrt(d),
+                                   flags=tt.TOPTH_VMC)
+
+    run()                                      # eager reference
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32)[0].item()) == 0, "exchange wait timed out"
+    mu_e, out_e = mu.clone(), [o.clone() for o in outs]
+    exact = np.stack([[vf[b, h, :steps[-1][b]].mean(0) for h in range(Hkv)] for b in range(B)])
+    np.testing.assert_allclose(mu_e.cpu().numpy().astype(np.float64), exact, rtol=1e-5, atol=1e-6)
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        mu.copy_(mu0)
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32)[0].item()) == 0, "exchange wait timed out"
+        assert torch.equal(mu, mu_e), f"replay {rep}: running mean"
+        for s in range(len(steps)):
+            assert torch.equal(outs[s], out_e[s]), f"replay {rep} step {s}"
