@@ -21,12 +21,15 @@ TOPTH_VMC, TOPTH_SDC_NONE = 0x1, 0x2
 TOPTH_SDC_EXPTH, TOPTH_SDC_OFFLINE = 0x4, 0x8
 TOPTH_OP_CALIBRATE, TOPTH_OP_PREFILL, TOPTH_OP_DECODE, TOPTH_OP_CALIBRATE_PRE_E = 0, 1, 2, 3
 TOPTH_MAX_NK = 8
+TOPTH_WS_HEADER_BYTES = 65536
+TOPTH_STATUS_EXCHANGE_TIMEOUT = 0x1
 
 EXPORTS = ("topth_strerror", "topth_workspace_size", "topth_workspace_init", "topth_calibrate",
            "topth_calibrate_finalize", "topth_prefill", "topth_decode", "topth_vmean",
            "topth_calibrate_pre", "topth_calibrate_finalize_etilde", "topth_prefill_pre",
            "topth_decode_pre", "topth_vmean_append", "topth_theta_fit", "topth_theta_eval",
-           "topth_decode_gqa", "topth_decode_append")
+           "topth_decode_gqa", "topth_decode_append", "topth_workspace_status",
+           "topth_workspace_set_spin_limit")
 
 
 class TopthError(RuntimeError):
@@ -54,6 +57,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topth_workspace_size.argtypes = [i] * 8
     lib.topth_workspace_init.restype = i
     lib.topth_workspace_init.argtypes = [vp, sz, vp]
+    lib.topth_workspace_status.restype = i
+    lib.topth_workspace_status.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_int), vp]
+    lib.topth_workspace_set_spin_limit.restype = i
+    lib.topth_workspace_set_spin_limit.argtypes = [vp, sz, u, vp]
     lib.topth_calibrate.restype = i
     lib.topth_calibrate.argtypes = [vp, vp, i, i, i, i, i, i, i, f, i, vp, i, vp, vp, vp, i, vp, sz, vp]
     lib.topth_calibrate_finalize.restype = i
@@ -138,6 +145,24 @@ def topth_workspace_init(ws: torch.Tensor, stream=None):
     _dev(ws, "ws", torch.uint8)
     _check("topth_workspace_init", load_library().topth_workspace_init(
         ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def topth_workspace_status(ws: torch.Tensor, stream=None) -> int:
+    """Status word of a decode workspace after the work enqueued so far (the
+    call synchronises the stream): 0 or TOPTH_STATUS_EXCHANGE_TIMEOUT."""
+    _dev(ws, "ws", torch.uint8)
+    out = ctypes.c_int(0)
+    _check("topth_workspace_status", load_library().topth_workspace_status(
+        ws.data_ptr(), ws.numel(), ctypes.byref(out), _stream(stream)))
+    return int(out.value)
+
+
+def topth_workspace_set_spin_limit(ws: torch.Tensor, limit: int, stream=None):
+    """Polls an exchange wait of later decode calls on ``ws`` makes before it
+    gives up (0: the default)."""
+    _dev(ws, "ws", torch.uint8)
+    _check("topth_workspace_set_spin_limit", load_library().topth_workspace_set_spin_limit(
+        ws.data_ptr(), ws.numel(), int(limit), _stream(stream)))
 
 
 def workspace(op: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, d: int, n_k: int = 1,

@@ -124,6 +124,21 @@ int topth_workspace_init(void* ws, size_t ws_bytes, void* stream) {
     return map_hip(e);
 }
 
+int topth_workspace_status(const void* ws, size_t ws_bytes, int* status, void* stream) {
+    if (!ws || !status || ws_bytes < kWsHeaderBytes) return TOPTH_EINVAL;
+    int word = 0;
+    hipError_t e = hipMemcpyAsync(&word, ws, sizeof(int), hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return TOPTH_EHIP;
+    *status = word;
+    return TOPTH_OK;
+}
+
+int topth_workspace_set_spin_limit(void* ws, size_t ws_bytes, unsigned limit, void* stream) {
+    if (!ws || ws_bytes < kWsHeaderBytes) return TOPTH_EINVAL;
+    return map_hip(launch_fill_u32((char*)ws + 4, 4, limit, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 namespace {

@@ -38,7 +38,7 @@ struct DecodeKArgs {
     const uint16_t* q; const uint16_t* k; const uint16_t* v; const int* seq_lens;
     const float* theta; const float* v_mean;
     uint16_t* out; int* kept_count; float* beta; int* vrows_read; unsigned char* kept_mask;
-    int* status;
+    int* status;       // workspace header: word 0 the status, word 1 the spin limit (0: default)
     // exchange slots, kWsSlotEmpty until published: (max, sum of exp2) per chunk
     // and head as one 64-bit word, and the partial outputs of chunks 1.. for chunk 0
     unsigned long long* part_ml; float* part_out; float* part_mass; int* part_cnt; int* part_union;
@@ -46,7 +46,6 @@ struct DecodeKArgs {
     int B, Hq, Hkv, Lmax, n_rows, chunks, items;
     float xscale;
     unsigned flags;
-    unsigned spin_limit;
     int xcd_map;       // 1: chunks of a group on one XCD (grid and items multiples of 8 * chunks)
     const float* e_tilde;   // pre-softmax offline estimate of E~ [Hq][n_rows], or NULL
     float gamma;            // pre-softmax exp-threshold estimate
@@ -133,18 +132,22 @@ __device__ __forceinline__ unsigned load32(const void* p) {
 __device__ __forceinline__ void store32(void* p, unsigned v) {
     __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A bounded wait: after `limit` polls that still find the slot empty it gives
+// up, sets the status bit in the workspace header and raises `failed`; the
+// caller's group then reports poisoned outputs instead of partial sums.
 __device__ __forceinline__ unsigned long long wait_slot64(const unsigned long long* p, unsigned long long v,
-                                                        unsigned limit, int* status) {
+                                                        unsigned limit, int* status, bool& failed) {
     for (unsigned spins = 0; v == kSlot64Empty; v = load64(p)) {
+        if (spins++ >= limit) { atomicOr(status, kStatusSpinTimeout); failed = true; break; }
         __builtin_amdgcn_s_sleep(1);
-        if (++spins > limit) { atomicOr(status, kStatusSpinTimeout); break; }
     }
     return v;
 }
-__device__ __forceinline__ unsigned wait_slot32(const void* p, unsigned v, unsigned limit, int* status) {
+__device__ __forceinline__ unsigned wait_slot32(const void* p, unsigned v, unsigned limit, int* status,
+                                                bool& failed) {
     for (unsigned spins = 0; v == kWsSlotEmpty; v = load32(p)) {
+        if (spins++ >= limit) { atomicOr(status, kStatusSpinTimeout); failed = true; break; }
         __builtin_amdgcn_s_sleep(1);
-        if (++spins > limit) { atomicOr(status, kStatusSpinTimeout); break; }
     }
     return v;
 }
@@ -152,7 +155,7 @@ __device__ __forceinline__ unsigned wait_slot32(const void* p, unsigned v, unsig
 // words); every slot read is set back to empty
 template <typename T>
 __device__ __forceinline__ T gather_chunks(T* base, size_t stride, int n, T first, unsigned limit,
-                                           int* status) {
+                                           int* status, bool& failed) {
     T x = first;
     for (int c0 = 1; c0 < n; c0 += 8) {
         unsigned v[8];
@@ -162,12 +165,53 @@ __device__ __forceinline__ T gather_chunks(T* base, size_t stride, int n, T firs
         for (int u = 0; u < 8; ++u) {
             if (c0 + u < n) {
                 T* p = base + (size_t)(c0 + u) * stride;
-                x += __builtin_bit_cast(T, wait_slot32(p, v[u], limit, status));
+                x += __builtin_bit_cast(T, wait_slot32(p, v[u], limit, status, failed));
                 store32(p, kWsSlotEmpty);
             }
         }
     }
     return x;
+}
+// The union sizes of chunks 1.. in chunk order; a chunk whose own waits gave
+// up publishes -1 - (its union size), which marks the group as failed.
+__device__ __forceinline__ int gather_union(int* base, int n, int first, unsigned limit, int* status,
+                                            bool& failed) {
+    int x = first;
+    for (int c0 = 1; c0 < n; c0 += 8) {
+        unsigned v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (c0 + u < n) ? load32(base + c0 + u) : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (c0 + u < n) {
+                int w = (int)wait_slot32(base + c0 + u, v[u], limit, status, failed);
+                if (w < 0) { failed = true; w = -1 - w; }
+                x += w;
+                store32(base + c0 + u, kWsSlotEmpty);
+            }
+        }
+    }
+    return x;
+}
+
+// Default number of polls of one exchange slot before a wait gives up (each
+// poll sleeps about 64 clocks: some 0.1 s in all); the workspace header can
+// lower it.
+constexpr unsigned kDefaultSpinLimit = 1u << 22;
+
+// Outputs of a group whose exchange did not complete: NaN outputs and beta,
+// -1 kept counts and V-row count.  The kept mask is left as it is.
+template <int D, int G>
+__device__ __forceinline__ void poison_group(const DecodeKArgs& a, int b, int kv, int group, int tid,
+                                             int nthreads) {
+    for (int idx = tid; idx < G * D; idx += nthreads)
+        a.out[((size_t)b * a.Hq + (size_t)kv * G) * D + idx] = 0x7FC0u;   // bfloat16 NaN
+    if (tid < G) {
+        const size_t o = (size_t)b * a.Hq + (size_t)kv * G + tid;
+        if (a.kept_count) a.kept_count[o] = -1;
+        if (a.beta) a.beta[o] = __uint_as_float(0x7FC00000u);
+    }
+    if (tid == 0 && a.vrows_read) a.vrows_read[group] = -1;
 }
 
 // Bit-sliced vote counts: plane i holds bit i of one count per tile bit.
@@ -291,6 +335,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
     __shared__ int s_cc[C::WAVES][G];
     __shared__ int s_un[C::WAVES];
     __shared__ float s_mu[D];                  // the appended running mean of V
+    __shared__ int s_fail;                     // some wait of this item gave up
+    __shared__ int s_sticky;                   // the workspace status was already set at launch
+    __shared__ unsigned s_limit;               // polls per exchange slot before a wait gives up
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -312,6 +359,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
         qrow_lds = ((i / C::GP == tt) && (hi < G)) ? hi : G;
     }
     for (int t = tid; t < D + 8; t += C::THREADS) s_q[G][t] = 0;
+    if (tid == 0) {
+        // A workspace whose status is set may hold exchange slots that a late
+        // chunk filled after its reader gave up: until topth_workspace_init
+        // prepares it again, every call reports poisoned outputs.
+        s_sticky = load32(a.status) != 0u;
+        const unsigned lim = load32(a.status + 1);
+        s_limit = lim != 0u ? lim : kDefaultSpinLimit;
+    }
+    __syncthreads();
+    const unsigned spin_limit = s_limit;
+    const bool sticky = s_sticky != 0;
 
     for (int slot = blockIdx.x; slot < a.items; slot += gridDim.x) {
         // Workgroups are dealt to the 8 XCDs round-robin by index; when the grid
@@ -327,6 +385,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
         const int b = group / a.Hkv, kv = group % a.Hkv;
         const int n = min(max(a.seq_lens[b], 1), a.Lmax);   // lengths outside [1, Lmax] are clamped
         const int wbase = chunk * C::KEYS_PER_WG + wave * NT * C::KT;
+        if (sticky) {                          // uniform over the workgroup
+            if (chunk == 0) {
+                poison_group<D, G>(a, b, kv, group, tid, C::THREADS);
+                if (a.v_mean_append != nullptr)
+                    for (int dd = tid; dd < D; dd += C::THREADS) {
+                        float* mu = a.v_mean_append + (size_t)group * D + dd;
+                        const double prev = n > 1 ? (double)(n - 1) * (double)*mu : 0.0;
+                        const double vn = (double)bf16_bits_to_f32(a.v[((size_t)group * a.Lmax + (n - 1)) * D + dd]);
+                        *mu = (float)((prev + vn) / (double)n);
+                    }
+            }
+            continue;
+        }
 
         // ---- the group's query rows to LDS
         {
@@ -337,6 +408,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
             }
         }
         __syncthreads();
+        // every read of the previous item's flag came before the barrier above;
+        // the first write of this item's comes after the next one
+        if (tid == 0) s_fail = 0;
 
         // ---- phase 1: scores of this wave's keys, kept in registers
         // K of the group goes from HBM straight into this wave's LDS stage
@@ -449,6 +523,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                 __hip_atomic_store(ml + (size_t)chunk * G, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             M = NEG_INF;
             L = 0.f;
+            bool failed = false;
             for (int c0 = 0; c0 < a.chunks; c0 += 4) {        // four slots in flight (the scores hold most registers)
                 unsigned long long v[4];
 #pragma unroll
@@ -459,7 +534,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     if (c0 + u < a.chunks) {
-                        const unsigned long long x = wait_slot64(ml + (size_t)(c0 + u) * G, v[u], a.spin_limit, a.status);
+                        const unsigned long long x =
+                            wait_slot64(ml + (size_t)(c0 + u) * G, v[u], spin_limit, a.status, failed);
                         const float m = __uint_as_float((unsigned)x), l = __uint_as_float((unsigned)(x >> 32));
                         if (l > 0.f) {
                             if (m > M) { L = L * exp2f(M - m) + l; M = m; }
@@ -468,6 +544,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                     }
                 }
             }
+            if (failed) s_fail = 1;
             const float lse2 = M + __log2f(L);
             const int h = kv * G + tid;
             const float th = a.theta[(size_t)h * a.n_rows + min(n - 1, a.n_rows - 1)];
@@ -609,6 +686,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                 }
             }
             lcount = ltotal;
+            // other lanes of this wave read the overflow weights back below:
+            // the stores must have completed first (fits is wave-uniform)
+            if (!fits) {
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                wait_vmem();
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            }
         }
         ucount = lcount;
         wait_lds();
@@ -825,18 +909,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
             if (tid == 0) {
                 int u = 0;
                 for (int w = 0; w < C::WAVES; ++w) u += s_un[w];
-                publish_i(a.part_union + pbase, u);
+                publish_i(a.part_union + pbase, s_fail ? -1 - u : u);
             }
         } else {
             // ---- chunk 0 combines, adding the partials in chunk order
             const bool renorm = (a.flags & 2u) != 0;
             const bool vmc = (a.flags & 1u) != 0 && !renorm;
             const size_t g0 = (size_t)group * a.chunks;
+            bool failed = false;
             if (tid < G) {
                 float m = 0.f; int c = 0;
                 for (int w = 0; w < C::WAVES; ++w) { m += s_cm[w][tid]; c += s_cc[w][tid]; }
-                m = gather_chunks(a.part_mass + g0 * G + tid, G, a.chunks, m, a.spin_limit, a.status);
-                c = gather_chunks(a.part_cnt + g0 * G + tid, G, a.chunks, c, a.spin_limit, a.status);
+                m = gather_chunks(a.part_mass + g0 * G + tid, G, a.chunks, m, spin_limit, a.status, failed);
+                c = gather_chunks(a.part_cnt + g0 * G + tid, G, a.chunks, c, spin_limit, a.status, failed);
                 // Eq. 4 scale of the kept softmax values and the Eq. 6 beta; the
                 // pre-softmax estimates of E~ relative to the full denominator:
                 // exp-threshold gamma (n - k~) e^(theta - lse), offline E~ e^(max - lse)
@@ -867,9 +952,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
             if (tid == 0) {
                 int u = 0;
                 for (int w = 0; w < C::WAVES; ++w) u += s_un[w];
-                u = gather_chunks(a.part_union + g0, 1, a.chunks, u, a.spin_limit, a.status);
+                u = gather_union(a.part_union + g0, a.chunks, u, spin_limit, a.status, failed);
                 if (a.vrows_read) a.vrows_read[group] = u;
             }
+            if (failed) s_fail = 1;
             // running mean of V (Sec. 3.2.2, kept during generation): rows
             // 0..n-2 had mean mu; with row n-1 appended it is
             // ((n-1) mu + V[n-1]) / n, formed in float64 like the stand-alone update
@@ -886,7 +972,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                 float x = 0.f;
 #pragma unroll
                 for (int w = 0; w < C::WAVES; ++w) x += (&s_red[w][0][0])[idx];
-                x = gather_chunks(a.part_out + g0 * G * D + idx, (size_t)G * D, a.chunks, x, a.spin_limit, a.status);
+                x = gather_chunks(a.part_out + g0 * G * D + idx, (size_t)G * D, a.chunks, x, spin_limit, a.status,
+                                  failed);
                 const float mass = s_cm[0][h];
                 if (renorm) x = (s_cc[0][h] > 0) ? x / mass : 0.f;
                 else if (a.flags & (kFlagExpth | kFlagOffline)) x *= s_T[h];
@@ -896,8 +983,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
             // every read of the previous mean happened before the barrier above
             if (mu_rw != nullptr)
                 for (int dd = tid; dd < D; dd += C::THREADS) mu_rw[(size_t)group * D + dd] = s_mu[dd];
+            if (failed) s_fail = 1;
         }
         __syncthreads();
+        // a wait of this group gave up (here, or in a chunk that flagged its
+        // union): its outputs are poisoned rather than left as partial sums
+        if (chunk == 0 && s_fail) poison_group<D, G>(a, b, kv, group, tid, C::THREADS);
     }
 #endif
 }
@@ -1021,10 +1112,6 @@ size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lmax, int d) {
     return bytes + 1024;
 }
 
-// Spin limit of the in-kernel exchange; a host test may lower it.
-static std::atomic<unsigned> g_spin_limit{1u << 22};
-void decode_set_spin_limit(unsigned v) { g_spin_limit.store(v, std::memory_order_relaxed); }
-
 int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     const int G = p.Hq / p.Hkv;
     const int groups = p.B * p.Hkv;
@@ -1085,7 +1172,6 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     a.chunks = chunks; a.items = items;
     a.xscale = p.scale * kLog2e;
     a.flags = p.flags;
-    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     a.xcd_map = (grid % (8 * chunks) == 0 && items % grid == 0) ? 1 : 0;
 
     return v.launch(grid, stream, a);

@@ -15,8 +15,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWave = 64;
 
-// Workspace: a header (status word at byte 0, the rest reserved), then the
-// decode exchange slots.  An empty slot holds kWsSlotEmpty in every 32-bit
+// Workspace: a header (status word at byte 0, spin limit at byte 4, the rest
+// reserved), then the decode exchange slots.  An empty slot holds kWsSlotEmpty in every 32-bit
 // word: a NaN payload that float arithmetic never produces (it returns the
 // default NaN 0x7FC00000) and no count or length reaches as an integer.
 constexpr size_t kWsHeaderBytes = 65536;

@@ -35,20 +35,48 @@
  *    work is enqueued asynchronously on it; nothing synchronises the host.
  *  - Errors: argument errors return a negative status before any GPU work
  *    is enqueued; a failed launch returns TOPTH_EHIP.  No C++ exception
- *    crosses this interface.  Calls are thread-safe.
+ *    crosses this interface.  A decode call that returns TOPTH_OK has been
+ *    enqueued; whether its cross-workgroup exchange completed on the GPU is
+ *    reported afterwards in the workspace (see "Workspace").
+ *  - Threads and global state: any host thread may call any entry point.  The
+ *    library's only process-wide state is a per-device cache of device
+ *    properties (CU count, resident workgroups per kernel), filled on first
+ *    use and never changed afterwards.
+ *  - GPU sharing: the key chunks of one decode call wait for each other, so a
+ *    decode call assumes that all of its workgroups are resident at once; it
+ *    sizes its grid to the whole GPU.  Run it with the GPU's compute units to
+ *    itself: work on other streams that holds compute units while a decode
+ *    call runs (another decode call included) can delay some of its chunks
+ *    past the bounded wait, and the affected groups then report poisoned
+ *    outputs (never silently wrong ones).
  *
  * Workspace
  * ---------
  *  Decode and calibration (and prefill with VMC) need a device workspace of
  *  at least topth_workspace_size(...) bytes.  Calibration and prefill use it
- *  as plain scratch.  Decode keeps a status word in its first
- *  TOPTH_WS_HEADER_BYTES and, after them, the slots through which the key
- *  chunks of one (batch, KV head) exchange partial results: a decode
- *  workspace must be prepared by topth_workspace_init before its first use,
- *  and every decode call that returns TOPTH_OK leaves it prepared again, so it
- *  serves any later decode call of any size up to its capacity.  A workspace
- *  that a calibration or prefill call has used must be prepared again before
- *  a decode call.  Two calls that overlap in time must not share a workspace.
+ *  as plain scratch.  Decode keeps a header of TOPTH_WS_HEADER_BYTES (32-bit
+ *  word 0: the status, word 1: the spin limit) and, after it, the slots
+ *  through which the key chunks of one (batch, KV head) exchange partial
+ *  results.  A decode workspace must be prepared by topth_workspace_init
+ *  before its first use; a decode call whose exchange completes leaves it
+ *  prepared again, so it serves any later decode call of any size up to its
+ *  capacity.  A workspace that a calibration or prefill call has used must be
+ *  prepared again before a decode call.  Two calls that overlap in time must
+ *  not share a workspace.
+ *
+ *  Exchange failures.  Every wait of the exchange is bounded (by default
+ *  about 4M polls of some 64 clocks each, about 0.1 s).  When one gives up,
+ *  the kernel still runs to its end, and
+ *    - the status word gets bit TOPTH_STATUS_EXCHANGE_TIMEOUT;
+ *    - every output of each (batch, KV head) group whose exchange did not
+ *      complete is poisoned: out and beta NaN, kept_count and vrows_read -1
+ *      (kept_mask entries are unspecified);
+ *    - slots may be left filled, so the workspace is no longer prepared:
+ *      while the status word is nonzero, every later decode call on it
+ *      poisons all of its outputs without reading the slots, until
+ *      topth_workspace_init prepares it again.
+ *  The running mean of topth_decode_append is updated in every case.  Read
+ *  the status with topth_workspace_status.
  */
 #ifndef TOPTH_H
 #define TOPTH_H
@@ -85,6 +113,7 @@ typedef enum { TOPTH_F32 = 0, TOPTH_BF16 = 1 } topth_dtype;
 #define TOPTH_OP_CALIBRATE_PRE_E 3   /* topth_calibrate_pre with esum != NULL */
 
 #define TOPTH_WS_HEADER_BYTES 65536
+#define TOPTH_STATUS_EXCHANGE_TIMEOUT 0x1   /* bit of the workspace status word */
 #define TOPTH_MAX_NK 8        /* most k values one calibration call can target */
 
 /* Human-readable text of a status code (static storage). */
@@ -105,9 +134,25 @@ const char* topth_strerror(int status);
 size_t topth_workspace_size(int op, int B, int Hq, int Hkv, int Lq, int Lk, int d, int n_k);
 
 /* Prepare a workspace (device, ws_bytes) on the stream: the header is zeroed
- * and every exchange slot after it marked empty.  Needed before the first
- * decode call that uses it (see "Workspace"). */
+ * (status 0, default spin limit) and every exchange slot after it marked
+ * empty.  Needed before the first decode call that uses it, and after a call
+ * that set the status (see "Workspace"). */
 int topth_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Status word of a decode workspace (0, or a combination of
+ * TOPTH_STATUS_EXCHANGE_TIMEOUT), as left by the work enqueued on the stream
+ * so far: the call waits for that work to finish (it synchronises the
+ * stream), then copies the word to *status (host).  ws device, ws_bytes >=
+ * TOPTH_WS_HEADER_BYTES. */
+int topth_workspace_status(const void* ws, size_t ws_bytes, int* status, void* stream);
+
+/* Number of polls an exchange wait of later decode calls on this workspace
+ * makes before it gives up; 0 restores the default.  Enqueued on the stream
+ * (no synchronisation); topth_workspace_init also restores the default.  A
+ * small limit makes waits give up whenever one chunk runs ahead of another,
+ * so the exchange-failure path can be exercised with every kernel still
+ * ending normally.  ws device, ws_bytes >= TOPTH_WS_HEADER_BYTES. */
+int topth_workspace_set_spin_limit(void* ws, size_t ws_bytes, unsigned limit, void* stream);
 
 /*
  * Calibration, Algorithm 1 of the paper adapted to post-softmax values

@@ -239,3 +239,14 @@ def test_decode_append_errors(lib):
     assert call(flags=0x10) == -1           # unknown flag
     assert call(d=96) == -1
     assert call(ws=None) == -3
+
+
+def test_workspace_status_and_spin_limit_errors(lib):
+    st = ctypes.c_int(5)
+    assert lib.topth_workspace_status(None, 1 << 20, ctypes.byref(st), None) == -1
+    assert lib.topth_workspace_status(FAKE, 1 << 20, None, None) == -1
+    assert lib.topth_workspace_status(FAKE, 1024, ctypes.byref(st), None) == -1   # smaller than the header
+    assert st.value == 5                                                          # untouched on error
+    assert lib.topth_workspace_set_spin_limit(None, 1 << 20, 1, None) == -1
+    assert lib.topth_workspace_set_spin_limit(FAKE, 100, 1, None) == -1
+    assert tt.TOPTH_WS_HEADER_BYTES == 65536 and tt.TOPTH_STATUS_EXCHANGE_TIMEOUT == 1
