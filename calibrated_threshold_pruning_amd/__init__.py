@@ -14,5 +14,5 @@ from ._lib import (  # noqa: F401
     topth_calibrate_finalize_etilde, topth_prefill_pre, topth_decode_pre,
     topth_vmean_append, topth_theta_fit, topth_theta_eval, topth_decode_gqa, topth_decode_append,
     TOPTH_WS_HEADER_BYTES, TOPTH_STATUS_EXCHANGE_TIMEOUT, topth_workspace_status,
-    topth_workspace_set_spin_limit,
+    topth_workspace_set_spin_limit, TOPTH_ESCRATCH, TOPTH_NOALLOC_SCRATCH_BYTES, topth_decode_noalloc,
 )

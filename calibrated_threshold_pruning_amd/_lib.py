@@ -23,13 +23,15 @@ TOPTH_OP_CALIBRATE, TOPTH_OP_PREFILL, TOPTH_OP_DECODE, TOPTH_OP_CALIBRATE_PRE_E 
 TOPTH_MAX_NK = 8
 TOPTH_WS_HEADER_BYTES = 65536
 TOPTH_STATUS_EXCHANGE_TIMEOUT = 0x1
+TOPTH_ESCRATCH = -5
+TOPTH_NOALLOC_SCRATCH_BYTES = 80 << 20
 
 EXPORTS = ("topth_strerror", "topth_workspace_size", "topth_workspace_init", "topth_calibrate",
            "topth_calibrate_finalize", "topth_prefill", "topth_decode", "topth_vmean",
            "topth_calibrate_pre", "topth_calibrate_finalize_etilde", "topth_prefill_pre",
            "topth_decode_pre", "topth_vmean_append", "topth_theta_fit", "topth_theta_eval",
            "topth_decode_gqa", "topth_decode_append", "topth_workspace_status",
-           "topth_workspace_set_spin_limit")
+           "topth_workspace_set_spin_limit", "topth_decode_noalloc")
 
 
 class TopthError(RuntimeError):
@@ -70,6 +72,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topth_decode.restype = i
     lib.topth_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, vp, u, vp, vp, vp, vp,
                                  vp, vp, sz, vp]
+    lib.topth_decode_noalloc.restype = i
+    lib.topth_decode_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, vp, u, vp, vp, vp, vp,
+                                         vp, vp]
     lib.topth_decode_append.restype = i
     lib.topth_decode_append.argtypes = list(lib.topth_decode.argtypes)
     lib.topth_vmean.restype = i
@@ -251,6 +256,30 @@ def topth_decode(q, k_cache, v_cache, seq_lens, theta, out, ws, *, scale: float,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv,
         Lmax, d, dt, float(scale), theta.data_ptr(), theta.shape[1], vm, int(flags),
         out.data_ptr(), kc, bt, vr, km, ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def topth_decode_noalloc(q, k_cache, v_cache, seq_lens, theta, out, *, scale: float, flags: int,
+                         v_mean=None, kept_count=None, beta=None, vrows_read=None, kept_mask=None,
+                         stream=None):
+    """topth_decode without a workspace: the library's static per-GPU scratch
+    serves instead (calls that overlap on one GPU race)."""
+    B, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    dt = _dtype_code(q)
+    _dev(q, "q"); _dev(k_cache, "k_cache", q.dtype, (B, Hkv, Lmax, d))
+    _dev(v_cache, "v_cache", q.dtype, (B, Hkv, Lmax, d))
+    _dev(seq_lens, "seq_lens", torch.int32, (B,))
+    _table(theta, "theta", Hq)
+    _dev(out, "out", q.dtype, (B, Hq, d))
+    vm = _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d), optional=True)
+    kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq), optional=True)
+    bt = _dev(beta, "beta", torch.float32, (B, Hq), optional=True)
+    vr = _dev(vrows_read, "vrows_read", torch.int32, (B, Hkv), optional=True)
+    km = _dev(kept_mask, "kept_mask", torch.uint8, (B, Hq, Lmax), optional=True)
+    _check("topth_decode_noalloc", load_library().topth_decode_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv,
+        Lmax, d, dt, float(scale), theta.data_ptr(), theta.shape[1], vm, int(flags),
+        out.data_ptr(), kc, bt, vr, km, _stream(stream)))
 
 
 def topth_decode_append(q, k_cache, v_cache, seq_lens, theta, out, ws, v_mean, *, scale: float, flags: int,

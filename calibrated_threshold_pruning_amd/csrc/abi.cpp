@@ -11,6 +11,9 @@ namespace topth {
 // defined in the kernel sources
 bool decode_bf16_supported(int d, int G);
 int launch_decode_bf16(const DecodeParams& p, hipStream_t s);
+int launch_decode_bf16_noalloc(DecodeParams p, bool* fits, hipStream_t s);
+int noalloc_scratch(void** out);
+size_t noalloc_scratch_bytes();
 int launch_decode_rowwise(const DecodeParams& p, uint32_t* masks_ws, hipStream_t s);
 size_t decode_rowwise_ws_bytes(int B, int Hq, int Lmax);
 int rowwise_max_keys();
@@ -30,6 +33,10 @@ int launch_theta_eval(const double* coef, const int* ks, int n_k, int Hq, int de
 }  // namespace topth
 
 using namespace topth;
+
+static_assert(kNoallocScratchBytes == (size_t)TOPTH_NOALLOC_SCRATCH_BYTES, "scratch size of the header");
+static_assert(kWsHeaderBytes == TOPTH_WS_HEADER_BYTES && kStatusSpinTimeout == TOPTH_STATUS_EXCHANGE_TIMEOUT,
+              "workspace header layout of the header");
 
 namespace {
 
@@ -90,6 +97,7 @@ const char* topth_strerror(int status) {
         case TOPTH_EUNSUPPORTED: return "unsupported shape or type";
         case TOPTH_EWORKSPACE: return "workspace missing or too small";
         case TOPTH_EHIP: return "HIP runtime error";
+        case TOPTH_ESCRATCH: return "shape needs more scratch than the library's static device buffer holds";
         default: return "unknown status";
     }
 }
@@ -331,6 +339,40 @@ int topth_decode_append(const void* q, const void* k_cache, const void* v_cache,
     return decode_common(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Lmax, d, dtype, scale, theta,
                          n_rows, v_mean, flags, out, kept_count, beta, vrows_read, kept_mask, ws,
                          ws_bytes, stream, false, nullptr, 0.f, 1, 0, v_mean);
+}
+
+int topth_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                         int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                         const float* theta, int n_rows, const float* v_mean, unsigned flags,
+                         void* out, int* kept_count, float* beta, int* vrows_read,
+                         unsigned char* kept_mask, void* stream) {
+    // the argument checks of topth_decode, with a workspace that always passes
+    // them; the scratch size is checked against the call's own plan below
+    if (!q || !k_cache || !v_cache || !seq_lens || !theta || !out) return TOPTH_EINVAL;
+    if (bad_dims(B, Hq, Hkv, Lmax, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
+    if (!isfinite(scale) || !(scale > 0.0f)) return TOPTH_EINVAL;
+    if ((flags & ~(TOPTH_VMC | TOPTH_SDC_NONE)) != 0) return TOPTH_EINVAL;
+    if ((flags & TOPTH_VMC) && !(flags & TOPTH_SDC_NONE) && !v_mean) return TOPTH_EINVAL;
+    if (too_big((long long)B * Hkv * Lmax, d)) return TOPTH_EUNSUPPORTED;
+    DecodeParams p = {};
+    p.q = q; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lmax = Lmax; p.d = d; p.dtype = dtype; p.scale = scale;
+    p.theta = theta; p.n_rows = n_rows; p.v_mean = v_mean; p.flags = flags;
+    p.out = out; p.kept_count = kept_count; p.beta = beta; p.vrows_read = vrows_read;
+    p.kept_mask = kept_mask; p.min_votes = 1; p.augment = 0;
+    if (dtype == TOPTH_BF16) {
+        if (!decode_bf16_supported(d, Hq / Hkv) || (long long)Lmax * d * 2 >= INT_MAX) return TOPTH_EUNSUPPORTED;
+        bool fits = false;
+        const int e = launch_decode_bf16_noalloc(p, &fits, (hipStream_t)stream);
+        if (e != 0) return TOPTH_EHIP;
+        return fits ? TOPTH_OK : TOPTH_ESCRATCH;
+    }
+    if (Lmax > rowwise_max_keys()) return TOPTH_EUNSUPPORTED;
+    // the float32 path writes its mask words before it reads them: nothing to prepare
+    if (kWsHeaderBytes + decode_rowwise_ws_bytes(B, Hq, Lmax) > noalloc_scratch_bytes()) return TOPTH_ESCRATCH;
+    void* ws = nullptr;
+    if (noalloc_scratch(&ws) != 0) return TOPTH_EHIP;
+    return map_hip(launch_decode_rowwise(p, (uint32_t*)((char*)ws + kWsHeaderBytes), (hipStream_t)stream));
 }
 
 int topth_decode_pre(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,

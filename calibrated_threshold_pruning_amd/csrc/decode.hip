@@ -993,10 +993,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
 #endif
 }
 
+// Workspace of topth_decode_noalloc (for callers that cannot allocate): a
+// static device array, one copy per GPU, large enough for the long-context
+// shapes (batch 8 x 8 KV heads x 32768 keys at group size 8 needs 68 MiB).
+constexpr size_t kScratchBytes = kNoallocScratchBytes;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 // ------------------------------------------------------------------ host side
 }  // namespace topth
 
 #include <atomic>
+#include <mutex>
 
 namespace topth {
 
@@ -1112,7 +1119,17 @@ size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lmax, int d) {
     return bytes + 1024;
 }
 
-int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
+// Launch plan of one decode call: the kernel variant, the grid and where the
+// exchange slots and overflow weights sit in the workspace.
+struct DecodePlan {
+    Variant v;
+    int chunks, items, grid;
+    size_t off_ml, off_out, off_mass, off_cnt, off_union, off_ovf;
+    size_t slots_end;      // end of the header and exchange slots (the part that must be prepared)
+    size_t ws_end;         // bytes of workspace the call uses
+};
+
+int plan_decode_bf16(const DecodeParams& p, DecodePlan* plan) {
     const int G = p.Hq / p.Hkv;
     const int groups = p.B * p.Hkv;
     int dev = 0;
@@ -1145,11 +1162,34 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
         if ((long long)chunks * groups <= capacity) break;
     }
     if (capacity <= 0 || chunks > capacity) return hipErrorInvalidConfiguration;
-    const int items = chunks * groups;
-    const int grid = std::min(items, (capacity / chunks) * chunks);
+    plan->v = v;
+    plan->chunks = chunks;
+    plan->items = chunks * groups;
+    plan->grid = std::min(plan->items, (capacity / chunks) * chunks);
 
-    // workspace carve-up (the header holds the status word)
+    // workspace carve-up (the header holds the status word and the spin limit)
+    const size_t pc = (size_t)plan->items;
+    size_t off = kWsHeaderBytes;
+    plan->off_ml = off; off += pc * G * sizeof(unsigned long long);
+    plan->off_out = off; off += pc * G * p.d * sizeof(float);
+    plan->off_mass = off; off += pc * G * sizeof(float);
+    plan->off_cnt = off; off += pc * G * sizeof(int);
+    plan->off_union = off; off += pc * sizeof(int);
+    plan->slots_end = off;
+    off = (off + 255) & ~(size_t)255;
+    plan->off_ovf = off; off += (size_t)groups * p.Lmax * (G < 4 ? 4 : G) * sizeof(float);
+    plan->ws_end = off;
+    return hipSuccess;
+}
+
+int launch_decode_bf16_planned(const DecodeParams& p, const DecodePlan& plan, bool prepare, hipStream_t stream) {
+    if (plan.ws_end > p.ws_bytes) return hipErrorInvalidValue;
     char* ws = (char*)p.ws;
+    if (prepare) {
+        // header zero, exchange slots empty: what a prepared workspace holds
+        int e = launch_ws_prepare(ws, kWsHeaderBytes, plan.slots_end, stream);
+        if (e != hipSuccess) return e;
+    }
     DecodeKArgs a = {};
     a.q = (const uint16_t*)p.q; a.k = (const uint16_t*)p.k; a.v = (const uint16_t*)p.v;
     a.seq_lens = p.seq_lens; a.theta = p.theta; a.v_mean = p.v_mean; a.v_mean_append = p.v_mean_append;
@@ -1158,23 +1198,70 @@ int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
     a.out = (uint16_t*)p.out; a.kept_count = p.kept_count; a.beta = p.beta; a.vrows_read = p.vrows_read;
     a.kept_mask = p.kept_mask;
     a.status = (int*)ws;
-    size_t off = kWsHeaderBytes;
-    const size_t pc = (size_t)items;
-    a.part_ml = (unsigned long long*)(ws + off); off += pc * G * sizeof(unsigned long long);
-    a.part_out = (float*)(ws + off); off += pc * G * p.d * sizeof(float);
-    a.part_mass = (float*)(ws + off); off += pc * G * sizeof(float);
-    a.part_cnt = (int*)(ws + off); off += pc * G * sizeof(int);
-    a.part_union = (int*)(ws + off); off += pc * sizeof(int);
-    off = (off + 255) & ~(size_t)255;
-    a.ovf_w = (float*)(ws + off); off += (size_t)groups * p.Lmax * (G < 4 ? 4 : G) * sizeof(float);
-    if (off > p.ws_bytes) return hipErrorInvalidValue;
+    a.part_ml = (unsigned long long*)(ws + plan.off_ml);
+    a.part_out = (float*)(ws + plan.off_out);
+    a.part_mass = (float*)(ws + plan.off_mass);
+    a.part_cnt = (int*)(ws + plan.off_cnt);
+    a.part_union = (int*)(ws + plan.off_union);
+    a.ovf_w = (float*)(ws + plan.off_ovf);
     a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Lmax = p.Lmax; a.n_rows = p.n_rows;
-    a.chunks = chunks; a.items = items;
+    a.chunks = plan.chunks; a.items = plan.items;
     a.xscale = p.scale * kLog2e;
     a.flags = p.flags;
-    a.xcd_map = (grid % (8 * chunks) == 0 && items % grid == 0) ? 1 : 0;
-
-    return v.launch(grid, stream, a);
+    a.xcd_map = (plan.grid % (8 * plan.chunks) == 0 && plan.items % plan.grid == 0) ? 1 : 0;
+    return plan.v.launch(plan.grid, stream, a);
 }
+
+int launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
+    DecodePlan plan;
+    const int e = plan_decode_bf16(p, &plan);
+    if (e != hipSuccess) return e;
+    return launch_decode_bf16_planned(p, plan, false, stream);
+}
+
+// ------------------------------------------------------------ no-allocation
+// topth_decode_noalloc takes its workspace from `scratch`, one copy per GPU
+// (held until the process ends).  In host code the array's name is only a
+// stand-in: its device address on the current GPU comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+std::mutex g_scratch_mu;
+void* g_scratch_addr[16] = {};
+
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
+
+size_t noalloc_scratch_bytes() { return kScratchBytes; }
+
+// Plans the call, checks that it fits the scratch (*fits = false otherwise,
+// nothing enqueued), then prepares the header and slots of this call's layout
+// and launches.  Every call prepares them anew, so a call whose exchange gave
+// up leaves nothing that a later call reads.
+int launch_decode_bf16_noalloc(DecodeParams p, bool* fits, hipStream_t stream) {
+    DecodePlan plan;
+    int e = plan_decode_bf16(p, &plan);
+    if (e != hipSuccess) return e;
+    *fits = plan.ws_end <= kScratchBytes;
+    if (!*fits) return hipSuccess;
+    e = scratch_address(&p.ws);
+    if (e != hipSuccess) return e;
+    p.ws_bytes = kScratchBytes;
+    return launch_decode_bf16_planned(p, plan, true, stream);
+}
+
+int noalloc_scratch(void** out) { return scratch_address(out); }
 
 }  // namespace topth

@@ -464,6 +464,14 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n_words, uint32_t value) {
         p[i] = value;
 }
 
+// a decode workspace as topth_workspace_init leaves it, up to `end_words`:
+// the header words zero, the exchange slots after them empty
+__global__ void ws_prepare_kernel(uint32_t* p, size_t header_words, size_t end_words) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < end_words;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = i < header_words ? 0u : kWsSlotEmpty;
+}
+
 // ------------------------------------------------------------------ launchers
 template <typename T, int D, int MODE>
 static int launch_rows(const RowArgs& a, int rows, int smem_floats, hipStream_t s) {
@@ -619,6 +627,15 @@ int launch_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, i
         if (d == 64) hipLaunchKernelGGL((vmean_kernel<uint16_t, 64>), grid, block, 0, s, (const uint16_t*)v, seq_lens, Hkv, Lmax, v_mean);
         else hipLaunchKernelGGL((vmean_kernel<uint16_t, 128>), grid, block, 0, s, (const uint16_t*)v, seq_lens, Hkv, Lmax, v_mean);
     }
+    return hipGetLastError();
+}
+
+int launch_ws_prepare(void* ws, size_t header_bytes, size_t end_bytes, hipStream_t s) {
+    const size_t words = end_bytes / 4;
+    if (words == 0) return hipSuccess;
+    unsigned blocks = (unsigned)((words + 255) / 256);
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(ws_prepare_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)ws, header_bytes / 4, words);
     return hipGetLastError();
 }
 

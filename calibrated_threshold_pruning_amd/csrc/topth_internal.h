@@ -22,6 +22,8 @@ constexpr int kWave = 64;
 constexpr size_t kWsHeaderBytes = 65536;
 constexpr uint32_t kWsSlotEmpty = 0x7FC0DEADu;
 constexpr int kStatusSpinTimeout = 1;
+// static device scratch of the no-allocation decode entry point, per GPU
+constexpr size_t kNoallocScratchBytes = (size_t)80 << 20;
 
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
@@ -153,5 +155,6 @@ int launch_finalize_etilde(const double* esum, const int* count, const int* ks, 
 int launch_vmean(const void* v, const int* seq_lens, int B, int Hkv, int Lmax, int d, int dtype,
                  float* v_mean, hipStream_t s);
 int launch_fill_u32(void* p, size_t bytes, uint32_t value, hipStream_t s);
+int launch_ws_prepare(void* ws, size_t header_bytes, size_t end_bytes, hipStream_t s);
 
 }  // namespace topth

@@ -92,7 +92,9 @@ typedef enum {
     TOPTH_EINVAL = -1,        /* NULL pointer, bad size or inconsistent shape   */
     TOPTH_EUNSUPPORTED = -2,  /* valid but not implemented (d, dtype, g, size)  */
     TOPTH_EWORKSPACE = -3,    /* workspace NULL or smaller than required        */
-    TOPTH_EHIP = -4           /* a HIP runtime call or kernel launch failed     */
+    TOPTH_EHIP = -4,          /* a HIP runtime call or kernel launch failed     */
+    TOPTH_ESCRATCH = -5       /* topth_decode_noalloc: the shape needs more than
+                                 its static scratch (TOPTH_NOALLOC_SCRATCH_BYTES) */
 } topth_status;
 
 typedef enum { TOPTH_F32 = 0, TOPTH_BF16 = 1 } topth_dtype;
@@ -115,6 +117,7 @@ typedef enum { TOPTH_F32 = 0, TOPTH_BF16 = 1 } topth_dtype;
 #define TOPTH_WS_HEADER_BYTES 65536
 #define TOPTH_STATUS_EXCHANGE_TIMEOUT 0x1   /* bit of the workspace status word */
 #define TOPTH_MAX_NK 8        /* most k values one calibration call can target */
+#define TOPTH_NOALLOC_SCRATCH_BYTES (80u << 20)   /* static scratch of topth_decode_noalloc, per GPU */
 
 /* Human-readable text of a status code (static storage). */
 const char* topth_strerror(int status);
@@ -236,6 +239,30 @@ int topth_decode(const void* q, const void* k_cache, const void* v_cache, const 
                  const float* theta, int n_rows, const float* v_mean, unsigned flags,
                  void* out, int* kept_count, float* beta, int* vrows_read,
                  unsigned char* kept_mask, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * topth_decode for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Arguments, results, flags and errors as
+ * topth_decode, without ws / ws_bytes.  The call allocates nothing: its
+ * workspace is a static device array of TOPTH_NOALLOC_SCRATCH_BYTES (80 MiB)
+ * inside the library, one copy on each GPU the library runs on, held until
+ * the process ends.  Each call enqueues a small kernel that prepares the part
+ * of the array it uses (header zero, exchange slots empty), then the decode
+ * kernels, so nothing a previous call left there is read; an exchange that
+ * gives up shows only as poisoned outputs of the affected groups (see
+ * "Exchange failures").  Shapes whose workspace would exceed the array (the
+ * exchange slots plus 4 * max(g, 4) bytes per cached key of every (batch,
+ * KV head); batch 8 x 8 KV heads x 32768 keys at g = 8 needs 68 MiB) return
+ * TOPTH_ESCRATCH before anything is enqueued.  All calls on one GPU share the
+ * array: calls that overlap in time on that GPU (on different streams, or
+ * from different host threads) race and may return wrong results.
+ */
+int topth_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                         int B, int Hq, int Hkv, int Lmax, int d, int dtype, float scale,
+                         const float* theta, int n_rows, const float* v_mean, unsigned flags,
+                         void* out, int* kept_count, float* beta, int* vrows_read,
+                         unsigned char* kept_mask, void* stream);
 
 /*
  * Mean of the first n = seq_lens[b] V rows of each (b, kv head): the mu of
