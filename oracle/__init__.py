@@ -23,6 +23,11 @@ KV-cache appends, thresholds fitted to the row position) and the GQA selection
 variants of Sec. 4.6, pinned by ``tests/test_oracle_serving_pins.py``; the
 fitted function's form is a reading the pages do not fix (parity unpinned for
 that choice).
+
+``oracle.mkc`` holds multi-k cumulative calibration (Appendix D, Algorithm 2,
+Eq. 8), pinned by ``tests/test_oracle_mkc_pins.py``: single-sample and
+identical-copy closed forms, the pooled-quantile closed form where every
+sample covers theta, and brute force over explicit interval lists.
 """
 from .topth import (  # noqa: F401
     scores, post_softmax, kth_largest, theta_row, row_weights, row_output, topth_row,
@@ -31,3 +36,4 @@ from .topth import (  # noqa: F401
 )
 from . import presoftmax  # noqa: F401,E402
 from . import serving  # noqa: F401,E402
+from . import mkc  # noqa: F401,E402

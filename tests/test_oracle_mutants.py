@@ -10,14 +10,16 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.mkc as M
 import oracle.presoftmax as P
 import oracle.serving as S
 import oracle.topth as T
+import test_oracle_mkc_pins
 import test_oracle_pins
 import test_oracle_presoftmax_pins
 import test_oracle_serving_pins
 
-PIN_MODULES = (test_oracle_pins, test_oracle_presoftmax_pins, test_oracle_serving_pins)
+PIN_MODULES = (test_oracle_pins, test_oracle_presoftmax_pins, test_oracle_serving_pins, test_oracle_mkc_pins)
 
 
 def _param_sets(fn):
@@ -55,7 +57,7 @@ def _patch(monkeypatch, module, name, make):
     """Replace `name` in `module` and wherever the oracle re-exports the same object."""
     orig = getattr(module, name)
     new = make(orig)
-    for mod in (oracle, T, P, S):
+    for mod in (oracle, T, P, S, M):
         if getattr(mod, name, None) is orig:
             monkeypatch.setattr(mod, name, new)
 
@@ -84,7 +86,48 @@ def _calib_n_minus_one(orig):
     return finalize
 
 
+def _kbar_strict(orig):
+    # the intervals of Appendix D as printed, [v_i, v_{i+1}) with the count of
+    # elements strictly greater than theta, in place of the >= reading
+    def merged_kbar(sorted_samples, thetas):
+        thetas = np.asarray(thetas, dtype=np.float64)
+        total, cov = np.zeros(thetas.shape), np.zeros(thetas.shape)
+        for v in sorted_samples:
+            inside = (v[0] <= thetas) & (thetas < v[-1])
+            total += np.where(inside, v.size - np.searchsorted(v, thetas, side="right"), 0)
+            cov += inside
+        return np.where(cov > 0, total / np.maximum(cov, 1), np.nan)
+    return merged_kbar
+
+
+def _kbar_every_sample(orig):
+    # samples that do not cover theta counted with what they keep (0 above
+    # their range, all below it) instead of being left out of Eq. 8's mean
+    def merged_kbar(sorted_samples, thetas):
+        thetas = np.asarray(thetas, dtype=np.float64)
+        return sum(v.size - np.searchsorted(v, thetas, side="left") for v in sorted_samples) / len(sorted_samples)
+    return merged_kbar
+
+
+def _inverse_smallest(orig):
+    # the smallest qualifying threshold instead of the largest
+    def theta_of_ks(samples, ks):
+        srt = [M.sample_intervals(s) for s in samples]
+        cands = np.unique(np.concatenate(srt))
+        kb = M.merged_kbar(srt, cands)
+        out = np.full(len(ks), -np.inf)
+        for t, k in enumerate(ks):
+            ok = np.flatnonzero(kb >= k)
+            if ok.size:
+                out[t] = cands[ok[0]]
+        return out
+    return theta_of_ks
+
+
 MUTANTS = {
+    "MKC effective k counts elements above theta only": (M, "merged_kbar", _kbar_strict),
+    "MKC mean over every sample, covering or not": (M, "merged_kbar", _kbar_every_sample),
+    "MKC inverse takes the smallest qualifying theta": (M, "theta_of_ks", _inverse_smallest),
     "score scale dropped": (T, "scores", lambda o: (lambda q, K, scale: o(q, K, 1.0))),
     "softmax over one unmasked padding score of 0": (T, "post_softmax", _softmax_with_padding),
     "k-th largest off by one": (T, "kth_largest", _kth_off_by_one),
