@@ -20,6 +20,8 @@ TOPTH_F32, TOPTH_BF16 = 0, 1
 TOPTH_VMC, TOPTH_SDC_NONE = 0x1, 0x2
 TOPTH_SDC_EXPTH, TOPTH_SDC_OFFLINE = 0x4, 0x8
 TOPTH_OP_CALIBRATE, TOPTH_OP_PREFILL, TOPTH_OP_DECODE, TOPTH_OP_CALIBRATE_PRE_E = 0, 1, 2, 3
+TOPTH_OP_CALIBRATE_MKC = 4
+TOPTH_MKC_MAX_TARGETS, TOPTH_MKC_MAX_SAMPLES, TOPTH_MKC_MAX_KEYS = 64, 4096, 32768
 TOPTH_MAX_NK = 8
 TOPTH_WS_HEADER_BYTES = 65536
 TOPTH_STATUS_EXCHANGE_TIMEOUT = 0x1
@@ -31,7 +33,7 @@ EXPORTS = ("topth_strerror", "topth_workspace_size", "topth_workspace_init", "to
            "topth_calibrate_pre", "topth_calibrate_finalize_etilde", "topth_prefill_pre",
            "topth_decode_pre", "topth_vmean_append", "topth_theta_fit", "topth_theta_eval",
            "topth_decode_gqa", "topth_decode_append", "topth_workspace_status",
-           "topth_workspace_set_spin_limit", "topth_decode_noalloc")
+           "topth_workspace_set_spin_limit", "topth_decode_noalloc", "topth_calibrate_mkc")
 
 
 class TopthError(RuntimeError):
@@ -65,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topth_workspace_set_spin_limit.argtypes = [vp, sz, u, vp]
     lib.topth_calibrate.restype = i
     lib.topth_calibrate.argtypes = [vp, vp, i, i, i, i, i, i, i, f, i, vp, i, vp, vp, vp, i, vp, sz, vp]
+    lib.topth_calibrate_mkc.restype = i
+    lib.topth_calibrate_mkc.argtypes = [vp, vp, i, i, i, i, i, i, i, f, i, i, vp, i, vp, i, vp, sz, vp]
     lib.topth_calibrate_finalize.restype = i
     lib.topth_calibrate_finalize.argtypes = [vp, vp, vp, vp, i, i, i, f, vp, vp]
     lib.topth_prefill.restype = i
@@ -201,6 +205,27 @@ def topth_calibrate(q, k, ks, sum_, sumsq, count, ws, *, scale: float, q_pos0: i
         q.data_ptr(), k.data_ptr(), S, Hq, Hkv, Lq, Lk, d, dt, float(scale), int(q_pos0),
         ctypes.cast(karr, ctypes.c_void_p), n_k, sum_.data_ptr(), sumsq.data_ptr(),
         count.data_ptr(), n_rows, ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def topth_calibrate_mkc(q, k, ks, theta, ws, *, scale: float, q_pos0: int = 0, pre: bool = False,
+                        stream=None):
+    """Multi-k cumulative calibration of all S sequences at once: q [S,Hq,Lq,d],
+    k [S,Hkv,Lk,d]; theta [n_k,Hq,n_rows] float32 gets theta_p(ks[t]) at rows
+    p = q_pos0 .. q_pos0 + Lq - 1."""
+    S, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    _dev(q, "q"); _dev(k, "k", q.dtype, (S, Hkv, Lk, d))
+    n_k = len(ks)
+    _dev(theta, "theta", torch.float32)
+    if theta.dim() != 3 or tuple(theta.shape[:2]) != (n_k, Hq):
+        raise ValueError("theta must be [n_k, Hq, n_rows]")
+    _dev(ws, "ws", torch.uint8)
+    karr = (ctypes.c_int * max(n_k, 1))(*[int(x) for x in ks])
+    _check("topth_calibrate_mkc", load_library().topth_calibrate_mkc(
+        q.data_ptr(), k.data_ptr(), S, Hq, Hkv, Lq, Lk, d, dt, float(scale), int(q_pos0), int(bool(pre)),
+        ctypes.cast(karr, ctypes.c_void_p), n_k, theta.data_ptr(), theta.shape[2], ws.data_ptr(), ws.numel(),
+        _stream(stream)))
 
 
 def topth_calibrate_finalize(sum_, sumsq, count, ks, theta, *, alpha: float = 0.0, stream=None):

@@ -20,7 +20,7 @@ OBJDIR = os.path.join(ROOT, "_build", "topth")
 LIB = os.path.join(PKG, "libtopth.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "rowwise.hip", "decode.hip", "prefill.hip", "calib.hip", "serving.hip"]
+SOURCES = ["abi.cpp", "rowwise.hip", "decode.hip", "prefill.hip", "calib.hip", "serving.hip", "mkc.hip"]
 
 # Packed fp32 VALU instructions are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -24,6 +24,11 @@ int launch_calibrate_rowwise(const CalibParams& p, float* samples_ws, hipStream_
 bool calib_bf16_supported(int d, int S, int Hq, int Lq, int q_pos0);
 int launch_calibrate_bf16(const CalibParams& p, float* samples_ws, hipStream_t s);
 int max_fit_degree();
+size_t mkc_ws_bytes(int S, int Hq, int Lq, int Lk);
+int mkc_max_samples();
+int mkc_max_targets();
+int mkc_max_keys();
+int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_t s);
 int launch_vmean_append(const void* v, const int* old_lens, const int* new_lens, int B, int Hkv, int Lmax,
                         int d, int dtype, float* v_mean, hipStream_t s);
 int launch_theta_fit(const float* theta, const int* count, int n_k, int Hq, int n_rows, int degree,
@@ -116,6 +121,10 @@ size_t topth_workspace_size(int op, int B, int Hq, int Hkv, int Lq, int Lk, int 
         case TOPTH_OP_DECODE:
             if (bad_dims(B, Hq, Hkv, Lk, d)) return 0;
             return decode_ws(B, Hq, Hkv, Lk, d);
+        case TOPTH_OP_CALIBRATE_MKC:
+            if (bad_dims(B, Hq, Hkv, Lq, d) || Lk <= 0 || Lq > Lk || B > mkc_max_samples() || Lk > mkc_max_keys())
+                return 0;
+            return mkc_ws_bytes(B, Hq, Lq, Lk);
         default:
             return 0;
     }
@@ -196,6 +205,27 @@ int topth_calibrate_pre(const void* q, const void* k, int S, int Hq, int Hkv, in
                         void* ws, size_t ws_bytes, void* stream) {
     return calibrate_common(q, k, S, Hq, Hkv, Lq, Lk, d, dtype, scale, q_pos0, ks, n_k, sum, sumsq,
                             count, n_rows, ws, ws_bytes, stream, true, esum);
+}
+
+int topth_calibrate_mkc(const void* q, const void* k, int S, int Hq, int Hkv, int Lq, int Lk, int d,
+                        int dtype, float scale, int q_pos0, int pre, const int* ks, int n_k,
+                        float* theta, int n_rows, void* ws, size_t ws_bytes, void* stream) {
+    if (!q || !k || !ks || !theta) return TOPTH_EINVAL;
+    if (bad_dims(S, Hq, Hkv, Lq, d) || bad_dtype(dtype) || Lk <= 0 || n_rows <= 0) return TOPTH_EINVAL;
+    if (!isfinite(scale) || !(scale > 0.0f) || q_pos0 < 0 || q_pos0 + Lq > Lk) return TOPTH_EINVAL;
+    if (pre != 0 && pre != 1) return TOPTH_EINVAL;
+    if (n_k < 1 || n_k > mkc_max_targets()) return TOPTH_EINVAL;
+    for (int t = 0; t < n_k; ++t)
+        if (ks[t] < 1) return TOPTH_EINVAL;
+    if (S > mkc_max_samples() || Lk > mkc_max_keys()) return TOPTH_EUNSUPPORTED;
+    if ((long long)S * Hq * Lq > INT_MAX || (long long)Hq * Lq > INT_MAX) return TOPTH_EUNSUPPORTED;
+    if (!ws) return TOPTH_EWORKSPACE;
+    if (ws_bytes < mkc_ws_bytes(S, Hq, Lq, Lk)) return TOPTH_EWORKSPACE;
+    CalibParams p = {};
+    p.q = q; p.k = k; p.S = S; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk; p.d = d;
+    p.dtype = dtype; p.scale = scale; p.q_pos0 = q_pos0; p.n_k = n_k; p.mkc_ks = ks;
+    p.n_rows = n_rows; p.ws = ws; p.ws_bytes = ws_bytes;
+    return map_hip(launch_calibrate_mkc(p, pre, theta, (hipStream_t)stream));
 }
 
 int topth_calibrate_finalize_etilde(const double* esum, const int* count, const int* ks, int n_k,

@@ -139,6 +139,7 @@ struct CalibParams {
     double* sum; double* sumsq; int* count; int n_rows;
     void* ws; size_t ws_bytes;
     bool pre; double* esum;               // pre-softmax samples; E~ sums or NULL
+    const int* mkc_ks;                    // multi-k calibration: host [n_k] target k (n_k <= 64)
 };
 
 // Each launcher validates nothing (the ABI layer did) and returns a hipError_t.

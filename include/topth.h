@@ -113,10 +113,14 @@ typedef enum { TOPTH_F32 = 0, TOPTH_BF16 = 1 } topth_dtype;
 #define TOPTH_OP_PREFILL   1
 #define TOPTH_OP_DECODE    2
 #define TOPTH_OP_CALIBRATE_PRE_E 3   /* topth_calibrate_pre with esum != NULL */
+#define TOPTH_OP_CALIBRATE_MKC 4     /* topth_calibrate_mkc */
 
 #define TOPTH_WS_HEADER_BYTES 65536
 #define TOPTH_STATUS_EXCHANGE_TIMEOUT 0x1   /* bit of the workspace status word */
 #define TOPTH_MAX_NK 8        /* most k values one calibration call can target */
+#define TOPTH_MKC_MAX_TARGETS 64     /* most k values one topth_calibrate_mkc call returns */
+#define TOPTH_MKC_MAX_SAMPLES 4096   /* most calibration sequences of one topth_calibrate_mkc call */
+#define TOPTH_MKC_MAX_KEYS 32768     /* longest key range of topth_calibrate_mkc */
 #define TOPTH_NOALLOC_SCRATCH_BYTES (80u << 20)   /* static scratch of topth_decode_noalloc, per GPU */
 
 /* Human-readable text of a status code (static storage). */
@@ -131,6 +135,7 @@ const char* topth_strerror(int status);
  *   TOPTH_OP_CALIBRATE_PRE_E: as TOPTH_OP_CALIBRATE (topth_calibrate_pre also
  *                       collecting the discarded mass; without it, the
  *                       TOPTH_OP_CALIBRATE size serves)
+ *   TOPTH_OP_CALIBRATE_MKC: B = sequences S, Hq, Hkv, Lq, Lk, d (n_k ignored)
  *   TOPTH_OP_PREFILL and TOPTH_OP_DECODE sizes serve the _pre calls too.
  * Returns 0 for arguments no call could accept.
  */
@@ -178,6 +183,37 @@ int topth_calibrate(const void* q, const void* k, int S, int Hq, int Hkv, int Lq
                     int d, int dtype, float scale, int q_pos0, const int* ks, int n_k,
                     double* sum, double* sumsq, int* count, int n_rows,
                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Multi-k cumulative calibration (Appendix D, Algorithm 2 and Eq. 8): instead
+ * of one threshold per target k, the S calibration samples of a row are
+ * merged into kbar(theta), the mean over the samples whose value range
+ * contains theta of the number of elements theta keeps, and theta(k) is read
+ * back for any k.  For every query head h and query row i (position
+ * p = q_pos0 + i, keys 0..p, m = p + 1 values per sample) and every target
+ * ks[t]:
+ *   theta[t][h][p] = max { theta : kbar(theta) >= ks[t] },
+ * a sample value (the k-th largest value when S = 1), or -INFINITY (keep all)
+ * where kbar never reaches ks[t] (always when ks[t] >= m).  A sample's range
+ * is (its minimum, its maximum] and it keeps #{v >= theta} (the >= of every
+ * compare in this library; the paper writes the count of elements greater
+ * than theta).  Values are post-softmax s (pre = 0) or the scores
+ * a = scale * q.k (pre = 1).  Rows p >= n_rows are not written; other rows of
+ * theta are left as they are.  MKC needs every sample of a row at once, so
+ * all S sequences come in one call (a long prefill can be calibrated in
+ * slices of rows with q_pos0).
+ *   q device [S][Hq][Lq][d], k device [S][Hkv][Lk][d]; 1 <= S <=
+ *   TOPTH_MKC_MAX_SAMPLES, Lk <= TOPTH_MKC_MAX_KEYS, q_pos0 + Lq <= Lk;
+ *   ks host [n_k], 1 <= n_k <= TOPTH_MKC_MAX_TARGETS, ks[t] >= 1;
+ *   theta device float [n_k][Hq][n_rows];
+ *   ws device, topth_workspace_size(TOPTH_OP_CALIBRATE_MKC, S, Hq, Hkv, Lq,
+ *   Lk, d, 0) bytes (the pooled values twice: 8 * S * Hq * Lq * Lk bytes).
+ * Results are exact for the float32 values the kernels compute (integer
+ * counts over a sort), so they do not vary from launch to launch.
+ */
+int topth_calibrate_mkc(const void* q, const void* k, int S, int Hq, int Hkv, int Lq, int Lk, int d,
+                        int dtype, float scale, int q_pos0, int pre, const int* ks, int n_k,
+                        float* theta, int n_rows, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Final step of Algorithm 1: theta[t][h][p] = sum/count + alpha * std

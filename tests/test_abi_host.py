@@ -250,3 +250,31 @@ def test_workspace_status_and_spin_limit_errors(lib):
     assert lib.topth_workspace_set_spin_limit(None, 1 << 20, 1, None) == -1
     assert lib.topth_workspace_set_spin_limit(FAKE, 100, 1, None) == -1
     assert tt.TOPTH_WS_HEADER_BYTES == 65536 and tt.TOPTH_STATUS_EXCHANGE_TIMEOUT == 1
+
+
+def _mkc(lib, **over):
+    ks = (ctypes.c_int * 3)(1, 8, 64)
+    a = dict(q=FAKE, k=FAKE, S=4, Hq=8, Hkv=2, Lq=1, Lk=512, d=128, dt=1, scale=0.1, q0=511, pre=0,
+             ks=ctypes.cast(ks, ctypes.c_void_p), n_k=3, theta=FAKE, n_rows=512, ws=FAKE, wsb=1 << 40)
+    a.update(over)
+    return lib.topth_calibrate_mkc(a["q"], a["k"], a["S"], a["Hq"], a["Hkv"], a["Lq"], a["Lk"], a["d"], a["dt"],
+                                   a["scale"], a["q0"], a["pre"], a["ks"], a["n_k"], a["theta"], a["n_rows"],
+                                   a["ws"], a["wsb"], None)
+
+
+def test_calibrate_mkc_argument_errors(lib):
+    assert _mkc(lib, q=None) == -1
+    assert _mkc(lib, ks=None) == -1
+    assert _mkc(lib, theta=None) == -1
+    assert _mkc(lib, q0=512) == -1                           # q_pos0 + Lq > Lk
+    assert _mkc(lib, pre=2) == -1
+    assert _mkc(lib, n_k=0) == -1 and _mkc(lib, n_k=65) == -1
+    bad = (ctypes.c_int * 1)(0)
+    assert _mkc(lib, ks=ctypes.cast(bad, ctypes.c_void_p), n_k=1) == -1
+    assert _mkc(lib, S=4097) == -2                           # more samples than one call merges
+    assert _mkc(lib, Lk=40000, q0=39999, n_rows=40000) == -2 # more keys than the LDS score row
+    assert _mkc(lib, ws=None) == -3
+    need = tt.topth_workspace_size(tt.TOPTH_OP_CALIBRATE_MKC, 4, 8, 2, 1, 512, 128, 0)
+    assert need >= 2 * 4 * 8 * 512 * 4
+    assert _mkc(lib, wsb=need - 1) == -3
+    assert tt.topth_workspace_size(tt.TOPTH_OP_CALIBRATE_MKC, 4097, 8, 2, 1, 512, 128, 0) == 0
