@@ -14,6 +14,10 @@ v_mean and seq_lens, divided by the average kernel duration (HIP events on the
 launch stream).  One JSON line is printed; it also carries the roofline object
 and the CPU oracle timed on the host as a reported baseline.
 
+The default run (``--workload all``) prints the decode_8b line with every
+other workload below as a sub-object of ``workloads``, each with its own
+roofline and CPU-oracle baseline, and a single-core oracle timing of decode_8b.
+
 Other workloads (``--workload``):
   * ``decode_70b_32k``: batch 8, 64/8 heads, 32768 cached keys, 4 sink keys, k=256.
   * ``prefill_8k``: causal prefill of 4 layers (32/8 heads, d=128, L=8192, bf16;
@@ -26,8 +30,10 @@ Other workloads (``--workload``):
   * ``prefill_8k_pre``: the prefill workload in the pre-softmax form (thresholds
     on the scores, calibrated on the scores; exp-threshold estimate of the
     discarded mass, gamma = 0.05): one sweep over the keys per query tile.
-The default run also appends ``prefill_8k`` and ``prefill_8k_pre`` summary
-objects (fewer steps).
+  * ``tiny_prefill_f32``: 1 head, d=64, L=256, fp32: calibration (k=32) from 64
+    sequences, then prefill of 8 test sequences with SDC + VMC (latency-bound).
+  * ``mkc``: multi-k cumulative calibration (Appendix D) over the decode_8b
+    calibration set (256 sequences, 32/8 heads, 4096 keys, row 4095).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -49,7 +55,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import calibrated_threshold_pruning_amd as tt  # noqa: E402
-from synth import CONFIG_IDS, ROLE_CALIB, ROLE_TEST, attention_inputs_device, to_f64  # noqa: E402
+from synth import (CONFIG_IDS, ROLE_CALIB, ROLE_TEST, attention_inputs, attention_inputs_device,  # noqa: E402
+                   batch_of_sequences, to_f64)
 
 METRIC = "decode Top-θ attn: HBM GB/s on bytes read (% of peak); prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -166,12 +173,11 @@ def theta_extrapolation(name, w, dev, buckets, buf, limit=2048):
     # near p + 1 = k the k-th largest is close to the row minimum, so theta first
     # rises with the row length before it falls: fits over all calibrated rows,
     # and fits over the rows with p + 1 >= 4 k only
-    far_cnt = cnt.clone()
-    far_cnt[:, :, :4 * w["k"] - 1] = 0
-    for label, c, deg in (("fitted_log_degree1", cnt, 1), ("fitted_log_degree2", cnt, 2),
-                          ("fitted_log_degree1_rows_from_4k", far_cnt, 1)):
+    for label, min_len, deg in (("fitted_log_degree1_all_rows", 0, 1), ("fitted_log_degree2_all_rows", 0, 2),
+                                ("fitted_log_degree1_rows_from_4k", 4, 1)):
         coef = torch.empty(1, w["Hq"], deg + 1, dtype=torch.float64, device=dev)
-        tt.topth_theta_fit(theta_near[None].contiguous(), c, coef, degree=deg, log_domain=True)
+        tt.topth_theta_fit(theta_near[None].contiguous(), cnt, coef, [w["k"]], degree=deg, log_domain=True,
+                           min_len_over_k=min_len)
         fitted = torch.empty(1, w["Hq"], w["n"], dtype=torch.float32, device=dev)
         tt.topth_theta_eval(coef, [w["k"]], fitted, log_domain=True)
         out[label] = kept_by_bucket(far, buf, fitted[0].contiguous(), w, dev)
@@ -220,7 +226,13 @@ def cpu_info():
     return model, threads
 
 
-def oracle_decode_baseline(bufs, lens, theta, vm, w, bytes_of, budget_s=20.0):
+def single_thread():
+    """Context in which NumPy's BLAS uses one thread (the single-core oracle)."""
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=1)
+
+
+def oracle_decode_baseline(bufs, lens, theta, vm, w, bytes_of, budget_s=20.0, threads=None):
     """Time the CPU oracle (float64 NumPy) on the first batch elements of the same
     decode workload; report GB/s over the same algorithmic bytes."""
     import oracle
@@ -245,8 +257,10 @@ def oracle_decode_baseline(bufs, lens, theta, vm, w, bytes_of, budget_s=20.0):
             break
     el = time.perf_counter() - t0
     nbytes = bytes_of(nb, vrows.sum()) * passes
-    model, threads = cpu_info()
-    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+    model, threads_used = cpu_info()
+    if threads is not None:
+        threads_used = threads
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": threads_used,
             "kind": "oracle",
             "sample": f"float64 NumPy oracle decode of batch elements 0..{nb - 1} of the same "
                       f"workload, {passes} pass(es), {el:.1f} s, host '{model}', "
@@ -368,6 +382,11 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
     if with_cpu:
         log("[bench] timing the CPU oracle on a sample of the same workload")
         res["cpu_baseline"] = oracle_decode_baseline(bufs[0], lens, theta, vms[0], w, read_bytes)
+        if name == "decode_8b":
+            log("[bench] timing the CPU oracle on one core")
+            with single_thread():
+                res["cpu_baseline_1core"] = oracle_decode_baseline(bufs[0], lens, theta, vms[0], w, read_bytes,
+                                                                   threads=1)
     return res
 
 
@@ -512,7 +531,7 @@ def calibrate_prefill_theta(w, layer, k, dev, pre=False):
     return theta[0].contiguous(), et[0].contiguous()
 
 
-def oracle_prefill_baseline(q, k, v, theta, w, budget_s=15.0, pre=False):
+def oracle_prefill_baseline(q, k, v, theta, w, budget_s=10.0, pre=False):
     """Time the CPU oracle on rows of layer 0, KV group 0 (its g query heads), spread
     over the whole length; report algorithmic TFLOP/s on the same flop count."""
     import oracle
@@ -635,28 +654,33 @@ def bench_prefill(steps, warmup, with_cpu, pre=False):
     return res
 
 
-def oracle_calib_baseline(w, dev, budget_s=15.0):
-    """Time the CPU oracle's calibration (Algorithm 1) on head 0 of one sequence;
-    report causal score elements per second."""
+def oracle_calib_baseline(w, dev, budget_s=10.0):
+    """Time the CPU oracle's calibration (Algorithm 1: every row's k-th largest
+    post-softmax value for each k) on whole sequences of layer 0, head after
+    head, until the time budget is spent; report causal score elements per
+    second."""
     import oracle
     cfg = CONFIG_IDS["calib_sweep"]
-    q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, 0, 0, B=1, Hq=1, Hkv=1, Lq=w["L"], Lk=w["L"],
-                                       d=w["d"], n_sinks=w["sinks"], device=dev, with_v=False)
-    qf = to_f64(q[0].cpu()); kf = to_f64(kk[0].cpu())
-    rng = np.random.default_rng(0)
-    rows = rng.permutation(w["L"])
+    L, d = w["L"], w["d"]
     t0 = time.perf_counter()
-    elems, done = 0, 0
-    while time.perf_counter() - t0 < budget_s and done < w["L"]:
-        for i in rows[done:done + 64]:
-            oracle.calibration_samples(qf[:, i:i + 1], kf, w["ks"], 1.0 / math.sqrt(w["d"]), q_pos0=int(i))
-            elems += int(i) + 1
-        done += 64
+    elems, heads = 0, 0
+    for seq in range(w["seqs"]):
+        q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, 0, seq, B=1, Hq=w["Hq"], Hkv=w["Hkv"], Lq=L, Lk=L,
+                                           d=d, n_sinks=w["sinks"], device=dev, with_v=False)
+        qf = to_f64(q[0].cpu()); kf = to_f64(kk[0].cpu())
+        for h in range(w["Hq"]):
+            oracle.calibration_samples(qf[h:h + 1], kf[h:h + 1], w["ks"], 1.0 / math.sqrt(d), q_pos0=0)
+            elems += L * (L + 1) // 2
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
     el = time.perf_counter() - t0
     model, threads = cpu_info()
     return {"value": round(elems / el, 1), "unit": "score elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"float64 NumPy oracle calibration of {min(done, w['L'])} random rows of head 0, "
-                      f"sequence 0, layer 0, {el:.1f} s, host '{model}'"}
+            "sample": f"float64 NumPy oracle calibration of {heads} (sequence, head) pairs of layer 0, all "
+                      f"{L} rows each, {el:.1f} s, host '{model}'"}
 
 
 def bench_calib(with_cpu):
@@ -722,6 +746,155 @@ def bench_calib(with_cpu):
     return res
 
 
+TINY_WORKLOAD = dict(L=256, d=64, k=32, calib=64, test=8)
+
+
+def bench_tiny(steps, with_cpu):
+    """The tiny fp32 workload end to end: calibration of theta (k=32) from 64
+    sequences, finalize, then prefill of 8 test sequences with SDC + VMC; each
+    step timed with events (the accumulators are zeroed before the event)."""
+    w = TINY_WORKLOAD
+    dev = torch.device("cuda:0")
+    cfg = CONFIG_IDS["tiny_prefill_f32"]
+    L, d, k = w["L"], w["d"], w["k"]
+    qc, kc, _ = batch_of_sequences(cfg, ROLE_CALIB, 0, 0, w["calib"], Hq=1, Hkv=1, Lq=L, Lk=L, d=d,
+                                   dtype=torch.float32)
+    q, kk, v = attention_inputs(cfg, ROLE_TEST, 0, 0, B=w["test"], Hq=1, Hkv=1, Lq=L, Lk=L, d=d,
+                                dtype=torch.float32)
+    qc, kc, q, kk, v = (t.to(dev) for t in (qc, kc, q, kk, v))
+    s1 = torch.zeros(1, 1, L, dtype=torch.float64, device=dev)
+    s2, cnt = torch.zeros_like(s1), torch.zeros(1, 1, L, dtype=torch.int32, device=dev)
+    theta = torch.empty(1, 1, L, dtype=torch.float32, device=dev)
+    wsc = tt.workspace(tt.TOPTH_OP_CALIBRATE, w["calib"], 1, 1, L, L, d, 1)
+    wsp = tt.workspace(tt.TOPTH_OP_PREFILL, w["test"], 1, 1, L, L, d)
+    out = torch.empty_like(q)
+    kcount = torch.empty(w["test"], 1, L, dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    times = []
+    for i in range(steps + 2):
+        s1.zero_(); s2.zero_(); cnt.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        tt.topth_calibrate(qc, kc, [k], s1, s2, cnt, wsc, scale=scale, q_pos0=0)
+        tt.topth_calibrate_finalize(s1, s2, cnt, [k], theta)
+        tt.topth_prefill(q, kk, v, theta[0], out, scale=scale, flags=tt.TOPTH_VMC, kept_count=kcount, ws=wsp)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(a.elapsed_time(b) * 1e-3)
+    t = float(np.mean(times))
+    seqs = w["calib"] + w["test"]
+    res = {"value": round(seqs / t, 1), "unit": "sequences/s (64 calibrated + 8 prefilled)",
+           "ms_per_step": round(t * 1e3, 4), "steps": steps, "dtype": "f32",
+           "config": {"workload": "tiny_prefill_f32", "heads": 1, "head_dim": d, "seq_len": L, "k": k,
+                      "calib_sequences": w["calib"], "test_sequences": w["test"], "sdc": "exact", "vmc": True},
+           "kept_over_k": round(kcount[:, :, k:].double().mean().item() / k, 4),
+           "roofline": None,
+           "roofline_note": "latency-bound: 4.2 MFLOP of scores per sequence; no roofline claim"}
+    if with_cpu:
+        log("[bench] timing the full CPU oracle of the tiny workload (all cores, then one core)")
+        qc64, kc64 = [to_f64(x.cpu()) for x in (qc, kc)]
+        q64, k64, v64 = [to_f64(x.cpu()) for x in (q, kk, v)]
+
+        def run_oracle():
+            import oracle
+            cal = oracle.Calibrator([k], 1, L)
+            for c in range(w["calib"]):
+                cal.observe(qc64[c], kc64[c], scale)
+            oracle.prefill(q64, k64, v64, cal.finalize()[0], scale, vmc=True)
+
+        def timed(budget_s=4.0):
+            t0, n = time.perf_counter(), 0
+            while True:
+                run_oracle()
+                n += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            return (time.perf_counter() - t0) / n, n
+
+        model, threads = cpu_info()
+        el, n = timed()
+        res["cpu_baseline"] = {"value": round(seqs / el, 2), "unit": res["unit"], "cores": threads, "kind": "oracle",
+                               "sample": f"the whole workload ({w['calib']} calibration + {w['test']} prefill "
+                                         f"sequences), {n} pass(es), {el:.2f} s each, host '{model}'"}
+        with single_thread():
+            el, n = timed()
+        res["cpu_baseline_1core"] = {"value": round(seqs / el, 2), "unit": res["unit"], "cores": 1, "kind": "oracle",
+                                     "sample": f"the whole workload, one BLAS thread, {n} pass(es), {el:.2f} s each"}
+    return res
+
+
+MKC_WORKLOAD = dict(S=256, Hq=32, Hkv=8, d=128, n=4096, ks=[64, 128, 256])
+
+
+def bench_mkc(with_cpu):
+    """Multi-k cumulative calibration over the decode_8b calibration set: all 256
+    sequences in one call (the merge needs every sample of a row at once); the
+    values kernel and the sort-and-walk kernel timed with events."""
+    w = MKC_WORKLOAD
+    dev = torch.device("cuda:0")
+    cfg = CONFIG_IDS["decode_8b"]
+    S, Hq, Hkv, d, n = w["S"], w["Hq"], w["Hkv"], w["d"], w["n"]
+    q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, 1, 0, B=S, Hq=Hq, Hkv=Hkv, Lq=1, Lk=n, d=d,
+                                       n_sinks=1, device=dev, with_v=False)
+    ws = torch.empty(tt.topth_workspace_size(tt.TOPTH_OP_CALIBRATE_MKC, S, Hq, Hkv, 1, n, d, 0), dtype=torch.uint8,
+                     device=dev)
+    theta = torch.empty(len(w["ks"]), Hq, n, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    tt.topth_calibrate_mkc(q, kk, w["ks"], theta, ws, scale=scale, q_pos0=n - 1)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        tt.topth_calibrate_mkc(q, kk, w["ks"], theta, ws, scale=scale, q_pos0=n - 1)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    t = float(np.mean(times))
+    pooled = S * Hq * n
+    # bytes the calibration must move at least: K of every sequence once, the
+    # query rows, and the pooled values written and read once by the merge
+    bytes_min = S * Hkv * n * d * 2 + S * Hq * d * 2 + 2 * pooled * 4
+    res = {"value": round(pooled / t / 1e9, 4), "unit": "G pooled values/s",
+           "ms_per_call": round(t * 1e3, 3), "dtype": "bf16",
+           "config": {"workload": "mkc", "calib_sequences": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                      "cache_len": n, "row": n - 1, "ks": w["ks"]},
+           "theta_row_4095": {str(k): round(float(theta[i, :, n - 1].mean().item()), 7) for i, k in enumerate(w["ks"])},
+           "roofline": {"bound": "hbm", "achieved": round(bytes_min / t / 1e9, 2), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(bytes_min / t / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "mkc_select_kernel + mkc_values_kernel",
+                        "note": "one workgroup per (head, row) sorts 1M pooled values: 32 of 256 CUs busy"}}
+    # thresholds for k = 128 from the merged function, applied to the decode_8b step
+    wd = DECODE_WORKLOADS["decode_8b"]
+    qt, kt, vt = attention_inputs_device(CONFIG_IDS["decode_8b"], ROLE_TEST, 0, 0, B=wd["B"], Hq=Hq, Hkv=Hkv, Lq=1,
+                                         Lk=n, d=d, n_sinks=1, device=dev)
+    qt = qt[:, :, 0].contiguous()
+    lens = torch.full((wd["B"],), n, dtype=torch.int32, device=dev)
+    vm = torch.empty(wd["B"], Hkv, d, dtype=torch.float32, device=dev)
+    tt.topth_vmean(vt, lens, vm)
+    out = torch.empty(wd["B"], Hq, d, dtype=torch.bfloat16, device=dev)
+    kc = torch.empty(wd["B"], Hq, dtype=torch.int32, device=dev)
+    wsd = tt.workspace(tt.TOPTH_OP_DECODE, wd["B"], Hq, Hkv, 1, n, d)
+    tt.topth_decode(qt, kt, vt, lens, theta[1].contiguous(), out, wsd, scale=scale, flags=tt.TOPTH_VMC, v_mean=vm,
+                    kept_count=kc)
+    torch.cuda.synchronize()
+    res["kept_over_k_decode_8b_k128"] = round(kc.double().mean().item() / 128, 4)
+    if with_cpu:
+        log("[bench] timing the CPU oracle of MKC on one head")
+        from oracle import mkc
+        qf, kf = to_f64(q[:, :1].cpu()), to_f64(kk[:, :1].cpu())
+        t0 = time.perf_counter()
+        mkc.mkc_calibrate(qf, kf, scale, n - 1, w["ks"])
+        el = time.perf_counter() - t0
+        model, threads = cpu_info()
+        res["cpu_baseline"] = {"value": round(S * n / el / 1e9, 6), "unit": res["unit"], "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"float64 NumPy oracle of head 0 ({S} samples x {n} values), {el:.1f} s, "
+                                         f"host '{model}'"}
+    return res
+
+
 def copy_probe(dev, mib=512):
     """One plain elementwise kernel of known traffic (reads and writes `mib` MiB),
     used to scale hardware byte counters."""
@@ -736,10 +909,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_8b",
-                    choices=sorted(DECODE_WORKLOADS) + ["prefill_8k", "prefill_8k_pre", "calib_sweep"])
-    ap.add_argument("--no-prefill-summary", action="store_true",
-                    help="default workload only: skip the appended prefill_8k summary")
+    ap.add_argument("--workload", default="all",
+                    choices=["all"] + sorted(DECODE_WORKLOADS) + ["prefill_8k", "prefill_8k_pre", "calib_sweep",
+                                                                  "tiny_prefill_f32", "mkc"])
+    ap.add_argument("--decode-only", action="store_true",
+                    help="with --workload all: only the decode_8b line (no sub-workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of "
                     "replaying a captured HIP graph")
@@ -759,15 +933,31 @@ def main():
         res = bench_prefill(args.steps, args.warmup, with_cpu, pre=args.workload == "prefill_8k_pre")
     elif args.workload == "calib_sweep":
         res = bench_calib(with_cpu)
+    elif args.workload == "tiny_prefill_f32":
+        res = bench_tiny(args.steps, with_cpu)
+    elif args.workload == "mkc":
+        res = bench_mkc(with_cpu)
+    elif args.workload == "all":
+        res = bench_decode("decode_8b", args.steps, args.warmup, with_cpu=with_cpu, eager=args.eager)
+        if not args.decode_only:
+            keep = ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data", "wall_s")
+            sub = {}
+            log("[bench] decode_70b_32k")
+            r = bench_decode("decode_70b_32k", min(args.steps, 100), args.warmup, with_cpu=with_cpu)
+            sub["decode_70b_32k"] = {k: v for k, v in r.items() if k not in keep}
+            for pre in (False, True):
+                r = bench_prefill(steps=5, warmup=1, with_cpu=with_cpu, pre=pre)
+                sub["prefill_8k_pre" if pre else "prefill_8k"] = {k: v for k, v in r.items() if k not in keep}
+            log("[bench] calib_sweep")
+            r = bench_calib(with_cpu)
+            sub["calib_sweep"] = {k: v for k, v in r.items() if k not in keep}
+            log("[bench] tiny_prefill_f32")
+            sub["tiny_prefill_f32"] = bench_tiny(10, with_cpu)
+            log("[bench] mkc")
+            sub["mkc"] = bench_mkc(with_cpu)
+            res["workloads"] = sub
     else:
         res = bench_decode(args.workload, args.steps, args.warmup, with_cpu=with_cpu, eager=args.eager)
-        if args.workload == "decode_8b" and not args.no_prefill_summary:
-            p = bench_prefill(steps=5, warmup=1, with_cpu=False)
-            keys = ("value", "unit", "ms_per_step", "qk_tflops_algorithmic", "pv_form", "mfma_tflops_executed",
-                    "mfma_executed_frac_of_peak", "per_layer", "roofline")
-            res["prefill_8k"] = {k: p[k] for k in keys}
-            p = bench_prefill(steps=5, warmup=1, with_cpu=False, pre=True)
-            res["prefill_8k_pre"] = {k: p[k] for k in keys + ("config",)}
     if args.copy_probe:
         copy_probe(torch.device("cuda:0"))
     print(json.dumps(res), flush=True)

@@ -94,7 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topth_vmean_append.restype = i
     lib.topth_vmean_append.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp]
     lib.topth_theta_fit.restype = i
-    lib.topth_theta_fit.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
+    lib.topth_theta_fit.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp]
     lib.topth_theta_eval.restype = i
     lib.topth_theta_eval.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
     lib.topth_decode_gqa.restype = i
@@ -442,14 +442,19 @@ def topth_vmean_append(v_cache, old_lens, new_lens, v_mean, stream=None):
         v_mean.data_ptr(), _stream(stream)))
 
 
-def topth_theta_fit(theta, count, coef, *, degree: int, log_domain: bool, stream=None):
-    """Fit coef [n_k,Hq,degree+1] (float64) to the observed rows of theta/count [n_k,Hq,n_rows]."""
+def topth_theta_fit(theta, count, coef, ks, *, degree: int, log_domain: bool, min_len_over_k: int = 4,
+                    stream=None):
+    """Fit coef [n_k,Hq,degree+1] (float64) to the observed rows of theta/count
+    [n_k,Hq,n_rows] with p + 1 >= min_len_over_k * ks[t] (0: every observed row)."""
     n_k, Hq, n_rows = theta.shape
     _dev(theta, "theta", torch.float32); _dev(count, "count", torch.int32, theta.shape)
     _dev(coef, "coef", torch.float64, (n_k, Hq, degree + 1))
+    if len(ks) != n_k:
+        raise ValueError("ks must have one k per slab")
+    karr = (ctypes.c_int * max(n_k, 1))(*[int(x) for x in ks])
     _check("topth_theta_fit", load_library().topth_theta_fit(
-        theta.data_ptr(), count.data_ptr(), n_k, Hq, n_rows, int(degree), int(bool(log_domain)),
-        coef.data_ptr(), _stream(stream)))
+        theta.data_ptr(), count.data_ptr(), ctypes.cast(karr, ctypes.c_void_p), n_k, Hq, n_rows, int(degree),
+        int(bool(log_domain)), int(min_len_over_k), coef.data_ptr(), _stream(stream)))
 
 
 def topth_theta_eval(coef, ks, theta_out, *, log_domain: bool, stream=None):

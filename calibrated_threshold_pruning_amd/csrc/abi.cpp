@@ -31,8 +31,8 @@ int mkc_max_keys();
 int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_t s);
 int launch_vmean_append(const void* v, const int* old_lens, const int* new_lens, int B, int Hkv, int Lmax,
                         int d, int dtype, float* v_mean, hipStream_t s);
-int launch_theta_fit(const float* theta, const int* count, int n_k, int Hq, int n_rows, int degree,
-                     int log_domain, double* coef, hipStream_t s);
+int launch_theta_fit(const float* theta, const int* count, const int* ks, int n_k, int Hq, int n_rows,
+                     int degree, int log_domain, int min_len_over_k, double* coef, hipStream_t s);
 int launch_theta_eval(const double* coef, const int* ks, int n_k, int Hq, int degree, int log_domain,
                       int n_out, float* theta_out, hipStream_t s);
 }  // namespace topth
@@ -433,14 +433,16 @@ int topth_vmean_append(const void* v_cache, const int* old_lens, const int* new_
                                        (hipStream_t)stream));
 }
 
-int topth_theta_fit(const float* theta, const int* count, int n_k, int Hq, int n_rows, int degree,
-                    int log_domain, double* coef, void* stream) {
-    if (!theta || !count || !coef) return TOPTH_EINVAL;
+int topth_theta_fit(const float* theta, const int* count, const int* ks, int n_k, int Hq, int n_rows,
+                    int degree, int log_domain, int min_len_over_k, double* coef, void* stream) {
+    if (!theta || !count || !ks || !coef) return TOPTH_EINVAL;
     if (n_k < 1 || n_k > TOPTH_MAX_NK || Hq <= 0 || n_rows <= 0) return TOPTH_EINVAL;
-    if (degree < 0 || degree > max_fit_degree()) return TOPTH_EINVAL;
+    if (degree < 0 || degree > max_fit_degree() || min_len_over_k < 0) return TOPTH_EINVAL;
+    for (int t = 0; t < n_k; ++t)
+        if (ks[t] < 1) return TOPTH_EINVAL;
     if ((long long)n_k * Hq > INT_MAX) return TOPTH_EUNSUPPORTED;
-    return map_hip(launch_theta_fit(theta, count, n_k, Hq, n_rows, degree, log_domain != 0, coef,
-                                    (hipStream_t)stream));
+    return map_hip(launch_theta_fit(theta, count, ks, n_k, Hq, n_rows, degree, log_domain != 0, min_len_over_k,
+                                    coef, (hipStream_t)stream));
 }
 
 int topth_theta_eval(const double* coef, const int* ks, int n_k, int Hq, int degree, int log_domain,

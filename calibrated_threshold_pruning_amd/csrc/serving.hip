@@ -60,8 +60,10 @@ __global__ __launch_bounds__(kAppendThreads) void vmean_append_kernel(
 // usable or the system is singular.
 constexpr int kFitThreads = 256;
 constexpr int kMaxFitDegree = 3;
+struct FitKList { int k[8]; };
 __global__ __launch_bounds__(kFitThreads) void theta_fit_kernel(
-        const float* theta, const int* count, int n_rows, int degree, int log_domain, double* coef) {
+        const float* theta, const int* count, FitKList p_min, int Hq, int n_rows, int degree, int log_domain,
+        double* coef) {
     constexpr int NS = 2 * kMaxFitDegree + 1;          // power sums x^0 .. x^(2 deg)
     constexpr int NT = kMaxFitDegree + 1;              // moments x^0 y .. x^deg y
     __shared__ double s_pow[kFitThreads][NS + NT + 1];
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(kFitThreads) void theta_fit_kernel(
     double sp[NS + NT + 1];
 #pragma unroll
     for (int i = 0; i < NS + NT + 1; ++i) sp[i] = 0.0;
-    for (int p = threadIdx.x; p < n_rows; p += kFitThreads) {
+    for (int p = p_min.k[blockIdx.x / Hq] + threadIdx.x; p < n_rows; p += kFitThreads) {
         if (count[base + p] <= 0) continue;
         const float th = theta[base + p];
         if (!isfinite(th) || (log_domain && !(th > 0.0f))) continue;
@@ -132,7 +134,6 @@ __global__ __launch_bounds__(kFitThreads) void theta_fit_kernel(
 
 // theta_out[t][h][p] = the fitted polynomial at ln(p + 1) (exponentiated in
 // the log domain) for p + 1 > k, -inf for rows that keep every element.
-struct FitKList { int k[8]; };
 __global__ void theta_eval_kernel(const double* coef, FitKList ks, int Hq, int degree, int log_domain,
                                   int n_out, float* theta_out) {
     const int th = blockIdx.y;                         // t * Hq + h
@@ -166,10 +167,15 @@ int launch_vmean_append(const void* v, const int* old_lens, const int* new_lens,
     return hipGetLastError();
 }
 
-int launch_theta_fit(const float* theta, const int* count, int n_k, int Hq, int n_rows, int degree,
-                     int log_domain, double* coef, hipStream_t s) {
-    hipLaunchKernelGGL(theta_fit_kernel, dim3(n_k * Hq), dim3(kFitThreads), 0, s, theta, count, n_rows,
-                       degree, log_domain, coef);
+int launch_theta_fit(const float* theta, const int* count, const int* ks, int n_k, int Hq, int n_rows,
+                     int degree, int log_domain, int min_len_over_k, double* coef, hipStream_t s) {
+    FitKList p_min = {};                               // first row of the fit, per k
+    for (int t = 0; t < n_k && t < 8; ++t) {
+        const long long r = (long long)min_len_over_k * ks[t] - 1;
+        p_min.k[t] = r < 0 ? 0 : (r > n_rows ? n_rows : (int)r);
+    }
+    hipLaunchKernelGGL(theta_fit_kernel, dim3(n_k * Hq), dim3(kFitThreads), 0, s, theta, count, p_min, Hq,
+                       n_rows, degree, log_domain, coef);
     return hipGetLastError();
 }
 

@@ -418,10 +418,16 @@ int topth_vmean_append(const void* v_cache, const int* old_lens, const int* new_
  * sequence reached (the paper fits the per-row thresholds to the sequence
  * length; the function is not given, so this library uses a least-squares
  * polynomial of degree 0..3 in x = ln(p + 1)).  topth_theta_fit fits, per
- * (t, h), the rows with count > 0 of a finalized slab: on ln(theta) when
- * log_domain != 0 (post-softmax thresholds, which fall roughly as a power of
- * the row length; rows with theta <= 0 are skipped), on theta otherwise
- * (pre-softmax thresholds).
+ * (t, h), the rows with count > 0 and p + 1 >= min_len_over_k * ks[t] of a
+ * finalized slab: on ln(theta) when log_domain != 0 (post-softmax thresholds,
+ * which fall roughly as a power of the row length; rows with theta <= 0 are
+ * skipped), on theta otherwise (pre-softmax thresholds).  Rows just above
+ * p + 1 = k do not follow that trend (the k-th largest value sits near the
+ * row's minimum there, so thresholds first rise with the row length): fits
+ * that include them and are extrapolated to much longer rows keep far too
+ * few or far too many keys.  min_len_over_k = 4 leaves them out and is the
+ * recommended setting; 0 fits every observed row.
+ *   ks host [n_k], the target k of each slab; min_len_over_k >= 0;
  *   theta device float, count device int [n_k][Hq][n_rows];
  *   coef device double [n_k][Hq][degree + 1], highest power first (output);
  *   NaN coefficients where fewer than degree + 1 rows are usable.  The fit
@@ -429,8 +435,8 @@ int topth_vmean_append(const void* v_cache, const int* old_lens, const int* new_
  *   ln(p + 1) is ill-conditioned, and its coefficients (not its values) may
  *   then differ in the leading digits from an orthogonal-factorisation solve.
  */
-int topth_theta_fit(const float* theta, const int* count, int n_k, int Hq, int n_rows, int degree,
-                    int log_domain, double* coef, void* stream);
+int topth_theta_fit(const float* theta, const int* count, const int* ks, int n_k, int Hq, int n_rows,
+                    int degree, int log_domain, int min_len_over_k, double* coef, void* stream);
 
 /*
  * Evaluate fitted thresholds into a slab of n_out rows (which may be longer

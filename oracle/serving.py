@@ -43,20 +43,23 @@ def running_mean_append(mu_old, n_old: int, V_new) -> np.ndarray:
     return total / n_new
 
 
-def fit_theta(theta_table, observed, degree: int, log_domain: bool):
+def fit_theta(theta_table, observed, degree: int, log_domain: bool, min_row: int = 0):
     """Coefficients (highest power first) of the least-squares polynomial of
-    ``degree`` in ln(p + 1) through the rows p where ``observed`` is true, on
-    ln(theta) if ``log_domain`` else on theta; one row of coefficients per
-    head.  theta_table and observed are [Hq, R].  A head with fewer than
-    degree + 1 usable rows gets NaN coefficients; in the log domain rows with
-    theta <= 0 are not usable."""
+    ``degree`` in ln(p + 1) through the rows p >= min_row where ``observed``
+    is true, on ln(theta) if ``log_domain`` else on theta; one row of
+    coefficients per head.  theta_table and observed are [Hq, R].  A head with
+    fewer than degree + 1 usable rows gets NaN coefficients; in the log domain
+    rows with theta <= 0 are not usable.  (Near p + 1 = k the k-th largest
+    value of a row sits close to the row's minimum, so thresholds first rise
+    with the row length and then fall; leaving out the rows below a few k
+    keeps that rise out of a fit that is extrapolated to longer rows.)"""
     th = _as64(theta_table)
     obs = np.asarray(observed, dtype=bool)
     Hq, R = th.shape
     coef = np.full((Hq, degree + 1), np.nan)
     x_all = np.log(np.arange(R) + 1.0)
     for h in range(Hq):
-        use = obs[h] & np.isfinite(th[h])
+        use = obs[h] & np.isfinite(th[h]) & (np.arange(R) >= min_row)
         if log_domain:
             use &= th[h] > 0
         if use.sum() < degree + 1:

@@ -212,9 +212,12 @@ def test_serving_helper_errors(lib):
     assert lib.topth_vmean_append(None, FAKE, FAKE, 2, 8, 64, 128, 1, FAKE, None) == -1
     assert lib.topth_vmean_append(FAKE, FAKE, FAKE, 2, 8, 64, 96, 1, FAKE, None) == -1     # d
     assert lib.topth_vmean_append(FAKE, FAKE, FAKE, 2, 8, 64, 128, 5, FAKE, None) == -1    # dtype
-    assert lib.topth_theta_fit(FAKE, FAKE, 1, 8, 64, 4, 1, FAKE, None) == -1               # degree > 3
-    assert lib.topth_theta_fit(FAKE, FAKE, 1, 8, 64, -1, 1, FAKE, None) == -1
-    assert lib.topth_theta_fit(FAKE, None, 1, 8, 64, 1, 1, FAKE, None) == -1
+    ks1 = ctypes.cast((ctypes.c_int * 1)(64), ctypes.c_void_p)
+    assert lib.topth_theta_fit(FAKE, FAKE, ks1, 1, 8, 64, 4, 1, 4, FAKE, None) == -1            # degree > 3
+    assert lib.topth_theta_fit(FAKE, FAKE, ks1, 1, 8, 64, -1, 1, 4, FAKE, None) == -1
+    assert lib.topth_theta_fit(FAKE, None, ks1, 1, 8, 64, 1, 1, 4, FAKE, None) == -1
+    assert lib.topth_theta_fit(FAKE, FAKE, None, 1, 8, 64, 1, 1, 4, FAKE, None) == -1
+    assert lib.topth_theta_fit(FAKE, FAKE, ks1, 1, 8, 64, 1, 1, -1, FAKE, None) == -1         # negative factor
     assert lib.topth_theta_eval(FAKE, kp, 1, 8, 2, 1, 0, FAKE, None) == -1                 # n_out
     assert lib.topth_theta_eval(FAKE, None, 1, 8, 2, 1, 100, FAKE, None) == -1
     assert lib.topth_theta_eval(FAKE, kp, 9, 8, 2, 1, 100, FAKE, None) == -1               # n_k

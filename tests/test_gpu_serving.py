@@ -58,10 +58,10 @@ def _noisy_table(rng, n_k, Hq, R, log_domain):
     return th.astype(np.float32)
 
 
-@pytest.mark.parametrize("degree", [0, 1, 2, 3])
+@pytest.mark.parametrize("degree,min_len", [(0, 0), (1, 0), (2, 0), (3, 0), (1, 4), (2, 4)])
 @pytest.mark.parametrize("log_domain", [True, False])
-def test_theta_fit_and_eval(degree, log_domain):
-    print(f"theta_fit degree={degree} log={log_domain}", flush=True)
+def test_theta_fit_and_eval(degree, min_len, log_domain):
+    print(f"theta_fit degree={degree} log={log_domain} min_len_over_k={min_len}", flush=True)
     dev = device()
     rng = np.random.default_rng(degree + 10 * log_domain)
     n_k, Hq, R, n_out = 2, 5, 4096, 32768
@@ -75,14 +75,14 @@ def test_theta_fit_and_eval(degree, log_domain):
     if log_domain:
         th[0, 1, probes[3]] = -1.0          # not usable in the log domain
     coef = torch.empty(n_k, Hq, degree + 1, dtype=torch.float64, device=dev)
-    tt.topth_theta_fit(torch.tensor(th, device=dev), torch.tensor(cnt, device=dev), coef, degree=degree,
-                       log_domain=log_domain)
+    tt.topth_theta_fit(torch.tensor(th, device=dev), torch.tensor(cnt, device=dev), coef, ks, degree=degree,
+                       log_domain=log_domain, min_len_over_k=min_len)
     out = torch.empty(n_k, Hq, n_out, dtype=torch.float32, device=dev)
     tt.topth_theta_eval(coef, ks, out, log_domain=log_domain)
     torch.cuda.synchronize()
     cg, og = coef.cpu().numpy(), out.cpu().numpy().astype(np.float64)
     for t in range(n_k):
-        cr = serving.fit_theta(th[t], cnt[t] > 0, degree, log_domain)
+        cr = serving.fit_theta(th[t], cnt[t] > 0, degree, log_domain, min_row=max(min_len * ks[t] - 1, 0))
         ref = serving.eval_theta(cr, ks[t], n_out, log_domain)
         for h in range(Hq):
             if h == 4:

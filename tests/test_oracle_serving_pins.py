@@ -76,6 +76,21 @@ def test_fit_is_the_least_squares_solution():
     np.testing.assert_allclose(coef[0], want, rtol=1e-9, atol=1e-12)
 
 
+def test_fit_from_a_minimum_row_ignores_the_short_rows():
+    """Rows below min_row are left out: thresholds on a power law from row 255
+    on but corrupted below it give back the exact power law, while a fit over
+    every row does not."""
+    R = 3000
+    p = np.arange(R)
+    th = (0.5 * (p + 1.0) ** -1.1)[None, :]
+    th[0, :255] = 0.001 * (p[:255] + 1.0) ** 0.7          # rising near p + 1 = k
+    obs = np.zeros_like(th, dtype=bool)
+    obs[0, ::37] = True
+    coef = serving.fit_theta(th, obs, 1, True, min_row=255)
+    np.testing.assert_allclose(coef[0], [-1.1, math.log(0.5)], rtol=1e-12)
+    assert abs(serving.fit_theta(th, obs, 1, True)[0, 0] + 1.1) > 0.1
+
+
 def test_fit_needs_enough_rows_and_skips_unusable_ones():
     th = np.full((3, 50), 0.1)
     obs = np.zeros_like(th, dtype=bool)
