@@ -71,8 +71,11 @@ size_t prefill_ws(int B, int Hq, int Hkv, int L, int d) {
     return mu + v16 + 256;
 }
 
+// per-sequence samples; then, for the tiled kernel, a counter and a list of
+// (row, target) entries for the exact fixup (at most one per sample)
 size_t calib_ws(int S, int Hq, int Lq, int n_k) {
-    return (size_t)S * n_k * Hq * Lq * sizeof(float) + 256;
+    const size_t n = (size_t)S * n_k * Hq * Lq;
+    return ((n * sizeof(float) + 255) & ~(size_t)255) + 256 + n * 16 + 256;
 }
 
 // flags of the pre-softmax calls: VMC plus at most one estimate of E~

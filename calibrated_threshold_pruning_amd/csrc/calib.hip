@@ -478,6 +478,585 @@ __global__ __launch_bounds__(kCalThreads) void calib_bf16_kernel(CalibKArgs a) {
 #endif
 }
 
+// --------------------------------------------- tiled calibration of prefill rows
+// Calibration of whole causal prefills (q_pos0 = 0, Lq = Lk) in the tile
+// layout of the prefill kernel: a workgroup of 4 waves takes 32 query rows
+// per wave of one KV group and streams the group's K tiles of 64 keys through
+// LDS three times (two tile buffers, one tile ahead), recomputing the scores
+// on MFMA each time instead of keeping them, so K is read once per 32 * RBW
+// rows and two workgroups fit on a CU (one's select phases overlap the
+// other's sweeps):
+//   sweep A  per row: maximum M, minimum, sum of scores and the softmax sum
+//            (the row log-sum-exp lse2);
+//   sweep B  a histogram of 256 bins of (M - x) over a window below M: the
+//            full range for rows shorter than 3 k_max, else the smaller of the
+//            full range and 1.1 (M - mean).  Counts are 8-bit, four to a word;
+//            the last (open-ended) bin is not counted but inferred from the
+//            row length, and each lane counts the in-window elements of its
+//            rows in a register, which exposes any 8-bit overflow.  A prefix
+//            over the bins gives, for every target k, the bin holding the k-th
+//            largest score and its rank inside that bin;
+//   sweep C  every lane appends the elements of its two rows that fall into a
+//            target bin to a private region of 32 slots, one row from each
+//            end (no atomics, no branches).  Then one lane per (row, target)
+//            reads the row's four regions and keeps the 32 largest members of
+//            the target bin in a register sorting network (the 32 smallest
+//            when the rank is nearer the bottom of the bin), so the member of
+//            that rank is exact for any bin of up to 64 members.
+// A row whose counts overflowed, whose members do not fit the regions, or
+// whose target bin holds more than 64 members is listed for
+// calib_fixup_kernel, which recomputes it and selects exactly by radix
+// select.  Bins are a pure function of the recomputed scores, which
+// every sweep forms identically, so the sweeps agree on every element.
+constexpr int kCtNB = 256;                      // histogram bins per row
+constexpr int kCtRowWords = kCtNB / 4 + 1;      // 8-bit counts, + 1 word: rows in other banks
+constexpr int kCtPool = 32 * kCtRowWords;       // words per wave: histogram, then candidate regions
+constexpr int kCtSlots = 32;                    // candidate slots per lane (both of its rows)
+constexpr int kCtNet = 32;                      // registers of the exact-select network
+constexpr int kCtMaxK = 4;                      // targets per call on this path
+constexpr int kCtEntries = 32 * kCtMaxK;        // (row, target) entries of a wave
+static_assert(64 * kCtSlots <= kCtPool, "candidate regions inside the histogram space");
+
+constexpr int kCtWaves = 4;
+
+template <int D, int G>
+struct CtCfg {
+    static constexpr int HPW = G < kCtWaves ? G : kCtWaves;   // query heads per workgroup
+    static constexpr int RBW = kCtWaves / HPW;      // 32-row blocks per workgroup
+    static constexpr int BMT = 32 * RBW;            // query rows per workgroup
+    static constexpr int BN = 64;                   // keys per tile
+    static constexpr int KSTEPS = D / 32;
+    static constexpr int CPR = D / 8;               // 16-byte chunks per K row
+    static constexpr int RPI = 64 / CPR;            // K rows per 1 KiB load instruction
+    static constexpr int KTILE = BN * D * 2;
+    static constexpr int NLD = KTILE / 1024 / kCtWaves;   // load instructions per wave per tile
+    static_assert(NLD >= 1, "a tile must give every wave a load");
+};
+
+struct CalibTArgs {
+    const uint16_t* q; const uint16_t* k;
+    int S, Hq, Hkv, L;
+    float xscale, scale;
+    int ks[kCtMaxK]; int n_k; int kmax;
+    float* samples;            // [S][n_k][Hq][L]
+    int pre;                   // samples are k-th largest scores (pre-softmax)
+    unsigned* fix_count;       // entries listed for the exact fixup
+    uint4* fix_list;           // (sequence, head, row | target << 16, lse2 bits)
+};
+
+__device__ __forceinline__ void ct_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+
+// LDS accesses written out: the compiler cannot tell an LDS atomic or store
+// from the buffer-to-LDS K loads in flight into the other tile buffer and
+// would wait for those loads before every one of them.  The histogram and
+// the candidate regions are never a target of those loads.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_add(uint32_t addr, uint32_t v) {
+    asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_store(uint32_t addr, float v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// The member of rank rr (counted from the top when `top`, else from the
+// bottom) of the target bin tbe of a row, from the candidate regions of the
+// row's four lanes (g16 + 16 src; row qb = 0 at the start of a region, row
+// qb = 1 at its end): an N-register sorting network keeps the N largest (or
+// smallest) members seen; rr <= N.
+template <int N>
+__device__ __forceinline__ float ct_select(const float* pool, int wave, const int (*ccnt)[64][2], int g16, int qb,
+                                           int tbe, float M, float bs, bool top, int rr) {
+    float r[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i] = top ? -INFINITY : INFINITY;
+#pragma unroll
+    for (int src = 0; src < 4; ++src) {
+        const int sl = g16 + 16 * src;
+        const int c = ccnt[wave][sl][qb];
+        for (int jj = 0; jj < c; ++jj) {
+            const float y = pool[kCtSlots * sl + (qb == 0 ? jj : kCtSlots - 1 - jj)];
+            if ((int)fminf((M - y) * bs, (float)(kCtNB - 1)) != tbe) continue;
+            float v = y;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const float keep = top ? fmaxf(r[i], v) : fminf(r[i], v);
+                v = top ? fminf(r[i], v) : fmaxf(r[i], v);
+                r[i] = keep;
+            }
+        }
+    }
+    float val = r[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) val = i == rr - 1 ? r[i] : val;
+    return val;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = CtCfg<D, G>;
+    constexpr int W = kCtWaves;
+    // two K tile buffers as separate objects, so that reads of one are not
+    // taken to alias the loads in flight into the other
+    __shared__ __attribute__((aligned(16))) unsigned char s_k0[C::KTILE];
+    __shared__ __attribute__((aligned(16))) unsigned char s_k1[C::KTILE];
+    __shared__ uint32_t s_hist[W][kCtPool];          // per wave: histogram, then the candidate regions
+    __shared__ int s_ccnt[W][64][2];                 // candidates per lane and row
+    __shared__ int s_lovf[W][16];                    // a lane of the group l16 overran its region
+    __shared__ float s_rM[W][32], s_rbs[W][32], s_rlse[W][32];   // maximum, bin scale and lse2 of each row
+    __shared__ int s_etb[W][kCtEntries];             // target bin (-1: none, or listed for the fixup)
+    __shared__ int s_ecnt[W][kCtEntries];            // members of the target bin
+    __shared__ int s_erank[W][kCtEntries];           // rank inside the bin; -1: listed for the fixup
+    __shared__ float s_eval[W][kCtEntries];          // the k-th largest score
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lq = lane >> 4;
+    const float NEG_INF = -INFINITY;
+    const int n_k = a.n_k;
+
+    const int nqt = (a.L + C::BMT - 1) / C::BMT;
+    const int qt = nqt - 1 - (int)blockIdx.x;                // longest query tiles first
+    const int kv = blockIdx.y / (G / C::HPW);
+    const int hblk = blockIdx.y % (G / C::HPW);
+    const int sq = blockIdx.z;
+    const int h = kv * G + hblk * C::HPW + wave % C::HPW;
+    const int row0 = qt * C::BMT + (wave / C::HPW) * 32;
+    const int wg_row_end = min(a.L, (qt + 1) * C::BMT);
+    const int ntiles = (wg_row_end + C::BN - 1) / C::BN;
+
+    const uint16_t* kg = a.k + ((size_t)sq * a.Hkv + kv) * (size_t)a.L * D;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kg), 0, a.L * D * 2, 0x00020000);
+
+    // Q^T fragments (B operand): query row row0 + 16 qb + l16, dims 32 s + 8 lq + e
+    bf16x8 qf[2][C::KSTEPS];
+    {
+        const uint16_t* qg = a.q + ((size_t)sq * a.Hq + h) * (size_t)a.L * D;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int r = min(row0 + 16 * qb + l16, a.L - 1);
+#pragma unroll
+            for (int st = 0; st < C::KSTEPS; ++st)
+                qf[qb][st] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qg + (size_t)r * D + 32 * st + 8 * lq));
+        }
+    }
+    // K tile staging (XOR-swizzled 16-byte chunks, as in the prefill kernel)
+    constexpr int NVO = C::CPR / C::RPI > 0 ? C::CPR / C::RPI : 1;
+    int vo[NVO];
+#pragma unroll
+    for (int j = 0; j < NVO; ++j) {
+        const int row = j * C::RPI + lane / C::CPR;
+        vo[j] = (lane / C::CPR) * (D * 2) + (((lane % C::CPR) ^ (row % C::CPR)) * 16);
+    }
+    auto issue_k = [&](unsigned char* dst, int tile) {
+#pragma unroll
+        for (int i = 0; i < C::NLD; ++i) {
+            const int li = wave * C::NLD + i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                krs, (__attribute__((address_space(3))) void*)(dst + li * 1024), 16,
+                vo[li % NVO], (tile * C::BN + li * C::RPI) * (D * 2), 0, 0);
+        }
+    };
+    // raw scores q.k of key tile j: keys 64 j + 16 kb + 4 lq + r, rows row0 + 16 qb + l16;
+    // keys past a row (and rows past L) are -inf
+    auto scores = [&](const unsigned char* buf, int j, f32x4 (&st)[2][4]) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int key = 16 * kb + l16;
+            const unsigned char* srow = buf + ((key / C::RPI) * 64 + (key % C::RPI) * C::CPR) * 16;
+            const int swz = key % C::CPR;
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st2 = 0; st2 < C::KSTEPS; ++st2) {
+                const int c = 4 * st2 + lq;
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(srow + (c ^ swz) * 16));
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][st2], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][st2], acc1, 0, 0, 0);
+            }
+            st[0][kb] = acc0;
+            st[1][kb] = acc1;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::KSTEPS, 0);
+#pragma unroll
+        for (int kb = 0; kb < 3; ++kb) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KSTEPS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, C::KSTEPS, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KSTEPS, 0);
+        if (j * C::BN + C::BN - 1 > row0) {              // the tile crosses this wave's diagonal
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int row = row0 + 16 * qb + l16;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (j * C::BN + 16 * kb + 4 * lq + r > row || row >= a.L) st[qb][kb][r] = NEG_INF;
+            }
+        }
+    };
+    // one pass over the key tiles: tile j + 1 loads while tile j is used
+    auto sweep = [&](auto&& body) {
+        issue_k(s_k0, 0);
+        for (int j = 0; j < ntiles; j += 2) {
+            ct_wait_vmem();
+            __syncthreads();                             // tile j landed; the other buffer is free
+            if (j + 1 < ntiles) issue_k(s_k1, j + 1);
+            f32x4 st[2][4];
+            scores(s_k0, j, st);
+            body(j, st);
+            if (j + 1 >= ntiles) break;
+            ct_wait_vmem();
+            __syncthreads();
+            if (j + 2 < ntiles) issue_k(s_k0, j + 2);
+            scores(s_k1, j + 1, st);
+            body(j + 1, st);
+        }
+        __syncthreads();                                 // both buffers free for the next sweep
+    };
+
+    // ======================= sweep A: row statistics ==========================
+    float m_l[2] = {NEG_INF, NEG_INF}, l_l[2] = {0.f, 0.f}, mn_l[2] = {INFINITY, INFINITY}, sx_l[2] = {0.f, 0.f};
+    sweep([&](int j, f32x4 (&st)[2][4]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float tmax = NEG_INF, tmin = INFINITY, tsum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = st[qb][kb][r];
+                    tmax = fmaxf(tmax, x);
+                    const bool ok = x > NEG_INF;
+                    tmin = fminf(tmin, ok ? x : INFINITY);
+                    tsum += ok ? x : 0.f;
+                }
+            mn_l[qb] = fminf(mn_l[qb], tmin);
+            sx_l[qb] += tsum;
+            const float mnew = fmaxf(m_l[qb], tmax);
+            if (mnew != NEG_INF) {
+                const float nmc = -mnew * a.xscale;
+                float sum = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(fmaf(st[qb][kb][r], a.xscale, nmc));
+                l_l[qb] = l_l[qb] * __builtin_amdgcn_exp2f((m_l[qb] - mnew) * a.xscale) + sum;
+                m_l[qb] = mnew;
+            }
+        }
+    });
+    // the four lanes of a row (16 apart) combine; every one of them gets the result
+    float rM[2], rbs[2], lse2[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float M = fmaxf(m_l[qb], __shfl_xor(m_l[qb], 16));
+        M = fmaxf(M, __shfl_xor(M, 32));
+        float part = (m_l[qb] == NEG_INF) ? 0.f : l_l[qb] * __builtin_amdgcn_exp2f((m_l[qb] - M) * a.xscale);
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        float mn = fminf(mn_l[qb], __shfl_xor(mn_l[qb], 16));
+        mn = fminf(mn, __shfl_xor(mn, 32));
+        float sx = sx_l[qb] + __shfl_xor(sx_l[qb], 16);
+        sx += __shfl_xor(sx, 32);
+        const int n = row0 + 16 * qb + l16 + 1;
+        lse2[qb] = M * a.xscale + __log2f(part);
+        float w = M - mn;
+        if (n >= 3 * a.kmax) w = fminf(w, 1.1f * (M - sx / (float)n));
+        w = fmaxf(w, 1e-30f);
+        rM[qb] = M;
+        rbs[qb] = (float)kCtNB / w;
+        if (lq == 0) {
+            s_rM[wave][16 * qb + l16] = M;
+            s_rbs[wave][16 * qb + l16] = rbs[qb];
+            s_rlse[wave][16 * qb + l16] = lse2[qb];
+        }
+    }
+    // bin of a score: monotone non-increasing in x; masked (-inf) elements and
+    // everything beyond the window land in the last bin
+    auto bin_of = [&](int qb, float x) -> int {
+        return (int)fminf((rM[qb] - x) * rbs[qb], (float)(kCtNB - 1));
+    };
+
+    // ======================= sweep B: histograms ==============================
+    uint32_t* hw = s_hist[wave];
+    const uint32_t hw_off = lds_offset(hw);
+    for (int i = lane; i < kCtPool; i += 64) hw[i] = 0u;
+    int inwin[2] = {0, 0};                              // this lane's elements in bins 0 .. NB - 2
+    sweep([&](int j, f32x4 (&st)[2][4]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const uint32_t rbase = hw_off + (uint32_t)((16 * qb + l16) * kCtRowWords) * 4u;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int b = bin_of(qb, st[qb][kb][r]);
+                    const bool in = b < kCtNB - 1;
+                    inwin[qb] += in ? 1 : 0;
+                    lds_add(rbase + (uint32_t)(b >> 2) * 4u, in ? 1u << ((b & 3) << 3) : 0u);
+                }
+        }
+    });
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the written-out atomics are done
+    // every entry starts as "no target"; the lanes that find a target set it after the barrier
+    for (int e = lane; e < kCtEntries; e += 64) {
+        s_etb[wave][e] = -1;
+        s_erank[wave][e] = 0;
+        s_eval[wave][e] = __uint_as_float(0x7FC00000u);   // NaN until the exact value is found
+    }
+    __syncthreads();
+    int winrow[2];                                      // in-window count of each of the lane's rows
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        int c = inwin[qb] + __shfl_xor(inwin[qb], 16);
+        winrow[qb] = c + __shfl_xor(c, 32);
+    }
+
+    // ---- bin and rank of each target: lane (rl, half) scans 128 bins of row rl
+    {
+        const int rl = lane & 31, half = lane >> 5;
+        const int n = row0 + rl + 1;
+        const bool live = row0 + rl < a.L;
+        // in-window count and lse2 of row rl live in lane rl % 16 (register rl / 16)
+        const int w0 = __shfl(winrow[0], rl & 15), w1 = __shfl(winrow[1], rl & 15);
+        const int win = rl < 16 ? w0 : w1;
+        const float l0 = __shfl(lse2[0], rl & 15), l1 = __shfl(lse2[1], rl & 15);
+        const float lrow = rl < 16 ? l0 : l1;
+        uint32_t wv[32];
+        int ws[32];                                     // count of each word's four bins
+        int local = 0;
+#pragma unroll
+        for (int w = 0; w < 32; ++w) {
+            wv[w] = hw[rl * kCtRowWords + 32 * half + w];
+            ws[w] = (int)__builtin_amdgcn_sad_u8(wv[w], 0u, 0u);
+            local += ws[w];
+        }
+        const int other = __shfl_xor(local, 32);
+        const int base = half ? other : 0;
+        const bool ovf = local + other != win;          // an 8-bit count wrapped
+        const int lastcnt = n - win;                    // elements beyond the window (bin NB - 1)
+        if (half) ws[31] += lastcnt;
+        for (int t = 0; t < n_k; ++t) {
+            const int kk = a.ks[t];
+            const int e = rl * n_k + t;
+            if (!(live && n > kk)) continue;
+            if (ovf) {
+                if (half == 0) {
+                    s_erank[wave][e] = -1;
+                    const unsigned idx = atomicAdd(a.fix_count, 1u);
+                    a.fix_list[idx] = make_uint4((unsigned)sq, (unsigned)h, (unsigned)(row0 + rl) | ((unsigned)t << 16),
+                                                 __float_as_uint(lrow));
+                }
+                continue;
+            }
+            if (base < kk && kk <= base + local + (half ? lastcnt : 0)) {
+                // the word holding the k-th largest, then the bin inside it
+                int cum = base, wsel = 0, cbefore = base;
+#pragma unroll
+                for (int w = 0; w < 32; ++w) {
+                    if (cum < kk && kk <= cum + ws[w]) { wsel = w; cbefore = cum; }
+                    cum += ws[w];
+                }
+                uint32_t word = 0u;
+#pragma unroll
+                for (int w = 0; w < 32; ++w) word = w == wsel ? wv[w] : word;
+                cum = cbefore;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int bin = 128 * half + 4 * wsel + i;
+                    const int c = bin == kCtNB - 1 ? lastcnt : (int)((word >> (8 * i)) & 0xffu);
+                    if (cum < kk && kk <= cum + c) {
+                        s_etb[wave][e] = bin;
+                        s_erank[wave][e] = kk - cum;
+                        s_ecnt[wave][e] = c;
+                    }
+                    cum += c;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ======================= sweep C: members of the target bins ==============
+    int tb[2][kCtMaxK];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int t = 0; t < kCtMaxK; ++t) tb[qb][t] = t < n_k ? s_etb[wave][(16 * qb + l16) * n_k + t] : -1;
+    // this lane's region: words 32 lane .. 32 lane + 31; row qb = 0 fills slots
+    // 0, 1, .. and row qb = 1 slots 31, 30, ..; each row's next free slot takes
+    // the stores of non-members (a later member overwrites it)
+    const uint32_t reg_off = hw_off + (uint32_t)(kCtSlots * lane) * 4u;
+    int cc[2] = {0, 0};
+    sweep([&](int j, f32x4 (&st)[2][4]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = st[qb][kb][r];
+                    const int b = bin_of(qb, x);
+                    // bitwise, not short-circuit: no branch per element
+                    const int hit = (int)(x > NEG_INF) & ((int)(b == tb[qb][0]) | (int)(b == tb[qb][1]) |
+                                                          (int)(b == tb[qb][2]) | (int)(b == tb[qb][3]));
+                    const int slot = qb == 0 ? min(cc[0], kCtSlots - 1) : max(kCtSlots - 1 - cc[1], 0);
+                    lds_store(reg_off + (uint32_t)slot * 4u, x);
+                    cc[qb] += hit;
+                }
+        }
+    });
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the written-out stores are done
+    s_ccnt[wave][lane][0] = cc[0];
+    s_ccnt[wave][lane][1] = cc[1];
+    {
+        // the two rows' members and their scratch slots must not meet
+        int o = cc[0] + cc[1] > kCtSlots - 1 ? 1 : 0;
+        o |= __shfl_xor(o, 16);
+        o |= __shfl_xor(o, 32);
+        if (lq == 0) s_lovf[wave][l16] = o;
+    }
+    __syncthreads();
+
+    // ---- exact value: one lane per (row, target) entry
+    {
+        const float* pool = reinterpret_cast<const float*>(hw);
+        for (int e = lane; e < 32 * n_k; e += 64) {
+            const int rl = e / n_k;
+            const int tbe = s_etb[wave][e];
+            const int rank = s_erank[wave][e];
+            const int m = s_ecnt[wave][e];
+            if (tbe < 0 || rank <= 0) continue;
+            const int qb = rl >> 4, g16 = rl & 15;
+            if (s_lovf[wave][g16] || m > 2 * kCtNet) {
+                s_erank[wave][e] = -1;
+                const unsigned idx = atomicAdd(a.fix_count, 1u);
+                const int t = e - rl * n_k;
+                a.fix_list[idx] = make_uint4((unsigned)sq, (unsigned)h, (unsigned)(row0 + rl) | ((unsigned)t << 16),
+                                             __float_as_uint(s_rlse[wave][rl]));
+                continue;
+            }
+            const bool top = rank <= kCtNet;            // keep the largest members, else the smallest
+            const int rr = top ? rank : m - rank + 1;
+            const float M = s_rM[wave][rl], bs = s_rbs[wave][rl];
+            // the network only needs rr registers: the smallest of 4, 8, 16, 32 that covers
+            // every active lane of the wave (the branch is wave-uniform)
+            int need = rr;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) need = max(need, __shfl_xor(need, o));
+            float val;
+            if (need <= 4) val = ct_select<4>(pool, wave, s_ccnt, g16, qb, tbe, M, bs, top, rr);
+            else if (need <= 8) val = ct_select<8>(pool, wave, s_ccnt, g16, qb, tbe, M, bs, top, rr);
+            else if (need <= 16) val = ct_select<16>(pool, wave, s_ccnt, g16, qb, tbe, M, bs, top, rr);
+            else val = ct_select<32>(pool, wave, s_ccnt, g16, qb, tbe, M, bs, top, rr);
+            s_eval[wave][e] = val;
+        }
+    }
+    __syncthreads();
+
+    // ---- samples: lanes 0..15 hold rows l16 and 16 + l16
+    if (lq == 0) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = row0 + 16 * qb + l16;
+            if (row >= a.L) continue;
+            for (int t = 0; t < n_k; ++t) {
+                const int e = (16 * qb + l16) * n_k + t;
+                const size_t o = (((size_t)sq * n_k + t) * a.Hq + h) * a.L + row;
+                if (row + 1 <= a.ks[t]) { a.samples[o] = NAN; continue; }
+                if (s_erank[wave][e] < 0) continue;     // the fixup writes it
+                const float xk = s_eval[wave][e];
+                a.samples[o] = a.pre ? xk * a.scale : exp2f(fmaf(xk, a.xscale, -lse2[qb]));
+            }
+        }
+    }
+#endif
+}
+
+// Exact samples of the listed (sequence, head, row, target) entries: the row's
+// scores from plain dot products into LDS, then a radix select (8-bit digits
+// of the order-preserving key, from the top) of the k-th largest.  Grid-stride
+// over the entries the tiled kernel listed.
+template <int D>
+__global__ __launch_bounds__(256) void calib_fixup_kernel(CalibTArgs a) {
+    extern __shared__ float fx[];                            // scores of one row
+    __shared__ uint32_t s_h[256];
+    __shared__ int s_dig, s_rem;
+    constexpr int LPR = D / 8;                               // lanes per key row (8 bf16 per lane)
+    constexpr int RPW = 64 / LPR;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sub = lane % LPR, grp = lane / LPR;
+    const unsigned total = *a.fix_count;
+    for (unsigned e = blockIdx.x; e < total; e += gridDim.x) {
+        const uint4 ent = a.fix_list[e];
+        const int sq = (int)ent.x, h = (int)ent.y, row = (int)(ent.z & 0xffffu), t = (int)(ent.z >> 16);
+        const float lse2 = __uint_as_float(ent.w);
+        const int n = row + 1;
+        const int g = a.Hq / a.Hkv;
+        const uint16_t* qr = a.q + (((size_t)sq * a.Hq + h) * a.L + row) * D;
+        const uint16_t* kg = a.k + ((size_t)sq * a.Hkv + h / g) * (size_t)a.L * D;
+        float qv[8];
+        {
+            const u32x4 u = *(const u32x4*)(qr + 8 * sub);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { qv[2 * i] = __uint_as_float(u[i] << 16); qv[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u); }
+        }
+        for (int j0 = wave * RPW; j0 < n; j0 += 4 * RPW) {
+            const int j = j0 + grp;
+            float dot = 0.f;
+            if (j < n) {
+                const u32x4 u = *(const u32x4*)(kg + (size_t)j * D + 8 * sub);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dot = fmaf(qv[2 * i], __uint_as_float(u[i] << 16), dot);
+                    dot = fmaf(qv[2 * i + 1], __uint_as_float(u[i] & 0xffff0000u), dot);
+                }
+            }
+#pragma unroll
+            for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);
+            if (j < n && sub == 0) fx[j] = dot;
+        }
+        __syncthreads();
+        uint32_t prefix = 0u, mask = 0u;
+        int rem = a.ks[t];
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            s_h[tid] = 0u;
+            __syncthreads();
+            for (int j = tid; j < n; j += 256) {
+                const uint32_t key = float_to_ordered(fx[j]);
+                if ((key & mask) == prefix) atomicAdd(&s_h[(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                int cum = 0, d = 255;
+                for (; d > 0; --d) {
+                    if (cum + (int)s_h[d] >= rem) break;
+                    cum += (int)s_h[d];
+                }
+                s_dig = d;
+                s_rem = rem - cum;
+            }
+            __syncthreads();
+            prefix |= (uint32_t)s_dig << shift;
+            mask |= 255u << shift;
+            rem = s_rem;
+            __syncthreads();
+        }
+        if (tid == 0) {
+            const float xk = ordered_to_float(prefix);
+            const size_t o = (((size_t)sq * a.n_k + t) * a.Hq + h) * a.L + row;
+            a.samples[o] = a.pre ? xk * a.scale : exp2f(fmaf(xk, a.xscale, -lse2));
+        }
+        __syncthreads();                                     // fx is rewritten by the next entry
+    }
+}
+
 // ------------------------------------------------------------------ host side
 int launch_calib_accumulate(const float* samples, const float* esamples, int S, int n_k, int Hq, int Lq,
                             int q_pos0, double* sum, double* sumsq, int* count, double* esum, int n_rows,
@@ -518,7 +1097,64 @@ static int launch_calib_d(const CalibKArgs& a, int cols, hipStream_t s) {
     }
 }
 
+template <int D, int G>
+static int launch_tiled_variant(const CalibTArgs& a, hipStream_t s) {
+    using C = CtCfg<D, G>;
+    const dim3 grid((a.L + C::BMT - 1) / C::BMT, a.Hkv * (G / C::HPW), a.S);
+    hipLaunchKernelGGL((calib_tiled_kernel<D, G>), grid, dim3(kCtWaves * 64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the listed entries (usually none): every workgroup reads the count and
+    // exits when there is nothing left for it
+    hipLaunchKernelGGL((calib_fixup_kernel<D>), dim3(256), dim3(256), (size_t)a.L * sizeof(float), s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+static int launch_tiled_d(const CalibTArgs& a, int G, hipStream_t s) {
+    switch (G) {
+        case 1: return launch_tiled_variant<D, 1>(a, s);
+        case 2: return launch_tiled_variant<D, 2>(a, s);
+        case 4: return launch_tiled_variant<D, 4>(a, s);
+        case 8: return launch_tiled_variant<D, 8>(a, s);
+        default: return launch_tiled_variant<D, 16>(a, s);
+    }
+}
+
+// whole causal prefills of up to 4096 keys with at most four targets and no
+// discarded-mass samples take the tiled kernel
+static bool tiled_path(const CalibParams& p) {
+    const int G = p.Hq / p.Hkv;
+    return p.q_pos0 == 0 && p.Lq == p.Lk && p.Lk <= 4096 && p.esum == nullptr && p.n_k <= kCtMaxK &&
+           (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) && p.S <= 65535;
+}
+
 int launch_calibrate_bf16(const CalibParams& p, float* samples_ws, hipStream_t s) {
+    if (tiled_path(p)) {
+        CalibTArgs t = {};
+        t.q = (const uint16_t*)p.q; t.k = (const uint16_t*)p.k;
+        t.S = p.S; t.Hq = p.Hq; t.Hkv = p.Hkv; t.L = p.Lq;
+        t.xscale = p.scale * kLog2e; t.scale = p.scale;
+        t.kmax = 0;
+        for (int i = 0; i < kCtMaxK; ++i) {
+            t.ks[i] = i < p.n_k ? p.ks[i] : 0;
+            if (i < p.n_k && p.ks[i] > t.kmax) t.kmax = p.ks[i];
+        }
+        t.n_k = p.n_k;
+        t.samples = samples_ws;
+        t.pre = p.pre ? 1 : 0;
+        // workspace: samples, the fixup count, the fixup list
+        const size_t n = (size_t)p.S * p.n_k * p.Hq * p.Lq;
+        char* base = (char*)samples_ws + ((n * sizeof(float) + 255) & ~(size_t)255);
+        t.fix_count = (unsigned*)base;
+        t.fix_list = (uint4*)(base + 256);
+        int e = launch_fill_u32(t.fix_count, 4, 0u, s);
+        if (e != hipSuccess) return e;
+        e = p.d == 64 ? launch_tiled_d<64>(t, p.Hq / p.Hkv, s) : launch_tiled_d<128>(t, p.Hq / p.Hkv, s);
+        if (e != hipSuccess) return e;
+        return launch_calib_accumulate(samples_ws, nullptr, p.S, p.n_k, p.Hq, p.Lq, p.q_pos0, p.sum, p.sumsq,
+                                       p.count, nullptr, p.n_rows, s);
+    }
     CalibKArgs a = {};
     a.q = (const uint16_t*)p.q; a.k = (const uint16_t*)p.k;
     a.S = p.S; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Lq = p.Lq; a.Lk = p.Lk; a.q_pos0 = p.q_pos0;
