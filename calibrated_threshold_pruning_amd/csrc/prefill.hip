@@ -29,11 +29,17 @@
 // P V in float16: when the caller's workspace has room, a pre-pass copies V to
 // float16 (exact for bfloat16 values of magnitude up to 16, which it checks)
 // and the P V product takes one f16 MFMA per block with P rounded to float16
-// (relative error 2^-11, so at most 2^-11 * 16 < 1e-2 on any output) instead
-// of the two bf16 MFMAs of the high/low split.  A V element beyond 16 (or not
-// finite) sets a flag.  Both kernels (F16 and not) are launched; each reads
-// the flag first and only the one that matches it does the work (the other
-// grid exits at once), so neither carries the other's registers.
+// instead of the two bf16 MFMAs of the high/low split.  P enters scaled by
+// 2^7 (folded into the exp2 offset of the row, undone in the epilogue): a
+// weight is at most 2^8 * 2^7 in float16, and only weights below 2^-21 fall
+// into the float16 subnormals, whose absolute rounding error is at most
+// 2^-25 * 2^-7.  Per output: 2^-11 * 16 from the relative rounding of the
+// normal weights (they sum to at most 1 after normalisation) plus at most
+// L * 2^-32 * 16 from the subnormal ones, under 8.1e-3 for L <= 2^16.  A V
+// element beyond 16 (or not finite) sets a flag.  Both kernels (F16 and not)
+// are launched; each reads the flag first and only the one that matches it
+// does the work (the other grid exits at once), so neither carries the
+// other's registers.
 #include "topth_internal.h"
 
 #include <math.h>
@@ -118,6 +124,7 @@ template <int D, int G, bool MASK, bool PRE, bool F16, bool MASS>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     using C = PrefillCfg<D, G>;
+    constexpr int PSC = F16 ? 7 : 0;                       // log2 of the P scale of the float16 P V form
     // four tile slots: sweep B double-buffers K in slots 0-1 and V in slots
     // 2-3; sweep A, which reads no V, rotates K through all four
     __shared__ __attribute__((aligned(16))) unsigned char s_kv[4][C::KTILE];
@@ -358,7 +365,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                         if (key <= row) kmask[(size_t)row * a.L + key] = st[qb][kb][r] >= thr[qb] ? 1 : 0;
                     }
             }
-            float nlse = -lse2[qb];
+            // float16 P V: weights scaled by 2^PSC (see the file header)
+            float nlse = -lse2[qb] + (float)PSC;
             if constexpr (PRE) {
                 float tmax = NEG_INF;
 #pragma unroll
@@ -378,7 +386,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                     mass[qb] *= f;
                     mref[qb] = tmax;
                 }
-                nlse = mref[qb] == NEG_INF ? 0.f : -mref[qb] * a.xscale;
+                nlse = (mref[qb] == NEG_INF ? 0.f : -mref[qb] * a.xscale) + (float)PSC;
             }
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -454,7 +462,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
 
-    // ---- epilogue: row totals, SDC_NONE / VMC, output
+    // ---- epilogue: row totals, SDC_NONE / VMC, output (weights, sums and
+    // accumulators lose the 2^PSC of the float16 form first)
+    const float unscale = 1.0f / (float)(1 << PSC);
     const bool renorm = (a.flags & 2u) != 0;
     const bool vmc = (a.flags & 1u) != 0 && !renorm;
     uint16_t* og = a.out + ((size_t)b * a.Hq + h) * (size_t)a.L * D;
@@ -466,6 +476,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         float m = mass[qb];
         m += __shfl_xor(m, 16);
         m += __shfl_xor(m, 32);
+        m *= unscale;
         const int row = row0 + 16 * qb + l16;
         if (row >= a.L) continue;
         float bta = renorm ? 0.f : 1.f - m;
@@ -475,6 +486,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
             float l = lall[qb];
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
+            l *= unscale;
             const int rid = min(row, a.n_rows - 1);
             float den;
             if (renorm) den = m;
@@ -500,7 +512,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int dim = 16 * db + 4 * lq + r;
-                float v = o[qb][db][r];
+                float v = o[qb][db][r] * unscale;
                 if (PRE || renorm) v = c > 0 ? v * inv : 0.f;
                 if (vmc) v = fmaf(bta, mu[dim], v);
                 y[r] = v;

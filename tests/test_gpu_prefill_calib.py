@@ -384,3 +384,30 @@ def test_prefill_bf16_pv_forms(case):
             continue                     # VMC needs the workspace
         g = run_prefill(q, k, v, theta, flags, with_ws=case != "no_ws", with_beta=with_beta)
         compare_prefill(g, q, k, v, theta, flags, torch.bfloat16)
+
+
+def test_prefill_f16_pv_long_keep_all_rows_large_v():
+    """The float16 P V form on its worst case: rows of up to 8192 keys that keep
+    every element, a peaked softmax (most weights far below the float16 normal
+    range) and every V element at +-15.875, just inside the float16 form's bound
+    of 16.  Sampled rows against the oracle at the bf16 tolerance."""
+    dev = device()
+    L, d = 8192, 128
+    print("prefill float16 P V, keep-all rows of 8192 keys, |V| = 15.875", flush=True)
+    q, k, _ = attention_inputs(UNIT, ROLE_TEST, 21, 0, B=1, Hq=1, Hkv=1, Lq=L, Lk=L, d=d, with_v=False)
+    q = (q.float() * 6.0).to(torch.bfloat16)          # wide score spread: many tiny weights
+    sign = torch.from_numpy(np.random.default_rng(3).integers(0, 2, size=(1, 1, L, d)) * 2 - 1)
+    v = (15.875 * sign).to(torch.bfloat16)
+    theta = np.full((1, 1), -np.inf)
+    out = torch.empty(1, 1, L, d, dtype=torch.bfloat16, device=dev)
+    ws = tt.workspace(tt.TOPTH_OP_PREFILL, 1, 1, 1, L, L, d)
+    tt.topth_prefill(q.to(dev), k.to(dev), v.to(dev), torch.tensor(theta, dtype=torch.float32, device=dev), out,
+                     scale=1.0 / np.sqrt(d), flags=0, ws=ws)
+    torch.cuda.synchronize()
+    rows = [(0, 0, p) for p in (8191, 6000, 4096, 100)]
+    ref = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), theta, 1.0 / np.sqrt(d), vmc=False, rows=rows)
+    g = out.float().cpu().numpy()
+    for (_, _, p) in rows:
+        s = oracle.post_softmax(oracle.scores(to_f64(q)[0, 0, p], to_f64(k)[0, 0, :p + 1], 1.0 / np.sqrt(d)))[0]
+        assert (s < 2.0 ** -14).sum() > p // 2            # most weights are float16 subnormals unscaled
+        check_out(g[0, 0, p], ref.out[0, 0, p], torch.bfloat16, f"row {p}")
