@@ -16,5 +16,5 @@ from ._lib import (  # noqa: F401
     TOPTH_WS_HEADER_BYTES, TOPTH_STATUS_EXCHANGE_TIMEOUT, topth_workspace_status,
     topth_workspace_set_spin_limit, TOPTH_ESCRATCH, TOPTH_NOALLOC_SCRATCH_BYTES, topth_decode_noalloc,
     TOPTH_OP_CALIBRATE_MKC, TOPTH_MKC_MAX_TARGETS, TOPTH_MKC_MAX_SAMPLES, TOPTH_MKC_MAX_KEYS,
-    topth_calibrate_mkc,
+    topth_calibrate_mkc, TOPTH_OUT_F32,
 )

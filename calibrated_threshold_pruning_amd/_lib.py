@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libtopth.so")
 TOPTH_F32, TOPTH_BF16 = 0, 1
 TOPTH_VMC, TOPTH_SDC_NONE = 0x1, 0x2
 TOPTH_SDC_EXPTH, TOPTH_SDC_OFFLINE = 0x4, 0x8
+TOPTH_OUT_F32 = 0x10
 TOPTH_OP_CALIBRATE, TOPTH_OP_PREFILL, TOPTH_OP_DECODE, TOPTH_OP_CALIBRATE_PRE_E = 0, 1, 2, 3
 TOPTH_OP_CALIBRATE_MKC = 4
 TOPTH_MKC_MAX_TARGETS, TOPTH_MKC_MAX_SAMPLES, TOPTH_MKC_MAX_KEYS = 64, 4096, 32768
@@ -118,6 +119,11 @@ def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return TOPTH_BF16
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _out_dtype(q: torch.Tensor, flags: int):
+    """dtype of the output: float32 with TOPTH_OUT_F32, else the input dtype"""
+    return torch.float32 if int(flags) & TOPTH_OUT_F32 else q.dtype
 
 
 def _dev(t, name, dtype=None, shape=None, optional=False):
@@ -247,7 +253,7 @@ def topth_prefill(q, k, v, theta, out, *, scale: float, flags: int, kept_count=N
     _dev(theta, "theta", torch.float32)
     if theta.dim() != 2 or theta.shape[0] != Hq:
         raise ValueError("theta must be [Hq, n_rows]")
-    _dev(out, "out", q.dtype, (B, Hq, L, d))
+    _dev(out, "out", _out_dtype(q, flags), (B, Hq, L, d))
     kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq, L), optional=True)
     bt = _dev(beta, "beta", torch.float32, (B, Hq, L), optional=True)
     km = _dev(kept_mask, "kept_mask", torch.uint8, (B, Hq, L, L), optional=True)
@@ -270,7 +276,7 @@ def topth_decode(q, k_cache, v_cache, seq_lens, theta, out, ws, *, scale: float,
     _dev(theta, "theta", torch.float32)
     if theta.dim() != 2 or theta.shape[0] != Hq:
         raise ValueError("theta must be [Hq, n_rows]")
-    _dev(out, "out", q.dtype, (B, Hq, d))
+    _dev(out, "out", _out_dtype(q, flags), (B, Hq, d))
     vm = _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d), optional=True)
     kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq), optional=True)
     bt = _dev(beta, "beta", torch.float32, (B, Hq), optional=True)
@@ -295,7 +301,7 @@ def topth_decode_noalloc(q, k_cache, v_cache, seq_lens, theta, out, *, scale: fl
     _dev(v_cache, "v_cache", q.dtype, (B, Hkv, Lmax, d))
     _dev(seq_lens, "seq_lens", torch.int32, (B,))
     _table(theta, "theta", Hq)
-    _dev(out, "out", q.dtype, (B, Hq, d))
+    _dev(out, "out", _out_dtype(q, flags), (B, Hq, d))
     vm = _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d), optional=True)
     kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq), optional=True)
     bt = _dev(beta, "beta", torch.float32, (B, Hq), optional=True)
@@ -321,7 +327,7 @@ def topth_decode_append(q, k_cache, v_cache, seq_lens, theta, out, ws, v_mean, *
     _dev(theta, "theta", torch.float32)
     if theta.dim() != 2 or theta.shape[0] != Hq:
         raise ValueError("theta must be [Hq, n_rows]")
-    _dev(out, "out", q.dtype, (B, Hq, d))
+    _dev(out, "out", _out_dtype(q, flags), (B, Hq, d))
     _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d))
     kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq), optional=True)
     bt = _dev(beta, "beta", torch.float32, (B, Hq), optional=True)
@@ -393,7 +399,7 @@ def topth_prefill_pre(q, k, v, theta, out, *, scale: float, flags: int, gamma: f
     _dev(q, "q"); _dev(k, "k", q.dtype, (B, Hkv, L, d)); _dev(v, "v", q.dtype, (B, Hkv, L, d))
     _table(theta, "theta", Hq)
     et = _table(e_tilde, "e_tilde", Hq, theta.shape[1], optional=True)
-    _dev(out, "out", q.dtype, (B, Hq, L, d))
+    _dev(out, "out", _out_dtype(q, flags), (B, Hq, L, d))
     kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq, L), optional=True)
     bt = _dev(beta, "beta", torch.float32, (B, Hq, L), optional=True)
     km = _dev(kept_mask, "kept_mask", torch.uint8, (B, Hq, L, L), optional=True)
@@ -416,7 +422,7 @@ def topth_decode_pre(q, k_cache, v_cache, seq_lens, theta, out, ws, *, scale: fl
     _dev(seq_lens, "seq_lens", torch.int32, (B,))
     _table(theta, "theta", Hq)
     et = _table(e_tilde, "e_tilde", Hq, theta.shape[1], optional=True)
-    _dev(out, "out", q.dtype, (B, Hq, d))
+    _dev(out, "out", _out_dtype(q, flags), (B, Hq, d))
     vm = _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d), optional=True)
     kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq), optional=True)
     bt = _dev(beta, "beta", torch.float32, (B, Hq), optional=True)
@@ -482,7 +488,7 @@ def topth_decode_gqa(q, k_cache, v_cache, seq_lens, theta, out, ws, *, scale: fl
     _dev(v_cache, "v_cache", q.dtype, (B, Hkv, Lmax, d))
     _dev(seq_lens, "seq_lens", torch.int32, (B,))
     _table(theta, "theta", Hq)
-    _dev(out, "out", q.dtype, (B, Hq, d))
+    _dev(out, "out", _out_dtype(q, flags), (B, Hq, d))
     vm = _dev(v_mean, "v_mean", torch.float32, (B, Hkv, d), optional=True)
     kc = _dev(kept_count, "kept_count", torch.int32, (B, Hq), optional=True)
     bt = _dev(beta, "beta", torch.float32, (B, Hq), optional=True)

@@ -40,6 +40,8 @@ int launch_theta_eval(const double* coef, const int* ks, int n_k, int Hq, int de
 using namespace topth;
 
 static_assert(kNoallocScratchBytes == (size_t)TOPTH_NOALLOC_SCRATCH_BYTES, "scratch size of the header");
+static_assert(kFlagOutF32 == TOPTH_OUT_F32 && kFlagVmc == TOPTH_VMC && kFlagNone == TOPTH_SDC_NONE &&
+                  kFlagExpth == TOPTH_SDC_EXPTH && kFlagOffline == TOPTH_SDC_OFFLINE, "flag bits of the header");
 static_assert(kWsHeaderBytes == TOPTH_WS_HEADER_BYTES && kStatusSpinTimeout == TOPTH_STATUS_EXCHANGE_TIMEOUT,
               "workspace header layout of the header");
 
@@ -265,6 +267,8 @@ int prefill_common(const void* q, const void* k, const void* v, int B, int Hq, i
     if (!q || !k || !v || !theta || !out) return TOPTH_EINVAL;
     if (bad_dims(B, Hq, Hkv, L, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
     if (!isfinite(scale) || !(scale > 0.0f)) return TOPTH_EINVAL;
+    const unsigned out_f32 = (flags & TOPTH_OUT_F32) && dtype == TOPTH_BF16 ? kFlagOutF32 : 0u;
+    flags &= ~TOPTH_OUT_F32;
     if (pre ? bad_pre_flags(flags, e_tilde, gamma) : (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE)) != 0)
         return TOPTH_EINVAL;
     if (too_big((long long)B * Hq * L, d)) return TOPTH_EUNSUPPORTED;
@@ -278,7 +282,7 @@ int prefill_common(const void* q, const void* k, const void* v, int B, int Hq, i
     }
     PrefillParams p = {};
     p.q = q; p.k = k; p.v = v; p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.d = d; p.dtype = dtype;
-    p.scale = scale; p.theta = theta; p.n_rows = n_rows; p.flags = flags;
+    p.scale = scale; p.theta = theta; p.n_rows = n_rows; p.flags = flags | out_f32;
     p.out = out; p.kept_count = kept_count; p.beta = beta; p.kept_mask = kept_mask;
     p.ws = ws; p.ws_bytes = ws_bytes;
     if (pre) { p.flags |= kFlagPre; p.e_tilde = e_tilde; p.gamma = gamma; }
@@ -320,6 +324,8 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
     if (!q || !k_cache || !v_cache || !seq_lens || !theta || !out) return TOPTH_EINVAL;
     if (bad_dims(B, Hq, Hkv, Lmax, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
     if (!isfinite(scale) || !(scale > 0.0f)) return TOPTH_EINVAL;
+    const unsigned out_f32 = (flags & TOPTH_OUT_F32) && dtype == TOPTH_BF16 ? kFlagOutF32 : 0u;
+    flags &= ~TOPTH_OUT_F32;
     if (pre ? bad_pre_flags(flags, e_tilde, gamma) : (flags & ~(TOPTH_VMC | TOPTH_SDC_NONE)) != 0)
         return TOPTH_EINVAL;
     if ((flags & TOPTH_VMC) && !(flags & TOPTH_SDC_NONE) && !v_mean) return TOPTH_EINVAL;
@@ -329,7 +335,7 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
     DecodeParams p = {};
     p.q = q; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lmax = Lmax; p.d = d; p.dtype = dtype; p.scale = scale;
-    p.theta = theta; p.n_rows = n_rows; p.v_mean = v_mean; p.flags = flags;
+    p.theta = theta; p.n_rows = n_rows; p.v_mean = v_mean; p.flags = flags | out_f32;
     p.out = out; p.kept_count = kept_count; p.beta = beta; p.vrows_read = vrows_read;
     p.kept_mask = kept_mask; p.ws = ws; p.ws_bytes = ws_bytes;
     if (pre) { p.flags |= kFlagPre; p.e_tilde = e_tilde; p.gamma = gamma; }
@@ -384,13 +390,15 @@ int topth_decode_noalloc(const void* q, const void* k_cache, const void* v_cache
     if (!q || !k_cache || !v_cache || !seq_lens || !theta || !out) return TOPTH_EINVAL;
     if (bad_dims(B, Hq, Hkv, Lmax, d) || bad_dtype(dtype) || n_rows <= 0) return TOPTH_EINVAL;
     if (!isfinite(scale) || !(scale > 0.0f)) return TOPTH_EINVAL;
+    const unsigned out_f32 = (flags & TOPTH_OUT_F32) && dtype == TOPTH_BF16 ? kFlagOutF32 : 0u;
+    flags &= ~TOPTH_OUT_F32;
     if ((flags & ~(TOPTH_VMC | TOPTH_SDC_NONE)) != 0) return TOPTH_EINVAL;
     if ((flags & TOPTH_VMC) && !(flags & TOPTH_SDC_NONE) && !v_mean) return TOPTH_EINVAL;
     if (too_big((long long)B * Hkv * Lmax, d)) return TOPTH_EUNSUPPORTED;
     DecodeParams p = {};
     p.q = q; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lmax = Lmax; p.d = d; p.dtype = dtype; p.scale = scale;
-    p.theta = theta; p.n_rows = n_rows; p.v_mean = v_mean; p.flags = flags;
+    p.theta = theta; p.n_rows = n_rows; p.v_mean = v_mean; p.flags = flags | out_f32;
     p.out = out; p.kept_count = kept_count; p.beta = beta; p.vrows_read = vrows_read;
     p.kept_mask = kept_mask; p.min_votes = 1; p.augment = 0;
     if (dtype == TOPTH_BF16) {

@@ -204,8 +204,11 @@ constexpr unsigned kDefaultSpinLimit = 1u << 22;
 template <int D, int G>
 __device__ __forceinline__ void poison_group(const DecodeKArgs& a, int b, int kv, int group, int tid,
                                              int nthreads) {
-    for (int idx = tid; idx < G * D; idx += nthreads)
-        a.out[((size_t)b * a.Hq + (size_t)kv * G) * D + idx] = 0x7FC0u;   // bfloat16 NaN
+    const size_t o0 = ((size_t)b * a.Hq + (size_t)kv * G) * D;
+    for (int idx = tid; idx < G * D; idx += nthreads) {
+        if (a.flags & kFlagOutF32) ((float*)a.out)[o0 + idx] = __uint_as_float(0x7FC00000u);
+        else a.out[o0 + idx] = 0x7FC0u;                                    // bfloat16 NaN
+    }
     if (tid < G) {
         const size_t o = (size_t)b * a.Hq + (size_t)kv * G + tid;
         if (a.kept_count) a.kept_count[o] = -1;
@@ -978,7 +981,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
                 if (renorm) x = (s_cc[0][h] > 0) ? x / mass : 0.f;
                 else if (a.flags & (kFlagExpth | kFlagOffline)) x *= s_T[h];
                 if (vmc) x = fmaf(s_M[h], mu_rw != nullptr ? s_mu[dd] : a.v_mean[(size_t)group * D + dd], x);
-                a.out[((size_t)b * a.Hq + (size_t)kv * G + h) * D + dd] = f32_to_bf16_bits(x);
+                const size_t oi = ((size_t)b * a.Hq + (size_t)kv * G + h) * D + dd;
+                if (a.flags & kFlagOutF32) ((float*)a.out)[oi] = x;
+                else a.out[oi] = f32_to_bf16_bits(x);
             }
             // every read of the previous mean happened before the barrier above
             if (mu_rw != nullptr)

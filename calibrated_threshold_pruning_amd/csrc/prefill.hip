@@ -467,7 +467,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
     const float unscale = 1.0f / (float)(1 << PSC);
     const bool renorm = (a.flags & 2u) != 0;
     const bool vmc = (a.flags & 1u) != 0 && !renorm;
-    uint16_t* og = a.out + ((size_t)b * a.Hq + h) * (size_t)a.L * D;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         int c = cnt[qb];
@@ -517,8 +516,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                 if (vmc) v = fmaf(bta, mu[dim], v);
                 y[r] = v;
             }
-            uint2 packed = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-            *(uint2*)(og + (size_t)row * D + 16 * db + 4 * lq) = packed;
+            const size_t oi = ((((size_t)b * a.Hq + h) * (size_t)a.L) + row) * D + 16 * db + 4 * lq;
+            if (a.flags & kFlagOutF32) {
+                *(float4*)((float*)a.out + oi) = make_float4(y[0], y[1], y[2], y[3]);
+            } else {
+                *(uint2*)(a.out + oi) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            }
         }
     }
 #endif

@@ -93,6 +93,7 @@ __device__ __forceinline__ float pre_log2_threshold(float theta) {
 // pre-softmax calls).  kFlagExpth / kFlagOffline select the estimate of the
 // discarded softmax mass E~; neither (and not kFlagNone) means exact E.
 constexpr unsigned kFlagVmc = 0x1u, kFlagNone = 0x2u, kFlagExpth = 0x4u, kFlagOffline = 0x8u;
+constexpr unsigned kFlagOutF32 = 0x10u;   // bfloat16 inputs: out is float32
 constexpr unsigned kFlagPre = 0x100u;
 
 // Scale f and beta of a row from its kept post-softmax mass S = R / (R + E),

@@ -107,6 +107,10 @@ typedef enum { TOPTH_F32 = 0, TOPTH_BF16 = 1 } topth_dtype;
    with none of TOPTH_SDC_NONE / _EXPTH / _OFFLINE set, E~ is the exact E      */
 #define TOPTH_SDC_EXPTH   0x4u  /* exp-threshold: E~ = gamma (n - k~) exp(theta - max a) */
 #define TOPTH_SDC_OFFLINE 0x8u  /* offline-calibrated: E~ = e_tilde[h][row]              */
+/* output format of every prefill and decode call: with TOPTH_BF16 inputs, out
+   is float32 (the float32 result before any bfloat16 rounding) instead of
+   bfloat16, same shape; with TOPTH_F32 inputs out is float32 either way      */
+#define TOPTH_OUT_F32     0x10u
 
 /* op codes of topth_workspace_size */
 #define TOPTH_OP_CALIBRATE 0
@@ -235,14 +239,16 @@ int topth_calibrate_finalize(const double* sum, const double* sumsq, const int* 
  * of V rows 0..p.  With TOPTH_SDC_NONE the kept weights are divided by their
  * sum (out = 0 for a row that keeps nothing) and beta = 0.
  *   q device [B][Hq][L][d]; k, v device [B][Hkv][L][d]; theta device
- *   [Hq][n_rows]; out device [B][Hq][L][d] of the input dtype;
+ *   [Hq][n_rows]; out device [B][Hq][L][d] of the input dtype (float32
+ *   with TOPTH_OUT_F32);
  *   kept_count device int [B][Hq][L] or NULL; beta device float [B][Hq][L]
  *   or NULL; kept_mask device uint8 [B][Hq][L][L] or NULL: 1 where key j <= p
  *   is kept by row p (entries j > p are not written); ws device, or NULL
  *   without TOPTH_VMC.  With topth_workspace_size(TOPTH_OP_PREFILL, ...)
  *   bytes the bfloat16 path copies V to float16 there and, when every V
- *   element is within 16 in magnitude, forms P V in float16 (P rounded to
- *   float16: at most 2^-11 * 16 absolute error per output); otherwise, or
+ *   element is within 16 in magnitude, forms P V in float16 (P scaled by 2^7
+ *   and rounded to float16: under 8.1e-3 absolute error per output for
+ *   L <= 65536); otherwise, or
  *   with a smaller workspace (VMC needs the first B*Hkv*L*d floats of it for
  *   the prefix means), P V uses a bfloat16 high/low split of P.
  */
@@ -263,7 +269,7 @@ int topth_prefill(const void* q, const void* k, const void* v, int B, int Hq, in
  *   that range); theta device [Hq][n_rows];
  *   v_mean device float [B][Hkv][d], the running mean of the first n V rows
  *   (Sec. 3.2.2), required iff TOPTH_VMC; out device [B][Hq][d] of the input
- *   dtype; kept_count device int [B][Hq] or NULL; beta device float [B][Hq]
+ *   dtype (float32 with TOPTH_OUT_F32); kept_count device int [B][Hq] or NULL; beta device float [B][Hq]
  *   or NULL; vrows_read device int [B][Hkv] or NULL: number of distinct V
  *   rows read for the group (the union of its heads' kept keys);
  *   kept_mask device uint8 [B][Hq][Lmax] or NULL: 1 where key j < n is kept

@@ -35,6 +35,19 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(tt.EXPORTS)
 
 
+def test_binding_constants_match_the_header():
+    """Every #define of the header that the binding mirrors has the same value."""
+    text = open(HEADER).read()
+    macros = {}
+    for name, val in re.findall(r"#define\s+(TOPTH_[A-Z0-9_]+)\s+(\(?[0-9xXa-fA-Fu <()]+\)?)", text):
+        macros[name] = eval(val.replace("u", ""), {})
+    mirrored = [n for n in macros if hasattr(tt._lib, n)]
+    assert {"TOPTH_VMC", "TOPTH_SDC_NONE", "TOPTH_SDC_EXPTH", "TOPTH_SDC_OFFLINE", "TOPTH_OUT_F32",
+            "TOPTH_WS_HEADER_BYTES", "TOPTH_NOALLOC_SCRATCH_BYTES", "TOPTH_MAX_NK"} <= set(mirrored)
+    for n in mirrored:
+        assert getattr(tt._lib, n) == macros[n], n
+
+
 def test_strerror(lib):
     assert tt.topth_strerror(0) == "success"
     assert "invalid" in tt.topth_strerror(-1)
@@ -97,7 +110,7 @@ def test_prefill_argument_errors(lib):
     assert call(theta=None) == -1
     assert call(L=0) == -1
     assert call(Hkv=3) == -1
-    assert call(flags=0x10) == -1
+    assert call(flags=0x20) == -1
     assert call(ws=None) == -3           # VMC needs the prefix-mean workspace
     assert call(wsb=16) == -3
 
@@ -178,7 +191,7 @@ def test_pre_flag_errors(lib):
         assert call(lib, flags=O) == -1                     # offline needs the E~ table
         assert call(lib, flags=E, gamma=float("nan")) == -1
         assert call(lib, flags=E, gamma=-0.5) == -1
-        assert call(lib, flags=0x10) == -1
+        assert call(lib, flags=0x20) == -1
         assert call(lib, theta=None) == -1
         assert call(lib, scale=0.0) == -1
     assert _decode_pre(lib, flags=tt.TOPTH_VMC, vm=None) == -1   # VMC needs the running mean
@@ -239,7 +252,7 @@ def test_decode_append_errors(lib):
                                        FAKE, None, None, None, None, ws, 1 << 30, None)
     assert call(vm=None) == -1              # the running mean is always read and updated
     assert call(vm=None, flags=0) == -1
-    assert call(flags=0x10) == -1           # unknown flag
+    assert call(flags=0x20) == -1           # unknown flag
     assert call(d=96) == -1
     assert call(ws=None) == -3
 
