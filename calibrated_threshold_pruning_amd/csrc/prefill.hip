@@ -27,8 +27,10 @@
 // (Sec. 3.2.1: exact, exp-threshold, offline-calibrated, or none).
 //
 // P V in float16: when the caller's workspace has room, a pre-pass copies V to
-// float16 (exact for bfloat16 values of magnitude up to 16, which it checks)
-// and the P V product takes one f16 MFMA per block with P rounded to float16
+// float16 (exact for bfloat16 values of magnitude in [2^-14, 16] and zero;
+// smaller ones land on the float16 subnormal grid, off by at most 2^-25, which
+// moves an output by at most 2^-25 since the weights sum to at most 1; the
+// bound of 16 is checked) and the P V product takes one f16 MFMA per block with P rounded to float16
 // instead of the two bf16 MFMAs of the high/low split.  P enters scaled by
 // 2^7 (folded into the exp2 offset of the row, undone in the epilogue): a
 // weight is at most 2^8 * 2^7 in float16, and only weights below 2^-21 fall

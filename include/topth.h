@@ -460,9 +460,8 @@ int topth_theta_eval(const double* coef, const int* ks, int n_k, int Hq, int deg
  * when at least min_votes (1 .. Hq/Hkv) of the group's heads keep it
  * (s >= theta), which discards V rows requested by only a few heads; with
  * augment = 0 each head then uses its own kept keys among the loaded ones,
- * with augment = 1 every head uses all loaded keys ("augmenting each head's
- * selections with the group's union"), weighted by its own post-softmax
- * values.  min_votes = 1, augment = 0 is topth_decode.  kept_count counts the
+ * with augment = 1 every head uses all loaded keys (each head's selection
+ * widened to the whole group's), weighted by its own post-softmax values.  min_votes = 1, augment = 0 is topth_decode.  kept_count counts the
  * keys a head uses; vrows_read the loaded keys; kept_mask marks, per head, the
  * keys it uses.  Other arguments and the workspace contract as topth_decode.
  */

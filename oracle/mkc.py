@@ -28,7 +28,7 @@ Readings of steps the pages leave open (each also listed in the design notes):
     then not monotone: near the top a sample whose maximum is passed joins the
     mean with effective k 1.
   * The inverse.  kbar is a step function that may skip integers and is not
-    monotone, so "the inverse at natural values" is read as
+    monotone, so inverting it at whole numbers k is read as
         theta(k) = max { theta : kbar(theta) >= k },
     the largest threshold that keeps at least k elements on average over the
     samples that cover it.  It is attained at a sample value, is non-increasing

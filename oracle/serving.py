@@ -5,15 +5,15 @@ Source: "Top-Theta Attention: Sparsifying Transformers by Compensated
 Thresholding" (arXiv 2502.08363), cited as [TT], and the Pith verdict page on
 the same paper, which paraphrases the paper's lost technical details.
 
-* Running mean of V ([TT] §3.2.2, after Eq. 7: during generative decoding mu
-  "can be maintained as a running mean"): appending rows n_old..n_new-1 to a
+* Running mean of V ([TT] §3.2.2, after Eq. 7: in generative decoding the
+  paper keeps mu up to date as a running mean): appending rows n_old..n_new-1 to a
   cache whose first n_old rows have mean mu_old gives the mean of the first
   n_new rows, mu_new = (n_old * mu_old + sum of the new rows) / n_new.  This is
   Eq. 5 over the longer cache, rewritten; a cache with n_old = 0 starts fresh.
-* Fitted thresholds (Pith verdict page: rows longer than the calibrated ones
-  use "the nearest calibrated threshold or a fitted function", and the paper
-  "fits the per-row thresholds as a function of sequence length, compressing
-  hundreds of parameters into a few fitted coefficients"; the function itself
+* Fitted thresholds (Pith verdict page, technical details: for rows beyond
+  the calibrated ones the paper takes the closest calibrated row's threshold
+  or a function of the row length fitted to the calibrated thresholds, which
+  replaces a per-row table by a handful of coefficients; the function itself
   is lost with the paper's Fig. 3 and technical details).  Reading: a
   least-squares polynomial of low degree in x = ln(p + 1) through the
   calibrated rows of each (k, head) -- on ln(theta) for post-softmax thresholds
@@ -89,10 +89,10 @@ def decode_gqa(q, K_cache, V_cache, seq_lens, theta, v_mean, scale: float, *, vm
                min_votes: int = 1, augment: bool = False, renorm: bool = False):
     """One decoding step with the GQA selection variants of [TT] §4.6: a key is
     loaded for a (b, KV head) group when at least ``min_votes`` of its g heads
-    keep it (s >= theta); each head then uses its own kept keys among those
-    (``augment`` False: "discarding V-rows requested by only a few heads") or
-    all of them ("augmenting each head's selections with the group's union"),
-    weighted by its own post-softmax values (exact SDC) and VMC as in Eq. 5-7.
+    keep it (s >= theta), so rows wanted by fewer heads are dropped; each head
+    then uses its own kept keys among those (``augment`` False) or all of them
+    (``augment`` True: every head takes the group's whole selection), weighted
+    by its own post-softmax values (exact SDC) and VMC as in Eq. 5-7.
     min_votes = 1 without augment is the plain per-head selection."""
     from .topth import DecodeResult, post_softmax, row_output, scores, theta_row
     q = _as64(q); K_cache = _as64(K_cache); V_cache = _as64(V_cache)

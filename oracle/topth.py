@@ -16,9 +16,9 @@ equation or algorithm number.  Readings of steps the paper leaves open:
 * Row id of a query = its 0-based position p; a decode step with n cached keys
   is row p = n - 1.  Rows past the end of a table use its last row; calibrated
   tables fill rows no calibration sequence reached from the nearest calibrated
-  row (smaller row on a tie), the "nearest calibrated threshold" rule that the
-  Pith verdict page on arXiv 2502.08363 (skeptic critique) paraphrases from the
-  paper's lost technical details.
+  row (smaller row on a tie): the closest-calibrated-row rule that the Pith
+  verdict page on arXiv 2502.08363 (skeptic critique) reports from the paper's
+  lost technical details.
 * SDC ([TT] §3.2.1, Eq. 4) in its "exact" form: the kept weights keep the full
   denominator R + E, i.e. they are the post-softmax values s themselves.  The
   alternative ``renorm`` divides by R only (softmax over the kept set).
