@@ -5,7 +5,7 @@ Thresholding" (arXiv 2502.08363), cited below as [TT] with its section,
 equation or algorithm number.  Readings of steps the paper leaves open:
 
 * Scores carry the 1/sqrt(d) factor and the causal mask that [TT] §2.2 says it
-  omits from Eq. 1 "for simplicity"; query row p sees keys 0..p.
+  leaves out of Eq. 1 to keep it short; query row p sees keys 0..p.
 * Post-softmax thresholding ([TT] §3.1, last paragraph): the calibrated sample of
   a row is taken on s = softmax(a), not on a.
 * The per-row quantile of [TT] Alg. 1 is read as the k-th largest valid
