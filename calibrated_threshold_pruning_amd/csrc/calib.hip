@@ -488,34 +488,41 @@ __global__ __launch_bounds__(kCalThreads) void calib_bf16_kernel(CalibKArgs a) {
 // other's sweeps):
 //   sweep A  per row: maximum M, minimum, sum of scores and the softmax sum
 //            (the row log-sum-exp lse2);
-//   sweep B  a histogram of 256 bins of (M - x) over a window below M: the
-//            full range for rows shorter than 3 k_max, else the smaller of the
-//            full range and 1.1 (M - mean).  Counts are 8-bit, four to a word;
-//            the last (open-ended) bin is not counted but inferred from the
-//            row length, and each lane counts the in-window elements of its
-//            rows in a register, which exposes any 8-bit overflow.  A prefix
-//            over the bins gives, for every target k, the bin holding the k-th
-//            largest score and its rank inside that bin;
-//   sweep C  every lane appends the elements of its two rows that fall into a
-//            target bin to a private region of 32 slots, one row from each
-//            end (no atomics, no branches).  Then one lane per (row, target)
-//            reads the row's four regions and keeps the 32 largest members of
-//            the target bin in a register sorting network (the 32 smallest
-//            when the rank is nearer the bottom of the bin), so the member of
-//            that rank is exact for any bin of up to 64 members.
-// A row whose counts overflowed, whose members do not fit the regions, or
-// whose target bin holds more than 64 members is listed for
-// calib_fixup_kernel, which recomputes it and selects exactly by radix
-// select.  Bins are a pure function of the recomputed scores, which
-// every sweep forms identically, so the sweeps agree on every element.
-constexpr int kCtNB = 256;                      // histogram bins per row
-constexpr int kCtRowWords = kCtNB / 4 + 1;      // 8-bit counts, + 1 word: rows in other banks
-constexpr int kCtPool = 32 * kCtRowWords;       // words per wave: histogram, then candidate regions
+//   sweep B  a histogram of 256 bins over a window below M: the full range
+//            for rows shorter than 3 k_max, else the smaller of the full range
+//            and 1.1 (M - mean).  The bin of a score x is read off the bits of
+//            one fma, fma(x, -bs, M bs + 2^23 + 1): a float in [2^23, 2^24)
+//            whose low bits are (M - x) bs + 1 rounded, so the bin is a
+//            monotone (non-increasing) function of x.  Counts are 8-bit, four to a
+//            word; everything past the window (and the masked keys) goes to a
+//            32-bit sink word after the 64 count words, so a row's counts plus
+//            its sink add up to the keys swept unless an 8-bit count wrapped.
+//            A prefix over the bins gives, for every target k, the bin holding
+//            the k-th largest score and its rank inside that bin;
+//   sweep C  every lane appends the elements of its two rows whose fma bits
+//            equal a target bin's to a private region of 32 slots, one row
+//            from each end (no atomics, no branches).  Then one lane per
+//            (row, target) reads the row's four regions and keeps the 32
+//            largest members of the target bin in a register sorting network
+//            (the 32 smallest when the rank is nearer the bottom of the bin),
+//            so the member of that rank is exact for any bin of up to 64
+//            members.
+// A row whose counts wrapped, whose k-th largest lies past the window, whose
+// members do not fit the regions, or whose target bin holds more than 64
+// members is listed for calib_fixup_kernel, which recomputes it and selects
+// exactly by radix select.  Bins are a pure function of the recomputed scores,
+// which every sweep forms identically, so the sweeps agree on every element.
+constexpr int kCtNB = 256;                      // histogram bins per row (in the window)
+constexpr int kCtRowWords = kCtNB / 4 + 1;      // 8-bit counts, + the sink word (also puts rows in other banks)
+constexpr uint32_t kCtBinBase = 0x4B000000u;    // bits of 2^23: bin 0
+constexpr float kCtBinOffset = 8388609.0f;      // 2^23 + 1
 constexpr int kCtSlots = 32;                    // candidate slots per lane (both of its rows)
+constexpr int kCtRegion = kCtSlots + 1;         // words between regions: equal slots of the 64 lanes in distinct banks
+constexpr int kCtPool = 64 * kCtRegion > 32 * kCtRowWords ? 64 * kCtRegion : 32 * kCtRowWords;   // words per wave
 constexpr int kCtNet = 32;                      // registers of the exact-select network
 constexpr int kCtMaxK = 4;                      // targets per call on this path
 constexpr int kCtEntries = 32 * kCtMaxK;        // (row, target) entries of a wave
-static_assert(64 * kCtSlots <= kCtPool, "candidate regions inside the histogram space");
+static_assert(64 * kCtRegion <= kCtPool && 32 * kCtRowWords <= kCtPool, "histogram and regions in the pool");
 
 constexpr int kCtWaves = 4;
 
@@ -562,13 +569,13 @@ __device__ __forceinline__ void lds_store(uint32_t addr, float v) {
 }
 
 // The member of rank rr (counted from the top when `top`, else from the
-// bottom) of the target bin tbe of a row, from the candidate regions of the
-// row's four lanes (g16 + 16 src; row qb = 0 at the start of a region, row
-// qb = 1 at its end): an N-register sorting network keeps the N largest (or
-// smallest) members seen; rr <= N.
+// bottom) of the target bin of a row (fma bits tbits), from the candidate
+// regions of the row's four lanes (g16 + 16 src; row qb = 0 at the start of a
+// region, row qb = 1 at its end): an N-register sorting network keeps the N
+// largest (or smallest) members seen; rr <= N.
 template <int N>
 __device__ __forceinline__ float ct_select(const float* pool, int wave, const int (*ccnt)[64][2], int g16, int qb,
-                                           int tbe, float M, float bs, bool top, int rr) {
+                                           uint32_t tbits, float nbs, float cb, bool top, int rr) {
     float r[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) r[i] = top ? -INFINITY : INFINITY;
@@ -577,8 +584,8 @@ __device__ __forceinline__ float ct_select(const float* pool, int wave, const in
         const int sl = g16 + 16 * src;
         const int c = ccnt[wave][sl][qb];
         for (int jj = 0; jj < c; ++jj) {
-            const float y = pool[kCtSlots * sl + (qb == 0 ? jj : kCtSlots - 1 - jj)];
-            if ((int)fminf((M - y) * bs, (float)(kCtNB - 1)) != tbe) continue;
+            const float y = pool[kCtRegion * sl + (qb == 0 ? jj : kCtSlots - 1 - jj)];
+            if (__float_as_uint(fmaf(y, nbs, cb)) != tbits) continue;
             float v = y;
 #pragma unroll
             for (int i = 0; i < N; ++i) {
@@ -606,7 +613,7 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
     __shared__ uint32_t s_hist[W][kCtPool];          // per wave: histogram, then the candidate regions
     __shared__ int s_ccnt[W][64][2];                 // candidates per lane and row
     __shared__ int s_lovf[W][16];                    // a lane of the group l16 overran its region
-    __shared__ float s_rM[W][32], s_rbs[W][32], s_rlse[W][32];   // maximum, bin scale and lse2 of each row
+    __shared__ float s_rnbs[W][32], s_rcb[W][32], s_rlse[W][32]; // bin fma operands and lse2 of each row
     __shared__ int s_etb[W][kCtEntries];             // target bin (-1: none, or listed for the fixup)
     __shared__ int s_ecnt[W][kCtEntries];            // members of the target bin
     __shared__ int s_erank[W][kCtEntries];           // rank inside the bin; -1: listed for the fixup
@@ -619,11 +626,21 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
     const float NEG_INF = -INFINITY;
     const int n_k = a.n_k;
 
+    // Workgroup w goes to XCD w % 8.  The logical workgroups of one (sequence,
+    // head block), which read the same K, are numbered consecutively and dealt
+    // to one XCD in order, so that XCD's L2 serves K to all of them (and to
+    // all three sweeps); a remainder of fewer than 8 keeps its own order.
     const int nqt = (a.L + C::BMT - 1) / C::BMT;
-    const int qt = nqt - 1 - (int)blockIdx.x;                // longest query tiles first
-    const int kv = blockIdx.y / (G / C::HPW);
-    const int hblk = blockIdx.y % (G / C::HPW);
-    const int sq = blockIdx.z;
+    const unsigned nhb = (unsigned)(a.Hkv * (G / C::HPW));
+    const unsigned nwg = gridDim.x, nfull = nwg & ~7u;
+    unsigned w = blockIdx.x;
+    if (w < nfull) w = (w & 7u) * (nfull >> 3) + (w >> 3);
+    const int qt = nqt - 1 - (int)(w % (unsigned)nqt);        // longest query tiles first
+    const unsigned grp = w / (unsigned)nqt;
+    const int hb = (int)(grp % nhb);
+    const int sq = (int)(grp / nhb);
+    const int kv = hb / (G / C::HPW);
+    const int hblk = hb % (G / C::HPW);
     const int h = kv * G + hblk * C::HPW + wave % C::HPW;
     const int row0 = qt * C::BMT + (wave / C::HPW) * 32;
     const int wg_row_end = min(a.L, (qt + 1) * C::BMT);
@@ -662,97 +679,151 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
                 vo[li % NVO], (tile * C::BN + li * C::RPI) * (D * 2), 0, 0);
         }
     };
-    // raw scores q.k of key tile j: keys 64 j + 16 kb + 4 lq + r, rows row0 + 16 qb + l16;
-    // keys past a row (and rows past L) are -inf
-    auto scores = [&](const unsigned char* buf, int j, f32x4 (&st)[2][4]) {
+    // K fragments of a tile (A operand): key 16 kb + l16, dims 32 st2 + 8 lq .. + 7
+    typedef bf16x8 KFrag[4][C::KSTEPS];
+    auto load_k = [&](const unsigned char* buf, KFrag& kf) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int key = 16 * kb + l16;
             const unsigned char* srow = buf + ((key / C::RPI) * 64 + (key % C::RPI) * C::CPR) * 16;
             const int swz = key % C::CPR;
+#pragma unroll
+            for (int st2 = 0; st2 < C::KSTEPS; ++st2)
+                kf[kb][st2] = __builtin_bit_cast(bf16x8, *(const u32x4*)(srow + ((4 * st2 + lq) ^ swz) * 16));
+        }
+    };
+    // raw scores q.k of a tile: keys 16 kb + 4 lq + r of the tile, rows row0 + 16 qb + l16
+    auto mfma_k = [&](const KFrag& kf, f32x4 (&st)[2][4]) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st2 = 0; st2 < C::KSTEPS; ++st2) {
-                const int c = 4 * st2 + lq;
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(srow + (c ^ swz) * 16));
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][st2], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][st2], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][st2], qf[0][st2], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][st2], qf[1][st2], acc1, 0, 0, 0);
             }
             st[0][kb] = acc0;
             st[1][kb] = acc1;
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::KSTEPS, 0);
+    };
+    // keys past a row, and rows past L, become -inf (tile j crosses the wave's diagonal)
+    auto mask = [&](int j, f32x4 (&st)[2][4]) {
 #pragma unroll
-        for (int kb = 0; kb < 3; ++kb) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KSTEPS, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, C::KSTEPS, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KSTEPS, 0);
-        if (j * C::BN + C::BN - 1 > row0) {              // the tile crosses this wave's diagonal
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = row0 + 16 * qb + l16;
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int row = row0 + 16 * qb + l16;
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (j * C::BN + 16 * kb + 4 * lq + r > row || row >= a.L) st[qb][kb][r] = NEG_INF;
-            }
+                for (int r = 0; r < 4; ++r)
+                    if (j * C::BN + 16 * kb + 4 * lq + r > row || row >= a.L) st[qb][kb][r] = NEG_INF;
         }
     };
-    // one pass over the key tiles: tile j + 1 loads while tile j is used
-    auto sweep = [&](auto&& body) {
+    // Tile tdiag holds keys row0 .. row0 + 31 (the wave's diagonal); tiles
+    // before it need no mask, tiles after it are all masked and are skipped.
+    const int tdiag = min(row0 / C::BN, ntiles);
+    // One pass over the key tiles, software-pipelined: at step j the MFMAs of
+    // tile j + 1 run between the VALU work of tile j (`plain`, one basic
+    // block), while tile j + 2 loads into the buffer tile j came from.  The
+    // diagonal tile is masked and goes to `diag`.  Tile t lives in buffer t & 1;
+    // the two buffers are separate objects so that reads of one are not taken
+    // to alias the loads in flight into the other.
+    auto sweep = [&](auto&& plain, auto&& diag) {
         issue_k(s_k0, 0);
+        if (ntiles > 1) {
+            issue_k(s_k1, 1);
+            __builtin_amdgcn_s_waitcnt(0x0F70 | C::NLD);    // vmcnt(NLD): tile 0 landed, tile 1 may not have
+        } else {
+            ct_wait_vmem();
+        }
+        __syncthreads();
+        f32x4 sa[2][4], sb[2][4];
+        {
+            KFrag kf;
+            load_k(s_k0, kf);
+            mfma_k(kf, sa);
+        }
+        auto step = [&](int j, unsigned char* load_into, const unsigned char* next_buf, f32x4 (&cur)[2][4],
+                        f32x4 (&nxt)[2][4]) {
+            ct_wait_vmem();
+            __syncthreads();                             // tile j + 1 landed; every wave is done with tile j's buffer
+            if (j + 2 < ntiles) issue_k(load_into, j + 2);
+            if (j < tdiag) {
+                if (j + 1 < ntiles) {
+                    KFrag kf;
+                    load_k(next_buf, kf);
+                    mfma_k(kf, nxt);
+                    plain(cur);
+                } else {
+                    plain(cur);
+                }
+            } else if (j == tdiag) {
+                mask(j, cur);
+                diag(cur);
+            }
+        };
         for (int j = 0; j < ntiles; j += 2) {
-            ct_wait_vmem();
-            __syncthreads();                             // tile j landed; the other buffer is free
-            if (j + 1 < ntiles) issue_k(s_k1, j + 1);
-            f32x4 st[2][4];
-            scores(s_k0, j, st);
-            body(j, st);
-            if (j + 1 >= ntiles) break;
-            ct_wait_vmem();
-            __syncthreads();
-            if (j + 2 < ntiles) issue_k(s_k0, j + 2);
-            scores(s_k1, j + 1, st);
-            body(j + 1, st);
+            step(j, s_k0, s_k1, sa, sb);
+            if (j + 1 < ntiles) step(j + 1, s_k1, s_k0, sb, sa);
         }
         __syncthreads();                                 // both buffers free for the next sweep
     };
 
     // ======================= sweep A: row statistics ==========================
     float m_l[2] = {NEG_INF, NEG_INF}, l_l[2] = {0.f, 0.f}, mn_l[2] = {INFINITY, INFINITY}, sx_l[2] = {0.f, 0.f};
-    sweep([&](int j, f32x4 (&st)[2][4]) {
+    // online softmax sum in the frame of the running maximum, branch-free: a
+    // row with no key yet keeps m = -inf and l = 0
+    auto fold_exp = [&](int qb, float tmax, const f32x4 (&st)[2][4]) {
+        const float mnew = fmaxf(m_l[qb], tmax);
+        const float mref = mnew == NEG_INF ? 0.f : mnew;
+        const float nmc = -mref * a.xscale;
+        float sum = 0.f;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float tmax = NEG_INF, tmin = INFINITY, tsum = 0.f;
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(fmaf(st[qb][kb][r], a.xscale, nmc));
+        l_l[qb] = l_l[qb] * __builtin_amdgcn_exp2f((m_l[qb] - mref) * a.xscale) + sum;
+        m_l[qb] = mnew;
+    };
+    sweep(
+        [&](f32x4 (&st)[2][4]) {                         // no masked key
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = st[qb][kb][r];
-                    tmax = fmaxf(tmax, x);
-                    const bool ok = x > NEG_INF;
-                    tmin = fminf(tmin, ok ? x : INFINITY);
-                    tsum += ok ? x : 0.f;
-                }
-            mn_l[qb] = fminf(mn_l[qb], tmin);
-            sx_l[qb] += tsum;
-            const float mnew = fmaxf(m_l[qb], tmax);
-            if (mnew != NEG_INF) {
-                const float nmc = -mnew * a.xscale;
-                float sum = 0.f;
+            for (int qb = 0; qb < 2; ++qb) {
+                float tmax = NEG_INF, tmin = INFINITY, tsum = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sum += __builtin_amdgcn_exp2f(fmaf(st[qb][kb][r], a.xscale, nmc));
-                l_l[qb] = l_l[qb] * __builtin_amdgcn_exp2f((m_l[qb] - mnew) * a.xscale) + sum;
-                m_l[qb] = mnew;
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = st[qb][kb][r];
+                        tmax = fmaxf(tmax, x);
+                        tmin = fminf(tmin, x);
+                        tsum += x;
+                    }
+                mn_l[qb] = fminf(mn_l[qb], tmin);
+                sx_l[qb] += tsum;
+                fold_exp(qb, tmax, st);
             }
-        }
-    });
+        },
+        [&](f32x4 (&st)[2][4]) {                         // masked keys: left out of the minimum and sum
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                float tmax = NEG_INF, tmin = INFINITY, tsum = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = st[qb][kb][r];
+                        tmax = fmaxf(tmax, x);
+                        const bool ok = x > NEG_INF;
+                        tmin = fminf(tmin, ok ? x : INFINITY);
+                        tsum += ok ? x : 0.f;
+                    }
+                mn_l[qb] = fminf(mn_l[qb], tmin);
+                sx_l[qb] += tsum;
+                fold_exp(qb, tmax, st);
+            }
+        });
     // the four lanes of a row (16 apart) combine; every one of them gets the result
-    float rM[2], rbs[2], lse2[2];
+    float nbs[2], cb[2], lse2[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         float M = fmaxf(m_l[qb], __shfl_xor(m_l[qb], 16));
@@ -769,26 +840,28 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
         float w = M - mn;
         if (n >= 3 * a.kmax) w = fminf(w, 1.1f * (M - sx / (float)n));
         w = fmaxf(w, 1e-30f);
-        rM[qb] = M;
-        rbs[qb] = (float)kCtNB / w;
+        // bins of width w / 253 from M down; |M| bs stays below 2^21, so M bs
+        // + 2^23 + 1 rounds by at most 1/2 and the bits of the fma are at
+        // least those of 2^23 for every x <= M (coarser bins where the whole
+        // row lies within 1.2e-4 relative of M)
+        float bs = (float)(kCtNB - 3) / w;
+        if (fabsf(M) * bs > 2097152.f) bs = 2097152.f / fabsf(M);
+        nbs[qb] = -bs;
+        cb[qb] = fmaf(M, bs, kCtBinOffset);
         if (lq == 0) {
-            s_rM[wave][16 * qb + l16] = M;
-            s_rbs[wave][16 * qb + l16] = rbs[qb];
+            s_rnbs[wave][16 * qb + l16] = nbs[qb];
+            s_rcb[wave][16 * qb + l16] = cb[qb];
             s_rlse[wave][16 * qb + l16] = lse2[qb];
         }
     }
-    // bin of a score: monotone non-increasing in x; masked (-inf) elements and
-    // everything beyond the window land in the last bin
-    auto bin_of = [&](int qb, float x) -> int {
-        return (int)fminf((rM[qb] - x) * rbs[qb], (float)(kCtNB - 1));
-    };
 
     // ======================= sweep B: histograms ==============================
+    // fma bits of x, capped at bin 256 (the sink word): word (bin >> 2) gets
+    // 1 << 8 (bin & 3); the sink's increment is 1
     uint32_t* hw = s_hist[wave];
     const uint32_t hw_off = lds_offset(hw);
-    for (int i = lane; i < kCtPool; i += 64) hw[i] = 0u;
-    int inwin[2] = {0, 0};                              // this lane's elements in bins 0 .. NB - 2
-    sweep([&](int j, f32x4 (&st)[2][4]) {
+    for (int i = lane; i < kCtPool; i += 64) hw[i] = 0u;    // the sweep's first barrier orders this
+    auto hist = [&](f32x4 (&st)[2][4]) {                 // masked keys land in the sink
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const uint32_t rbase = hw_off + (uint32_t)((16 * qb + l16) * kCtRowWords) * 4u;
@@ -796,13 +869,12 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int b = bin_of(qb, st[qb][kb][r]);
-                    const bool in = b < kCtNB - 1;
-                    inwin[qb] += in ? 1 : 0;
-                    lds_add(rbase + (uint32_t)(b >> 2) * 4u, in ? 1u << ((b & 3) << 3) : 0u);
+                    const uint32_t bits = min(__float_as_uint(fmaf(st[qb][kb][r], nbs[qb], cb[qb])), kCtBinBase + 256u);
+                    lds_add(rbase + (bits & 0x1FCu), 1u << ((bits << 3) & 31u));
                 }
         }
-    });
+    };
+    sweep(hist, hist);
     __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the written-out atomics are done
     // every entry starts as "no target"; the lanes that find a target set it after the barrier
     for (int e = lane; e < kCtEntries; e += 64) {
@@ -811,23 +883,13 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
         s_eval[wave][e] = __uint_as_float(0x7FC00000u);   // NaN until the exact value is found
     }
     __syncthreads();
-    int winrow[2];                                      // in-window count of each of the lane's rows
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        int c = inwin[qb] + __shfl_xor(inwin[qb], 16);
-        winrow[qb] = c + __shfl_xor(c, 32);
-    }
 
     // ---- bin and rank of each target: lane (rl, half) scans 128 bins of row rl
     {
         const int rl = lane & 31, half = lane >> 5;
         const int n = row0 + rl + 1;
         const bool live = row0 + rl < a.L;
-        // in-window count and lse2 of row rl live in lane rl % 16 (register rl / 16)
-        const int w0 = __shfl(winrow[0], rl & 15), w1 = __shfl(winrow[1], rl & 15);
-        const int win = rl < 16 ? w0 : w1;
-        const float l0 = __shfl(lse2[0], rl & 15), l1 = __shfl(lse2[1], rl & 15);
-        const float lrow = rl < 16 ? l0 : l1;
+        const float lrow = s_rlse[wave][rl];
         uint32_t wv[32];
         int ws[32];                                     // count of each word's four bins
         int local = 0;
@@ -839,14 +901,14 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
         }
         const int other = __shfl_xor(local, 32);
         const int base = half ? other : 0;
-        const bool ovf = local + other != win;          // an 8-bit count wrapped
-        const int lastcnt = n - win;                    // elements beyond the window (bin NB - 1)
-        if (half) ws[31] += lastcnt;
+        const int sink = (int)hw[rl * kCtRowWords + kCtNB / 4];
+        // the sweeps stop after the diagonal tile: every row saw (tdiag + 1) 64 keys
+        const bool ovf = local + other + sink != min(tdiag + 1, ntiles) * C::BN;   // an 8-bit count wrapped
         for (int t = 0; t < n_k; ++t) {
             const int kk = a.ks[t];
             const int e = rl * n_k + t;
             if (!(live && n > kk)) continue;
-            if (ovf) {
+            if (ovf || kk > local + other) {            // wrapped, or the k-th largest lies past the window
                 if (half == 0) {
                     s_erank[wave][e] = -1;
                     const unsigned idx = atomicAdd(a.fix_count, 1u);
@@ -855,7 +917,7 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
                 }
                 continue;
             }
-            if (base < kk && kk <= base + local + (half ? lastcnt : 0)) {
+            if (base < kk && kk <= base + local) {
                 // the word holding the k-th largest, then the bin inside it
                 int cum = base, wsel = 0, cbefore = base;
 #pragma unroll
@@ -870,7 +932,7 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int bin = 128 * half + 4 * wsel + i;
-                    const int c = bin == kCtNB - 1 ? lastcnt : (int)((word >> (8 * i)) & 0xffu);
+                    const int c = (int)((word >> (8 * i)) & 0xffu);
                     if (cum < kk && kk <= cum + c) {
                         s_etb[wave][e] = bin;
                         s_erank[wave][e] = kk - cum;
@@ -884,17 +946,22 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
     __syncthreads();
 
     // ======================= sweep C: members of the target bins ==============
-    int tb[2][kCtMaxK];
+    // fma bits of each target bin (0: no target; no score's bits are 0)
+    uint32_t tb[2][kCtMaxK];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int t = 0; t < kCtMaxK; ++t) tb[qb][t] = t < n_k ? s_etb[wave][(16 * qb + l16) * n_k + t] : -1;
-    // this lane's region: words 32 lane .. 32 lane + 31; row qb = 0 fills slots
+        for (int t = 0; t < kCtMaxK; ++t) {
+            const int b = t < n_k ? s_etb[wave][(16 * qb + l16) * n_k + t] : -1;
+            tb[qb][t] = b >= 0 ? kCtBinBase + (uint32_t)b : 0u;
+        }
+    // this lane's region: words 33 lane .. 33 lane + 31; row qb = 0 fills slots
     // 0, 1, .. and row qb = 1 slots 31, 30, ..; each row's next free slot takes
-    // the stores of non-members (a later member overwrites it)
-    const uint32_t reg_off = hw_off + (uint32_t)(kCtSlots * lane) * 4u;
+    // the stores of non-members (a later member overwrites it).  Masked keys
+    // have the bits of +inf and match no target.
+    const uint32_t reg_off = hw_off + (uint32_t)(kCtRegion * lane) * 4u;
     int cc[2] = {0, 0};
-    sweep([&](int j, f32x4 (&st)[2][4]) {
+    auto collect = [&](f32x4 (&st)[2][4]) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -902,16 +969,17 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float x = st[qb][kb][r];
-                    const int b = bin_of(qb, x);
+                    const uint32_t bits = __float_as_uint(fmaf(x, nbs[qb], cb[qb]));
                     // bitwise, not short-circuit: no branch per element
-                    const int hit = (int)(x > NEG_INF) & ((int)(b == tb[qb][0]) | (int)(b == tb[qb][1]) |
-                                                          (int)(b == tb[qb][2]) | (int)(b == tb[qb][3]));
-                    const int slot = qb == 0 ? min(cc[0], kCtSlots - 1) : max(kCtSlots - 1 - cc[1], 0);
+                    const int hit = (int)(bits == tb[qb][0]) | (int)(bits == tb[qb][1]) |
+                                    (int)(bits == tb[qb][2]) | (int)(bits == tb[qb][3]);
+                    const int slot = qb == 0 ? min(cc[0], kCtSlots - 1) : kCtSlots - 1 - min(cc[1], kCtSlots - 1);
                     lds_store(reg_off + (uint32_t)slot * 4u, x);
                     cc[qb] += hit;
                 }
         }
-    });
+    };
+    sweep(collect, collect);
     __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the written-out stores are done
     s_ccnt[wave][lane][0] = cc[0];
     s_ccnt[wave][lane][1] = cc[1];
@@ -944,17 +1012,18 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
             }
             const bool top = rank <= kCtNet;            // keep the largest members, else the smallest
             const int rr = top ? rank : m - rank + 1;
-            const float M = s_rM[wave][rl], bs = s_rbs[wave][rl];
+            const float rnbs = s_rnbs[wave][rl], rcb = s_rcb[wave][rl];
+            const uint32_t tbits = kCtBinBase + (uint32_t)tbe;
             // the network only needs rr registers: the smallest of 4, 8, 16, 32 that covers
             // every active lane of the wave (the branch is wave-uniform)
             int need = rr;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) need = max(need, __shfl_xor(need, o));
             float val;
-            if (need <= 4) val = ct_select<4>(pool, wave, s_ccnt, g16, qb, tbe, M, bs, top, rr);
-            else if (need <= 8) val = ct_select<8>(pool, wave, s_ccnt, g16, qb, tbe, M, bs, top, rr);
-            else if (need <= 16) val = ct_select<16>(pool, wave, s_ccnt, g16, qb, tbe, M, bs, top, rr);
-            else val = ct_select<32>(pool, wave, s_ccnt, g16, qb, tbe, M, bs, top, rr);
+            if (need <= 4) val = ct_select<4>(pool, wave, s_ccnt, g16, qb, tbits, rnbs, rcb, top, rr);
+            else if (need <= 8) val = ct_select<8>(pool, wave, s_ccnt, g16, qb, tbits, rnbs, rcb, top, rr);
+            else if (need <= 16) val = ct_select<16>(pool, wave, s_ccnt, g16, qb, tbits, rnbs, rcb, top, rr);
+            else val = ct_select<32>(pool, wave, s_ccnt, g16, qb, tbits, rnbs, rcb, top, rr);
             s_eval[wave][e] = val;
         }
     }
@@ -1100,8 +1169,8 @@ static int launch_calib_d(const CalibKArgs& a, int cols, hipStream_t s) {
 template <int D, int G>
 static int launch_tiled_variant(const CalibTArgs& a, hipStream_t s) {
     using C = CtCfg<D, G>;
-    const dim3 grid((a.L + C::BMT - 1) / C::BMT, a.Hkv * (G / C::HPW), a.S);
-    hipLaunchKernelGGL((calib_tiled_kernel<D, G>), grid, dim3(kCtWaves * 64), 0, s, a);
+    const unsigned nwg = (unsigned)((a.L + C::BMT - 1) / C::BMT) * (unsigned)(a.Hkv * (G / C::HPW)) * (unsigned)a.S;
+    hipLaunchKernelGGL((calib_tiled_kernel<D, G>), dim3(nwg), dim3(kCtWaves * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // the listed entries (usually none): every workgroup reads the count and
@@ -1125,8 +1194,9 @@ static int launch_tiled_d(const CalibTArgs& a, int G, hipStream_t s) {
 // discarded-mass samples take the tiled kernel
 static bool tiled_path(const CalibParams& p) {
     const int G = p.Hq / p.Hkv;
+    // one grid dimension: (query tiles of at most 32 rows) x Hq x S workgroups at most
     return p.q_pos0 == 0 && p.Lq == p.Lk && p.Lk <= 4096 && p.esum == nullptr && p.n_k <= kCtMaxK &&
-           (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) && p.S <= 65535;
+           (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) && (long long)((p.Lq + 31) / 32) * p.Hq * p.S < (1LL << 31);
 }
 
 int launch_calibrate_bf16(const CalibParams& p, float* samples_ws, hipStream_t s) {
