@@ -502,14 +502,14 @@ __global__ __launch_bounds__(kCalThreads) void calib_bf16_kernel(CalibKArgs a) {
 //   sweep C  every lane appends the elements of its two rows whose fma bits
 //            equal a target bin's to a private region of 32 slots, one row
 //            from each end (no atomics, no branches).  Then one lane per
-//            (row, target) reads the row's four regions and keeps the 32
-//            largest members of the target bin in a register sorting network
-//            (the 32 smallest when the rank is nearer the bottom of the bin),
-//            so the member of that rank is exact for any bin of up to 64
-//            members.
+//            (row, target) reads the row's four regions and keeps the largest
+//            members of the target bin in a register sorting network of up to
+//            32 (the smallest when the rank is nearer the bottom of the bin),
+//            so the member of that rank is exact whenever it is within 32 of
+//            either end of its bin.
 // A row whose counts wrapped, whose k-th largest lies past the window, whose
-// members do not fit the regions, or whose target bin holds more than 64
-// members is listed for calib_fixup_kernel, which recomputes it and selects
+// members do not fit the regions, or whose k-th largest is more than 32 from
+// either end of its bin is listed for calib_fixup_kernel, which recomputes it and selects
 // exactly by radix select.  Bins are a pure function of the recomputed scores,
 // which every sweep forms identically, so the sweeps agree on every element.
 constexpr int kCtNB = 256;                      // histogram bins per row (in the window)
@@ -568,37 +568,38 @@ __device__ __forceinline__ void lds_store(uint32_t addr, float v) {
     asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
-// The member of rank rr (counted from the top when `top`, else from the
-// bottom) of the target bin of a row (fma bits tbits), from the candidate
+// The member of rank rr of the target bin (fma bits tbits) of a row, counted
+// from the top (flip = 0) or from the bottom (flip = ~0), from the candidate
 // regions of the row's four lanes (g16 + 16 src; row qb = 0 at the start of a
-// region, row qb = 1 at its end): an N-register sorting network keeps the N
-// largest (or smallest) members seen; rr <= N.
+// region, row qb = 1 at its end; c[src] candidates each).  Members enter an
+// N-register network as order-preserving keys xor flip, everything else as 0
+// (below every key); the network keeps the N largest, rr <= N.  No branch
+// per candidate: the lanes of a wave walk their rows' candidates together.
 template <int N>
-__device__ __forceinline__ float ct_select(const float* pool, int wave, const int (*ccnt)[64][2], int g16, int qb,
-                                           uint32_t tbits, float nbs, float cb, bool top, int rr) {
-    float r[N];
+__device__ __forceinline__ float ct_select(const float* pool, const int (&c)[4], int g16, int qb, uint32_t tbits,
+                                           float nbs, float cb, uint32_t flip, int rr) {
+    uint32_t r[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) r[i] = top ? -INFINITY : INFINITY;
+    for (int i = 0; i < N; ++i) r[i] = 0u;
 #pragma unroll
     for (int src = 0; src < 4; ++src) {
-        const int sl = g16 + 16 * src;
-        const int c = ccnt[wave][sl][qb];
-        for (int jj = 0; jj < c; ++jj) {
-            const float y = pool[kCtRegion * sl + (qb == 0 ? jj : kCtSlots - 1 - jj)];
-            if (__float_as_uint(fmaf(y, nbs, cb)) != tbits) continue;
-            float v = y;
+        const float* reg = pool + kCtRegion * (g16 + 16 * src) + (qb == 0 ? 0 : kCtSlots - 1);
+        const int step = qb == 0 ? 1 : -1;
+        for (int jj = 0; jj < c[src]; ++jj) {
+            const float y = reg[step * jj];
+            uint32_t v = __float_as_uint(fmaf(y, nbs, cb)) == tbits ? float_to_ordered(y) ^ flip : 0u;
 #pragma unroll
             for (int i = 0; i < N; ++i) {
-                const float keep = top ? fmaxf(r[i], v) : fminf(r[i], v);
-                v = top ? fminf(r[i], v) : fmaxf(r[i], v);
-                r[i] = keep;
+                const uint32_t hi = max(r[i], v);
+                v = min(r[i], v);
+                r[i] = hi;
             }
         }
     }
-    float val = r[0];
+    uint32_t k = r[0];
 #pragma unroll
-    for (int i = 1; i < N; ++i) val = i == rr - 1 ? r[i] : val;
-    return val;
+    for (int i = 1; i < N; ++i) k = i == rr - 1 ? r[i] : k;
+    return ordered_to_float(k ^ flip);
 }
 
 template <int D, int G>
@@ -992,39 +993,47 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
     }
     __syncthreads();
 
-    // ---- exact value: one lane per (row, target) entry
+    // ---- exact value: one lane per (row, target) entry, 64 entries at a time
     {
         const float* pool = reinterpret_cast<const float*>(hw);
-        for (int e = lane; e < 32 * n_k; e += 64) {
-            const int rl = e / n_k;
-            const int tbe = s_etb[wave][e];
-            const int rank = s_erank[wave][e];
-            const int m = s_ecnt[wave][e];
-            if (tbe < 0 || rank <= 0) continue;
+        for (int e0 = 0; e0 < 32 * n_k; e0 += 64) {
+            const int e = e0 + lane;
+            const bool valid = e < 32 * n_k;
+            const int rl = valid ? e / n_k : 0;
             const int qb = rl >> 4, g16 = rl & 15;
-            if (s_lovf[wave][g16] || m > 2 * kCtNet) {
+            const int tbe = valid ? s_etb[wave][e] : -1;
+            const int rank = valid ? s_erank[wave][e] : 0;
+            const int m = valid ? s_ecnt[wave][e] : 0;
+            bool act = tbe >= 0 && rank > 0;
+            // the rank counted from the nearer end of the bin
+            const bool top = rank <= m - rank + 1;
+            const int rr = top ? rank : m - rank + 1;
+            if (act && (s_lovf[wave][g16] || rr > kCtNet)) {
                 s_erank[wave][e] = -1;
                 const unsigned idx = atomicAdd(a.fix_count, 1u);
                 const int t = e - rl * n_k;
                 a.fix_list[idx] = make_uint4((unsigned)sq, (unsigned)h, (unsigned)(row0 + rl) | ((unsigned)t << 16),
                                              __float_as_uint(s_rlse[wave][rl]));
-                continue;
+                act = false;
             }
-            const bool top = rank <= kCtNet;            // keep the largest members, else the smallest
-            const int rr = top ? rank : m - rank + 1;
-            const float rnbs = s_rnbs[wave][rl], rcb = s_rcb[wave][rl];
-            const uint32_t tbits = kCtBinBase + (uint32_t)tbe;
-            // the network only needs rr registers: the smallest of 4, 8, 16, 32 that covers
-            // every active lane of the wave (the branch is wave-uniform)
-            int need = rr;
+            // the network needs rr registers: the smallest of 4, 8, 16, 32 that
+            // covers every lane of the wave (all lanes take part: uniform)
+            int need = act ? rr : 0;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) need = max(need, __shfl_xor(need, o));
+            if (need == 0) continue;
+            int c[4];
+#pragma unroll
+            for (int src = 0; src < 4; ++src) c[src] = act ? s_ccnt[wave][g16 + 16 * src][qb] : 0;   // <= 31: no overrun
+            const float rnbs = s_rnbs[wave][rl], rcb = s_rcb[wave][rl];
+            const uint32_t tbits = act ? kCtBinBase + (uint32_t)tbe : 0u;
+            const uint32_t flip = top ? 0u : ~0u;
             float val;
-            if (need <= 4) val = ct_select<4>(pool, wave, s_ccnt, g16, qb, tbits, rnbs, rcb, top, rr);
-            else if (need <= 8) val = ct_select<8>(pool, wave, s_ccnt, g16, qb, tbits, rnbs, rcb, top, rr);
-            else if (need <= 16) val = ct_select<16>(pool, wave, s_ccnt, g16, qb, tbits, rnbs, rcb, top, rr);
-            else val = ct_select<32>(pool, wave, s_ccnt, g16, qb, tbits, rnbs, rcb, top, rr);
-            s_eval[wave][e] = val;
+            if (need <= 4) val = ct_select<4>(pool, c, g16, qb, tbits, rnbs, rcb, flip, rr);
+            else if (need <= 8) val = ct_select<8>(pool, c, g16, qb, tbits, rnbs, rcb, flip, rr);
+            else if (need <= 16) val = ct_select<16>(pool, c, g16, qb, tbits, rnbs, rcb, flip, rr);
+            else val = ct_select<32>(pool, c, g16, qb, tbits, rnbs, rcb, flip, rr);
+            if (act) s_eval[wave][e] = val;
         }
     }
     __syncthreads();
@@ -1173,9 +1182,10 @@ static int launch_tiled_variant(const CalibTArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((calib_tiled_kernel<D, G>), dim3(nwg), dim3(kCtWaves * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // the listed entries (usually none): every workgroup reads the count and
-    // exits when there is nothing left for it
-    hipLaunchKernelGGL((calib_fixup_kernel<D>), dim3(256), dim3(256), (size_t)a.L * sizeof(float), s, a);
+    // the listed entries (a few hundred per million): one workgroup each, up
+    // to 2048 at once; every workgroup reads the count and exits when there is
+    // nothing left for it
+    hipLaunchKernelGGL((calib_fixup_kernel<D>), dim3(2048), dim3(256), (size_t)a.L * sizeof(float), s, a);
     return hipGetLastError();
 }
 
