@@ -31,6 +31,8 @@
 // Sec. 3.2.1), from one more pass over the column's scores.
 #include "topth_internal.h"
 
+#include <type_traits>
+
 #include <math.h>
 
 namespace topth {
@@ -962,25 +964,36 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
     // have the bits of +inf and match no target.
     const uint32_t reg_off = hw_off + (uint32_t)(kCtRegion * lane) * 4u;
     int cc[2] = {0, 0};
-    auto collect = [&](f32x4 (&st)[2][4]) {
+    // NT compares per element: one sweep per target count (uniform branch)
+    auto collect_sweep = [&](auto nt_tag) {
+        constexpr int NT = decltype(nt_tag)::value;
+        auto collect = [&](f32x4 (&st)[2][4]) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+            for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+                for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = st[qb][kb][r];
-                    const uint32_t bits = __float_as_uint(fmaf(x, nbs[qb], cb[qb]));
-                    // bitwise, not short-circuit: no branch per element
-                    const int hit = (int)(bits == tb[qb][0]) | (int)(bits == tb[qb][1]) |
-                                    (int)(bits == tb[qb][2]) | (int)(bits == tb[qb][3]);
-                    const int slot = qb == 0 ? min(cc[0], kCtSlots - 1) : kCtSlots - 1 - min(cc[1], kCtSlots - 1);
-                    lds_store(reg_off + (uint32_t)slot * 4u, x);
-                    cc[qb] += hit;
-                }
-        }
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = st[qb][kb][r];
+                        const uint32_t bits = __float_as_uint(fmaf(x, nbs[qb], cb[qb]));
+                        // bitwise, not short-circuit: no branch per element
+                        int hit = (int)(bits == tb[qb][0]);
+#pragma unroll
+                        for (int t = 1; t < NT; ++t) hit |= (int)(bits == tb[qb][t]);
+                        const int slot = qb == 0 ? min(cc[0], kCtSlots - 1) : kCtSlots - 1 - min(cc[1], kCtSlots - 1);
+                        lds_store(reg_off + (uint32_t)slot * 4u, x);
+                        cc[qb] += hit;
+                    }
+            }
+        };
+        sweep(collect, collect);
     };
-    sweep(collect, collect);
+    switch (n_k) {
+        case 1: collect_sweep(std::integral_constant<int, 1>{}); break;
+        case 2: collect_sweep(std::integral_constant<int, 2>{}); break;
+        case 3: collect_sweep(std::integral_constant<int, 3>{}); break;
+        default: collect_sweep(std::integral_constant<int, kCtMaxK>{}); break;
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the written-out stores are done
     s_ccnt[wave][lane][0] = cc[0];
     s_ccnt[wave][lane][1] = cc[1];
