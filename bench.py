@@ -736,7 +736,7 @@ def bench_calib(with_cpu):
         "theta_finite_frac_layer0": round(fin.float().mean().item(), 4),
         "roofline": {"bound": "alu", "achieved": round(eps / 1e12, 4), "peak": EXP_PEAK_PER_S / 1e12,
                      "unit": "T exp/s", "frac": round(eps / EXP_PEAK_PER_S, 4), "traffic": None,
-                     "kernel": "calib_bf16_kernel",
+                     "kernel": "calib_tiled_kernel",
                      "mfma_qk_tflops": round(qk, 2), "mfma_frac": round(qk / BF16_PEAK_TFLOPS, 4)},
         "wall_s": round(wall, 3),
     }

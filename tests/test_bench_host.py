@@ -57,3 +57,19 @@ def test_committed_decode_summaries_name_their_source_hash(bench_module):
         text = open(path).read()
         assert "source_sha256:" in text and "traffic_bytes_per_dispatch:" in text
         assert wl in b.DECODE_WORKLOADS
+
+
+def test_every_profile_summary_names_its_command_and_source():
+    """Each committed rocprofv3 summary gives the command that made it (bench.py
+    runs only) and, for the library's own kernels, the hash of their device
+    code at the time."""
+    d = os.path.join(ROOT, "profiles")
+    names = sorted(os.listdir(d))
+    assert names
+    for name in names:
+        text = open(os.path.join(d, name)).read()
+        assert "Command (from the repository root" in text, name
+        assert "python3 bench.py" in text and "_work" not in text, name
+        if name.split(".")[0].startswith(("decode_bf16_kernel", "prefill_bf16_kernel", "calib_tiled_kernel",
+                                         "mkc_select_kernel")):
+            assert "source_sha256:" in text, name
