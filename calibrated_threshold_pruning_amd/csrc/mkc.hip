@@ -15,12 +15,16 @@
 // theta(k) is the value at the first such position.  The kernels therefore
 //   1. compute each sample row's values (post-softmax, or the scores) and
 //      its min and max (one workgroup per sample row, scores in LDS);
-//   2. sort the pooled values of each (head, row) in descending order (a
-//      stable LSD radix sort of the order-preserving 32-bit keys, by one
-//      workgroup, in global memory), then scan the positions, each thread
-//      evaluating the condition at its own positions with binary searches in
-//      the sorted sample maxima and minima, and keep for every target k the
-//      smallest qualifying position (an LDS atomic min).
+//   2. sort each (head, row)'s sample maxima and minima (one workgroup each);
+//   3. sort the pooled values of each (head, row) in descending order: a
+//      stable LSD radix sort of the order-preserving 32-bit keys, 8 bits per
+//      pass, spread over workgroups of 32768 values (per pass: a histogram
+//      per chunk, a scan per (head, row) into every chunk's output positions,
+//      then a stable scatter of every chunk);
+//   4. walk the sorted positions, chunk by chunk, each thread evaluating the
+//      condition at its own positions with binary searches in the sorted
+//      maxima and minima, and keep for every target k the smallest
+//      qualifying position (a global atomic min); then read theta there.
 // Integer counts and the sort make the result exact for the values computed:
 // the same values give the same theta on any launch.
 #include "topth_internal.h"
@@ -28,10 +32,14 @@
 #include <math.h>
 #include <limits.h>
 
+#include <type_traits>
+
 namespace topth {
 
 constexpr int kMkcValThreads = 256;
 constexpr int kMkcSelThreads = 1024;
+constexpr int kMkcChunk = 32768;         // pooled values per workgroup of the sort passes
+constexpr int kMkcWalkChunk = 8192;      // sorted positions per workgroup of the walk
 constexpr int kMkcMaxSamples = 4096;
 constexpr int kMkcMaxTargets = 64;
 constexpr int kMkcMaxKeys = 32768;
@@ -43,7 +51,10 @@ struct MkcArgs {
     float scale;
     float* pool;             // [Hq][Lq] segments of S * m values (sample s at s * m)
     float* pool2;            // second buffer of the radix sort, same layout
-    float* smin; float* smax;  // [Hq][Lq][S]
+    float* smin; float* smax;  // [Hq][Lq][S], ascending after mkc_sortmm_kernel
+    int* hist;               // [Hq * Lq][256][wps]: counts per (digit, chunk), then output positions
+    int* best;               // [Hq * Lq][n_k]: first qualifying sorted position per target
+    int wps;                 // chunks (workgroups) per (head, row): ceil(S * m_max / kMkcChunk)
     int n_k;
     int ks[kMkcMaxTargets];
     float* theta;            // [n_k][Hq][n_rows]
@@ -53,25 +64,6 @@ struct MkcArgs {
 __host__ __device__ __forceinline__ long long mkc_row_prefix(int q_pos0, int i) {
     return (long long)i * (q_pos0 + 1) + (long long)i * (i - 1) / 2;
 }
-
-template <typename T> struct MkcLoad;
-template <> struct MkcLoad<uint16_t> {   // bfloat16: 8 per 16-byte chunk
-    static constexpr int EPC = 8;
-    static __device__ __forceinline__ void unpack(const u32x4& u, float* f) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __uint_as_float(u[i] << 16);
-            f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-        }
-    }
-};
-template <> struct MkcLoad<float> {
-    static constexpr int EPC = 4;
-    static __device__ __forceinline__ void unpack(const u32x4& u, float* f) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(u[i]);
-    }
-};
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
 #pragma unroll
@@ -89,80 +81,168 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 }
 
 // ---------------------------------------------------------------- values
-// One workgroup per (sample s, head h, row i): scores of keys 0..p into LDS
-// (a group of lanes per key reads its K row in 16-byte chunks), then the
-// post-softmax values s_j = exp2(x_j - lse2) (or the scores) to the pool, and
-// the row's min and max.
-template <typename T, int D>
-__global__ __launch_bounds__(kMkcValThreads) void mkc_values_kernel(MkcArgs a) {
-    extern __shared__ float s_sc[];
+// One workgroup per (sample s, HPW query heads h0.. of one KV group, row i):
+// the scores of keys 0..p of every head go to LDS (s_sc[u * m + j], exp2
+// domain unless pre), then mkc_emit_rows writes each head's values to the
+// pool with the row's min and max.
+
+// after every score of the HPW heads is in s_sc: per head, the row max, the
+// log-sum-exp and the values s_j = exp2(x_j - lse2) (or the scores), then
+// the min and max of the written values
+template <int HPW>
+__device__ __forceinline__ void mkc_emit_rows(const MkcArgs& a, const float* s_sc, float* s_red, int s, int h0,
+                                              int i, int m) {
+    __syncthreads();                           // every score is in LDS
+#pragma unroll 1
+    for (int u = 0; u < HPW; ++u) {
+        const int h = h0 + u;
+        const float* sc = s_sc + u * m;
+        float out_min = INFINITY, out_max = -INFINITY;
+        float* dst = a.pool + (size_t)h * a.S * mkc_row_prefix(a.q_pos0, a.Lq) +
+                     (size_t)a.S * mkc_row_prefix(a.q_pos0, i) + (size_t)s * m;
+        if (a.pre) {
+            for (int j = threadIdx.x; j < m; j += kMkcValThreads) {
+                const float v = sc[j] + 0.0f;  // -0 becomes +0: one key per value
+                dst[j] = v;
+                out_min = fminf(out_min, v);
+                out_max = fmaxf(out_max, v);
+            }
+        } else {
+            float mx = -INFINITY;
+            for (int j = threadIdx.x; j < m; j += kMkcValThreads) mx = fmaxf(mx, sc[j]);
+            mx = block_reduce(mx, s_red, true);
+            float l = 0.f;
+            for (int j = threadIdx.x; j < m; j += kMkcValThreads) l += exp2f(sc[j] - mx);
+            l = block_reduce(l, s_red, false);
+            const float lse2 = mx + log2f(l);
+            for (int j = threadIdx.x; j < m; j += kMkcValThreads) {
+                const float v = exp2f(sc[j] - lse2);
+                dst[j] = v;
+                out_min = fminf(out_min, v);
+                out_max = fmaxf(out_max, v);
+            }
+        }
+        out_min = -block_reduce(-out_min, s_red, true);
+        out_max = block_reduce(out_max, s_red, true);
+        if (threadIdx.x == 0) {
+            const size_t o = ((size_t)h * a.Lq + i) * a.S + s;
+            a.smin[o] = out_min;
+            a.smax[o] = out_max;
+        }
+    }
+}
+
+// float32: a group of lanes per key reads its K row in 16-byte chunks once
+// for all HPW heads and reduces the HPW dot products across the group
+template <int D, int HPW>
+__global__ __launch_bounds__(kMkcValThreads) void mkc_values_f32_kernel(MkcArgs a) {
+    extern __shared__ float s_sc[];            // [HPW][m]
     __shared__ float s_red[kMkcValThreads / 64];
-    constexpr int EPC = MkcLoad<T>::EPC;
+    constexpr int EPC = 4;                     // floats per 16-byte chunk
     constexpr int LPR = D / EPC;               // lanes per key row
     constexpr int RPW = 64 / LPR;              // key rows per wave step
-    const int row = blockIdx.x;                // ((s * Hq) + h) * Lq + i
+    const int nhb = a.Hq / HPW;                // head blocks
+    const int row = blockIdx.x;                // ((s * nhb) + hb) * Lq + i
     const int i = row % a.Lq;
-    const int h = (row / a.Lq) % a.Hq;
-    const int s = row / (a.Lq * a.Hq);
+    const int hb = (row / a.Lq) % nhb;
+    const int s = row / (a.Lq * nhb);
     const int g = a.Hq / a.Hkv;
-    const int p = a.q_pos0 + i;
-    const int m = p + 1;
+    const int h0 = hb * HPW;                   // HPW divides g: one KV head
+    const int m = a.q_pos0 + i + 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPR, grp = lane / LPR;
+    const float mul = a.pre ? a.scale : a.xscale;
 
-    const T* qrow = (const T*)a.q + (((size_t)s * a.Hq + h) * a.Lq + i) * D;
-    const T* kg = (const T*)a.k + ((size_t)s * a.Hkv + h / g) * (size_t)a.Lk * D;
-    float qf[EPC];
-    MkcLoad<T>::unpack(*(const u32x4*)(qrow + sub * EPC), qf);
-
-    float mx = -INFINITY;
+    const float* kg = (const float*)a.k + ((size_t)s * a.Hkv + h0 / g) * (size_t)a.Lk * D;
+    float qf[HPW][EPC];
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
+        const float* qrow = (const float*)a.q + (((size_t)s * a.Hq + h0 + u) * a.Lq + i) * D;
+        const u32x4 w = *(const u32x4*)(qrow + sub * EPC);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) qf[u][e] = __uint_as_float(w[e]);
+    }
     for (int j0 = wave * RPW; j0 < m; j0 += (kMkcValThreads / 64) * RPW) {
         const int j = j0 + grp;
-        float dot = 0.f;
+        float kf[EPC] = {0.f, 0.f, 0.f, 0.f};
         if (j < m) {
-            float kf[EPC];
-            MkcLoad<T>::unpack(*(const u32x4*)(kg + (size_t)j * D + sub * EPC), kf);
+            const u32x4 w = *(const u32x4*)(kg + (size_t)j * D + sub * EPC);
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) dot = fmaf(qf[e], kf[e], dot);
+            for (int e = 0; e < EPC; ++e) kf[e] = __uint_as_float(w[e]);
         }
 #pragma unroll
-        for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);
-        if (j < m && sub == 0) {
-            const float x = a.pre ? dot * a.scale : dot * a.xscale;
-            s_sc[j] = x;
-            mx = fmaxf(mx, x);
+        for (int u = 0; u < HPW; ++u) {
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) dot = fmaf(qf[u][e], kf[e], dot);
+#pragma unroll
+            for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);
+            if (j < m && sub == 0) s_sc[u * m + j] = dot * mul;
         }
     }
-    mx = block_reduce(mx, s_red, true);        // its barriers also publish s_sc
-    float out_min = INFINITY, out_max = -INFINITY;
-    float* dst = a.pool + (size_t)h * a.S * mkc_row_prefix(a.q_pos0, a.Lq) +
-                 (size_t)a.S * mkc_row_prefix(a.q_pos0, i) + (size_t)s * m;
-    if (a.pre) {
-        for (int j = threadIdx.x; j < m; j += kMkcValThreads) {
-            const float v = s_sc[j] + 0.0f;    // -0 becomes +0: one key per value
-            dst[j] = v;
-            out_min = fminf(out_min, v);
-            out_max = fmaxf(out_max, v);
-        }
-    } else {
-        float l = 0.f;
-        for (int j = threadIdx.x; j < m; j += kMkcValThreads) l += exp2f(s_sc[j] - mx);
-        l = block_reduce(l, s_red, false);
-        const float lse2 = mx + log2f(l);
-        for (int j = threadIdx.x; j < m; j += kMkcValThreads) {
-            const float v = exp2f(s_sc[j] - lse2);
-            dst[j] = v;
-            out_min = fminf(out_min, v);
-            out_max = fmaxf(out_max, v);
+    mkc_emit_rows<HPW>(a, s_sc, s_red, s, h0, i, m);
+}
+
+// bfloat16: v_mfma_f32_16x16x32_bf16 with the HPW query heads in the A
+// operand's rows (rows past HPW are zero) and 16 keys in B's columns.  Every
+// lane loads its B fragments (8 elements of one K row per k-step) straight
+// from memory, kNtk key tiles at a time, so that 4 * kNtk (d = 128) 16-byte
+// loads per lane are in flight before the MFMAs that consume them; lanes
+// 0..15 (and 16..31 for HPW = 8) then hold 4 heads' scores of their key.
+constexpr int kMkcNtk = 4;
+template <int D, int HPW>
+__global__ __launch_bounds__(kMkcValThreads) void mkc_values_bf16_kernel(MkcArgs a) {
+    extern __shared__ float s_sc[];            // [HPW][m]
+    __shared__ float s_red[kMkcValThreads / 64];
+    constexpr int ST = D / 32;                 // k-steps
+    constexpr int NW = kMkcValThreads / 64;
+    const int nhb = a.Hq / HPW;
+    const int row = blockIdx.x;                // ((s * nhb) + hb) * Lq + i
+    const int i = row % a.Lq;
+    const int hb = (row / a.Lq) % nhb;
+    const int s = row / (a.Lq * nhb);
+    const int g = a.Hq / a.Hkv;
+    const int h0 = hb * HPW;
+    const int m = a.q_pos0 + i + 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, kq = lane >> 4;
+    const float mul = a.pre ? a.scale : a.xscale;
+
+    bf16x8 qa[ST];
+    {
+        const uint16_t* qrow = (const uint16_t*)a.q + (((size_t)s * a.Hq + h0 + min(col, HPW - 1)) * a.Lq + i) * D;
+#pragma unroll
+        for (int st = 0; st < ST; ++st) {
+            u32x4 w = *(const u32x4*)(qrow + 32 * st + 8 * kq);
+            if (col >= HPW) w = u32x4{0u, 0u, 0u, 0u};
+            qa[st] = __builtin_bit_cast(bf16x8, w);
         }
     }
-    out_min = -block_reduce(-out_min, s_red, true);
-    out_max = block_reduce(out_max, s_red, true);
-    if (threadIdx.x == 0) {
-        const size_t o = ((size_t)h * a.Lq + i) * a.S + s;
-        a.smin[o] = out_min;
-        a.smax[o] = out_max;
+    const uint16_t* kg = (const uint16_t*)a.k + ((size_t)s * a.Hkv + h0 / g) * (size_t)a.Lk * D;
+    for (int t0 = wave * 16 * kMkcNtk; t0 < m; t0 += NW * 16 * kMkcNtk) {
+        u32x4 kb[kMkcNtk][ST];
+#pragma unroll
+        for (int tk = 0; tk < kMkcNtk; ++tk) {
+            const int key = min(t0 + 16 * tk + col, m - 1);      // keys past the row repeat its last
+#pragma unroll
+            for (int st = 0; st < ST; ++st) kb[tk][st] = *(const u32x4*)(kg + (size_t)key * D + 32 * st + 8 * kq);
+        }
+#pragma unroll
+        for (int tk = 0; tk < kMkcNtk; ++tk) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < ST; ++st)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], __builtin_bit_cast(bf16x8, kb[tk][st]), acc, 0,
+                                                              0, 0);
+            const int key = t0 + 16 * tk + col;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int u = 4 * kq + r;
+                if (u < HPW && key < m) s_sc[u * m + key] = acc[r] * mul;
+            }
+        }
     }
+    mkc_emit_rows<HPW>(a, s_sc, s_red, s, h0, i, m);
 }
 
 // ---------------------------------------------------------------- select
@@ -196,136 +276,225 @@ __device__ __forceinline__ int count_ge(const float* x, int n2, float v) {
     return n2 - lo;
 }
 
-// One workgroup of 1024 threads per (head h, row i).
-__global__ __launch_bounds__(kMkcSelThreads) void mkc_select_kernel(MkcArgs a) {
-    __shared__ float s_max[kMkcMaxSamples], s_min[kMkcMaxSamples];
-    __shared__ int s_hist[256], s_base[256], s_tile[256];
-    __shared__ int s_cnt[kMkcSelThreads / 64][256];
-    __shared__ int s_best[kMkcMaxTargets];
-    constexpr int NW = kMkcSelThreads / 64;
-    const int seg = blockIdx.x;                // h * Lq + i
-    const int i = seg % a.Lq, h = seg / a.Lq;
-    const int p = a.q_pos0 + i;
-    const int m = p + 1;
-    const int S = a.S;
-    const int N = S * m;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t off = (size_t)h * S * mkc_row_prefix(a.q_pos0, a.Lq) + (size_t)S * mkc_row_prefix(a.q_pos0, i);
-    float* src = a.pool + off;
-    float* dst = a.pool2 + off;
+// the pooled values of (head h, row i) = segment h * Lq + i: offset and count
+struct MkcSeg { size_t off; int N; int m; int p; int h; };
+__device__ __forceinline__ MkcSeg mkc_seg(const MkcArgs& a, int seg) {
+    MkcSeg g;
+    const int i = seg % a.Lq;
+    g.h = seg / a.Lq;
+    g.p = a.q_pos0 + i;
+    g.m = g.p + 1;
+    g.N = a.S * g.m;
+    g.off = (size_t)g.h * a.S * mkc_row_prefix(a.q_pos0, a.Lq) + (size_t)a.S * mkc_row_prefix(a.q_pos0, i);
+    return g;
+}
 
-    // sample maxima and minima, ascending, padded with -inf to a power of two
+// One workgroup per (head, row): its S sample maxima and minima, ascending.
+__global__ __launch_bounds__(kMkcSelThreads) void mkc_sortmm_kernel(MkcArgs a) {
+    __shared__ float s_x[kMkcMaxSamples];
+    const int seg = blockIdx.x;
     int n2 = 1;
-    while (n2 < S) n2 <<= 1;
-    for (int c = tid; c < n2; c += kMkcSelThreads) {
-        const size_t o = ((size_t)h * a.Lq + i) * S + c;
-        s_max[c] = c < S ? a.smax[o] : -INFINITY;
-        s_min[c] = c < S ? a.smin[o] : -INFINITY;
+    while (n2 < a.S) n2 <<= 1;
+    for (int which = 0; which < 2; ++which) {
+        float* v = (which ? a.smax : a.smin) + (size_t)seg * a.S;
+        __syncthreads();                       // s_x is free
+        for (int c = threadIdx.x; c < n2; c += blockDim.x) s_x[c] = c < a.S ? v[c] : -INFINITY;
+        lds_bitonic_asc(s_x, n2);              // the -inf padding sorts to the front
+        for (int c = threadIdx.x; c < a.S; c += blockDim.x) v[c] = s_x[n2 - a.S + c];
     }
-    for (int t = tid; t < kMkcMaxTargets; t += kMkcSelThreads) s_best[t] = INT_MAX;
+}
+
+// Sort pass, step 1: the 256-bin histogram of digit (key >> sh) & 255 of one
+// chunk, to hist[(seg * 256 + digit) * wps + chunk] (chunks past the
+// segment's end count nothing).
+__global__ __launch_bounds__(256) void mkc_hist_kernel(MkcArgs a, const float* src, int sh) {
+    __shared__ int s_h[256];
+    const int seg = blockIdx.x / a.wps, ck = blockIdx.x % a.wps;
+    const MkcSeg g = mkc_seg(a, seg);
+    s_h[threadIdx.x] = 0;
+    __syncthreads();
+    const int end = min(g.N, (ck + 1) * kMkcChunk);
+    for (int j = ck * kMkcChunk + threadIdx.x; j < end; j += 256)
+        atomicAdd(&s_h[(mkc_key(src[g.off + j]) >> sh) & 255u], 1);
+    __syncthreads();
+    a.hist[((size_t)seg * 256 + threadIdx.x) * a.wps + ck] = s_h[threadIdx.x];
+}
+
+// Sort pass, step 2: exclusive scan of one segment's counts in (digit,
+// chunk) order, in place: the first output position of every (digit, chunk).
+__global__ __launch_bounds__(kMkcSelThreads) void mkc_scan_kernel(MkcArgs a) {
+    __shared__ int s_w[kMkcSelThreads / 64];
+    int* x = a.hist + (size_t)blockIdx.x * 256 * a.wps;
+    const int n = 256 * a.wps;
+    const int per = (n + kMkcSelThreads - 1) / kMkcSelThreads;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
+    int sum = 0;
+    for (int j = b0; j < b1; ++j) sum += x[j];
+    int incl = sum;                            // scan of the thread sums: wave, then across waves
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int w = __shfl_up(incl, o);
+        if (lane >= o) incl += w;
+    }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += s_w[w];
+    int run = before + incl - sum;
+    for (int j = b0; j < b1; ++j) { const int c = x[j]; x[j] = run; run += c; }
+}
+
+// Sort pass, step 3: stable scatter of one chunk, in tiles of 1024 values
+// (ranks inside a wave from ballots on the digit bits, then a prefix over
+// the waves), to the positions the scan gave this chunk.
+__global__ __launch_bounds__(kMkcSelThreads) void mkc_scatter_kernel(MkcArgs a, const float* src, float* dst,
+                                                                     int sh) {
+    __shared__ int s_base[256], s_tile[256];
+    __shared__ int s_cnt[kMkcSelThreads / 64][256];
+    constexpr int NW = kMkcSelThreads / 64;
+    const int seg = blockIdx.x / a.wps, ck = blockIdx.x % a.wps;
+    const MkcSeg g = mkc_seg(a, seg);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < 256) s_base[tid] = a.hist[((size_t)seg * 256 + tid) * a.wps + ck];
     for (int t = tid; t < NW * 256; t += kMkcSelThreads) (&s_cnt[0][0])[t] = 0;
-    lds_bitonic_asc(s_max, n2);
-    lds_bitonic_asc(s_min, n2);
-
-    // stable LSD radix sort, 8 bits per pass, of the keys of the N values
+    __syncthreads();
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int sh = 0; sh < 32; sh += 8) {
-        for (int t = tid; t < 256; t += kMkcSelThreads) s_hist[t] = 0;
+    const int end = min(g.N, (ck + 1) * kMkcChunk);
+    for (int t0 = ck * kMkcChunk; t0 < end; t0 += kMkcSelThreads) {
+        const int j = t0 + tid;
+        const bool valid = j < end;
+        const float v = valid ? src[g.off + j] : 0.f;
+        const int dg = valid ? (int)((mkc_key(v) >> sh) & 255u) : 0;
+        // lanes of this wave with the same digit, in lane order
+        unsigned long long peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const unsigned long long bb = __ballot(valid && ((dg >> b) & 1));
+            peers &= ((dg >> b) & 1) ? bb : ~bb;
+        }
+        const int rank = __popcll(peers & lt);
+        if (valid && rank == 0) s_cnt[wave][dg] = __popcll(peers);
         __syncthreads();
-        for (int j = tid; j < N; j += kMkcSelThreads)
-            atomicAdd(&s_hist[(mkc_key(src[j]) >> sh) & 255u], 1);
-        __syncthreads();
-        if (tid < 64) {                        // exclusive scan of the 256 bins, 4 per lane
-            int v[4], sum = 0;
+        if (tid < 256) {                       // prefix over the waves, per digit
+            int run = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { v[e] = s_hist[4 * tid + e]; sum += v[e]; }
-            int incl = sum;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int w = __shfl_up(incl, o);
-                if (lane >= o) incl += w;
-            }
-            int run = incl - sum;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { s_base[4 * tid + e] = run; run += v[e]; }
+            for (int w = 0; w < NW; ++w) { const int c = s_cnt[w][tid]; s_cnt[w][tid] = run; run += c; }
+            s_tile[tid] = run;
         }
         __syncthreads();
-        for (int t0 = 0; t0 < N; t0 += kMkcSelThreads) {
-            const int j = t0 + tid;
-            const bool valid = j < N;
-            const float v = valid ? src[j] : 0.f;
-            const int dg = valid ? (int)((mkc_key(v) >> sh) & 255u) : 0;
-            // lanes of this wave with the same digit, in lane order
-            unsigned long long peers = __ballot(valid);
+        if (valid) dst[g.off + s_base[dg] + s_cnt[wave][dg] + rank] = v;
+        __syncthreads();
+        if (tid < 256) {
+            s_base[tid] += s_tile[tid];
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const unsigned long long bb = __ballot(valid && ((dg >> b) & 1));
-                peers &= ((dg >> b) & 1) ? bb : ~bb;
-            }
-            const int rank = __popcll(peers & lt);
-            if (valid && rank == 0) s_cnt[wave][dg] = __popcll(peers);
-            __syncthreads();
-            if (tid < 256) {                   // prefix over the waves, per digit
-                int run = 0;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) { const int c = s_cnt[w][tid]; s_cnt[w][tid] = run; run += c; }
-                s_tile[tid] = run;
-            }
-            __syncthreads();
-            if (valid) dst[s_base[dg] + s_cnt[wave][dg] + rank] = v;
-            __syncthreads();
-            if (tid < 256) {
-                s_base[tid] += s_tile[tid];
-#pragma unroll
-                for (int w = 0; w < NW; ++w) s_cnt[w][tid] = 0;
-            }
-            __syncthreads();
+            for (int w = 0; w < NW; ++w) s_cnt[w][tid] = 0;
         }
-        float* t = src; src = dst; dst = t;    // the sorted pass is the next source
+        __syncthreads();
     }
-    // after four passes the values are back in the first buffer, descending
+}
 
-    // the walk: every position that ends a run of equal values
-    for (int j = tid; j < N; j += kMkcSelThreads) {
-        const float x = src[j];
-        if (j + 1 < N && src[j + 1] == x) continue;
-        const int Mx = count_ge(s_max, n2, x);
-        const int Nl = count_ge(s_min, n2, x);
+// The walk over one chunk of sorted positions: every position that ends a
+// run of equal values is tested; the smallest qualifying one per target
+// goes to best[seg][t].  Each thread visits its positions in increasing
+// order, so its first hit for a target is its smallest: it records that one
+// (an LDS atomic min) and stops testing the target; the workgroup then
+// makes one global atomic min per target.
+__global__ __launch_bounds__(256) void mkc_walk_kernel(MkcArgs a, const float* sorted, int wpw) {
+    __shared__ float s_max[kMkcMaxSamples], s_min[kMkcMaxSamples];
+    __shared__ int s_best[kMkcMaxTargets];
+    const int seg = blockIdx.x / wpw, ck = blockIdx.x % wpw;
+    const MkcSeg g = mkc_seg(a, seg);
+    const int S = a.S;
+    for (int c = threadIdx.x; c < S; c += 256) {
+        s_max[c] = a.smax[(size_t)seg * S + c];
+        s_min[c] = a.smin[(size_t)seg * S + c];
+    }
+    for (int t = threadIdx.x; t < a.n_k; t += 256) s_best[t] = INT_MAX;
+    __syncthreads();
+    const float* x = sorted + g.off;
+    const int end = min(g.N, (ck + 1) * kMkcWalkChunk);
+    const unsigned long long all = a.n_k == 64 ? ~0ull : ((1ull << a.n_k) - 1ull);
+    unsigned long long done = 0ull;
+    for (int j = ck * kMkcWalkChunk + threadIdx.x; j < end && done != all; j += 256) {
+        const float v = x[j];
+        if (j + 1 < g.N && x[j + 1] == v) continue;
+        const int Mx = count_ge(s_max, S, v);
+        const int Nl = count_ge(s_min, S, v);
         const long long C = (long long)Mx - Nl;
         if (C <= 0) continue;
-        const long long T = (long long)(j + 1) - (long long)m * Nl;
+        const long long T = (long long)(j + 1) - (long long)g.m * Nl;
         for (int t = 0; t < a.n_k; ++t)
-            if (T >= (long long)a.ks[t] * C) atomicMin(&s_best[t], j);
+            if (!((done >> t) & 1ull) && T >= (long long)a.ks[t] * C) {
+                atomicMin(&s_best[t], j);
+                done |= 1ull << t;
+            }
     }
     __syncthreads();
-    if (p < a.n_rows)
-        for (int t = tid; t < a.n_k; t += kMkcSelThreads) {
-            const int b = s_best[t];
-            a.theta[((size_t)t * a.Hq + h) * a.n_rows + p] = b == INT_MAX ? -INFINITY : src[b];
-        }
+    for (int t = threadIdx.x; t < a.n_k; t += 256)
+        if (s_best[t] != INT_MAX) atomicMin(&a.best[(size_t)seg * a.n_k + t], s_best[t]);
+}
+
+// theta at every target's first qualifying position (-inf where none)
+__global__ void mkc_theta_kernel(MkcArgs a, const float* sorted) {
+    const int seg = blockIdx.x;
+    const MkcSeg g = mkc_seg(a, seg);
+    if (g.p >= a.n_rows) return;
+    for (int t = threadIdx.x; t < a.n_k; t += blockDim.x) {
+        const int b = a.best[(size_t)seg * a.n_k + t];
+        a.theta[((size_t)t * a.Hq + g.h) * a.n_rows + g.p] = b == INT_MAX ? -INFINITY : sorted[g.off + b];
+    }
 }
 
 // ------------------------------------------------------------------ host side
+// chunks per (head, row) for rows of at most m_max keys
+static long long mkc_wps(int S, int m_max) { return ((long long)S * m_max + kMkcChunk - 1) / kMkcChunk; }
+// chunks per (head, row) of the walk
+static long long mkc_wpw(int S, int m_max) { return ((long long)S * m_max + kMkcWalkChunk - 1) / kMkcWalkChunk; }
+
 size_t mkc_ws_bytes(int S, int Hq, int Lq, int Lk) {
     const size_t seg = (size_t)S * Hq * Lq * Lk;          // bound of the pooled values
-    return 2 * seg * sizeof(float) + 2 * (size_t)Hq * Lq * S * sizeof(float) + 1024;
+    const size_t hist = (size_t)Hq * Lq * 256 * (size_t)mkc_wps(S, Lk);
+    return 2 * seg * sizeof(float) + 2 * (size_t)Hq * Lq * S * sizeof(float) + hist * sizeof(int) +
+           (size_t)Hq * Lq * kMkcMaxTargets * sizeof(int) + 4096;
 }
 
 int mkc_max_samples() { return kMkcMaxSamples; }
 int mkc_max_targets() { return kMkcMaxTargets; }
 int mkc_max_keys() { return kMkcMaxKeys; }
 
-template <typename T, int D>
-static int launch_values(const MkcArgs& a, hipStream_t s) {
+template <typename T, int D, int HPW>
+static int launch_values_hpw(const MkcArgs& a, hipStream_t s) {
+    const void* fn = std::is_same<T, float>::value ? (const void*)mkc_values_f32_kernel<D, HPW>
+                                                    : (const void*)mkc_values_bf16_kernel<D, HPW>;
     const int m_max = a.q_pos0 + a.Lq;
-    const size_t smem = (size_t)m_max * sizeof(float);
+    const size_t smem = (size_t)HPW * m_max * sizeof(float);
     if (smem > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)mkc_values_kernel<T, D>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((mkc_values_kernel<T, D>), dim3(a.S * a.Hq * a.Lq), dim3(kMkcValThreads), smem, s, a);
+    const dim3 grid(a.S * (a.Hq / HPW) * a.Lq), block(kMkcValThreads);
+    if (std::is_same<T, float>::value)
+        hipLaunchKernelGGL((mkc_values_f32_kernel<D, HPW>), grid, block, smem, s, a);
+    else
+        hipLaunchKernelGGL((mkc_values_bf16_kernel<D, HPW>), grid, block, smem, s, a);
     return hipGetLastError();
+}
+
+// heads per workgroup: the largest power of two up to 8 that divides the
+// group size and keeps HPW rows of scores within 128 KiB of LDS
+template <typename T, int D>
+static int launch_values(const MkcArgs& a, hipStream_t s) {
+    const int g = a.Hq / a.Hkv;
+    const long long m_max = a.q_pos0 + a.Lq;
+    int hpw = 8;
+    while (hpw > 1 && (g % hpw != 0 || hpw * m_max * 4 > 131072)) hpw >>= 1;
+    switch (hpw) {
+        case 8: return launch_values_hpw<T, D, 8>(a, s);
+        case 4: return launch_values_hpw<T, D, 4>(a, s);
+        case 2: return launch_values_hpw<T, D, 2>(a, s);
+        default: return launch_values_hpw<T, D, 1>(a, s);
+    }
 }
 
 int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_t s) {
@@ -339,6 +508,13 @@ int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_
     a.pool2 = a.pool + seg;
     a.smin = a.pool2 + seg;
     a.smax = a.smin + (size_t)p.Hq * p.Lq * p.S;
+    a.hist = (int*)(a.smax + (size_t)p.Hq * p.Lq * p.S);
+    const long long wps = mkc_wps(p.S, p.q_pos0 + p.Lq);
+    const long long nseg = (long long)p.Hq * p.Lq;
+    const long long wpw = mkc_wpw(p.S, p.q_pos0 + p.Lq);
+    if (wpw * nseg >= (1LL << 31)) return hipErrorInvalidValue;   // one grid dimension
+    a.wps = (int)wps;
+    a.best = a.hist + (size_t)nseg * 256 * (size_t)wps;
     a.n_k = p.n_k;
     for (int t = 0; t < p.n_k; ++t) a.ks[t] = p.mkc_ks[t];
     a.theta = theta;
@@ -346,7 +522,22 @@ int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_
     if (p.dtype == 1) e = p.d == 64 ? launch_values<uint16_t, 64>(a, s) : launch_values<uint16_t, 128>(a, s);
     else e = p.d == 64 ? launch_values<float, 64>(a, s) : launch_values<float, 128>(a, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mkc_select_kernel, dim3(p.Hq * p.Lq), dim3(kMkcSelThreads), 0, s, a);
+    e = launch_fill_u32(a.best, (size_t)nseg * p.n_k * sizeof(int), (uint32_t)INT_MAX, s);
+    if (e != hipSuccess) return e;
+    const unsigned nseg_u = (unsigned)nseg, nwg = (unsigned)(wps * nseg);
+    hipLaunchKernelGGL(mkc_sortmm_kernel, dim3(nseg_u), dim3(kMkcSelThreads), 0, s, a);
+    // four passes of 8 bits; after them the values are back in the pool, descending
+    float* src = a.pool;
+    float* dst = a.pool2;
+    for (int sh = 0; sh < 32; sh += 8) {
+        hipLaunchKernelGGL(mkc_hist_kernel, dim3(nwg), dim3(256), 0, s, a, (const float*)src, sh);
+        hipLaunchKernelGGL(mkc_scan_kernel, dim3(nseg_u), dim3(kMkcSelThreads), 0, s, a);
+        hipLaunchKernelGGL(mkc_scatter_kernel, dim3(nwg), dim3(kMkcSelThreads), 0, s, a, (const float*)src, dst, sh);
+        float* t = src; src = dst; dst = t;
+    }
+    hipLaunchKernelGGL(mkc_walk_kernel, dim3((unsigned)(wpw * nseg)), dim3(256), 0, s, a, (const float*)src,
+                       (int)wpw);
+    hipLaunchKernelGGL(mkc_theta_kernel, dim3(nseg_u), dim3(64), 0, s, a, (const float*)src);
     return hipGetLastError();
 }
 

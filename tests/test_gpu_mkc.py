@@ -135,3 +135,18 @@ def test_mkc_decode_8b_calibration_size_sampled_heads():
         ref = mkc.mkc_calibrate(to_f64(q[:, h:h + 1]), to_f64(k[:, h // 4:h // 4 + 1]), 1.0 / np.sqrt(d), n - 1,
                                 ks, pre=False)
         compare(got[:, h:h + 1, n - 1:], ref, 1e-5, f"decode_8b calibration, head {h}")
+
+
+@pytest.mark.parametrize("dtype,d,Lk", [(torch.bfloat16, 64, 300), (torch.float32, 128, 9000)])
+def test_mkc_eight_query_heads_per_kv_head(dtype, d, Lk):
+    # one KV head shared by 8 query heads: short rows put the scores of all 8
+    # heads in one workgroup's LDS, a 9000-key row only those of 2
+    print(f"mkc g = 8 {dtype} d={d} Lk={Lk}", flush=True)
+    S, Hq, Hkv = 6, 8, 1
+    q, k, _ = attention_inputs(UNIT, ROLE_CALIB, 9, 0, B=S, Hq=Hq, Hkv=Hkv, Lq=1, Lk=Lk, d=d, n_sinks=1,
+                               dtype=dtype, with_v=False)
+    ks = [1, 8, 100, Lk - 1]
+    for pre in (False, True):
+        got = run_mkc(q, k, ks, Lk - 1, pre=pre)
+        ref = mkc.mkc_calibrate(to_f64(q), to_f64(k), 1.0 / np.sqrt(d), Lk - 1, ks, pre=pre)
+        compare(got[:, :, Lk - 1:], ref, 1e-5, f"g = 8, Lk = {Lk}, pre = {pre}")
