@@ -314,8 +314,17 @@ __global__ __launch_bounds__(256) void mkc_hist_kernel(MkcArgs a, const float* s
     s_h[threadIdx.x] = 0;
     __syncthreads();
     const int end = min(g.N, (ck + 1) * kMkcChunk);
-    for (int j = ck * kMkcChunk + threadIdx.x; j < end; j += 256)
-        atomicAdd(&s_h[(mkc_key(src[g.off + j]) >> sh) & 255u], 1);
+    const float* sp = src + g.off;
+    // 8 loads in flight per thread (indices past the chunk read its last value
+    // and are not counted)
+    for (int j0 = ck * kMkcChunk + threadIdx.x; j0 < end; j0 += 256 * 8) {
+        float v[8];
+#pragma unroll
+        for (int it = 0; it < 8; ++it) v[it] = sp[min(j0 + it * 256, end - 1)];
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+            if (j0 + it * 256 < end) atomicAdd(&s_h[(mkc_key(v[it]) >> sh) & 255u], 1);
+    }
     __syncthreads();
     a.hist[((size_t)seg * 256 + threadIdx.x) * a.wps + ck] = s_h[threadIdx.x];
 }
@@ -345,52 +354,123 @@ __global__ __launch_bounds__(kMkcSelThreads) void mkc_scan_kernel(MkcArgs a) {
     for (int j = b0; j < b1; ++j) { const int c = x[j]; x[j] = run; run += c; }
 }
 
-// Sort pass, step 3: stable scatter of one chunk, in tiles of 1024 values
-// (ranks inside a wave from ballots on the digit bits, then a prefix over
-// the waves), to the positions the scan gave this chunk.
-__global__ __launch_bounds__(kMkcSelThreads) void mkc_scatter_kernel(MkcArgs a, const float* src, float* dst,
-                                                                     int sh) {
-    __shared__ int s_base[256], s_tile[256];
-    __shared__ int s_cnt[kMkcSelThreads / 64][256];
-    constexpr int NW = kMkcSelThreads / 64;
+// Sort pass, step 3: stable scatter of one chunk, in tiles of 8192 values
+// (16 per thread).  Wave w owns the tile's values w * 1024 .. w * 1024 + 1023
+// and ranks them in index order, 64 at a time: lanes with equal digits find
+// each other through a per-wave LDS lane mask per digit, and a per-wave LDS
+// counter per digit carries the count of the earlier rounds.  A prefix over the waves and over the
+// digits then gives every value its place in the tile sorted by digit; the
+// tile is staged in LDS in that order and written out in order of place, so
+// that each digit's run (about 32 values) is written contiguously at the
+// position the scan gave this chunk for that digit.
+constexpr int kMkcScatThreads = 512;       // two workgroups per CU
+constexpr int kMkcScatItems = 16;
+constexpr int kMkcScatTile = kMkcScatThreads * kMkcScatItems;
+__global__ __launch_bounds__(kMkcScatThreads, 4) void mkc_scatter_kernel(MkcArgs a, const float* src, float* dst,
+                                                                         int sh) {
+    constexpr int NW = kMkcScatThreads / 64;
+    constexpr int PER_WAVE = 64 * kMkcScatItems;
+    __shared__ int s_wc[NW][256];              // per-wave counts, then the wave's offset inside the digit
+    __shared__ int s_base[256];                // next output position of each digit in this chunk
+    __shared__ int s_start[256];               // first place of each digit in the sorted tile
+    __shared__ int s_part[4];
+    __shared__ float s_out[kMkcScatTile];
+    __shared__ unsigned long long s_peer[NW][256];   // lanes per digit of the current round, zero between rounds
     const int seg = blockIdx.x / a.wps, ck = blockIdx.x % a.wps;
     const MkcSeg g = mkc_seg(a, seg);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid < 256) s_base[tid] = a.hist[((size_t)seg * 256 + tid) * a.wps + ck];
-    for (int t = tid; t < NW * 256; t += kMkcSelThreads) (&s_cnt[0][0])[t] = 0;
+    for (int t = tid; t < NW * 256; t += kMkcScatThreads) {
+        (&s_wc[0][0])[t] = 0;
+        (&s_peer[0][0])[t] = 0ull;
+    }
     __syncthreads();
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int end = min(g.N, (ck + 1) * kMkcChunk);
-    for (int t0 = ck * kMkcChunk; t0 < end; t0 += kMkcSelThreads) {
-        const int j = t0 + tid;
-        const bool valid = j < end;
-        const float v = valid ? src[g.off + j] : 0.f;
-        const int dg = valid ? (int)((mkc_key(v) >> sh) & 255u) : 0;
-        // lanes of this wave with the same digit, in lane order
-        unsigned long long peers = __ballot(valid);
+    const float* sp = src + g.off;
+    // the next tile's values are loaded while this one is ranked and written;
+    // the loads are unconditional (indices past the chunk read its last value,
+    // which is never used) so that the wait before ranking counts only the
+    // current tile's loads
+    auto load_tile = [&](int t0, float (&v)[kMkcScatItems]) {
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const unsigned long long bb = __ballot(valid && ((dg >> b) & 1));
-            peers &= ((dg >> b) & 1) ? bb : ~bb;
+        for (int it = 0; it < kMkcScatItems; ++it) v[it] = sp[min(t0 + wave * PER_WAVE + it * 64 + lane, end - 1)];
+    };
+    float v[kMkcScatItems], nv[kMkcScatItems];
+    if (ck * kMkcChunk < end) load_tile(ck * kMkcChunk, v);
+    for (int t0 = ck * kMkcChunk; t0 < end; t0 += kMkcScatTile) {
+        const int n = min(kMkcScatTile, end - t0);
+        int rk[kMkcScatItems];
+        load_tile(t0 + kMkcScatTile, nv);
+#pragma unroll
+        for (int it = 0; it < kMkcScatItems; ++it) {
+            const bool valid = wave * PER_WAVE + it * 64 + lane < n;
+            const int dg = (int)((mkc_key(v[it]) >> sh) & 255u);
+            // the lanes of this round with the same digit: each sets its bit in
+            // the wave's mask of that digit and reads the mask back; the first
+            // of them then adds the round's count and clears the mask.  LDS
+            // instructions of one wave execute in order, so every lane reads the
+            // complete mask and the old count before that lane's writes.
+            unsigned long long peers = 0ull;
+            int before = 0;
+            if (valid) {
+                atomicOr(&s_peer[wave][dg], 1ull << lane);
+                peers = s_peer[wave][dg];
+                before = s_wc[wave][dg];
+            }
+            const int r = __popcll(peers & lt);
+            if (valid && r == 0) {
+                s_wc[wave][dg] = before + __popcll(peers);
+                s_peer[wave][dg] = 0ull;
+            }
+            rk[it] = before + r;
         }
-        const int rank = __popcll(peers & lt);
-        if (valid && rank == 0) s_cnt[wave][dg] = __popcll(peers);
         __syncthreads();
+        int tot = 0;
         if (tid < 256) {                       // prefix over the waves, per digit
-            int run = 0;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) { const int c = s_cnt[w][tid]; s_cnt[w][tid] = run; run += c; }
-            s_tile[tid] = run;
+            for (int w = 0; w < NW; ++w) { const int c = s_wc[w][tid]; s_wc[w][tid] = tot; tot += c; }
         }
-        __syncthreads();
-        if (valid) dst[g.off + s_base[dg] + s_cnt[wave][dg] + rank] = v;
+        // exclusive scan of the tile's digit counts: places of the digits
+        int incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int w = __shfl_up(incl, o);
+            if (lane >= o) incl += w;
+        }
+        if (tid < 256 && lane == 63) s_part[wave] = incl;
         __syncthreads();
         if (tid < 256) {
-            s_base[tid] += s_tile[tid];
-#pragma unroll
-            for (int w = 0; w < NW; ++w) s_cnt[w][tid] = 0;
+            int before = 0;
+            for (int w = 0; w < wave; ++w) before += s_part[w];
+            s_start[tid] = before + incl - tot;
         }
         __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kMkcScatItems; ++it)
+            if (wave * PER_WAVE + it * 64 + lane < n) {
+                const int dg = (int)((mkc_key(v[it]) >> sh) & 255u);
+                s_out[s_start[dg] + s_wc[wave][dg] + rk[it]] = v[it];
+            }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kMkcScatItems; ++it) {
+            const int pl = it * kMkcScatThreads + tid;
+            if (pl < n) {
+                const float x = s_out[pl];
+                const int d = (int)((mkc_key(x) >> sh) & 255u);
+                dst[g.off + s_base[d] + (pl - s_start[d])] = x;
+            }
+        }
+        __syncthreads();
+        if (tid < 256) {
+            s_base[tid] += tot;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) s_wc[w][tid] = 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kMkcScatItems; ++it) v[it] = nv[it];
     }
 }
 
@@ -532,7 +612,7 @@ int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_
     for (int sh = 0; sh < 32; sh += 8) {
         hipLaunchKernelGGL(mkc_hist_kernel, dim3(nwg), dim3(256), 0, s, a, (const float*)src, sh);
         hipLaunchKernelGGL(mkc_scan_kernel, dim3(nseg_u), dim3(kMkcSelThreads), 0, s, a);
-        hipLaunchKernelGGL(mkc_scatter_kernel, dim3(nwg), dim3(kMkcSelThreads), 0, s, a, (const float*)src, dst, sh);
+        hipLaunchKernelGGL(mkc_scatter_kernel, dim3(nwg), dim3(kMkcScatThreads), 0, s, a, (const float*)src, dst, sh);
         float* t = src; src = dst; dst = t;
     }
     hipLaunchKernelGGL(mkc_walk_kernel, dim3((unsigned)(wpw * nseg)), dim3(256), 0, s, a, (const float*)src,
