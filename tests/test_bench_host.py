@@ -71,5 +71,5 @@ def test_every_profile_summary_names_its_command_and_source():
         assert "Command (from the repository root" in text, name
         assert "python3 bench.py" in text and "_work" not in text, name
         if name.split(".")[0].startswith(("decode_bf16_kernel", "prefill_bf16_kernel", "calib_tiled_kernel",
-                                         "mkc_select_kernel")):
+                                         "mkc_values_bf16_kernel")):
             assert "source_sha256:" in text, name
