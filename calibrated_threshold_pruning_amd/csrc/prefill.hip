@@ -224,8 +224,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
     // ======================= sweep A: row log-sum-exp =========================
     // K tiles go three ahead through the four slots: at step j the loads of
     // tiles j+1 and j+2 may still be in flight (loads retire in issue order,
-    // so waiting until at most their count is outstanding completes tile j)
+    // so waiting until at most their count is outstanding completes tile j).
+    // Each lane sums exp2(scale (s - m)) against a reference m that is a score
+    // it has seen (so the sum is at least 1 and every term is positive: no
+    // cancellation, whatever m is).  The tile maximum is only taken when the
+    // tile's sum is not finite or above 2^64: on the first tile (m = -inf) and
+    // when a score lies 64 or more above m in exp2 units.
     float m_l[2] = {NEG_INF, NEG_INF}, l_l[2] = {0.f, 0.f};
+    float nmc_l[2] = {INFINITY, INFINITY};                 // -m * xscale
     if constexpr (!PRE) {
         issue_k(0, 0);
         if (ntiles > 1) issue_k(1, 1);
@@ -240,8 +246,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         if (j + 3 < ntiles) issue_k(j + 3, (j + 3) & 3);
         f32x4 st[2][4];
         scores(j & 3, st);
-        // statistics in raw score units (the scale is positive): max, then
-        // sum of exp2(scale * (s - max)); only tiles that cross the diagonal mask
+        // statistics in raw score units (the scale is positive); only tiles
+        // that cross the diagonal mask
         const bool diag = j * C::BN + C::BN - 1 > row0;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -253,22 +259,31 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                     for (int r = 0; r < 4; ++r)
                         if (j * C::BN + 16 * kb + 4 * lq + r > row) st[qb][kb][r] = NEG_INF;
             }
-            float tmax = NEG_INF;
+            float sum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[qb][kb][r]);
-            const float mn = fmaxf(m_l[qb], tmax);
-            if (mn != NEG_INF) {
-                const float nmc = -mn * a.xscale;
-                float sum = 0.f;
+                for (int r = 0; r < 4; ++r) sum += pf_exp2(fmaf(st[qb][kb][r], a.xscale, nmc_l[qb]));
+            if (!(sum <= 0x1p64f)) {                       // also NaN: m = -inf meets a masked score
+                float tmax = NEG_INF;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sum += pf_exp2(fmaf(st[qb][kb][r], a.xscale, nmc));
-                l_l[qb] = l_l[qb] * pf_exp2((m_l[qb] - mn) * a.xscale) + sum;
-                m_l[qb] = mn;
+                    for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[qb][kb][r]);
+                const float mn = fmaxf(m_l[qb], tmax);
+                sum = 0.f;
+                if (mn != NEG_INF) {                       // else no score of this lane yet
+                    const float nmc = -mn * a.xscale;
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) sum += pf_exp2(fmaf(st[qb][kb][r], a.xscale, nmc));
+                    l_l[qb] *= pf_exp2((m_l[qb] - mn) * a.xscale);     // 0 while m = -inf (l = 0)
+                    m_l[qb] = mn;
+                    nmc_l[qb] = nmc;
+                }
             }
+            l_l[qb] += sum;
         }
     }
     // the four lanes of a row (16 lanes apart) hold partial statistics
