@@ -46,6 +46,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace topth {
 
 struct PrefillKArgs {
@@ -355,12 +357,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
     if constexpr (!PRE) __syncthreads();                   // sweep A is done with both K buffers
     issue_k(0, 0);
     issue_v(0, 0);
-    for (int j = 0; j < ntiles; ++j) {
+    // tile j lives in buffer j & 1; the loop takes two tiles per trip so that
+    // the buffer is a constant in each half and its LDS base folds into the
+    // read instructions' offsets
+    auto step_b = [&](int j, auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
         pf_wait_vmem();
         __syncthreads();                                   // K, V tile j landed; tile j-1 fully used
-        if (j + 1 < ntiles) { issue_k(j + 1, (j + 1) & 1); issue_v(j + 1, (j + 1) & 1); }
+        if (j + 1 < ntiles) { issue_k(j + 1, 1 - buf); issue_v(j + 1, 1 - buf); }
         f32x4 st[2][4];
-        scores(j & 1, st);
+        scores(buf, st);
         const bool diag = j * C::BN + C::BN - 1 > row0;
         unsigned pk[2][4][2], pl[2][4][2];                 // P^T fragments, packed bf16 (hi, lo)
 #pragma unroll
@@ -442,7 +448,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                 }
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) {
-                    const pf_f16x8 vtf = __builtin_bit_cast(pf_f16x8, vt_frag(j & 1, ks, db));
+                    const pf_f16x8 vtf = __builtin_bit_cast(pf_f16x8, vt_frag(buf, ks, db));
 #pragma unroll
                     for (int qb = 0; qb < 2; ++qb)
                         o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vtf, pb[qb], o[qb][db], 0, 0, 0);
@@ -451,7 +457,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
             pf_ds_mfma_pipeline<1, 4, 0>();
             pf_ds_mfma_pipeline<2 * C::DB - 1, 2, 2>();
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            continue;
+            return;
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -465,7 +471,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
             }
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-                const bf16x8 vtf = vt_frag(j & 1, ks, db);
+                const bf16x8 vtf = vt_frag(buf, ks, db);
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
                     o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtf, pb[qb], o[qb][db], 0, 0, 0);
@@ -477,6 +483,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         pf_ds_mfma_pipeline<1, 4, 0>();
         pf_ds_mfma_pipeline<2 * C::DB - 1, 2, 4>();
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    for (int j = 0; j < ntiles; j += 2) {
+        step_b(j, std::integral_constant<int, 0>{});
+        if (j + 1 < ntiles) step_b(j + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- epilogue: row totals, SDC_NONE / VMC, output (weights, sums and
