@@ -527,6 +527,9 @@ constexpr int kCtEntries = 32 * kCtMaxK;        // (row, target) entries of a wa
 static_assert(64 * kCtRegion <= kCtPool && 32 * kCtRowWords <= kCtPool, "histogram and regions in the pool");
 
 constexpr int kCtWaves = 4;
+// longest row of the tiled path: the fixup list packs a row into 16 bits, and
+// calib_fixup_kernel holds one row of scores in LDS (64 KiB at this length)
+constexpr int kCtMaxL = 16384;
 
 template <int D, int G>
 struct CtCfg {
@@ -1198,7 +1201,13 @@ static int launch_tiled_variant(const CalibTArgs& a, hipStream_t s) {
     // the listed entries (a few hundred per million): one workgroup each, up
     // to 2048 at once; every workgroup reads the count and exits when there is
     // nothing left for it
-    hipLaunchKernelGGL((calib_fixup_kernel<D>), dim3(2048), dim3(256), (size_t)a.L * sizeof(float), s, a);
+    const size_t smem = (size_t)a.L * sizeof(float);
+    if (smem > 48 * 1024) {
+        e = hipFuncSetAttribute((const void*)calib_fixup_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)smem);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((calib_fixup_kernel<D>), dim3(2048), dim3(256), smem, s, a);
     return hipGetLastError();
 }
 
@@ -1213,12 +1222,12 @@ static int launch_tiled_d(const CalibTArgs& a, int G, hipStream_t s) {
     }
 }
 
-// whole causal prefills of up to 4096 keys with at most four targets and no
+// whole causal prefills of up to kCtMaxL keys with at most four targets and no
 // discarded-mass samples take the tiled kernel
 static bool tiled_path(const CalibParams& p) {
     const int G = p.Hq / p.Hkv;
     // one grid dimension: (query tiles of at most 32 rows) x Hq x S workgroups at most
-    return p.q_pos0 == 0 && p.Lq == p.Lk && p.Lk <= 4096 && p.esum == nullptr && p.n_k <= kCtMaxK &&
+    return p.q_pos0 == 0 && p.Lq == p.Lk && p.Lk <= kCtMaxL && p.esum == nullptr && p.n_k <= kCtMaxK &&
            (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) && (long long)((p.Lq + 31) / 32) * p.Hq * p.S < (1LL << 31);
 }
 

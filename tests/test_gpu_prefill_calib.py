@@ -315,6 +315,32 @@ def test_prefill_bf16_group_sizes(Hq, Hkv, L, d):
     compare_prefill(g, q, k, v, theta, tt.TOPTH_VMC, torch.bfloat16)
 
 
+def test_calibrate_long_prefill_sampled_rows():
+    """Whole causal prefills of 8192 keys (4 query heads per KV head, d=128,
+    k = 128 and 512) through the tiled calibration: counts on every row, theta
+    on sampled rows (both sides of 4096 and of each k) against the oracle."""
+    Hq, Hkv, L, d, S = 4, 1, 8192, 128, 2
+    ks = [128, 512]
+    print("calibrate 8192-key prefills", flush=True)
+    q, k, _ = batch_of_sequences(CONFIG_IDS["prefill_8k"], ROLE_CALIB, 1, 0, S, Hq=Hq, Hkv=Hkv,
+                                 Lq=L, Lk=L, d=d)
+    th_gpu, cnt_gpu = gpu_calibrate(q, k, ks, L)
+    for ki, kk in enumerate(ks):
+        assert (cnt_gpu[ki, :, :kk] == 0).all() and (cnt_gpu[ki, :, kk:] == S).all()
+        assert np.isneginf(th_gpu[ki, :, :kk]).all()
+    rows = [128, 129, 511, 512, 513, 2000, 4095, 4096, 4097, 6000, 8190, 8191]
+    qf, kf = to_f64(q), to_f64(k)
+    for i in rows:
+        obs = {}
+        for s in range(S):
+            for key, t in oracle.calibration_samples(qf[s][:, i:i + 1], kf[s], ks, 1.0 / np.sqrt(d),
+                                                     q_pos0=i).items():
+                obs.setdefault(key, []).append(t)
+        for (ki, h, p), vals in obs.items():
+            ref = float(np.mean(vals))
+            assert abs(th_gpu[ki, h, p] - ref) <= 1e-5 * abs(ref), (ki, h, p)
+
+
 def test_prefill_8k_full_size_sampled_rows():
     """One layer of the 8k prefill workload (32/8 heads, d=128, L=8192, k=128,
     SDC, no VMC), checked on sampled rows that span the whole causal range."""
