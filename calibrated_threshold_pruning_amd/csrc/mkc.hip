@@ -16,12 +16,16 @@
 //   1. compute each sample row's values (post-softmax, or the scores) and
 //      its min and max (one workgroup per sample row, scores in LDS);
 //   2. sort each (head, row)'s sample maxima and minima (one workgroup each);
-//   3. sort the pooled values of each (head, row) in descending order: a
-//      stable LSD radix sort of the order-preserving 32-bit keys, 8 bits per
-//      pass, spread over workgroups of 32768 values (per pass: a histogram
-//      per chunk, a scan per (head, row) into every chunk's output positions,
-//      then a stable scatter of every chunk);
-//   4. walk the sorted positions, chunk by chunk, each thread evaluating the
+//   3. find a bound below which no theta of the (head, row) lies: the
+//      highest boundary of a two-level histogram of the pooled keys at which
+//      the condition holds for the largest target below m;
+//   4. move the pooled values at or above the bound to the front of the
+//      other buffer, and sort those in descending order: a stable LSD radix
+//      sort of the order-preserving 32-bit keys, 8 bits per pass, spread over
+//      workgroups of 8192 values (per pass: a histogram per chunk, a scan
+//      per (head, row) into every chunk's output positions, then a stable
+//      scatter of every chunk);
+//   5. walk the sorted positions, chunk by chunk, each thread evaluating the
 //      condition at its own positions with binary searches in the sorted
 //      maxima and minima, and keep for every target k the smallest
 //      qualifying position (a global atomic min); then read theta there.
@@ -38,8 +42,11 @@ namespace topth {
 
 constexpr int kMkcValThreads = 256;
 constexpr int kMkcSelThreads = 1024;
-constexpr int kMkcChunk = 32768;         // pooled values per workgroup of the sort passes
-constexpr int kMkcWalkChunk = 8192;      // sorted positions per workgroup of the walk
+constexpr int kMkcChunk = 8192;          // sorted values per workgroup of the sort passes
+constexpr int kMkcWalkChunk = 2048;      // sorted positions per workgroup of the walk
+constexpr int kMkcCompThreads = 1024;    // bound histograms and compaction: 32 values per thread
+constexpr int kMkcCompItems = 32;
+constexpr int kMkcCompChunk = kMkcCompThreads * kMkcCompItems;   // pooled values per workgroup there
 constexpr int kMkcMaxSamples = 4096;
 constexpr int kMkcMaxTargets = 64;
 constexpr int kMkcMaxKeys = 32768;
@@ -54,7 +61,13 @@ struct MkcArgs {
     float* smin; float* smax;  // [Hq][Lq][S], ascending after mkc_sortmm_kernel
     int* hist;               // [Hq * Lq][256][wps]: counts per (digit, chunk), then output positions
     int* best;               // [Hq * Lq][n_k]: first qualifying sorted position per target
-    int wps;                 // chunks (workgroups) per (head, row): ceil(S * m_max / kMkcChunk)
+    unsigned* h1;            // [Hq * Lq][512]: pooled values per bin of the top 9 key bits
+    unsigned* h2;            // [Hq * Lq][256]: those of the selected bin per bin of the next 8 bits
+    int* sel;                // [Hq * Lq][2]: the selected top-9-bit bin (-1: none), values in the bins above it
+    uint32_t* lb;            // [Hq * Lq]: key bound: every theta of the segment is at or above it, or -inf
+    int* cnt;                // [Hq * Lq]: pooled values at or above lb, moved to the front of pool2
+    int wps;                 // sort chunks per (head, row): ceil(S * m_max / kMkcChunk)
+    int wpc;                 // chunks of the bound histograms and the compaction: ceil(S * m_max / kMkcCompChunk)
     int n_k;
     int ks[kMkcMaxTargets];
     float* theta;            // [n_k][Hq][n_rows]
@@ -302,6 +315,187 @@ __global__ __launch_bounds__(kMkcSelThreads) void mkc_sortmm_kernel(MkcArgs a) {
         lds_bitonic_asc(s_x, n2);              // the -inf padding sorts to the front
         for (int c = threadIdx.x; c < a.S; c += blockDim.x) v[c] = s_x[n2 - a.S + c];
     }
+    // the segment's bound histograms and compaction count start at zero
+    for (int c = threadIdx.x; c < 512; c += blockDim.x) a.h1[(size_t)seg * 512 + c] = 0u;
+    for (int c = threadIdx.x; c < 256; c += blockDim.x) a.h2[(size_t)seg * 256 + c] = 0u;
+    if (threadIdx.x == 0) a.cnt[seg] = 0;
+}
+
+// ---- the bound.  kp is the largest target below m (a target k >= m gives
+// -inf).  The Eq. 8 condition for kp at a threshold x only uses P, Mx and Nl
+// at x; between x and the smallest pooled value x' >= x lies no pooled value,
+// no sample maximum and no minimum, so all three agree there.  If the
+// condition holds at x it holds at x', so theta(kp) >= x' >= x, and theta(k)
+// >= theta(kp) for every target k <= kp (the condition for kp implies it for
+// smaller k).  The highest bin boundary of the pooled values at which the
+// condition holds is therefore a bound below which no theta lies: taken
+// first over bins of the top 9 bits of the order-preserving keys, then over
+// the next 8 bits inside the bin above that boundary.
+__device__ __forceinline__ int mkc_kp(const MkcArgs& a, int m) {
+    int kp = 0;
+    for (int t = 0; t < a.n_k; ++t)
+        if (a.ks[t] < m) kp = max(kp, a.ks[t]);
+    return kp;
+}
+
+// number of entries with key >= k in an ascending array of n floats
+__device__ __forceinline__ int count_ge_key(const float* x, int n, uint32_t k) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (float_to_ordered(x[mid]) < k) lo = mid + 1; else hi = mid;
+    }
+    return n - lo;
+}
+
+// Bound, steps 1 and 3: the histogram of one chunk's pooled values by the top
+// 9 key bits (LEVEL 1), or of those in the selected bin by the next 8 bits
+// (LEVEL 2), added into the segment's counts.
+template <int LEVEL>
+__global__ __launch_bounds__(kMkcCompThreads) void mkc_phist_kernel(MkcArgs a) {
+    __shared__ unsigned s_h[512];
+    const int seg = blockIdx.x / a.wpc, ck = blockIdx.x % a.wpc;
+    const MkcSeg g = mkc_seg(a, seg);
+    const int j0 = ck * kMkcCompChunk;
+    const int sel = LEVEL == 2 ? a.sel[2 * seg] : 0;
+    // the whole workgroup: past the segment, no target below m, or no bin selected
+    if (j0 >= g.N || mkc_kp(a, g.m) == 0 || sel < 0) return;
+    const int tid = threadIdx.x;
+    for (int b = tid; b < 512; b += kMkcCompThreads) s_h[b] = 0u;
+    __syncthreads();
+    const int end = min(g.N, j0 + kMkcCompChunk);
+    const float* sp = a.pool + g.off;
+    float v[kMkcCompItems];
+#pragma unroll
+    for (int it = 0; it < kMkcCompItems; ++it) v[it] = sp[min(j0 + it * kMkcCompThreads + tid, end - 1)];
+#pragma unroll
+    for (int it = 0; it < kMkcCompItems; ++it) {
+        if (j0 + it * kMkcCompThreads + tid >= end) continue;
+        const uint32_t key = float_to_ordered(v[it]);
+        if (LEVEL == 1) atomicAdd(&s_h[key >> 23], 1u);
+        else if ((key >> 23) == (uint32_t)sel) atomicAdd(&s_h[(key >> 15) & 255u], 1u);
+    }
+    __syncthreads();
+    unsigned* dst = LEVEL == 1 ? a.h1 + (size_t)seg * 512 : a.h2 + (size_t)seg * 256;
+    for (int b = tid; b < (LEVEL == 1 ? 512 : 256); b += kMkcCompThreads)
+        if (s_h[b] != 0u) atomicAdd(&dst[b], s_h[b]);
+}
+
+// Bound, steps 2 and 4: one workgroup per segment tests the condition at
+// every bin boundary (thread t holds the BPT bins below the top NB - BPT t,
+// so a prefix over the threads counts the values from the top down) and
+// keeps the highest boundary where it holds.
+template <int LEVEL>
+__global__ __launch_bounds__(256) void mkc_decide_kernel(MkcArgs a) {
+    constexpr int NB = LEVEL == 1 ? 512 : 256, BPT = NB / 256;
+    __shared__ float s_max[kMkcMaxSamples], s_min[kMkcMaxSamples];
+    __shared__ int s_w[4], s_best;
+    const int seg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const MkcSeg g = mkc_seg(a, seg);
+    const int kp = mkc_kp(a, g.m);
+    const int sel = LEVEL == 2 ? a.sel[2 * seg] : 0;
+    if (kp == 0 || sel < 0) {                  // no bound: every pooled value is sorted
+        if (tid == 0) {
+            if (LEVEL == 1) a.sel[2 * seg] = -1;
+            else a.lb[seg] = 0u;
+        }
+        return;
+    }
+    const int S = a.S;
+    for (int c = tid; c < S; c += 256) {
+        s_max[c] = a.smax[(size_t)seg * S + c];
+        s_min[c] = a.smin[(size_t)seg * S + c];
+    }
+    if (tid == 0) s_best = -1;
+    const unsigned* h = LEVEL == 1 ? a.h1 + (size_t)seg * 512 : a.h2 + (size_t)seg * 256;
+    int cb[BPT], c = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) { cb[i] = (int)h[NB - 1 - BPT * tid - i]; c += cb[i]; }
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int w = __shfl_up(incl, d);
+        if (lane >= d) incl += w;
+    }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) incl += s_w[w];
+    const long long above = LEVEL == 1 ? 0 : a.sel[2 * seg + 1];   // values in the bins above the selected one
+    long long P = above + incl - c;            // values above this thread's bins
+    int best = -1;
+    long long best_above = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        const int b = NB - 1 - BPT * tid - i;
+        P += cb[i];                            // values at or above boundary b
+        const uint32_t key = LEVEL == 1 ? (uint32_t)b << 23 : ((uint32_t)sel << 23) | ((uint32_t)b << 15);
+        const long long Mx = count_ge_key(s_max, S, key), Nl = count_ge_key(s_min, S, key);
+        const long long C = Mx - Nl;
+        if (best < 0 && C > 0 && P - (long long)g.m * Nl >= (long long)kp * C) {
+            best = b;
+            best_above = P - cb[i];
+        }
+    }
+    if (best >= 0) atomicMax(&s_best, best);
+    __syncthreads();
+    const int b = s_best;
+    if (LEVEL == 1) {
+        if (tid == 0 && b < 0) a.sel[2 * seg] = -1;
+        if (b >= 0 && best == b) {             // the thread that holds it
+            a.sel[2 * seg] = b;
+            a.sel[2 * seg + 1] = (int)best_above;
+        }
+    } else if (tid == 0) {
+        // the selected bin's lower boundary holds the condition, so b >= 0
+        a.lb[seg] = ((uint32_t)sel << 23) | ((uint32_t)max(b, 0) << 15);
+    }
+}
+
+// The pooled values at or above the segment's bound, moved (in any order)
+// to the front of the segment in pool2: per chunk of kMkcCompChunk values, one
+// thread takes 32 of them, a prefix over the workgroup places its kept ones,
+// and one atomic add on the segment's count reserves the workgroup's range.
+__global__ __launch_bounds__(kMkcCompThreads) void mkc_compact_kernel(MkcArgs a) {
+    __shared__ int s_w[kMkcCompThreads / 64];
+    __shared__ int s_base;
+    const int seg = blockIdx.x / a.wpc, ck = blockIdx.x % a.wpc;
+    const MkcSeg g = mkc_seg(a, seg);
+    const int j0 = ck * kMkcCompChunk;
+    if (j0 >= g.N) return;                     // the whole workgroup: past the segment
+    const int end = min(g.N, j0 + kMkcCompChunk);
+    const uint32_t lb = a.lb[seg];
+    const float* sp = a.pool + g.off;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float v[kMkcCompItems];
+    uint32_t keep = 0u;
+    int c = 0;
+#pragma unroll
+    for (int it = 0; it < kMkcCompItems; ++it) {
+        const int j = j0 + it * kMkcCompThreads + tid;
+        v[it] = sp[min(j, end - 1)];
+        const bool k = j < end && float_to_ordered(v[it]) >= lb;
+        keep |= (uint32_t)k << it;
+        c += k ? 1 : 0;
+    }
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int w = __shfl_up(incl, d);
+        if (lane >= d) incl += w;
+    }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < kMkcCompThreads / 64; ++w) {
+        before += w < wave ? s_w[w] : 0;
+        total += s_w[w];
+    }
+    if (tid == 0) s_base = total > 0 ? atomicAdd(&a.cnt[seg], total) : 0;
+    __syncthreads();
+    float* dp = a.pool2 + g.off + s_base + before + incl - c;
+#pragma unroll
+    for (int it = 0; it < kMkcCompItems; ++it)
+        if ((keep >> it) & 1u) *dp++ = v[it];
 }
 
 // Sort pass, step 1: the 256-bin histogram of digit (key >> sh) & 255 of one
@@ -310,10 +504,11 @@ __global__ __launch_bounds__(kMkcSelThreads) void mkc_sortmm_kernel(MkcArgs a) {
 __global__ __launch_bounds__(256) void mkc_hist_kernel(MkcArgs a, const float* src, int sh) {
     __shared__ int s_h[256];
     const int seg = blockIdx.x / a.wps, ck = blockIdx.x % a.wps;
+    if (ck * kMkcChunk >= a.cnt[seg]) return;  // the whole workgroup: no compacted value here
     const MkcSeg g = mkc_seg(a, seg);
     s_h[threadIdx.x] = 0;
     __syncthreads();
-    const int end = min(g.N, (ck + 1) * kMkcChunk);
+    const int end = min(a.cnt[seg], (ck + 1) * kMkcChunk);
     const float* sp = src + g.off;
     // 8 loads in flight per thread (indices past the chunk read its last value
     // and are not counted)
@@ -333,13 +528,17 @@ __global__ __launch_bounds__(256) void mkc_hist_kernel(MkcArgs a, const float* s
 // chunk) order, in place: the first output position of every (digit, chunk).
 __global__ __launch_bounds__(kMkcSelThreads) void mkc_scan_kernel(MkcArgs a) {
     __shared__ int s_w[kMkcSelThreads / 64];
-    int* x = a.hist + (size_t)blockIdx.x * 256 * a.wps;
-    const int n = 256 * a.wps;
+    // only the chunks that hold compacted values have counts: entry f is
+    // (digit f / act, chunk f % act)
+    int* const xb = a.hist + (size_t)blockIdx.x * 256 * a.wps;
+    const int act = (a.cnt[blockIdx.x] + kMkcChunk - 1) / kMkcChunk;
+    const int n = 256 * act;
+    auto x = [&](int f) -> int& { return xb[(size_t)(f / act) * a.wps + f % act]; };
     const int per = (n + kMkcSelThreads - 1) / kMkcSelThreads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
     int sum = 0;
-    for (int j = b0; j < b1; ++j) sum += x[j];
+    for (int j = b0; j < b1; ++j) sum += x(j);
     int incl = sum;                            // scan of the thread sums: wave, then across waves
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -351,7 +550,7 @@ __global__ __launch_bounds__(kMkcSelThreads) void mkc_scan_kernel(MkcArgs a) {
     int before = 0;
     for (int w = 0; w < wave; ++w) before += s_w[w];
     int run = before + incl - sum;
-    for (int j = b0; j < b1; ++j) { const int c = x[j]; x[j] = run; run += c; }
+    for (int j = b0; j < b1; ++j) { const int c = x(j); x(j) = run; run += c; }
 }
 
 // Sort pass, step 3: stable scatter of one chunk, in tiles of 8192 values
@@ -377,6 +576,7 @@ __global__ __launch_bounds__(kMkcScatThreads, 4) void mkc_scatter_kernel(MkcArgs
     __shared__ float s_out[kMkcScatTile];
     __shared__ unsigned long long s_peer[NW][256];   // lanes per digit of the current round, zero between rounds
     const int seg = blockIdx.x / a.wps, ck = blockIdx.x % a.wps;
+    if (ck * kMkcChunk >= a.cnt[seg]) return;  // the whole workgroup: no compacted value here
     const MkcSeg g = mkc_seg(a, seg);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid < 256) s_base[tid] = a.hist[((size_t)seg * 256 + tid) * a.wps + ck];
@@ -386,7 +586,7 @@ __global__ __launch_bounds__(kMkcScatThreads, 4) void mkc_scatter_kernel(MkcArgs
     }
     __syncthreads();
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int end = min(g.N, (ck + 1) * kMkcChunk);
+    const int end = min(a.cnt[seg], (ck + 1) * kMkcChunk);
     const float* sp = src + g.off;
     // the next tile's values are loaded while this one is ranked and written;
     // the loads are unconditional (indices past the chunk read its last value,
@@ -484,6 +684,7 @@ __global__ __launch_bounds__(256) void mkc_walk_kernel(MkcArgs a, const float* s
     __shared__ float s_max[kMkcMaxSamples], s_min[kMkcMaxSamples];
     __shared__ int s_best[kMkcMaxTargets];
     const int seg = blockIdx.x / wpw, ck = blockIdx.x % wpw;
+    if (ck * kMkcWalkChunk >= a.cnt[seg]) return;   // the whole workgroup: past the sorted values
     const MkcSeg g = mkc_seg(a, seg);
     const int S = a.S;
     for (int c = threadIdx.x; c < S; c += 256) {
@@ -493,12 +694,13 @@ __global__ __launch_bounds__(256) void mkc_walk_kernel(MkcArgs a, const float* s
     for (int t = threadIdx.x; t < a.n_k; t += 256) s_best[t] = INT_MAX;
     __syncthreads();
     const float* x = sorted + g.off;
-    const int end = min(g.N, (ck + 1) * kMkcWalkChunk);
+    const int N = a.cnt[seg];                  // the sorted values at or above the bound
+    const int end = min(N, (ck + 1) * kMkcWalkChunk);
     const unsigned long long all = a.n_k == 64 ? ~0ull : ((1ull << a.n_k) - 1ull);
     unsigned long long done = 0ull;
     for (int j = ck * kMkcWalkChunk + threadIdx.x; j < end && done != all; j += 256) {
         const float v = x[j];
-        if (j + 1 < g.N && x[j + 1] == v) continue;
+        if (j + 1 < N && x[j + 1] == v) continue;
         const int Mx = count_ge(s_max, S, v);
         const int Nl = count_ge(s_min, S, v);
         const long long C = (long long)Mx - Nl;
@@ -529,14 +731,17 @@ __global__ void mkc_theta_kernel(MkcArgs a, const float* sorted) {
 // ------------------------------------------------------------------ host side
 // chunks per (head, row) for rows of at most m_max keys
 static long long mkc_wps(int S, int m_max) { return ((long long)S * m_max + kMkcChunk - 1) / kMkcChunk; }
+// chunks per (head, row) of the bound histograms and the compaction
+static long long mkc_wpc(int S, int m_max) { return ((long long)S * m_max + kMkcCompChunk - 1) / kMkcCompChunk; }
 // chunks per (head, row) of the walk
 static long long mkc_wpw(int S, int m_max) { return ((long long)S * m_max + kMkcWalkChunk - 1) / kMkcWalkChunk; }
 
 size_t mkc_ws_bytes(int S, int Hq, int Lq, int Lk) {
     const size_t seg = (size_t)S * Hq * Lq * Lk;          // bound of the pooled values
-    const size_t hist = (size_t)Hq * Lq * 256 * (size_t)mkc_wps(S, Lk);
-    return 2 * seg * sizeof(float) + 2 * (size_t)Hq * Lq * S * sizeof(float) + hist * sizeof(int) +
-           (size_t)Hq * Lq * kMkcMaxTargets * sizeof(int) + 4096;
+    const size_t nseg = (size_t)Hq * Lq;
+    const size_t hist = nseg * 256 * (size_t)mkc_wps(S, Lk);
+    return 2 * seg * sizeof(float) + 2 * nseg * S * sizeof(float) + hist * sizeof(int) +
+           nseg * kMkcMaxTargets * sizeof(int) + nseg * (512 + 256 + 2 + 1 + 1) * sizeof(int) + 4096;
 }
 
 int mkc_max_samples() { return kMkcMaxSamples; }
@@ -594,7 +799,13 @@ int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_
     const long long wpw = mkc_wpw(p.S, p.q_pos0 + p.Lq);
     if (wpw * nseg >= (1LL << 31)) return hipErrorInvalidValue;   // one grid dimension
     a.wps = (int)wps;
+    a.wpc = (int)mkc_wpc(p.S, p.q_pos0 + p.Lq);
     a.best = a.hist + (size_t)nseg * 256 * (size_t)wps;
+    a.h1 = (unsigned*)(a.best + (size_t)nseg * kMkcMaxTargets);
+    a.h2 = a.h1 + (size_t)nseg * 512;
+    a.sel = (int*)(a.h2 + (size_t)nseg * 256);
+    a.lb = (uint32_t*)(a.sel + (size_t)nseg * 2);
+    a.cnt = (int*)(a.lb + nseg);
     a.n_k = p.n_k;
     for (int t = 0; t < p.n_k; ++t) a.ks[t] = p.mkc_ks[t];
     a.theta = theta;
@@ -606,9 +817,16 @@ int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_
     if (e != hipSuccess) return e;
     const unsigned nseg_u = (unsigned)nseg, nwg = (unsigned)(wps * nseg);
     hipLaunchKernelGGL(mkc_sortmm_kernel, dim3(nseg_u), dim3(kMkcSelThreads), 0, s, a);
-    // four passes of 8 bits; after them the values are back in the pool, descending
-    float* src = a.pool;
-    float* dst = a.pool2;
+    const unsigned nwc = (unsigned)(a.wpc * nseg);
+    hipLaunchKernelGGL(mkc_phist_kernel<1>, dim3(nwc), dim3(kMkcCompThreads), 0, s, a);
+    hipLaunchKernelGGL(mkc_decide_kernel<1>, dim3(nseg_u), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mkc_phist_kernel<2>, dim3(nwc), dim3(kMkcCompThreads), 0, s, a);
+    hipLaunchKernelGGL(mkc_decide_kernel<2>, dim3(nseg_u), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mkc_compact_kernel, dim3(nwc), dim3(kMkcCompThreads), 0, s, a);
+    // four passes of 8 bits over the compacted values; after them they are
+    // back in pool2, descending
+    float* src = a.pool2;
+    float* dst = a.pool;
     for (int sh = 0; sh < 32; sh += 8) {
         hipLaunchKernelGGL(mkc_hist_kernel, dim3(nwg), dim3(256), 0, s, a, (const float*)src, sh);
         hipLaunchKernelGGL(mkc_scan_kernel, dim3(nseg_u), dim3(kMkcSelThreads), 0, s, a);
