@@ -863,10 +863,11 @@ def bench_mkc(with_cpu):
            "theta_row_4095": {str(k): round(float(theta[i, :, n - 1].mean().item()), 7) for i, k in enumerate(w["ks"])},
            "roofline": {"bound": "hbm", "achieved": round(bytes_min / t / 1e9, 2), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(bytes_min / t / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                        "kernel": "whole call: mkc_values_bf16_kernel, then the radix sort and walk kernels",
-                        "note": "the values kernel streams K once per KV head; the sort makes 4 passes of 8 bits "
-                                "over the 33.5M pooled values (read and written once each), which this "
-                                "minimum does not count"}}
+                        "kernel": "whole call: mkc_values_bf16_kernel, the bound, compaction, radix sort and "
+                                  "walk kernels",
+                        "note": "the values kernel streams K once per KV head; the pooled values are read three "
+                                "more times (two bound histograms, the compaction) and only those above the "
+                                "bound on theta are sorted, which this minimum does not count"}}
     # thresholds for k = 128 from the merged function, applied to the decode_8b step
     wd = DECODE_WORKLOADS["decode_8b"]
     qt, kt, vt = attention_inputs_device(CONFIG_IDS["decode_8b"], ROLE_TEST, 0, 0, B=wd["B"], Hq=Hq, Hkv=Hkv, Lq=1,
