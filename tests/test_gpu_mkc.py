@@ -150,3 +150,23 @@ def test_mkc_eight_query_heads_per_kv_head(dtype, d, Lk):
         got = run_mkc(q, k, ks, Lk - 1, pre=pre)
         ref = mkc.mkc_calibrate(to_f64(q), to_f64(k), 1.0 / np.sqrt(d), Lk - 1, ks, pre=pre)
         compare(got[:, :, Lk - 1:], ref, 1e-5, f"g = 8, Lk = {Lk}, pre = {pre}")
+
+
+def test_mkc_bound_and_compaction_exact_with_ties():
+    # decode rows of 3000 keys from 300 samples (900k pooled values: several
+    # compaction and sort chunks) with integer-valued scores, so values repeat
+    # everywhere, also at the bound below which values are left unsorted;
+    # pre-softmax thresholds must match bit for bit
+    print("mkc bound and compaction, 300 x 3000 integer scores", flush=True)
+    rng = np.random.default_rng(12)
+    S, Hq, Hkv, d, Lk = 300, 2, 1, 64, 3000
+    q = torch.tensor(rng.integers(-2, 3, size=(S, Hq, 1, d)), dtype=torch.float32)
+    k = torch.tensor(rng.integers(-1, 2, size=(S, Hkv, Lk, d)), dtype=torch.float32)
+    # with k = 2999 the bound sits near the bottom; with k <= 50 it prunes hard
+    for ks in ([1, 50, 300, 2999, 3000], [3, 50]):
+        got = run_mkc(q, k, ks, Lk - 1, pre=True, scale=0.125)
+        ref = mkc.mkc_calibrate(to_f64(q), to_f64(k), 0.125, Lk - 1, ks, pre=True)
+        compare(got[:, :, Lk - 1:], ref, 0, f"pre-softmax, 300 x 3000 integer scores, ks {ks}")
+        got = run_mkc(q, k, ks, Lk - 1, pre=False, scale=0.125)
+        ref = mkc.mkc_calibrate(to_f64(q), to_f64(k), 0.125, Lk - 1, ks, pre=False)
+        compare(got[:, :, Lk - 1:], ref, 1e-5, f"post-softmax, 300 x 3000 integer scores, ks {ks}")
