@@ -170,3 +170,18 @@ def test_mkc_bound_and_compaction_exact_with_ties():
         got = run_mkc(q, k, ks, Lk - 1, pre=False, scale=0.125)
         ref = mkc.mkc_calibrate(to_f64(q), to_f64(k), 0.125, Lk - 1, ks, pre=False)
         compare(got[:, :, Lk - 1:], ref, 1e-5, f"post-softmax, 300 x 3000 integer scores, ks {ks}")
+
+
+def test_mkc_most_samples():
+    # the largest sample count one call takes (4096: the maxima and minima
+    # sorted in one workgroup, the bound tested against all of them), on
+    # 20-key decode rows
+    print("mkc 4096 samples", flush=True)
+    rng = np.random.default_rng(13)
+    S, Hq, Hkv, d, Lk = tt.TOPTH_MKC_MAX_SAMPLES, 2, 1, 64, 20
+    q = torch.tensor(rng.standard_normal((S, Hq, 1, d)), dtype=torch.float32)
+    k = torch.tensor(rng.standard_normal((S, Hkv, Lk, d)), dtype=torch.float32)
+    ks = [1, 5, 19, 20]
+    got = run_mkc(q, k, ks, Lk - 1, pre=False, scale=0.125)
+    ref = mkc.mkc_calibrate(to_f64(q), to_f64(k), 0.125, Lk - 1, ks, pre=False)
+    compare(got[:, :, Lk - 1:], ref, 1e-5, "4096 samples")
