@@ -236,6 +236,21 @@ def test_calibrate_bf16_column_variants(name, Hq, Hkv, Lq, Lk, q_pos0, S, ks, d)
     check_theta(th_gpu, th_ref)
 
 
+@pytest.mark.parametrize("Hq,Hkv,L,d", [(16, 2, 333, 128), (16, 1, 200, 64), (2, 1, 257, 64)])
+def test_calibrate_tiled_group_sizes(Hq, Hkv, L, d):
+    """Whole causal prefills through the tiled calibration at 8, 16 and 2
+    query heads per KV head: every mapping of heads and 32-row blocks onto
+    its workgroups (several head blocks per KV head, several row blocks of
+    two heads)."""
+    print(f"calibrate tiled Hq={Hq} Hkv={Hkv} L={L} d={d}", flush=True)
+    q, k, _ = batch_of_sequences(UNIT, ROLE_CALIB, 14, 0, 2, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    ks = [16, 100]
+    th_gpu, cnt_gpu = gpu_calibrate(q, k, ks, L)
+    th_ref, cnt_ref = oracle_calibrate(q, k, ks, L)
+    assert np.array_equal(cnt_gpu, cnt_ref)
+    check_theta(th_gpu, th_ref)
+
+
 def test_calibrate_bf16_ties():
     """Keys drawn from three distinct rows: every score row holds long runs of
     equal values, so the bin of the k-th largest overflows the copy space and
