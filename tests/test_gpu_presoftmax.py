@@ -66,8 +66,8 @@ def calib_tables(cfg, Hq, Hkv, L, d, k, n_seq, dtype, q_pos0=0, Lq=None):
 
 # --------------------------------------------------------------- calibration
 @pytest.mark.parametrize("dtype,Hq,Hkv,L,d,ks,q_pos0,Lq", [
-    (torch.bfloat16, 4, 2, 300, 128, [8, 32, 100], 0, 300),   # tiled kernel, prefill-style
-    (torch.bfloat16, 8, 2, 1500, 64, [64], 1499, 1),          # tiled kernel, decode-style
+    (torch.bfloat16, 4, 2, 300, 128, [8, 32, 100], 0, 300),   # column kernel, prefill-style
+    (torch.bfloat16, 8, 2, 1500, 64, [64], 1499, 1),          # column kernel, decode-style
     (torch.float32, 2, 1, 200, 64, [16, 199], 0, 200),        # row kernel
     (torch.bfloat16, 2, 1, 2100, 64, [64, 700], 0, 2100),    # 8 columns of 2 waves each
     (torch.bfloat16, 4, 1, 5000, 128, [64, 300], 4999, 1),   # 4 columns of 4 waves each
@@ -106,6 +106,37 @@ def test_calibrate_pre_parity(dtype, Hq, Hkv, L, d, ks, q_pos0, Lq):
     rel = np.abs(etg - et_ref) / np.maximum(np.abs(et_ref), 1e-30)
     assert rel[et_ref > 0].max() <= 1e-4, rel[et_ref > 0].max()
     assert (etg[et_ref == 0] == 0).all()
+
+
+@pytest.mark.parametrize("Hq,Hkv,L,d,ks", [(4, 2, 300, 128, [1, 8, 100, 299]), (16, 1, 200, 64, [16, 64])])
+def test_calibrate_pre_tiled(Hq, Hkv, L, d, ks):
+    """Pre-softmax calibration of whole causal prefills without the discarded
+    mass takes the tiled kernel (the k-th largest scores): four targets, from
+    the row maximum to L - 1, and 16 query heads per KV head."""
+    print(f"calibrate_pre tiled Hq={Hq} Hkv={Hkv} L={L} ks={ks}", flush=True)
+    dev = device()
+    S = 3
+    q, kk, _ = batch_of_sequences(UNIT, ROLE_CALIB, 6, 0, S, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    scale = 1.0 / np.sqrt(d)
+    nk = len(ks)
+    s1 = torch.zeros(nk, Hq, L, dtype=torch.float64, device=dev)
+    s2 = torch.zeros_like(s1)
+    cnt = torch.zeros(nk, Hq, L, dtype=torch.int32, device=dev)
+    ws = tt.workspace(tt.TOPTH_OP_CALIBRATE, S, Hq, Hkv, L, L, d, nk)
+    tt.topth_calibrate_pre(q.to(dev), kk.to(dev), ks, s1, s2, cnt, ws, scale=scale, q_pos0=0)
+    th = torch.empty(nk, Hq, L, dtype=torch.float32, device=dev)
+    tt.topth_calibrate_finalize(s1, s2, cnt, ks, th)
+    torch.cuda.synchronize()
+    cal = pre.PreCalibrator(ks, Hq, L)
+    for s in range(S):
+        cal.observe(to_f64(q[s]), to_f64(kk[s]), scale, 0)
+    th_ref = cal.finalize()
+    assert np.array_equal(cnt.cpu().numpy(), cal.counts())
+    thg = th.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(th_ref)
+    assert np.array_equal(np.isfinite(thg), fin)
+    err = np.abs(thg[fin] - th_ref[fin]) / np.maximum(1.0, np.abs(th_ref[fin]))
+    assert err.max() <= 1e-5, err.max()
 
 
 # ------------------------------------------------------------------ prefill
