@@ -265,6 +265,27 @@ def test_calibrate_bf16_ties():
     check_theta(th_gpu, th_ref)
 
 
+def test_calibrate_tiled_longest_rows_with_ties():
+    """The longest rows of the tiled calibration (16384 keys) with keys drawn
+    from three distinct rows, so every score row is three long runs of equal
+    values: the rows go to the exact fixup, whose row of scores then needs more
+    than 48 KiB of LDS.  Counts on every row, theta on sampled rows (one
+    sequence: theta is the k-th largest value itself)."""
+    Hq, L, d = 2, 16384, 64
+    print("calibrate 16384-key rows with ties", flush=True)
+    q, k, _ = batch_of_sequences(UNIT, ROLE_CALIB, 15, 0, 1, Hq=Hq, Hkv=1, Lq=L, Lk=L, d=d)
+    k = k[:, :, torch.arange(L) % 3].contiguous()
+    ks = [50, 3000]
+    th_gpu, cnt_gpu = gpu_calibrate(q, k, ks, L)
+    for ki, kk in enumerate(ks):
+        assert (cnt_gpu[ki, :, :kk] == 0).all() and (cnt_gpu[ki, :, kk:] == 1).all()
+    qf, kf = to_f64(q), to_f64(k)
+    for i in [50, 51, 2999, 3000, 12287, 12288, 16000, 16383]:
+        for (ki, h, p), t in oracle.calibration_samples(qf[0][:, i:i + 1], kf[0], ks, 1.0 / np.sqrt(d),
+                                                        q_pos0=i).items():
+            assert abs(th_gpu[ki, h, p] - t) <= 1e-5 * abs(t), (ki, h, p)
+
+
 def test_calibrate_sweep_shape_sampled_rows():
     """Calibration-sweep shape (8 independent heads, d=128, L=2048, k in
     {64, 128, 256}) on a few sequences: counts on every row, theta on sampled
