@@ -185,3 +185,18 @@ def test_mkc_most_samples():
     got = run_mkc(q, k, ks, Lk - 1, pre=False, scale=0.125)
     ref = mkc.mkc_calibrate(to_f64(q), to_f64(k), 0.125, Lk - 1, ks, pre=False)
     compare(got[:, :, Lk - 1:], ref, 1e-5, "4096 samples")
+
+
+def test_mkc_rows_spanning_several_chunks():
+    # 24 query rows at positions 500..523 of 64 samples: every (head, row)
+    # pools 32k-34k values, so each spans several sort chunks, with a ragged
+    # last chunk that differs from row to row
+    print("mkc 24 rows of ~33k pooled values", flush=True)
+    S, Hq, Hkv, d, Lq, q0 = 64, 2, 1, 64, 24, 500
+    q, k, _ = attention_inputs(UNIT, ROLE_CALIB, 16, 0, B=S, Hq=Hq, Hkv=Hkv, Lq=Lq, Lk=q0 + Lq, d=d,
+                               n_sinks=1, dtype=torch.float32, with_v=False)
+    ks = [4, 40, 200]
+    for pre in (False, True):
+        got = run_mkc(q, k, ks, q0, pre=pre)
+        ref = mkc.mkc_calibrate(to_f64(q), to_f64(k), 1.0 / np.sqrt(d), q0, ks, pre=pre)
+        compare(got[:, :, q0:], ref, 1e-5, f"24 rows, pre = {pre}")
