@@ -22,7 +22,7 @@
 //   4. move the pooled values at or above the bound to the front of the
 //      other buffer, and sort those in descending order: a stable LSD radix
 //      sort of the order-preserving 32-bit keys, 8 bits per pass, spread over
-//      workgroups of 8192 values (per pass: a histogram per chunk, a scan
+//      workgroups of 4096 values (per pass: a histogram per chunk, a scan
 //      per (head, row) into every chunk's output positions, then a stable
 //      scatter of every chunk);
 //   5. walk the sorted positions, chunk by chunk, each thread evaluating the
@@ -42,7 +42,7 @@ namespace topth {
 
 constexpr int kMkcValThreads = 256;
 constexpr int kMkcSelThreads = 1024;
-constexpr int kMkcChunk = 8192;          // sorted values per workgroup of the sort passes
+constexpr int kMkcChunk = 4096;          // sorted values per workgroup of the sort passes
 constexpr int kMkcWalkChunk = 2048;      // sorted positions per workgroup of the walk
 constexpr int kMkcCompThreads = 1024;    // bound histograms and compaction: 32 values per thread
 constexpr int kMkcCompItems = 32;
@@ -553,17 +553,17 @@ __global__ __launch_bounds__(kMkcSelThreads) void mkc_scan_kernel(MkcArgs a) {
     for (int j = b0; j < b1; ++j) { const int c = x(j); x(j) = run; run += c; }
 }
 
-// Sort pass, step 3: stable scatter of one chunk, in tiles of 8192 values
-// (16 per thread).  Wave w owns the tile's values w * 1024 .. w * 1024 + 1023
+// Sort pass, step 3: stable scatter of one chunk, in tiles of 4096 values
+// (8 per thread).  Wave w owns the tile's values w * 512 .. w * 512 + 511
 // and ranks them in index order, 64 at a time: lanes with equal digits find
 // each other through a per-wave LDS lane mask per digit, and a per-wave LDS
-// counter per digit carries the count of the earlier rounds.  A prefix over the waves and over the
-// digits then gives every value its place in the tile sorted by digit; the
-// tile is staged in LDS in that order and written out in order of place, so
-// that each digit's run (about 32 values) is written contiguously at the
+// counter per digit carries the count of the earlier rounds.  A prefix over
+// the waves and over the digits then gives every value its place in the tile
+// sorted by digit; the tile is staged in LDS in that order and written out in
+// order of place, so that each digit's run is written contiguously at the
 // position the scan gave this chunk for that digit.
 constexpr int kMkcScatThreads = 512;       // two workgroups per CU
-constexpr int kMkcScatItems = 16;
+constexpr int kMkcScatItems = 8;
 constexpr int kMkcScatTile = kMkcScatThreads * kMkcScatItems;
 __global__ __launch_bounds__(kMkcScatThreads, 4) void mkc_scatter_kernel(MkcArgs a, const float* src, float* dst,
                                                                          int sh) {
