@@ -47,6 +47,10 @@ constexpr int kMkcWalkChunk = 2048;      // sorted positions per workgroup of th
 constexpr int kMkcCompThreads = 1024;    // bound histograms and compaction: 32 values per thread
 constexpr int kMkcCompItems = 32;
 constexpr int kMkcCompChunk = kMkcCompThreads * kMkcCompItems;   // pooled values per workgroup there
+// The sort passes and the walk loop over (chunk, segment) work items, chunk
+// first, on at most this many workgroups: only the items below a segment's
+// compacted count do work, and they come first.
+constexpr int kMkcLoopGrid = 2048;
 constexpr int kMkcMaxSamples = 4096;
 constexpr int kMkcMaxTargets = 64;
 constexpr int kMkcMaxKeys = 32768;
@@ -499,29 +503,34 @@ __global__ __launch_bounds__(kMkcCompThreads) void mkc_compact_kernel(MkcArgs a)
 }
 
 // Sort pass, step 1: the 256-bin histogram of digit (key >> sh) & 255 of one
-// chunk, to hist[(seg * 256 + digit) * wps + chunk] (chunks past the
-// segment's end count nothing).
+// chunk, to hist[(seg * 256 + digit) * wps + chunk]; the chunks past the
+// segment's compacted count are skipped, and the scan reads none of them.
 __global__ __launch_bounds__(256) void mkc_hist_kernel(MkcArgs a, const float* src, int sh) {
     __shared__ int s_h[256];
-    const int seg = blockIdx.x / a.wps, ck = blockIdx.x % a.wps;
-    if (ck * kMkcChunk >= a.cnt[seg]) return;  // the whole workgroup: no compacted value here
-    const MkcSeg g = mkc_seg(a, seg);
-    s_h[threadIdx.x] = 0;
-    __syncthreads();
-    const int end = min(a.cnt[seg], (ck + 1) * kMkcChunk);
-    const float* sp = src + g.off;
-    // 8 loads in flight per thread (indices past the chunk read its last value
-    // and are not counted)
-    for (int j0 = ck * kMkcChunk + threadIdx.x; j0 < end; j0 += 256 * 8) {
-        float v[8];
+    const int nseg = a.Hq * a.Lq, items = a.wps * nseg;
+    for (int w = blockIdx.x; w < items; w += gridDim.x) {
+        const int ck = w / nseg, seg = w % nseg;
+        const int n = a.cnt[seg];
+        if (ck * kMkcChunk >= n) continue;     // the whole workgroup: no compacted value here
+        const MkcSeg g = mkc_seg(a, seg);
+        s_h[threadIdx.x] = 0;
+        __syncthreads();
+        const int end = min(n, (ck + 1) * kMkcChunk);
+        const float* sp = src + g.off;
+        // 8 loads in flight per thread (indices past the chunk read its last
+        // value and are not counted)
+        for (int j0 = ck * kMkcChunk + threadIdx.x; j0 < end; j0 += 256 * 8) {
+            float v[8];
 #pragma unroll
-        for (int it = 0; it < 8; ++it) v[it] = sp[min(j0 + it * 256, end - 1)];
+            for (int it = 0; it < 8; ++it) v[it] = sp[min(j0 + it * 256, end - 1)];
 #pragma unroll
-        for (int it = 0; it < 8; ++it)
-            if (j0 + it * 256 < end) atomicAdd(&s_h[(mkc_key(v[it]) >> sh) & 255u], 1);
+            for (int it = 0; it < 8; ++it)
+                if (j0 + it * 256 < end) atomicAdd(&s_h[(mkc_key(v[it]) >> sh) & 255u], 1);
+        }
+        __syncthreads();
+        a.hist[((size_t)seg * 256 + threadIdx.x) * a.wps + ck] = s_h[threadIdx.x];
+        __syncthreads();                       // s_h is read before the next item clears it
     }
-    __syncthreads();
-    a.hist[((size_t)seg * 256 + threadIdx.x) * a.wps + ck] = s_h[threadIdx.x];
 }
 
 // Sort pass, step 2: exclusive scan of one segment's counts in (digit,
@@ -575,103 +584,109 @@ __global__ __launch_bounds__(kMkcScatThreads, 4) void mkc_scatter_kernel(MkcArgs
     __shared__ int s_part[4];
     __shared__ float s_out[kMkcScatTile];
     __shared__ unsigned long long s_peer[NW][256];   // lanes per digit of the current round, zero between rounds
-    const int seg = blockIdx.x / a.wps, ck = blockIdx.x % a.wps;
-    if (ck * kMkcChunk >= a.cnt[seg]) return;  // the whole workgroup: no compacted value here
-    const MkcSeg g = mkc_seg(a, seg);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < 256) s_base[tid] = a.hist[((size_t)seg * 256 + tid) * a.wps + ck];
-    for (int t = tid; t < NW * 256; t += kMkcScatThreads) {
-        (&s_wc[0][0])[t] = 0;
-        (&s_peer[0][0])[t] = 0ull;
-    }
-    __syncthreads();
-    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int end = min(a.cnt[seg], (ck + 1) * kMkcChunk);
-    const float* sp = src + g.off;
-    // the next tile's values are loaded while this one is ranked and written;
-    // the loads are unconditional (indices past the chunk read its last value,
-    // which is never used) so that the wait before ranking counts only the
-    // current tile's loads
-    auto load_tile = [&](int t0, float (&v)[kMkcScatItems]) {
-#pragma unroll
-        for (int it = 0; it < kMkcScatItems; ++it) v[it] = sp[min(t0 + wave * PER_WAVE + it * 64 + lane, end - 1)];
-    };
-    float v[kMkcScatItems], nv[kMkcScatItems];
-    if (ck * kMkcChunk < end) load_tile(ck * kMkcChunk, v);
-    for (int t0 = ck * kMkcChunk; t0 < end; t0 += kMkcScatTile) {
-        const int n = min(kMkcScatTile, end - t0);
-        int rk[kMkcScatItems];
-        load_tile(t0 + kMkcScatTile, nv);
-#pragma unroll
-        for (int it = 0; it < kMkcScatItems; ++it) {
-            const bool valid = wave * PER_WAVE + it * 64 + lane < n;
-            const int dg = (int)((mkc_key(v[it]) >> sh) & 255u);
-            // the lanes of this round with the same digit: each sets its bit in
-            // the wave's mask of that digit and reads the mask back; the first
-            // of them then adds the round's count and clears the mask.  LDS
-            // instructions of one wave execute in order, so every lane reads the
-            // complete mask and the old count before that lane's writes.
-            unsigned long long peers = 0ull;
-            int before = 0;
-            if (valid) {
-                atomicOr(&s_peer[wave][dg], 1ull << lane);
-                peers = s_peer[wave][dg];
-                before = s_wc[wave][dg];
-            }
-            const int r = __popcll(peers & lt);
-            if (valid && r == 0) {
-                s_wc[wave][dg] = before + __popcll(peers);
-                s_peer[wave][dg] = 0ull;
-            }
-            rk[it] = before + r;
+    const int nseg = a.Hq * a.Lq, items = a.wps * nseg;
+    // one chunk of one segment (the whole workgroup returns where the chunk
+    // holds no compacted value); the last tile ends at a barrier, so the next
+    // item may set the LDS state up again at once
+    auto item = [&](const int seg, const int ck) {
+        if (ck * kMkcChunk >= a.cnt[seg]) return;
+        const MkcSeg g = mkc_seg(a, seg);
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        if (tid < 256) s_base[tid] = a.hist[((size_t)seg * 256 + tid) * a.wps + ck];
+        for (int t = tid; t < NW * 256; t += kMkcScatThreads) {
+            (&s_wc[0][0])[t] = 0;
+            (&s_peer[0][0])[t] = 0ull;
         }
         __syncthreads();
-        int tot = 0;
-        if (tid < 256) {                       // prefix over the waves, per digit
+        const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const int end = min(a.cnt[seg], (ck + 1) * kMkcChunk);
+        const float* sp = src + g.off;
+        // the next tile's values are loaded while this one is ranked and written;
+        // the loads are unconditional (indices past the chunk read its last value,
+        // which is never used) so that the wait before ranking counts only the
+        // current tile's loads
+        auto load_tile = [&](int t0, float (&v)[kMkcScatItems]) {
 #pragma unroll
-            for (int w = 0; w < NW; ++w) { const int c = s_wc[w][tid]; s_wc[w][tid] = tot; tot += c; }
-        }
-        // exclusive scan of the tile's digit counts: places of the digits
-        int incl = tot;
+            for (int it = 0; it < kMkcScatItems; ++it) v[it] = sp[min(t0 + wave * PER_WAVE + it * 64 + lane, end - 1)];
+        };
+        float v[kMkcScatItems], nv[kMkcScatItems];
+        if (ck * kMkcChunk < end) load_tile(ck * kMkcChunk, v);
+        for (int t0 = ck * kMkcChunk; t0 < end; t0 += kMkcScatTile) {
+            const int n = min(kMkcScatTile, end - t0);
+            int rk[kMkcScatItems];
+            load_tile(t0 + kMkcScatTile, nv);
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int w = __shfl_up(incl, o);
-            if (lane >= o) incl += w;
-        }
-        if (tid < 256 && lane == 63) s_part[wave] = incl;
-        __syncthreads();
-        if (tid < 256) {
-            int before = 0;
-            for (int w = 0; w < wave; ++w) before += s_part[w];
-            s_start[tid] = before + incl - tot;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < kMkcScatItems; ++it)
-            if (wave * PER_WAVE + it * 64 + lane < n) {
+            for (int it = 0; it < kMkcScatItems; ++it) {
+                const bool valid = wave * PER_WAVE + it * 64 + lane < n;
                 const int dg = (int)((mkc_key(v[it]) >> sh) & 255u);
-                s_out[s_start[dg] + s_wc[wave][dg] + rk[it]] = v[it];
+                // the lanes of this round with the same digit: each sets its bit in
+                // the wave's mask of that digit and reads the mask back; the first
+                // of them then adds the round's count and clears the mask.  LDS
+                // instructions of one wave execute in order, so every lane reads the
+                // complete mask and the old count before that lane's writes.
+                unsigned long long peers = 0ull;
+                int before = 0;
+                if (valid) {
+                    atomicOr(&s_peer[wave][dg], 1ull << lane);
+                    peers = s_peer[wave][dg];
+                    before = s_wc[wave][dg];
+                }
+                const int r = __popcll(peers & lt);
+                if (valid && r == 0) {
+                    s_wc[wave][dg] = before + __popcll(peers);
+                    s_peer[wave][dg] = 0ull;
+                }
+                rk[it] = before + r;
             }
-        __syncthreads();
+            __syncthreads();
+            int tot = 0;
+            if (tid < 256) {                       // prefix over the waves, per digit
 #pragma unroll
-        for (int it = 0; it < kMkcScatItems; ++it) {
-            const int pl = it * kMkcScatThreads + tid;
-            if (pl < n) {
-                const float x = s_out[pl];
-                const int d = (int)((mkc_key(x) >> sh) & 255u);
-                dst[g.off + s_base[d] + (pl - s_start[d])] = x;
+                for (int w = 0; w < NW; ++w) { const int c = s_wc[w][tid]; s_wc[w][tid] = tot; tot += c; }
             }
-        }
-        __syncthreads();
-        if (tid < 256) {
-            s_base[tid] += tot;
+            // exclusive scan of the tile's digit counts: places of the digits
+            int incl = tot;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) s_wc[w][tid] = 0;
-        }
-        __syncthreads();
+            for (int o = 1; o < 64; o <<= 1) {
+                const int w = __shfl_up(incl, o);
+                if (lane >= o) incl += w;
+            }
+            if (tid < 256 && lane == 63) s_part[wave] = incl;
+            __syncthreads();
+            if (tid < 256) {
+                int before = 0;
+                for (int w = 0; w < wave; ++w) before += s_part[w];
+                s_start[tid] = before + incl - tot;
+            }
+            __syncthreads();
 #pragma unroll
-        for (int it = 0; it < kMkcScatItems; ++it) v[it] = nv[it];
-    }
+            for (int it = 0; it < kMkcScatItems; ++it)
+                if (wave * PER_WAVE + it * 64 + lane < n) {
+                    const int dg = (int)((mkc_key(v[it]) >> sh) & 255u);
+                    s_out[s_start[dg] + s_wc[wave][dg] + rk[it]] = v[it];
+                }
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < kMkcScatItems; ++it) {
+                const int pl = it * kMkcScatThreads + tid;
+                if (pl < n) {
+                    const float x = s_out[pl];
+                    const int d = (int)((mkc_key(x) >> sh) & 255u);
+                    dst[g.off + s_base[d] + (pl - s_start[d])] = x;
+                }
+            }
+            __syncthreads();
+            if (tid < 256) {
+                s_base[tid] += tot;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) s_wc[w][tid] = 0;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < kMkcScatItems; ++it) v[it] = nv[it];
+        }
+    };
+    for (int w = blockIdx.x; w < items; w += gridDim.x) item(w % nseg, w / nseg);
 }
 
 // The walk over one chunk of sorted positions: every position that ends a
@@ -683,8 +698,10 @@ __global__ __launch_bounds__(kMkcScatThreads, 4) void mkc_scatter_kernel(MkcArgs
 __global__ __launch_bounds__(256) void mkc_walk_kernel(MkcArgs a, const float* sorted, int wpw) {
     __shared__ float s_max[kMkcMaxSamples], s_min[kMkcMaxSamples];
     __shared__ int s_best[kMkcMaxTargets];
-    const int seg = blockIdx.x / wpw, ck = blockIdx.x % wpw;
-    if (ck * kMkcWalkChunk >= a.cnt[seg]) return;   // the whole workgroup: past the sorted values
+    const int nseg = a.Hq * a.Lq, items = wpw * nseg;
+    for (int w = blockIdx.x; w < items; w += gridDim.x) {
+    const int seg = w % nseg, ck = w / nseg;
+    if (ck * kMkcWalkChunk >= a.cnt[seg]) continue;   // the whole workgroup: past the sorted values
     const MkcSeg g = mkc_seg(a, seg);
     const int S = a.S;
     for (int c = threadIdx.x; c < S; c += 256) {
@@ -715,6 +732,8 @@ __global__ __launch_bounds__(256) void mkc_walk_kernel(MkcArgs a, const float* s
     __syncthreads();
     for (int t = threadIdx.x; t < a.n_k; t += 256)
         if (s_best[t] != INT_MAX) atomicMin(&a.best[(size_t)seg * a.n_k + t], s_best[t]);
+    __syncthreads();   // s_max, s_min and s_best are set up again for the next item
+    }
 }
 
 // theta at every target's first qualifying position (-inf where none)
@@ -797,7 +816,7 @@ int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_
     const long long wps = mkc_wps(p.S, p.q_pos0 + p.Lq);
     const long long nseg = (long long)p.Hq * p.Lq;
     const long long wpw = mkc_wpw(p.S, p.q_pos0 + p.Lq);
-    if (wpw * nseg >= (1LL << 31)) return hipErrorInvalidValue;   // one grid dimension
+    if (wpw * nseg >= (1LL << 31)) return hipErrorInvalidValue;   // the item counts are int
     a.wps = (int)wps;
     a.wpc = (int)mkc_wpc(p.S, p.q_pos0 + p.Lq);
     a.best = a.hist + (size_t)nseg * 256 * (size_t)wps;
@@ -815,7 +834,12 @@ int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_
     if (e != hipSuccess) return e;
     e = launch_fill_u32(a.best, (size_t)nseg * p.n_k * sizeof(int), (uint32_t)INT_MAX, s);
     if (e != hipSuccess) return e;
-    const unsigned nseg_u = (unsigned)nseg, nwg = (unsigned)(wps * nseg);
+    // the sort passes and the walk loop over (chunk, segment) items, chunk
+    // major, on a grid of at most kMkcLoopGrid workgroups: the chunks that
+    // hold compacted values are the first ones of every segment
+    const unsigned nseg_u = (unsigned)nseg;
+    const unsigned nwg = (unsigned)std::min<long long>(wps * nseg, kMkcLoopGrid);
+    const unsigned nww = (unsigned)std::min<long long>(wpw * nseg, kMkcLoopGrid);
     hipLaunchKernelGGL(mkc_sortmm_kernel, dim3(nseg_u), dim3(kMkcSelThreads), 0, s, a);
     const unsigned nwc = (unsigned)(a.wpc * nseg);
     hipLaunchKernelGGL(mkc_phist_kernel<1>, dim3(nwc), dim3(kMkcCompThreads), 0, s, a);
@@ -833,8 +857,7 @@ int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_
         hipLaunchKernelGGL(mkc_scatter_kernel, dim3(nwg), dim3(kMkcScatThreads), 0, s, a, (const float*)src, dst, sh);
         float* t = src; src = dst; dst = t;
     }
-    hipLaunchKernelGGL(mkc_walk_kernel, dim3((unsigned)(wpw * nseg)), dim3(256), 0, s, a, (const float*)src,
-                       (int)wpw);
+    hipLaunchKernelGGL(mkc_walk_kernel, dim3(nww), dim3(256), 0, s, a, (const float*)src, (int)wpw);
     hipLaunchKernelGGL(mkc_theta_kernel, dim3(nseg_u), dim3(64), 0, s, a, (const float*)src);
     return hipGetLastError();
 }
