@@ -61,15 +61,16 @@ bool too_big(long long rows, long long cols) {
 
 int map_hip(int e) { return e == 0 ? TOPTH_OK : TOPTH_EHIP; }
 
-// prefix means of V (VMC), then a float16 copy of V and a flag word (bf16 P V
-// in float16); a workspace with only the first part still serves VMC
+// prefix means of V (VMC), then a float16 copy of V (transposed 64-key tiles)
+// and a flag word (bf16 P V in float16); a workspace with only the first part
+// still serves VMC
 size_t prefill_ws_vmc(int B, int Hkv, int L, int d) {
     return (size_t)B * Hkv * L * d * sizeof(float) + 256;
 }
 size_t prefill_ws(int B, int Hq, int Hkv, int L, int d) {
     (void)Hq;
     const size_t mu = ((size_t)B * Hkv * L * d * sizeof(float) + 255) & ~(size_t)255;
-    const size_t v16 = ((size_t)B * Hkv * L * d * sizeof(uint16_t) + 255) & ~(size_t)255;
+    const size_t v16 = ((size_t)B * Hkv * (size_t)((L + 63) / 64) * 64 * d * sizeof(uint16_t) + 255) & ~(size_t)255;
     return mu + v16 + 256;
 }
 

@@ -16,7 +16,8 @@
 //            into a bf16 high part and a bf16 remainder (two MFMAs).
 // Workgroup: one KV head's query tile, 4 waves, each wave one query head and
 // 32 rows; K tiles of 64 keys are staged by buffer_load...lds into a swizzled,
-// double-buffered LDS tile shared by the waves; V tiles are staged transposed.
+// double-buffered LDS tile shared by the waves; V tiles are staged as they
+// are and read transposed (bf16), or come as float16 V^T image tiles.
 //
 // Pre-softmax form (PRE): the compare a >= theta needs no row statistics, so
 // sweep A is skipped and sweep B alone keeps an online softmax: a row-uniform
@@ -27,11 +28,13 @@
 // (Sec. 3.2.1: exact, exp-threshold, offline-calibrated, or none).
 //
 // P V in float16: when the caller's workspace has room, a pre-pass copies V to
-// float16 (exact for bfloat16 values of magnitude in [2^-14, 16] and zero;
-// smaller ones land on the float16 subnormal grid, off by at most 2^-25, which
-// moves an output by at most 2^-25 since the weights sum to at most 1; the
-// bound of 16 is checked) and the P V product takes one f16 MFMA per block with P rounded to float16
-// instead of the two bf16 MFMAs of the high/low split.  P enters scaled by
+// float16 V^T tiles laid out as the kernel's LDS tile, so that every V^T
+// fragment is one plain 16-byte LDS read (the conversion is exact for
+// bfloat16 values of magnitude in [2^-14, 16] and zero; smaller ones land on
+// the float16 subnormal grid, off by at most 2^-25, which moves an output by
+// at most 2^-25 since the weights sum to at most 1; the bound of 16 is
+// checked), and the P V product takes one f16 MFMA per block with P rounded
+// to float16 instead of the two bf16 MFMAs of the high/low split.  P enters scaled by
 // 2^7 (folded into the exp2 offset of the row, undone in the epilogue): a
 // weight is at most 2^8 * 2^7 in float16, and only weights below 2^-21 fall
 // into the float16 subnormals, whose absolute rounding error is at most
@@ -74,7 +77,8 @@ struct PrefillCfg {
     static constexpr int DB = D / 16;               // 16-wide dimension blocks of the output
     static constexpr int CPR = D / 8;               // 16-byte chunks per K row
     static constexpr int RPI = 64 / CPR;            // K rows per 1 KiB load instruction
-    static constexpr int KTILE = BN * D * 2;        // bytes of one K tile
+    static constexpr int KTILE = BN * D * 2;        // bytes of one K tile (and of one V^T image tile)
+    static constexpr int VROW = BN * 2;             // bytes of one dimension row of a V^T image tile
     static constexpr int NLD = KTILE / 1024 / 4;    // load instructions per wave per K tile
 };
 
@@ -155,11 +159,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
     constexpr bool f16pv = F16;
     if (a.vflag != nullptr && ((*a.vflag == 0u) != F16)) return;
     const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kv) * (size_t)a.L * D;
-    const uint16_t* vg = (f16pv ? a.v16 : a.v) + ((size_t)b * a.Hkv + kv) * (size_t)a.L * D;
+    // V: row-major bfloat16, or the float16 V^T image (whole 64-key tiles)
+    const int nimg = (a.L + C::BN - 1) / C::BN;
+    const uint16_t* vg = f16pv ? a.v16 + ((size_t)b * a.Hkv + kv) * (size_t)nimg * (C::KTILE / 2)
+                               : a.v + ((size_t)b * a.Hkv + kv) * (size_t)a.L * D;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kg), 0, a.L * D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vg), 0, a.L * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vg), 0, f16pv ? nimg * C::KTILE : a.L * D * 2, 0x00020000);
 
     // ---- Q^T fragments (B operand): query row row0 + 16 qb + l16, dims 32 s + 8 lq + e
     bf16x8 qf[2][C::KSTEPS];
@@ -194,7 +201,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         }
     };
     auto issue_k = [&](int tile, int slot) { issue_tile(krs, s_kv[slot], tile); };
-    auto issue_v = [&](int tile, int buf) { issue_tile(vrs, s_kv[2 + buf], tile); };
+    // a V^T image tile is already laid out as in LDS: a straight copy
+    auto issue_vimg = [&](int tile, int buf) {
+#pragma unroll
+        for (int i = 0; i < C::NLD; ++i) {
+            const int li = wave * C::NLD + i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vrs, (__attribute__((address_space(3))) void*)(s_kv[2 + buf] + li * 1024), 16,
+                lane * 16, tile * C::KTILE + li * 1024, 0, 0);
+        }
+    };
+    auto issue_v = [&](int tile, int buf) {
+        if constexpr (f16pv) issue_vimg(tile, buf);
+        else issue_tile(vrs, s_kv[2 + buf], tile);
+    };
     // S^T block (keys 16 kb + 4 lq + r, query rows 16 qb + l16) of one K tile
     auto scores = [&](int buf, f32x4 (&st)[2][4]) {
 #pragma unroll
@@ -354,6 +374,23 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
         return __builtin_bit_cast(bf16x8, both);
     };
 
+    // float16 form: V^T fragments are single 16-byte reads of the image tile.
+    // Dimension row d (VROW bytes) holds the tile's keys in P^T fragment
+    // order (position 32 h + 8 q + e holds key 32 h + 16 (e / 4) + 4 q + e % 4),
+    // 16-byte chunk c in slot c ^ (d % 8) ^ ((d / 8) % 2), so that any 16
+    // consecutive dimensions at one chunk fall in 16 distinct 16-byte bank
+    // groups.  Lane (l16, lq) reads dimension 16 db + l16, chunk 4 ks + lq.
+    int vimg_off[2];
+    {
+        const int sw = (l16 & 7) ^ ((l16 >> 3) & 1);
+        vimg_off[0] = l16 * C::VROW + ((lq ^ sw) * 16);
+        vimg_off[1] = vimg_off[0] ^ 64;                     // chunk 4 + lq: bit 2 of the chunk flips
+    }
+    auto vt_frag16 = [&](int buf, int ks, int db) -> pf_f16x8 {
+        return __builtin_bit_cast(pf_f16x8,
+                                  *(const u32x4*)&s_kv[2 + buf][vimg_off[ks] + db * 16 * C::VROW]);
+    };
+
     if constexpr (!PRE) __syncthreads();                   // sweep A is done with both K buffers
     issue_k(0, 0);
     issue_v(0, 0);
@@ -448,14 +485,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
                 }
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) {
-                    const pf_f16x8 vtf = __builtin_bit_cast(pf_f16x8, vt_frag(buf, ks, db));
+                    const pf_f16x8 vtf = vt_frag16(buf, ks, db);
 #pragma unroll
                     for (int qb = 0; qb < 2; ++qb)
                         o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vtf, pb[qb], o[qb][db], 0, 0, 0);
                 }
             }
-            pf_ds_mfma_pipeline<1, 4, 0>();
-            pf_ds_mfma_pipeline<2 * C::DB - 1, 2, 2>();
+            pf_ds_mfma_pipeline<1, 2, 0>();
+            pf_ds_mfma_pipeline<2 * C::DB - 1, 1, 2>();
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             return;
         }
@@ -554,20 +591,48 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 #endif
 }
 
-// float16 copy of a bfloat16 V (16-byte pieces); any element beyond 16 in
-// magnitude, or not finite, sets *flag (every writer stores the same value).
-__global__ void v_to_f16_kernel(const uint16_t* v, size_t n8, uint16_t* v16, unsigned* flag) {
+// The float16 V^T image of one 64-key tile of one (sequence, KV head), in the
+// layout the prefill kernel's LDS tile has (see vt_frag16 there): keys past L
+// are zero.  The tile goes through LDS (rows padded by one word, so that the
+// eight keys of one output chunk sit in distinct banks); any element beyond
+// 16 in magnitude, or not finite, sets *flag (every writer stores the same
+// value).  Grid: (tiles, B * Hkv), 256 threads.
+template <int D>
+__global__ __launch_bounds__(256) void v_to_f16t_kernel(const uint16_t* v, int L, uint16_t* img, unsigned* flag) {
+    constexpr int PW = D / 2 + 1;                        // words per LDS row (bf16 pairs + pad)
+    constexpr int CPR = D / 8;                           // 16-byte chunks per V row
+    constexpr int NCH = 64 * D / 8;                      // 16-byte chunks per tile
+    __shared__ unsigned s_v[64 * PW];
+    const int t = blockIdx.x;
+    const size_t bkv = blockIdx.y;
+    const uint16_t* vt = v + (bkv * (size_t)L + (size_t)t * 64) * D;
+    for (int idx = threadIdx.x; idx < NCH; idx += 256) {
+        const int key = idx / CPR, part = idx % CPR;
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (t * 64 + key < L) raw = *(const u32x4*)(vt + (size_t)key * D + 8 * part);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) s_v[key * PW + 4 * part + w] = raw[w];
+    }
+    __syncthreads();
+    const int nimg = (L + 63) / 64;
+    uint16_t* it = img + (bkv * (size_t)nimg + t) * (size_t)(64 * D);
     bool bad = false;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (size_t)gridDim.x * blockDim.x) {
-        const u32x4 raw = *(const u32x4*)(v + 8 * i);
+    for (int q = threadIdx.x; q < NCH; q += 256) {
+        const int d = q / 8, slot = q % 8;
+        const int c = slot ^ (d & 7) ^ ((d >> 3) & 1);   // chunk held in this slot
+        const int h = c / 4, qq = c % 4;                 // positions 32 h + 8 qq + e
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int key = 32 * h + 16 * (e / 4) + 4 * qq + e % 4;
+            const unsigned wd = s_v[key * PW + d / 2];
+            x[e] = __uint_as_float((d & 1) ? (wd & 0xffff0000u) : (wd << 16));
+            bad |= !(fabsf(x[e]) <= 16.0f);
+        }
         u32x4 o;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float lo = __uint_as_float(raw[w] << 16), hi = __uint_as_float(raw[w] & 0xffff0000u);
-            bad |= !(fabsf(lo) <= 16.0f) || !(fabsf(hi) <= 16.0f);
-            o[w] = pack_f16x2(lo, hi);
-        }
-        *(u32x4*)(v16 + 8 * i) = o;
+        for (int w = 0; w < 4; ++w) o[w] = pack_f16x2(x[2 * w], x[2 * w + 1]);
+        *(u32x4*)(it + 8 * q) = o;
     }
     if (bad) *flag = 1u;
 }
@@ -621,7 +686,10 @@ static int launch_prefill_d(const PrefillKArgs& a, int G, hipStream_t s) {
 }
 
 size_t prefill_mu_bytes(int B, int Hkv, int L, int d) { return (size_t)B * Hkv * L * d * sizeof(float); }
-size_t prefill_v16_bytes(int B, int Hkv, int L, int d) { return (size_t)B * Hkv * L * d * sizeof(uint16_t); }
+// the float16 V^T image: whole 64-key tiles
+size_t prefill_v16_bytes(int B, int Hkv, int L, int d) {
+    return (size_t)B * Hkv * (size_t)((L + 63) / 64) * 64 * d * sizeof(uint16_t);
+}
 
 int launch_prefill_bf16(const PrefillParams& p, float* mu_ws, hipStream_t s) {
     const bool vmc = (p.flags & 1u) && !(p.flags & 2u);
@@ -639,10 +707,9 @@ int launch_prefill_bf16(const PrefillParams& p, float* mu_ws, hipStream_t s) {
         vflag = (unsigned*)((char*)p.ws + mu_b + v16_b);
         int e = launch_fill_u32(vflag, 4, 0u, s);
         if (e != hipSuccess) return e;
-        const size_t n8 = (size_t)p.B * p.Hkv * p.L * p.d / 8;
-        unsigned blocks = (unsigned)((n8 + 255) / 256);
-        if (blocks > 8192) blocks = 8192;
-        hipLaunchKernelGGL(v_to_f16_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)p.v, n8, v16, vflag);
+        const dim3 grid((unsigned)((p.L + 63) / 64), (unsigned)(p.B * p.Hkv));
+        if (p.d == 64) hipLaunchKernelGGL(v_to_f16t_kernel<64>, grid, dim3(256), 0, s, (const uint16_t*)p.v, p.L, v16, vflag);
+        else hipLaunchKernelGGL(v_to_f16t_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)p.v, p.L, v16, vflag);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

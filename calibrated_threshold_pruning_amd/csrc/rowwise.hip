@@ -353,18 +353,67 @@ __global__ __launch_bounds__(kVmeanThreads) void vmean_kernel(const T* v, const 
     }
 }
 
-// causal prefix means mu_p = mean of V rows 0..p (Eq. 5 read causally)
+// causal prefix means mu_p = mean of V rows 0..p (Eq. 5 read causally), as a
+// scan over chunks of rows, all sums in double in row order within a chunk:
+//   chunk c holds rows [64 c, 64 c + 64), the last one also the rows past the
+//   last multiple of 64 (so every chunk after the first has at least 64 rows);
+//   1. every chunk but the last sums its rows; the sum goes to the slot of
+//      the next chunk: D doubles over the first float rows of that chunk's
+//      own output region, which its writer reads before overwriting;
+//   2. one thread per (group, dimension) turns the slots into running sums
+//      (the sum of all rows before the chunk);
+//   3. every chunk adds its rows to its slot's sum row by row and writes the
+//      means.
+// One thread per dimension (D = blockDim.x, at most 128); grid (chunks, groups).
+constexpr int kPrefixChunk = 64;
+
+__device__ __forceinline__ int prefix_chunks(int L) { return L / kPrefixChunk > 1 ? L / kPrefixChunk : 1; }
+__device__ __forceinline__ int prefix_chunk_end(int c, int nch, int L) {
+    return c == nch - 1 ? L : (c + 1) * kPrefixChunk;
+}
+__device__ __forceinline__ double* prefix_slot(float* mu, int g, int c, int L, int D) {
+    return reinterpret_cast<double*>(mu + ((size_t)g * L + (size_t)c * kPrefixChunk) * D);
+}
+
 template <typename T>
-__global__ void prefix_mean_kernel(const T* v, int L, int D, float* mu) {
-    const int bk = blockIdx.x;
-    const T* base = v + (size_t)bk * L * D;
-    float* o = mu + (size_t)bk * L * D;
-    for (int t = threadIdx.x; t < D; t += blockDim.x) {
-        double acc = 0.0;
-        for (int p = 0; p < L; ++p) {
-            acc += (double)Elem<T>::load(base + (size_t)p * D + t);
-            o[(size_t)p * D + t] = (float)(acc / (double)(p + 1));
-        }
+__global__ void prefix_chunk_sum_kernel(const T* v, int L, float* mu) {
+    const int D = blockDim.x, t = threadIdx.x, c = blockIdx.x, g = blockIdx.y;
+    const int nch = prefix_chunks(L);
+    const T* base = v + (size_t)g * L * D;
+    double acc = 0.0;
+    for (int p = c * kPrefixChunk; p < prefix_chunk_end(c, nch, L); ++p)
+        acc += (double)Elem<T>::load(base + (size_t)p * D + t);
+    prefix_slot(mu, g, c + 1, L, D)[t] = acc;
+}
+
+__global__ void prefix_chunk_scan_kernel(int L, int D, int groups, float* mu) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= groups * D) return;
+    const int g = i / D, t = i % D;
+    const int nch = prefix_chunks(L);
+    double run = 0.0;
+    for (int c = 1; c < nch; ++c) {
+        double* slot = prefix_slot(mu, g, c, L, D);
+        run += slot[t];
+        slot[t] = run;
+    }
+}
+
+template <typename T>
+__global__ void prefix_mean_write_kernel(const T* v, int L, float* mu) {
+    __shared__ double s_pre[128];
+    const int D = blockDim.x, t = threadIdx.x, c = blockIdx.x, g = blockIdx.y;
+    const int nch = prefix_chunks(L);
+    // the slot goes through LDS, so that every entry has arrived before any
+    // row of the chunk (which the slot overlaps) is written
+    s_pre[t] = c == 0 ? 0.0 : prefix_slot(mu, g, c, L, D)[t];
+    __syncthreads();
+    double acc = s_pre[t];
+    const T* base = v + (size_t)g * L * D;
+    float* o = mu + (size_t)g * L * D;
+    for (int p = c * kPrefixChunk; p < prefix_chunk_end(c, nch, L); ++p) {
+        acc += (double)Elem<T>::load(base + (size_t)p * D + t);
+        o[(size_t)p * D + t] = (float)(acc / (double)(p + 1));
     }
 }
 
@@ -537,25 +586,27 @@ int launch_decode_rowwise(const DecodeParams& p, uint32_t* masks_ws, hipStream_t
     return e;
 }
 
-int launch_prefix_mean(const void* v, int groups, int L, int d, int dtype, float* mu, hipStream_t s) {
-    if (dtype == 0)
-        hipLaunchKernelGGL(prefix_mean_kernel<float>, dim3(groups), dim3(128), 0, s, (const float*)v, L, d, mu);
-    else
-        hipLaunchKernelGGL(prefix_mean_kernel<uint16_t>, dim3(groups), dim3(128), 0, s, (const uint16_t*)v, L,
-                           d, mu);
+template <typename T>
+static int launch_prefix_mean_t(const T* v, int groups, int L, int d, float* mu, hipStream_t s) {
+    const int nch = L / kPrefixChunk > 1 ? L / kPrefixChunk : 1;
+    if (nch > 1) {
+        hipLaunchKernelGGL(prefix_chunk_sum_kernel<T>, dim3(nch - 1, groups), dim3(d), 0, s, v, L, mu);
+        const int n = groups * d;
+        hipLaunchKernelGGL(prefix_chunk_scan_kernel, dim3((n + 255) / 256), dim3(256), 0, s, L, d, groups, mu);
+    }
+    hipLaunchKernelGGL(prefix_mean_write_kernel<T>, dim3(nch, groups), dim3(d), 0, s, v, L, mu);
     return hipGetLastError();
+}
+
+int launch_prefix_mean(const void* v, int groups, int L, int d, int dtype, float* mu, hipStream_t s) {
+    if (dtype == 0) return launch_prefix_mean_t((const float*)v, groups, L, d, mu, s);
+    return launch_prefix_mean_t((const uint16_t*)v, groups, L, d, mu, s);
 }
 
 int launch_prefill_rowwise(const PrefillParams& p, float* mu_ws, hipStream_t s) {
     const bool vmc = (p.flags & 1u) && !(p.flags & 2u);
     if (vmc) {
-        if (p.dtype == 0)
-            hipLaunchKernelGGL(prefix_mean_kernel<float>, dim3(p.B * p.Hkv), dim3(128), 0, s,
-                               (const float*)p.v, p.L, p.d, mu_ws);
-        else
-            hipLaunchKernelGGL(prefix_mean_kernel<uint16_t>, dim3(p.B * p.Hkv), dim3(128), 0, s,
-                               (const uint16_t*)p.v, p.L, p.d, mu_ws);
-        hipError_t e = hipGetLastError();
+        const int e = launch_prefix_mean(p.v, p.B * p.Hkv, p.L, p.d, p.dtype, mu_ws, s);
         if (e != hipSuccess) return e;
     }
     RowArgs a = {};

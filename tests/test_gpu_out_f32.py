@@ -204,3 +204,33 @@ def test_decode_out_f32(entry, Hq, Hkv, d, Lmax, lens):
                 check_row_mask(gk, s, theta_of(theta, h, n - 1), f"b{b} h{h}")
                 ro, _ = oracle.row_output(s, gk, vf[b, kv, :n], vm[b, kv], vmc=True, renorm=False)
             flat_check(g[b, h], ro, f"b{b} h{h}")
+
+
+@pytest.mark.parametrize("dtype,L,d", [(torch.bfloat16, 4133, 128), (torch.bfloat16, 191, 64),
+                                       (torch.bfloat16, 127, 128), (torch.float32, 300, 64)])
+def test_prefill_vmc_keeps_nothing_is_prefix_mean(dtype, L, d):
+    """theta above every probability, with VMC: nothing is kept, beta = 1, and
+    the float32 output of row p is the causal mean of V rows 0..p.  Every row
+    is checked against the oracle's prefix mean, at lengths whose running sums
+    span one chunk of 64 rows (127), three with a longer last one (191) and 64
+    with a ragged last one (4133)."""
+    print(f"prefill vmc prefix mean {dtype} L={L} d={d}", flush=True)
+    dev = device()
+    Hq, Hkv = 2, 2
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 12, L, B=1, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d, dtype=dtype)
+    th = torch.full((Hq, L), 1.5, dtype=torch.float32, device=dev)
+    out = torch.full((1, Hq, L, d), 7.0, dtype=torch.float32, device=dev)
+    kc = torch.full((1, Hq, L), -7, dtype=torch.int32, device=dev)
+    bt = torch.full((1, Hq, L), -7.0, dtype=torch.float32, device=dev)
+    ws = tt.workspace(tt.TOPTH_OP_PREFILL, 1, Hq, Hkv, L, L, d)
+    tt.topth_prefill(q.to(dev), k.to(dev), v.to(dev), th, out, scale=1.0 / np.sqrt(d),
+                     flags=tt.TOPTH_VMC | tt.TOPTH_OUT_F32, kept_count=kc, beta=bt, ws=ws)
+    torch.cuda.synchronize()
+    assert (kc.cpu().numpy() == 0).all()
+    assert (bt.cpu().numpy() == 1.0).all()
+    g = out.cpu().numpy()[0]
+    vf = to_f64(v)
+    for h in range(Hq):
+        mu = oracle.prefix_mean(vf[0, h])
+        err = np.abs(g[h] - mu) / np.maximum(np.abs(mu), 1e-30)
+        assert (np.abs(g[h] - mu) <= 2.0 ** -23 * np.abs(mu) + 1e-30).all(), (h, float(err.max()))
