@@ -149,6 +149,90 @@ __device__ __forceinline__ void mkc_emit_rows(const MkcArgs& a, const float* s_s
     }
 }
 
+// (m, l) pairs of an online exp2 sum: l is relative to m; m = -inf: empty
+__device__ __forceinline__ void mkc_lse_merge(float& m, float& l, float m2, float l2) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) return;
+    l = l * __builtin_amdgcn_exp2f(m - M) + l2 * __builtin_amdgcn_exp2f(m2 - M);
+    m = M;
+}
+
+// As mkc_emit_rows, from statistics the lanes gathered while storing the
+// scores (lane statistics of head u = 4 kq + r, kq = lane / 16): one merge
+// per head, then one pass that writes every head's values.  The written
+// minimum and maximum are the value function at the score minimum and
+// maximum (it is monotone in the score).
+template <int HPW>
+__device__ __forceinline__ void mkc_emit_rows_stats(const MkcArgs& a, const float* s_sc, const float (&st_m)[4],
+                                                    const float (&st_l)[4], const float (&st_n)[4], int s, int h0,
+                                                    int i, int m) {
+    constexpr int NW = kMkcValThreads / 64;
+    __shared__ float s_pm[NW][16], s_pl[NW][16], s_pn[NW][16];
+    __shared__ float s_off[16];                   // per head: lse2 (0 for pre)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float mm = st_m[r], ll = st_l[r], nn = st_n[r];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {        // the 16 lanes of the group
+            const float m2 = __shfl_xor(mm, o), l2 = __shfl_xor(ll, o);
+            mkc_lse_merge(mm, ll, m2, l2);
+            nn = fminf(nn, __shfl_xor(nn, o));
+        }
+        const int u = 4 * kq + r;
+        if (col == 0 && u < HPW) { s_pm[wave][u] = mm; s_pl[wave][u] = ll; s_pn[wave][u] = nn; }
+    }
+    __syncthreads();                              // every score is in LDS, every partial too
+    if (threadIdx.x < HPW) {
+        const int u = threadIdx.x;
+        float mm = s_pm[0][u], ll = s_pl[0][u], nn = s_pn[0][u];
+        for (int w = 1; w < NW; ++w) {
+            mkc_lse_merge(mm, ll, s_pm[w][u], s_pl[w][u]);
+            nn = fminf(nn, s_pn[w][u]);
+        }
+        float off = 0.f, vmin, vmax;
+        if (a.pre) {
+            vmin = nn + 0.0f;
+            vmax = mm + 0.0f;
+        } else {
+            off = mm + log2f(ll);
+            vmin = exp2f(nn - off);
+            vmax = exp2f(mm - off);
+        }
+        s_off[u] = off;
+        const size_t o = ((size_t)(h0 + u) * a.Lq + i) * a.S + s;
+        a.smin[o] = vmin;
+        a.smax[o] = vmax;
+    }
+    __syncthreads();
+    // 16-byte stores where the row of every head starts 16-byte aligned
+    // (m a multiple of 4 and the row's pool offset too), else 4-byte ones
+    const float* dst0 = a.pool + (size_t)a.S * mkc_row_prefix(a.q_pos0, i) + (size_t)s * m;
+    const bool vec = (m & 3) == 0 && (((uintptr_t)dst0 & 15u) == 0) &&
+                     ((((size_t)a.S * mkc_row_prefix(a.q_pos0, a.Lq)) & 3u) == 0);
+    const bool pre = a.pre != 0;
+    auto val = [&](float x, float off) { return pre ? x + 0.0f : exp2f(x - off); };   // -0 becomes +0
+#pragma unroll 1
+    for (int u = 0; u < HPW; ++u) {
+        const float* sc = s_sc + u * m;
+        const float off = s_off[u];
+        float* dst = a.pool + (size_t)(h0 + u) * a.S * mkc_row_prefix(a.q_pos0, a.Lq) +
+                     (size_t)a.S * mkc_row_prefix(a.q_pos0, i) + (size_t)s * m;
+        // nontemporal stores: the pool is only read back by later kernels
+        if (vec) {
+            typedef float f32x4v __attribute__((ext_vector_type(4)));
+            for (int j = 4 * threadIdx.x; j < m; j += 4 * kMkcValThreads) {
+                const f32x4v x = *(const f32x4v*)(sc + j);
+                const f32x4v y = {val(x[0], off), val(x[1], off), val(x[2], off), val(x[3], off)};
+                __builtin_nontemporal_store(y, (f32x4v*)(dst + j));
+            }
+        } else {
+            for (int j = threadIdx.x; j < m; j += kMkcValThreads) __builtin_nontemporal_store(val(sc[j], off), dst + j);
+        }
+    }
+}
+
 // float32: a group of lanes per key reads its K row in 16-byte chunks once
 // for all HPW heads and reduces the HPW dot products across the group
 template <int D, int HPW>
@@ -209,8 +293,7 @@ __global__ __launch_bounds__(kMkcValThreads) void mkc_values_f32_kernel(MkcArgs 
 constexpr int kMkcNtk = 4;
 template <int D, int HPW>
 __global__ __launch_bounds__(kMkcValThreads) void mkc_values_bf16_kernel(MkcArgs a) {
-    extern __shared__ float s_sc[];            // [HPW][m]
-    __shared__ float s_red[kMkcValThreads / 64];
+    extern __shared__ __attribute__((aligned(16))) float s_sc[];   // [HPW][m]
     constexpr int ST = D / 32;                 // k-steps
     constexpr int NW = kMkcValThreads / 64;
     const int nhb = a.Hq / HPW;
@@ -221,7 +304,7 @@ __global__ __launch_bounds__(kMkcValThreads) void mkc_values_bf16_kernel(MkcArgs
     const int g = a.Hq / a.Hkv;
     const int h0 = hb * HPW;
     const int m = a.q_pos0 + i + 1;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, kq = lane >> 4;
     const float mul = a.pre ? a.scale : a.xscale;
 
@@ -236,14 +319,29 @@ __global__ __launch_bounds__(kMkcValThreads) void mkc_values_bf16_kernel(MkcArgs
         }
     }
     const uint16_t* kg = (const uint16_t*)a.k + ((size_t)s * a.Hkv + h0 / g) * (size_t)a.Lk * D;
-    for (int t0 = wave * 16 * kMkcNtk; t0 < m; t0 += NW * 16 * kMkcNtk) {
-        u32x4 kb[kMkcNtk][ST];
+    // Each wave takes groups of kMkcNtk 16-key tiles, NW groups apart, with
+    // the next group's loads in flight while the current one is scored (two
+    // register buffers, the loop unrolled by two so that each is named at
+    // compile time).  Keys past the row read its last key, so every load and
+    // MFMA is issued unconditionally (a group past the row is scored but not
+    // stored): a conditional exit inside the body would make the compiler
+    // wait for every load in flight at the top of each trip.
+    constexpr int GSTEP = NW * 16 * kMkcNtk;
+    auto load = [&](u32x4 (&kb)[kMkcNtk][ST], int t0) {
 #pragma unroll
         for (int tk = 0; tk < kMkcNtk; ++tk) {
-            const int key = min(t0 + 16 * tk + col, m - 1);      // keys past the row repeat its last
+            const int key = min(t0 + 16 * tk + col, m - 1);
 #pragma unroll
             for (int st = 0; st < ST; ++st) kb[tk][st] = *(const u32x4*)(kg + (size_t)key * D + 32 * st + 8 * kq);
         }
+    };
+    // lane statistics of the scores it stores (head u = 4 kq + r): maximum,
+    // sum of exp2 relative to it (online; not needed for pre), minimum
+    float st_m[4], st_l[4], st_n[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { st_m[r] = -INFINITY; st_l[r] = 0.f; st_n[r] = INFINITY; }
+    const bool pre = a.pre != 0;
+    auto score = [&](const u32x4 (&kb)[kMkcNtk][ST], int t0) {
 #pragma unroll
         for (int tk = 0; tk < kMkcNtk; ++tk) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -255,11 +353,28 @@ __global__ __launch_bounds__(kMkcValThreads) void mkc_values_bf16_kernel(MkcArgs
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int u = 4 * kq + r;
-                if (u < HPW && key < m) s_sc[u * m + key] = acc[r] * mul;
+                if (u < HPW && key < m) {
+                    const float v = acc[r] * mul;
+                    s_sc[u * m + key] = v;
+                    const float nm = fmaxf(st_m[r], v);
+                    if (!pre)
+                        st_l[r] = st_l[r] * __builtin_amdgcn_exp2f(st_m[r] - nm) + __builtin_amdgcn_exp2f(v - nm);
+                    st_m[r] = nm;
+                    st_n[r] = fminf(st_n[r], v);
+                }
             }
         }
+    };
+    u32x4 k0[kMkcNtk][ST], k1[kMkcNtk][ST];
+    const int tw = wave * 16 * kMkcNtk;
+    if (tw < m) load(k0, tw);
+    for (int t0 = tw; t0 < m; t0 += 2 * GSTEP) {
+        load(k1, t0 + GSTEP);
+        score(k0, t0);
+        load(k0, t0 + 2 * GSTEP);
+        score(k1, t0 + GSTEP);
     }
-    mkc_emit_rows<HPW>(a, s_sc, s_red, s, h0, i, m);
+    mkc_emit_rows_stats<HPW>(a, s_sc, st_m, st_l, st_n, s, h0, i, m);
 }
 
 // ---------------------------------------------------------------- select
@@ -357,7 +472,12 @@ __device__ __forceinline__ int count_ge_key(const float* x, int n, uint32_t k) {
 // (LEVEL 2), added into the segment's counts.
 template <int LEVEL>
 __global__ __launch_bounds__(kMkcCompThreads) void mkc_phist_kernel(MkcArgs a) {
-    __shared__ unsigned s_h[512];
+    // level 1: 16 copies of the histogram, one per lane % 16, 513 words apart
+    // (distinct banks): the values crowd into few exponent bins, and lanes
+    // adding to one LDS word in one instruction are serialised (level 2 bins
+    // the mantissa of one exponent and keeps one copy)
+    constexpr int NC = LEVEL == 1 ? 16 : 1, CS = 513;
+    __shared__ unsigned s_h[NC * CS];
     const int seg = blockIdx.x / a.wpc, ck = blockIdx.x % a.wpc;
     const MkcSeg g = mkc_seg(a, seg);
     const int j0 = ck * kMkcCompChunk;
@@ -365,10 +485,12 @@ __global__ __launch_bounds__(kMkcCompThreads) void mkc_phist_kernel(MkcArgs a) {
     // the whole workgroup: past the segment, no target below m, or no bin selected
     if (j0 >= g.N || mkc_kp(a, g.m) == 0 || sel < 0) return;
     const int tid = threadIdx.x;
-    for (int b = tid; b < 512; b += kMkcCompThreads) s_h[b] = 0u;
+    constexpr int NB = LEVEL == 1 ? 512 : 256;
+    for (int b = tid; b < NC * CS; b += kMkcCompThreads) s_h[b] = 0u;
     __syncthreads();
     const int end = min(g.N, j0 + kMkcCompChunk);
     const float* sp = a.pool + g.off;
+    unsigned* const hc = s_h + (tid & (NC - 1)) * CS;
     float v[kMkcCompItems];
 #pragma unroll
     for (int it = 0; it < kMkcCompItems; ++it) v[it] = sp[min(j0 + it * kMkcCompThreads + tid, end - 1)];
@@ -376,13 +498,17 @@ __global__ __launch_bounds__(kMkcCompThreads) void mkc_phist_kernel(MkcArgs a) {
     for (int it = 0; it < kMkcCompItems; ++it) {
         if (j0 + it * kMkcCompThreads + tid >= end) continue;
         const uint32_t key = float_to_ordered(v[it]);
-        if (LEVEL == 1) atomicAdd(&s_h[key >> 23], 1u);
-        else if ((key >> 23) == (uint32_t)sel) atomicAdd(&s_h[(key >> 15) & 255u], 1u);
+        if (LEVEL == 1) atomicAdd(&hc[key >> 23], 1u);
+        else if ((key >> 23) == (uint32_t)sel) atomicAdd(&hc[(key >> 15) & 255u], 1u);
     }
     __syncthreads();
     unsigned* dst = LEVEL == 1 ? a.h1 + (size_t)seg * 512 : a.h2 + (size_t)seg * 256;
-    for (int b = tid; b < (LEVEL == 1 ? 512 : 256); b += kMkcCompThreads)
-        if (s_h[b] != 0u) atomicAdd(&dst[b], s_h[b]);
+    for (int b = tid; b < NB; b += kMkcCompThreads) {
+        unsigned c = 0u;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) c += s_h[k * CS + b];
+        if (c != 0u) atomicAdd(&dst[b], c);
+    }
 }
 
 // Bound, steps 2 and 4: one workgroup per segment tests the condition at
