@@ -14,7 +14,8 @@
 //   all m), so kbar(x) >= k  <=>  C > 0 and T >= k * C.
 // theta(k) is the value at the first such position.  The kernels therefore
 //   1. compute each sample row's values (post-softmax, or the scores) and
-//      its min and max (one workgroup per sample row, scores in LDS);
+//      its min and max (one workgroup per sample row, scores in LDS); for
+//      bf16 the same pass counts them into step 3's first histogram;
 //   2. sort each (head, row)'s sample maxima and minima (one workgroup each);
 //   3. find a bound below which no theta of the (head, row) lies: the
 //      highest boundary of a two-level histogram of the pooled keys at which
@@ -161,7 +162,9 @@ __device__ __forceinline__ void mkc_lse_merge(float& m, float& l, float m2, floa
 // scores (lane statistics of head u = 4 kq + r, kq = lane / 16): one merge
 // per head, then one pass that writes every head's values.  The written
 // minimum and maximum are the value function at the score minimum and
-// maximum (it is monotone in the score).
+// maximum (it is monotone in the score).  The same pass counts the values
+// into the bound's level-1 histogram (top 9 key bits), first in LDS, then
+// one global add per nonzero bin: no separate pass over the pool for it.
 template <int HPW>
 __device__ __forceinline__ void mkc_emit_rows_stats(const MkcArgs& a, const float* s_sc, const float (&st_m)[4],
                                                     const float (&st_l)[4], const float (&st_n)[4], int s, int h0,
@@ -169,6 +172,8 @@ __device__ __forceinline__ void mkc_emit_rows_stats(const MkcArgs& a, const floa
     constexpr int NW = kMkcValThreads / 64;
     __shared__ float s_pm[NW][16], s_pl[NW][16], s_pn[NW][16];
     __shared__ float s_off[16];                   // per head: lse2 (0 for pre)
+    __shared__ unsigned s_h1[HPW * 512];          // per head: the bound's level-1 histogram of the values
+    for (int b = threadIdx.x; b < HPW * 512; b += kMkcValThreads) s_h1[b] = 0u;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, kq = lane >> 4;
 #pragma unroll
@@ -212,11 +217,17 @@ __device__ __forceinline__ void mkc_emit_rows_stats(const MkcArgs& a, const floa
     const bool vec = (m & 3) == 0 && (((uintptr_t)dst0 & 15u) == 0) &&
                      ((((size_t)a.S * mkc_row_prefix(a.q_pos0, a.Lq)) & 3u) == 0);
     const bool pre = a.pre != 0;
-    auto val = [&](float x, float off) { return pre ? x + 0.0f : exp2f(x - off); };   // -0 becomes +0
+    auto val0 = [&](float x, float off) { return pre ? x + 0.0f : exp2f(x - off); };   // -0 becomes +0
 #pragma unroll 1
     for (int u = 0; u < HPW; ++u) {
         const float* sc = s_sc + u * m;
         const float off = s_off[u];
+        unsigned* const hu = s_h1 + u * 512;
+        auto val = [&](float x, float o) {
+            const float y = val0(x, o);
+            atomicAdd(&hu[float_to_ordered(y) >> 23], 1u);
+            return y;
+        };
         float* dst = a.pool + (size_t)(h0 + u) * a.S * mkc_row_prefix(a.q_pos0, a.Lq) +
                      (size_t)a.S * mkc_row_prefix(a.q_pos0, i) + (size_t)s * m;
         // nontemporal stores: the pool is only read back by later kernels
@@ -230,6 +241,12 @@ __device__ __forceinline__ void mkc_emit_rows_stats(const MkcArgs& a, const floa
         } else {
             for (int j = threadIdx.x; j < m; j += kMkcValThreads) __builtin_nontemporal_store(val(sc[j], off), dst + j);
         }
+    }
+    // this sample's counts join the row's histogram (nonzero bins only)
+    __syncthreads();
+    for (int b = threadIdx.x; b < HPW * 512; b += kMkcValThreads) {
+        const unsigned c = s_h1[b];
+        if (c != 0u) atomicAdd(&a.h1[((size_t)(h0 + b / 512) * a.Lq + i) * 512 + (b % 512)], c);
     }
 }
 
@@ -434,8 +451,8 @@ __global__ __launch_bounds__(kMkcSelThreads) void mkc_sortmm_kernel(MkcArgs a) {
         lds_bitonic_asc(s_x, n2);              // the -inf padding sorts to the front
         for (int c = threadIdx.x; c < a.S; c += blockDim.x) v[c] = s_x[n2 - a.S + c];
     }
-    // the segment's bound histograms and compaction count start at zero
-    for (int c = threadIdx.x; c < 512; c += blockDim.x) a.h1[(size_t)seg * 512 + c] = 0u;
+    // the segment's level-2 histogram and compaction count start at zero
+    // (the level-1 histogram is cleared before the values kernel)
     for (int c = threadIdx.x; c < 256; c += blockDim.x) a.h2[(size_t)seg * 256 + c] = 0u;
     if (threadIdx.x == 0) a.cnt[seg] = 0;
 }
@@ -954,7 +971,8 @@ int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_
     a.n_k = p.n_k;
     for (int t = 0; t < p.n_k; ++t) a.ks[t] = p.mkc_ks[t];
     a.theta = theta;
-    int e;
+    int e = launch_fill_u32(a.h1, (size_t)nseg * 512 * sizeof(unsigned), 0u, s);   // the bf16 values kernel adds to it
+    if (e != hipSuccess) return e;
     if (p.dtype == 1) e = p.d == 64 ? launch_values<uint16_t, 64>(a, s) : launch_values<uint16_t, 128>(a, s);
     else e = p.d == 64 ? launch_values<float, 64>(a, s) : launch_values<float, 128>(a, s);
     if (e != hipSuccess) return e;
@@ -968,7 +986,8 @@ int launch_calibrate_mkc(const CalibParams& p, int pre, float* theta, hipStream_
     const unsigned nww = (unsigned)std::min<long long>(wpw * nseg, kMkcLoopGrid);
     hipLaunchKernelGGL(mkc_sortmm_kernel, dim3(nseg_u), dim3(kMkcSelThreads), 0, s, a);
     const unsigned nwc = (unsigned)(a.wpc * nseg);
-    hipLaunchKernelGGL(mkc_phist_kernel<1>, dim3(nwc), dim3(kMkcCompThreads), 0, s, a);
+    if (p.dtype != 1)                          // the bf16 values kernel counted level 1 itself
+        hipLaunchKernelGGL(mkc_phist_kernel<1>, dim3(nwc), dim3(kMkcCompThreads), 0, s, a);
     hipLaunchKernelGGL(mkc_decide_kernel<1>, dim3(nseg_u), dim3(256), 0, s, a);
     hipLaunchKernelGGL(mkc_phist_kernel<2>, dim3(nwc), dim3(kMkcCompThreads), 0, s, a);
     hipLaunchKernelGGL(mkc_decide_kernel<2>, dim3(nseg_u), dim3(256), 0, s, a);
