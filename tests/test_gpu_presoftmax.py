@@ -276,6 +276,32 @@ def test_prefill_pre_8k_full_size_sampled_rows():
                 ok.append((b, h, p))
         assert len(ok) >= 0.9 * len(rows)
         compare_prefill_pre(q, k, v, theta, et, sdc, False, g, torch.bfloat16, ok)
+    # the same launch with the byte mask (2 GiB at this size): every sampled
+    # row, ambiguous elements included, element by element against the oracle
+    # re-evaluated with the GPU's decisions
+    print("prefill_pre 8k sampled rows with the kept mask", flush=True)
+    km = torch.zeros((1, Hq, L, L), dtype=torch.uint8, device=dev)
+    out = torch.empty(1, Hq, L, d, dtype=q.dtype, device=dev)
+    kc = torch.full((1, Hq, L), -7, dtype=torch.int32, device=dev)
+    bt = torch.full((1, Hq, L), -7.0, dtype=torch.float32, device=dev)
+    tt.topth_prefill_pre(q.to(dev), k.to(dev), v.to(dev), torch.tensor(theta, dtype=torch.float32, device=dev), out,
+                         scale=1.0 / np.sqrt(d), flags=MODES["expth"], gamma=GAMMA,
+                         e_tilde=torch.tensor(et, dtype=torch.float32, device=dev),
+                         kept_count=kc, beta=bt, kept_mask=km)
+    torch.cuda.synchronize()
+
+    class SampledRowMasks:
+        """kept_mask[b, h, p, :p + 1] of the sampled rows only, copied to the host."""
+        def __init__(self, rows):
+            self.m = {(b, h, p): km[b, h, p, :p + 1].cpu().numpy().astype(bool) for (b, h, p) in rows}
+
+        def __getitem__(self, idx):
+            b, h, p, sl = idx
+            return self.m[(b, h, p)][sl]
+
+    g = (out.float().cpu().numpy(), kc.cpu().numpy(), bt.cpu().numpy(), SampledRowMasks(rows))
+    del km
+    compare_prefill_pre(q, k, v, theta, et, "expth", False, g, torch.bfloat16, rows)
 
 
 # ------------------------------------------------------------------- decode
