@@ -865,9 +865,10 @@ def bench_mkc(with_cpu):
                         "unit": "GB/s", "frac": round(bytes_min / t / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
                         "kernel": "whole call: mkc_values_bf16_kernel, the bound, compaction, radix sort and "
                                   "walk kernels",
-                        "note": "the values kernel streams K once per KV head; the pooled values are read three "
-                                "more times (two bound histograms, the compaction) and only those above the "
-                                "bound on theta are sorted, which this minimum does not count"}}
+                        "note": "the values kernel streams K once per KV head and counts the bound's first "
+                                "histogram as it writes the pooled values; they are read twice more (the second "
+                                "histogram, the compaction) and only those above the bound on theta are sorted, "
+                                "which this minimum does not count"}}
     # thresholds for k = 128 from the merged function, applied to the decode_8b step
     wd = DECODE_WORKLOADS["decode_8b"]
     qt, kt, vt = attention_inputs_device(CONFIG_IDS["decode_8b"], ROLE_TEST, 0, 0, B=wd["B"], Hq=Hq, Hkv=Hkv, Lq=1,
