@@ -693,27 +693,39 @@ def bench_calib(with_cpu):
     ws = tt.workspace(tt.TOPTH_OP_CALIBRATE, w["chunk"], Hq, Hkv, L, L, d, n_k)
     total_s, wall = 0.0, 0.0
     thetas = []
+    # one untimed call first (kernel loading, LDS attributes)
+    q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, 0, 0, B=w["chunk"], Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d,
+                                       n_sinks=w["sinks"], device=dev, with_v=False)
+    s1 = torch.zeros(n_k, Hq, L, dtype=torch.float64, device=dev)
+    tt.topth_calibrate(q, kk, ks, s1, torch.zeros_like(s1), torch.zeros(n_k, Hq, L, dtype=torch.int32, device=dev),
+                       ws, scale=scale, q_pos0=0)
+    torch.cuda.synchronize()
+    del q, kk
     for layer in range(w["timed_layers"]):
         s1 = torch.zeros(n_k, Hq, L, dtype=torch.float64, device=dev)
         s2 = torch.zeros_like(s1)
         cnt = torch.zeros(n_k, Hq, L, dtype=torch.int32, device=dev)
+        theta = torch.empty(n_k, Hq, L, dtype=torch.float32, device=dev)
+        # every call's inputs resident in HBM first (about 4.3 GB per layer),
+        # then the layer's calls and the finalize back to back in one timed region
+        chunks = []
         for done in range(0, w["seqs"], w["chunk"]):
             S = min(w["chunk"], w["seqs"] - done)
             q, kk, _ = attention_inputs_device(cfg, ROLE_CALIB, layer, done, B=S, Hq=Hq, Hkv=Hkv, Lq=L,
                                                Lk=L, d=d, n_sinks=w["sinks"], device=dev, with_v=False)
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t0 = time.perf_counter()
-            a.record()
+            chunks.append((q, kk))
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record()
+        for q, kk in chunks:
             tt.topth_calibrate(q, kk, ks, s1, s2, cnt, ws, scale=scale, q_pos0=0)
-            if done + S >= w["seqs"]:
-                theta = torch.empty(n_k, Hq, L, dtype=torch.float32, device=dev)
-                tt.topth_calibrate_finalize(s1, s2, cnt, ks, theta)
-            b.record()
-            torch.cuda.synchronize()
-            wall += time.perf_counter() - t0
-            total_s += a.elapsed_time(b) * 1e-3
-            del q, kk
+        tt.topth_calibrate_finalize(s1, s2, cnt, ks, theta)
+        b.record()
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - t0
+        total_s += a.elapsed_time(b) * 1e-3
+        del chunks
         thetas.append(theta)
         log(f"[bench] calib_sweep: layer {layer} done ({total_s:.3f} s GPU so far)")
     seq_layers = w["seqs"] * w["timed_layers"]

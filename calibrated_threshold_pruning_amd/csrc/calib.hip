@@ -1101,20 +1101,27 @@ __global__ __launch_bounds__(256) void calib_fixup_kernel(CalibTArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) { qv[2 * i] = __uint_as_float(u[i] << 16); qv[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u); }
         }
-        for (int j0 = wave * RPW; j0 < n; j0 += 4 * RPW) {
-            const int j = j0 + grp;
-            float dot = 0.f;
-            if (j < n) {
-                const u32x4 u = *(const u32x4*)(kg + (size_t)j * D + 8 * sub);
+        // UN key steps per trip, their loads issued together (keys past the
+        // row read its last key and are not stored)
+        constexpr int UN = 8;
+        for (int j0 = wave * RPW; j0 < n; j0 += 4 * RPW * UN) {
+            u32x4 u[UN];
+#pragma unroll
+            for (int s2 = 0; s2 < UN; ++s2)
+                u[s2] = *(const u32x4*)(kg + (size_t)min(j0 + s2 * 4 * RPW + grp, n - 1) * D + 8 * sub);
+#pragma unroll
+            for (int s2 = 0; s2 < UN; ++s2) {
+                const int j = j0 + s2 * 4 * RPW + grp;
+                float dot = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    dot = fmaf(qv[2 * i], __uint_as_float(u[i] << 16), dot);
-                    dot = fmaf(qv[2 * i + 1], __uint_as_float(u[i] & 0xffff0000u), dot);
+                    dot = fmaf(qv[2 * i], __uint_as_float(u[s2][i] << 16), dot);
+                    dot = fmaf(qv[2 * i + 1], __uint_as_float(u[s2][i] & 0xffff0000u), dot);
                 }
-            }
 #pragma unroll
-            for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);
-            if (j < n && sub == 0) fx[j] = dot;
+                for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);
+                if (j < n && sub == 0) fx[j] = dot;
+            }
         }
         __syncthreads();
         uint32_t prefix = 0u, mask = 0u;
@@ -1127,14 +1134,28 @@ __global__ __launch_bounds__(256) void calib_fixup_kernel(CalibTArgs a) {
                 if ((key & mask) == prefix) atomicAdd(&s_h[(key >> shift) & 255u], 1u);
             }
             __syncthreads();
-            if (tid == 0) {
-                int cum = 0, d = 255;
-                for (; d > 0; --d) {
-                    if (cum + (int)s_h[d] >= rem) break;
-                    cum += (int)s_h[d];
+            // the digit that holds the rem-th largest, counted from the top:
+            // lane l of wave 0 sums bins 255 - 4 l .. 252 - 4 l, a prefix over
+            // the lanes gives the count above each lane's bins, and the one
+            // lane whose range covers rem finds the digit among its four
+            if (wave == 0) {
+                int c[4], sum = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { c[i] = (int)s_h[255 - 4 * lane - i]; sum += c[i]; }
+                int incl = sum;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int w = __shfl_up(incl, o);
+                    if (lane >= o) incl += w;
                 }
-                s_dig = d;
-                s_rem = rem - cum;
+                int cum = incl - sum;
+                if (cum < rem && rem <= incl) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (cum + c[i] >= rem) { s_dig = 255 - 4 * lane - i; s_rem = rem - cum; break; }
+                        cum += c[i];
+                    }
+                }
             }
             __syncthreads();
             prefix |= (uint32_t)s_dig << shift;
