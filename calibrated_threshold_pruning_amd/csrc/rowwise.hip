@@ -432,11 +432,23 @@ __global__ void calib_accumulate_kernel(const float* samples, const float* esamp
     if (p >= n_rows) return;
     double s1 = 0.0, s2 = 0.0, e1 = 0.0;
     int c = 0;
-    for (int s = 0; s < S; ++s) {
-        const float x = samples[(size_t)s * per + idx];
-        if (x == x) {
-            s1 += (double)x; s2 += (double)x * (double)x; ++c;
-            if (esamples) e1 += (double)esamples[(size_t)s * per + idx];
+    // eight sequences per trip, their loads issued together; the sums still
+    // run in sequence order
+    constexpr int UN = 8;
+    for (int s0 = 0; s0 < S; s0 += UN) {
+        float x[UN], ex[UN];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const size_t o = (size_t)min(s0 + u, S - 1) * per + idx;
+            x[u] = samples[o];
+            ex[u] = esamples ? esamples[o] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            if (s0 + u < S && x[u] == x[u]) {
+                s1 += (double)x[u]; s2 += (double)x[u] * (double)x[u]; ++c;
+                e1 += (double)ex[u];
+            }
         }
     }
     if (c) {
