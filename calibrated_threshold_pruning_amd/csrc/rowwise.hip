@@ -381,8 +381,16 @@ __global__ void prefix_chunk_sum_kernel(const T* v, int L, float* mu) {
     const int nch = prefix_chunks(L);
     const T* base = v + (size_t)g * L * D;
     double acc = 0.0;
-    for (int p = c * kPrefixChunk; p < prefix_chunk_end(c, nch, L); ++p)
-        acc += (double)Elem<T>::load(base + (size_t)p * D + t);
+    constexpr int UN = 8;                            // eight rows' loads per trip
+    const int p1 = prefix_chunk_end(c, nch, L);
+    for (int p0 = c * kPrefixChunk; p0 < p1; p0 += UN) {
+        float x[UN];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) x[u] = Elem<T>::load(base + (size_t)min(p0 + u, p1 - 1) * D + t);
+#pragma unroll
+        for (int u = 0; u < UN; ++u)
+            if (p0 + u < p1) acc += (double)x[u];
+    }
     prefix_slot(mu, g, c + 1, L, D)[t] = acc;
 }
 
@@ -392,10 +400,19 @@ __global__ void prefix_chunk_scan_kernel(int L, int D, int groups, float* mu) {
     const int g = i / D, t = i % D;
     const int nch = prefix_chunks(L);
     double run = 0.0;
-    for (int c = 1; c < nch; ++c) {
-        double* slot = prefix_slot(mu, g, c, L, D);
-        run += slot[t];
-        slot[t] = run;
+    // eight chunk sums per trip, their loads issued before any store
+    constexpr int UN = 8;
+    for (int c0 = 1; c0 < nch; c0 += UN) {
+        double x[UN];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) x[u] = prefix_slot(mu, g, min(c0 + u, nch - 1), L, D)[t];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            if (c0 + u < nch) {
+                run += x[u];
+                prefix_slot(mu, g, c0 + u, L, D)[t] = run;
+            }
+        }
     }
 }
 
@@ -411,9 +428,20 @@ __global__ void prefix_mean_write_kernel(const T* v, int L, float* mu) {
     double acc = s_pre[t];
     const T* base = v + (size_t)g * L * D;
     float* o = mu + (size_t)g * L * D;
-    for (int p = c * kPrefixChunk; p < prefix_chunk_end(c, nch, L); ++p) {
-        acc += (double)Elem<T>::load(base + (size_t)p * D + t);
-        o[(size_t)p * D + t] = (float)(acc / (double)(p + 1));
+    // eight rows per trip, their loads issued together
+    constexpr int UN = 8;
+    const int p1 = prefix_chunk_end(c, nch, L);
+    for (int p0 = c * kPrefixChunk; p0 < p1; p0 += UN) {
+        float x[UN];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) x[u] = Elem<T>::load(base + (size_t)min(p0 + u, p1 - 1) * D + t);
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            if (p0 + u < p1) {
+                acc += (double)x[u];
+                o[(size_t)(p0 + u) * D + t] = (float)(acc / (double)(p0 + u + 1));
+            }
+        }
     }
 }
 
