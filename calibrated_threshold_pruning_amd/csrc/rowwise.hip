@@ -337,11 +337,20 @@ __global__ __launch_bounds__(kVmeanThreads) void vmean_kernel(const T* v, const 
     double acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
-    for (int j = r0; j < n; j += RS) {
-        const u32x4 raw = *(const u32x4*)(base + (size_t)j * D + c * EPC);
-        const T* x = reinterpret_cast<const T*>(&raw);
+    // four rows' loads per trip (rows past n re-read row n - 1 and are not added)
+    constexpr int UN = 4;
+    for (int j0 = r0; j0 < n; j0 += UN * RS) {
+        u32x4 raw[UN];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] += (double)Elem<T>::load(x + e);
+        for (int u = 0; u < UN; ++u) raw[u] = *(const u32x4*)(base + (size_t)min(j0 + u * RS, n - 1) * D + c * EPC);
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            if (j0 + u * RS < n) {
+                const T* x = reinterpret_cast<const T*>(&raw[u]);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc[e] += (double)Elem<T>::load(x + e);
+            }
+        }
     }
 #pragma unroll
     for (int e = 0; e < EPC; ++e) part[r0][c * EPC + e] = acc[e];
