@@ -448,6 +448,36 @@ def test_prefill_bf16_pv_forms(case):
         compare_prefill(g, q, k, v, theta, flags, torch.bfloat16)
 
 
+@pytest.mark.parametrize("Hq,Hkv,L,d", [(8, 2, 300, 128), (4, 1, 200, 64), (16, 2, 333, 128), (2, 2, 65, 128)])
+def test_prefill_benchmark_form_all_rows(Hq, Hkv, L, d):
+    """The kernel form the benchmark times: float16 P V (workspace given), no
+    byte mask, no beta, exact SDC without VMC.  Every row: the kept count equals
+    the oracle's outside the 1e-5 band around theta (and differs by at most the
+    band's element count inside it); outputs within the bf16 tolerance."""
+    print(f"prefill benchmark form Hq={Hq} Hkv={Hkv} L={L} d={d}", flush=True)
+    dev = device()
+    qc, kc, _ = batch_of_sequences(UNIT, ROLE_CALIB, 11, 0, 2, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    theta = oracle_calibrate(qc, kc, [16], L)[0][0]
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 11, L, B=2, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    scale = 1.0 / np.sqrt(d)
+    out = torch.empty(2, Hq, L, d, dtype=torch.bfloat16, device=dev)
+    kc_ = torch.empty(2, Hq, L, dtype=torch.int32, device=dev)
+    ws = tt.workspace(tt.TOPTH_OP_PREFILL, 2, Hq, Hkv, L, L, d)
+    tt.topth_prefill(q.to(dev), k.to(dev), v.to(dev), torch.tensor(theta, dtype=torch.float32, device=dev), out,
+                     scale=scale, flags=0, kept_count=kc_, ws=ws)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(to_f64(q), to_f64(k), to_f64(v), theta, scale, vmc=False, keep_rows=True)
+    go, gk = out.float().cpu().numpy(), kc_.cpu().numpy()
+    for b in range(2):
+        for h in range(Hq):
+            for p in range(L):
+                th = theta_of(theta, h, p)
+                sv = ref.s[b][h][p]
+                amb = int((np.abs(sv - th) <= 1e-5 * abs(th)).sum()) if np.isfinite(th) else 0
+                assert abs(int(gk[b, h, p]) - int(ref.kept_count[b, h, p])) <= amb, (b, h, p)
+                check_out(go[b, h, p], ref.out[b, h, p], torch.bfloat16, f"b{b} h{h} p{p}")
+
+
 def test_prefill_f16_pv_long_keep_all_rows_large_v():
     """The float16 P V form on its worst case: rows of up to 8192 keys that keep
     every element, a peaked softmax (most weights far below the float16 normal
