@@ -213,6 +213,44 @@ def test_prefill_pre_bf16_shapes(Hq, Hkv, L, d):
         compare_prefill_pre(q, k, v, theta, et, sdc, True, g, torch.bfloat16, rows)
 
 
+@pytest.mark.parametrize("Hq,Hkv,L,d", [(8, 2, 300, 128), (4, 1, 200, 64)])
+def test_prefill_pre_benchmark_form_all_rows(Hq, Hkv, L, d):
+    """The kernel form the benchmark times: float16 P V (workspace given), no
+    byte mask, no VMC.  Every row with no element in the ambiguity band is
+    checked element by element against the oracle; the others by their count,
+    which must lie between the strict and the banded count."""
+    print(f"prefill_pre benchmark form Hq={Hq} Hkv={Hkv} L={L} d={d}", flush=True)
+    dev = device()
+    theta, et = calib_tables(UNIT, Hq, Hkv, L, d, 16, 2, torch.bfloat16)
+    q, k, v = attention_inputs(UNIT, ROLE_TEST, 3, 5, B=1, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d,
+                               dtype=torch.bfloat16)
+    qf, kf = to_f64(q), to_f64(k)
+    for sdc in ("expth", "exact"):
+        out = torch.empty(1, Hq, L, d, dtype=q.dtype, device=dev)
+        kc = torch.full((1, Hq, L), -7, dtype=torch.int32, device=dev)
+        bt = torch.full((1, Hq, L), -7.0, dtype=torch.float32, device=dev)
+        ws = tt.workspace(tt.TOPTH_OP_PREFILL, 1, Hq, Hkv, L, L, d)
+        tt.topth_prefill_pre(q.to(dev), k.to(dev), v.to(dev), torch.tensor(theta, dtype=torch.float32, device=dev),
+                             out, scale=1.0 / np.sqrt(d), flags=MODES[sdc], gamma=GAMMA,
+                             e_tilde=torch.tensor(et, dtype=torch.float32, device=dev), kept_count=kc, beta=bt,
+                             ws=ws)
+        torch.cuda.synchronize()
+        g = (out.float().cpu().numpy(), kc.cpu().numpy(), bt.cpu().numpy(), None)
+        ok = []
+        for h in range(Hq):
+            for p in range(L):
+                a = (kf[0, h // (Hq // Hkv), :p + 1] @ qf[0, h, p]) / np.sqrt(d)
+                thv = pre.table_row(theta, h, p)
+                amb = ambiguous(a, thv)
+                if amb.any():
+                    lo = int(((a >= thv) & ~amb).sum())
+                    assert lo <= g[1][0, h, p] <= lo + int(amb.sum()), (h, p)
+                else:
+                    ok.append((0, h, p))
+        assert len(ok) >= 0.9 * Hq * L
+        compare_prefill_pre(q, k, v, theta, et, sdc, False, g, torch.bfloat16, ok)
+
+
 @pytest.mark.parametrize("sdc", list(MODES))
 def test_prefill_pre_f32(sdc):
     print(f"prefill_pre f32 sdc={sdc}", flush=True)
