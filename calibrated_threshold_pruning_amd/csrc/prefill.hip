@@ -8,8 +8,9 @@
 //
 // Post-softmax thresholding needs the exact row log-sum-exp before the first
 // compare, so every query tile sweeps its causal key range twice:
-//   sweep A  S^T = K Q^T on MFMA; lane-local online (max, sum of exp2); the
-//            four lanes of a row combine into the row LSE at the end.
+//   sweep A  S^T = K Q^T on MFMA; a lane-local sum of exp2 against a lazily
+//            raised reference maximum; the four lanes of a row combine into
+//            the row LSE at the end.
 //   sweep B  S^T again; compare x >= log2(theta) + lse2; P = exp2(x - lse2)
 //            for kept elements (0 otherwise) is taken straight from the
 //            accumulator registers as the B operand of O^T += V^T P^T, split
@@ -34,11 +35,11 @@
 // the float16 subnormal grid, off by at most 2^-25, which moves an output by
 // at most 2^-25 since the weights sum to at most 1; the bound of 16 is
 // checked), and the P V product takes one f16 MFMA per block with P rounded
-// to float16 instead of the two bf16 MFMAs of the high/low split.  P enters scaled by
-// 2^7 (folded into the exp2 offset of the row, undone in the epilogue): a
-// weight is at most 2^8 * 2^7 in float16, and only weights below 2^-21 fall
-// into the float16 subnormals, whose absolute rounding error is at most
-// 2^-25 * 2^-7.  Per output: 2^-11 * 16 from the relative rounding of the
+// to float16 instead of the two bf16 MFMAs of the high/low split.  P enters
+// scaled by 2^7 (folded into the exp2 offset of the row, undone in the
+// epilogue): a weight is at most 2^8 * 2^7 in float16, and only weights below
+// 2^-21 fall into the float16 subnormals, whose absolute rounding error is at
+// most 2^-25 * 2^-7.  Per output: 2^-11 * 16 from the relative rounding of the
 // normal weights (they sum to at most 1 after normalisation) plus at most
 // L * 2^-32 * 16 from the subnormal ones, under 8.1e-3 for L <= 2^16.  A V
 // element beyond 16 (or not finite) sets a flag.  Both kernels (F16 and not)
