@@ -597,15 +597,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillKArgs a) {
 // are zero.  The tile goes through LDS (rows padded by one word, so that the
 // eight keys of one output chunk sit in distinct banks); any element beyond
 // 16 in magnitude, or not finite, sets *flag (every writer stores the same
-// value).  Grid: (tiles, B * Hkv), 256 threads.
+// value).  One workgroup per (sequence and KV head, tile), tile fastest;
+// 256 threads.
 template <int D>
 __global__ __launch_bounds__(256) void v_to_f16t_kernel(const uint16_t* v, int L, uint16_t* img, unsigned* flag) {
     constexpr int PW = D / 2 + 1;                        // words per LDS row (bf16 pairs + pad)
     constexpr int CPR = D / 8;                           // 16-byte chunks per V row
     constexpr int NCH = 64 * D / 8;                      // 16-byte chunks per tile
     __shared__ unsigned s_v[64 * PW];
-    const int t = blockIdx.x;
-    const size_t bkv = blockIdx.y;
+    const int nimg = (L + 63) / 64;
+    const int t = (int)(blockIdx.x % (unsigned)nimg);
+    const size_t bkv = blockIdx.x / (unsigned)nimg;
     const uint16_t* vt = v + (bkv * (size_t)L + (size_t)t * 64) * D;
     for (int idx = threadIdx.x; idx < NCH; idx += 256) {
         const int key = idx / CPR, part = idx % CPR;
@@ -615,7 +617,6 @@ __global__ __launch_bounds__(256) void v_to_f16t_kernel(const uint16_t* v, int L
         for (int w = 0; w < 4; ++w) s_v[key * PW + 4 * part + w] = raw[w];
     }
     __syncthreads();
-    const int nimg = (L + 63) / 64;
     uint16_t* it = img + (bkv * (size_t)nimg + t) * (size_t)(64 * D);
     bool bad = false;
     for (int q = threadIdx.x; q < NCH; q += 256) {
@@ -708,7 +709,7 @@ int launch_prefill_bf16(const PrefillParams& p, float* mu_ws, hipStream_t s) {
         vflag = (unsigned*)((char*)p.ws + mu_b + v16_b);
         int e = launch_fill_u32(vflag, 4, 0u, s);
         if (e != hipSuccess) return e;
-        const dim3 grid((unsigned)((p.L + 63) / 64), (unsigned)(p.B * p.Hkv));
+        const dim3 grid((unsigned)((size_t)((p.L + 63) / 64) * p.B * p.Hkv));
         if (p.d == 64) hipLaunchKernelGGL(v_to_f16t_kernel<64>, grid, dim3(256), 0, s, (const uint16_t*)p.v, p.L, v16, vflag);
         else hipLaunchKernelGGL(v_to_f16t_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)p.v, p.L, v16, vflag);
         e = hipGetLastError();

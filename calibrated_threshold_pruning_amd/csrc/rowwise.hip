@@ -373,7 +373,8 @@ __global__ __launch_bounds__(kVmeanThreads) void vmean_kernel(const T* v, const 
 //      (the sum of all rows before the chunk);
 //   3. every chunk adds its rows to its slot's sum row by row and writes the
 //      means.
-// One thread per dimension (D = blockDim.x, at most 128); grid (chunks, groups).
+// One thread per dimension (D = blockDim.x, at most 128); one workgroup per
+// (group, chunk), chunk fastest.
 constexpr int kPrefixChunk = 64;
 
 __device__ __forceinline__ int prefix_chunks(int L) { return L / kPrefixChunk > 1 ? L / kPrefixChunk : 1; }
@@ -386,8 +387,8 @@ __device__ __forceinline__ double* prefix_slot(float* mu, int g, int c, int L, i
 
 template <typename T>
 __global__ void prefix_chunk_sum_kernel(const T* v, int L, float* mu) {
-    const int D = blockDim.x, t = threadIdx.x, c = blockIdx.x, g = blockIdx.y;
     const int nch = prefix_chunks(L);
+    const int D = blockDim.x, t = threadIdx.x, c = blockIdx.x % (nch - 1), g = blockIdx.x / (nch - 1);
     const T* base = v + (size_t)g * L * D;
     double acc = 0.0;
     constexpr int UN = 8;                            // eight rows' loads per trip
@@ -428,8 +429,8 @@ __global__ void prefix_chunk_scan_kernel(int L, int D, int groups, float* mu) {
 template <typename T>
 __global__ void prefix_mean_write_kernel(const T* v, int L, float* mu) {
     __shared__ double s_pre[128];
-    const int D = blockDim.x, t = threadIdx.x, c = blockIdx.x, g = blockIdx.y;
     const int nch = prefix_chunks(L);
+    const int D = blockDim.x, t = threadIdx.x, c = blockIdx.x % nch, g = blockIdx.x / nch;
     // the slot goes through LDS, so that every entry has arrived before any
     // row of the chunk (which the slot overlaps) is written
     s_pre[t] = c == 0 ? 0.0 : prefix_slot(mu, g, c, L, D)[t];
@@ -639,11 +640,11 @@ template <typename T>
 static int launch_prefix_mean_t(const T* v, int groups, int L, int d, float* mu, hipStream_t s) {
     const int nch = L / kPrefixChunk > 1 ? L / kPrefixChunk : 1;
     if (nch > 1) {
-        hipLaunchKernelGGL(prefix_chunk_sum_kernel<T>, dim3(nch - 1, groups), dim3(d), 0, s, v, L, mu);
+        hipLaunchKernelGGL(prefix_chunk_sum_kernel<T>, dim3((unsigned)((nch - 1) * groups)), dim3(d), 0, s, v, L, mu);
         const int n = groups * d;
         hipLaunchKernelGGL(prefix_chunk_scan_kernel, dim3((n + 255) / 256), dim3(256), 0, s, L, d, groups, mu);
     }
-    hipLaunchKernelGGL(prefix_mean_write_kernel<T>, dim3(nch, groups), dim3(d), 0, s, v, L, mu);
+    hipLaunchKernelGGL(prefix_mean_write_kernel<T>, dim3((unsigned)(nch * groups)), dim3(d), 0, s, v, L, mu);
     return hipGetLastError();
 }
 
