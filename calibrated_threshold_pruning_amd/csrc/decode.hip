@@ -591,7 +591,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void decode_bf16_kernel(Decod
         float (*s_wl)[C::GW] = reinterpret_cast<float (*)[C::GW]>(stage);
         float* ovf = a.ovf_w + (size_t)group * a.Lmax * C::GW;
         int lcount = 0;
-        const int vlane = (lane % C::LPR) * C::DPL * 2;
         const int keylane = lane - 16 * cc;      // lane that stands for this lane's key
         unsigned char* kmask = a.kept_mask ? a.kept_mask + ((size_t)b * a.Hq + (size_t)kv * G) * a.Lmax : nullptr;
         // the per-head kept mask, only where it is asked for
