@@ -369,6 +369,8 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
                      "kernel": "decode_bf16_kernel", "avg_kernel_us": round(avg * 1e6, 3)},
         "wall_s": round(wall, 4),
     }
+    log("[bench] library streaming reference over the same K caches")
+    res["stream_reference"] = stream_reference([buf[1] for buf in bufs])
     if name == "decode_8b":
         log("[bench] GQA selection variants on the same caches")
         res["gqa_variants"] = gqa_variants(bufs, vms, lens_d, theta, w, dev, read_bytes, steps=min(steps, 100))
@@ -387,6 +389,28 @@ def bench_decode(name, steps, warmup, with_cpu, eager=False):
             with single_thread():
                 res["cpu_baseline_1core"] = oracle_decode_baseline(bufs[0], lens, theta, vms[0], w, read_bytes,
                                                                    threads=1)
+    return res
+
+
+def stream_reference(ks, steps=30):
+    """Context for the decode line: what plain library kernels reach on the same
+    K caches (rotated like the decode steps, so the MALL does not hold them):
+    a reduction that reads each cache once, and a copy that reads and writes it."""
+    nb = ks[0].numel() * ks[0].element_size()
+    ops = (("read_GBps", lambda t: torch.sum(t, dtype=torch.float32), 1),
+           ("copy_GBps_read_plus_write", lambda t: t.clone(), 2))
+    res = {"ops": "torch.sum(K, dtype=float32); K.clone()", "bytes_per_cache": int(nb)}
+    for key, fn, factor in ops:
+        for t in ks:
+            fn(t)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            fn(ks[i % len(ks)])
+        b.record()
+        torch.cuda.synchronize()
+        res[key] = round(factor * nb * steps / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
     return res
 
 
