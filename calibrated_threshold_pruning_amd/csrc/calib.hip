@@ -572,6 +572,22 @@ __device__ __forceinline__ void lds_add(uint32_t addr, uint32_t v) {
 __device__ __forceinline__ void lds_store(uint32_t addr, float v) {
     asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
+// c + hit and c - hit in one VALU instruction each: the lane mask of the hits
+// (compares straight into a scalar register pair) is the carry (borrow)
+// input of an integer add (subtract) of zero
+__device__ __forceinline__ uint64_t eq_mask(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 32); }
+__device__ __forceinline__ int add_hit(int c, uint64_t m) {
+    int r;
+    uint64_t co;
+    asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(r), "=s"(co) : "v"(c), "s"(m));
+    return r;
+}
+__device__ __forceinline__ int sub_hit(int c, uint64_t m) {
+    int r;
+    uint64_t co;
+    asm("v_subb_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(r), "=s"(co) : "v"(c), "s"(m));
+    return r;
+}
 
 // The member of rank rr of the target bin (fma bits tbits) of a row, counted
 // from the top (flip = 0) or from the bottom (flip = ~0), from the candidate
@@ -966,7 +982,9 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
     // the stores of non-members (a later member overwrites it).  Masked keys
     // have the bits of +inf and match no target.
     const uint32_t reg_off = hw_off + (uint32_t)(kCtRegion * lane) * 4u;
-    int cc[2] = {0, 0};
+    // members so far: row qb = 0 counts up from 0, row qb = 1 down from the
+    // last slot (both unclamped; the store slot is clamped to the region)
+    int c_up = 0, c_dn = kCtSlots - 1;
     // NT compares per element: one sweep per target count (uniform branch)
     auto collect_sweep = [&](auto nt_tag) {
         constexpr int NT = decltype(nt_tag)::value;
@@ -980,12 +998,16 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
                         const float x = st[qb][kb][r];
                         const uint32_t bits = __float_as_uint(fmaf(x, nbs[qb], cb[qb]));
                         // bitwise, not short-circuit: no branch per element
-                        int hit = (int)(bits == tb[qb][0]);
+                        uint64_t hit = eq_mask(bits, tb[qb][0]);
 #pragma unroll
-                        for (int t = 1; t < NT; ++t) hit |= (int)(bits == tb[qb][t]);
-                        const int slot = qb == 0 ? min(cc[0], kCtSlots - 1) : kCtSlots - 1 - min(cc[1], kCtSlots - 1);
-                        lds_store(reg_off + (uint32_t)slot * 4u, x);
-                        cc[qb] += hit;
+                        for (int t = 1; t < NT; ++t) hit |= eq_mask(bits, tb[qb][t]);
+                        if (qb == 0) {
+                            lds_store(reg_off + (uint32_t)min(c_up, kCtSlots - 1) * 4u, x);
+                            c_up = add_hit(c_up, hit);
+                        } else {
+                            lds_store(reg_off + (uint32_t)max(c_dn, 0) * 4u, x);
+                            c_dn = sub_hit(c_dn, hit);
+                        }
                     }
             }
         };
@@ -998,6 +1020,7 @@ __global__ __launch_bounds__(kCtWaves * 64, 2) void calib_tiled_kernel(CalibTArg
         default: collect_sweep(std::integral_constant<int, kCtMaxK>{}); break;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the written-out stores are done
+    const int cc[2] = {c_up, kCtSlots - 1 - c_dn};
     s_ccnt[wave][lane][0] = cc[0];
     s_ccnt[wave][lane][1] = cc[1];
     {
