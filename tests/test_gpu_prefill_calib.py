@@ -251,6 +251,20 @@ def test_calibrate_tiled_group_sizes(Hq, Hkv, L, d):
     check_theta(th_gpu, th_ref)
 
 
+@pytest.mark.parametrize("ks", [[7], [12, 90], [5, 40, 90], [3, 40, 90, 250]], ids=["1k", "2k", "3k", "4k"])
+def test_calibrate_tiled_target_counts(ks):
+    """Whole causal prefills through the tiled calibration with one to four
+    targets: the member sweep is compiled once per target count, and each
+    form has to find every row's k-th largest exactly."""
+    Hq, Hkv, L, d = 8, 2, 700, 128
+    print(f"calibrate tiled ks={ks}", flush=True)
+    q, k, _ = batch_of_sequences(UNIT, ROLE_CALIB, 15, 0, 2, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, d=d)
+    th_gpu, cnt_gpu = gpu_calibrate(q, k, ks, L)
+    th_ref, cnt_ref = oracle_calibrate(q, k, ks, L)
+    assert np.array_equal(cnt_gpu, cnt_ref)
+    check_theta(th_gpu, th_ref)
+
+
 def test_calibrate_bf16_ties():
     """Keys drawn from three distinct rows: every score row holds long runs of
     equal values, so the bin of the k-th largest overflows the copy space and
